@@ -1,0 +1,148 @@
+"""Plain fp64 CPU oracle for causal Forgetting-Transformer (FoX) attention.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this module. The product path (the HIP
+library and its Python binding) never calls it, and this module imports
+nothing from the product.
+
+What is computed (the plain definition, written out; no tiling, no online
+softmax, no split-K):
+
+* Gate scan -- ``c_i = sum_{t<=i} log f_t`` along the sequence, per (batch,
+  head).  Source: "Forgetting Transformer (FoX) Attention" module page
+  (frankenstein-transformer docs), ``ForgettingAttention.forward``: the
+  cumulative sum of the log forget gates over the sequence axis.
+* Scores -- for key j <= query i,
+  ``s_ij = scale * q_i . k_j + (c_i - c_j)``, i.e. the bias is the sum of
+  ``log f_t`` for t = j+1 .. i and is *not* multiplied by ``scale``.
+  Sources: the same ``forward`` (bias ``cum[i] - cum[j]`` added after the
+  scaled product, scale = head_dim ** -0.5) and the "foxwindow" README,
+  opening paragraph (score = q_i . k_j + sum over t = j+1..i of log g_t).
+  Keys j > i get weight exactly 0: decoder-mode causal mask, which masks the
+  strict upper triangle and keeps the diagonal.
+* Softmax over keys and the weighted sum of values -- same ``forward``.
+  ``lse_i`` is the natural-log log-sum-exp of the full logits row (scale and
+  bias included); the pages do not define it, this is the plainest reading.
+* Decode -- the single query row i = L-1 of a sequence whose key/value cache
+  holds slots 0..L-1 (the new token's k, v already at slot L-1) and whose
+  cached prefix sums hold slots 0..L-2; the new prefix sum is
+  ``c_{L-1} = c_{L-2} + log f_new`` (``c_0 = log f_new`` when L = 1).
+  The pages define no decode; this reading follows the attention definition
+  above applied to the last row.
+
+Every function takes and returns float64 numpy arrays; callers pass the exact
+values the GPU sees (bf16 inputs widened exactly, fp32 gates widened, the
+fp32 ``scale`` widened).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "logf_cumsum",
+    "fwd_head_rows",
+    "attn_fwd",
+    "attn_fwd_rows",
+    "attn_decode",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def logf_cumsum(logf) -> np.ndarray:
+    """Inclusive prefix sum of the log forget gates along the last axis.
+
+    FoX module page, ``ForgettingAttention.forward``: cumulative sum of
+    ``log f`` over the sequence dimension.  ``c_i = sum_{t=0}^{i} logf_t``.
+    """
+    return np.cumsum(_f64(logf), axis=-1)
+
+
+def fwd_head_rows(q, k, v, logf, scale, rows, chunk: int = 256):
+    """Definition of causal FoX attention for one head, for selected rows.
+
+    q, k, v: [N, d]; logf: [N]; rows: 1-D integer array of query indices.
+    Returns (O[rows] [len(rows), d], lse[rows] [len(rows)]).
+
+    FoX module page, ``ForgettingAttention.forward`` (decoder mode):
+    logits = scale * q k^T + (c_i - c_j), strict upper triangle set to -inf,
+    softmax over keys, times v.  ``lse`` is log sum_j exp(logit_ij).
+    Each row is computed from the definition independently; ``chunk`` only
+    bounds how many rows are held in memory at once.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    c = logf_cumsum(logf)
+    rows = np.asarray(rows, dtype=np.int64)
+    n = q.shape[0]
+    keys = np.arange(n)
+    out = np.empty((rows.size, v.shape[1]), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    for lo in range(0, rows.size, chunk):
+        r = rows[lo:lo + chunk]
+        kmax = int(r.max()) + 1 if r.size else 0
+        # logits over keys 0..kmax-1 (keys beyond every selected row are masked anyway)
+        s = scale * (q[r] @ k[:kmax].T) + (c[r][:, None] - c[None, :kmax])
+        s = np.where(keys[None, :kmax] > r[:, None], -np.inf, s)
+        m = s.max(axis=1)
+        z = np.exp(s - m[:, None]).sum(axis=1)
+        row_lse = m + np.log(z)
+        p = np.exp(s - row_lse[:, None])
+        out[lo:lo + chunk] = p @ v[:kmax]
+        lse[lo:lo + chunk] = row_lse
+    return out, lse
+
+
+def attn_fwd_rows(q, k, v, logf, scale, rows):
+    """Rows ``rows`` of every (batch, head): q,k,v [B,H,N,d], logf [B,H,N].
+
+    Returns (O [B,H,len(rows),d], lse [B,H,len(rows)]).
+    """
+    q = _f64(q)
+    bsz, nh, _, d = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((bsz, nh, rows.size, d), dtype=np.float64)
+    lse = np.empty((bsz, nh, rows.size), dtype=np.float64)
+    for b in range(bsz):
+        for h in range(nh):
+            out[b, h], lse[b, h] = fwd_head_rows(q[b, h], k[b, h], v[b, h], logf[b, h], scale, rows)
+    return out, lse
+
+
+def attn_fwd(q, k, v, logf, scale):
+    """Full causal FoX attention: q,k,v [B,H,N,d], logf [B,H,N].
+
+    Returns (O [B,H,N,d], lse [B,H,N], c [B,H,N]) in float64.
+    """
+    n = np.asarray(q).shape[2]
+    out, lse = attn_fwd_rows(q, k, v, logf, scale, np.arange(n))
+    return out, lse, logf_cumsum(logf)
+
+
+def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale):
+    """One decode step of causal FoX attention against a cache.
+
+    q: [S,H,d]; k_cache, v_cache: [S,H,L,d] with the new token at slot L-1;
+    c_cache: [S,H,L] whose slots 0..L-2 hold the cached prefix sums (slot L-1
+    is ignored); logf_new: [S,H].
+    Returns (O [S,H,d], lse [S,H], c_new [S,H]) where
+    ``c_new = c_cache[..., L-2] + logf_new`` (``logf_new`` when L = 1).
+
+    This is the last row i = L-1 of the forward definition: logits
+    ``scale * q . k_j + (c_new - c_j)`` for j = 0..L-1 with ``c_{L-1} = c_new``.
+    """
+    q, kc, vc, cc = _f64(q), _f64(k_cache), _f64(v_cache), _f64(c_cache)
+    ln = _f64(logf_new)
+    L = kc.shape[2]
+    c_prev = cc[..., L - 2] if L >= 2 else np.zeros_like(ln)
+    c_new = c_prev + ln
+    c_all = np.concatenate([cc[..., : L - 1], c_new[..., None]], axis=-1)  # [S,H,L]
+    s = scale * np.einsum("shd,shld->shl", q, kc) + (c_new[..., None] - c_all)
+    m = s.max(axis=-1)
+    z = np.exp(s - m[..., None]).sum(axis=-1)
+    lse = m + np.log(z)
+    p = np.exp(s - lse[..., None])
+    out = np.einsum("shl,shld->shd", p, vc)
+    return out, lse, c_new
