@@ -1,0 +1,260 @@
+"""Benchmark of the causal FoX attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline] [--only]
+
+A step is one call of the library entry point on one batch of synthetic,
+seeded, device-resident input:
+  * fox_attn_fwd (gate scan fused in; one kernel) for the forward workloads,
+  * fox_attn_decode (split + combine kernels) for the decode workload.
+The headline workload is the bf16 forward B=4 H=12 N=1024 d=64; the JSON line
+also carries the long forward workloads and the decode workload (the metric
+quotes prefill TFLOP/s and decode GB/s) unless --only is given.
+
+Timing: W untimed warm-up steps, then K steps between two HIP events on the
+stream the library launches on (torch's current stream), bracketed by
+synchronisation.  Per-launch event pairs over the same number of calls give the
+dominant kernel's average launch duration for the roofline object.
+
+Algorithmic work (what the method must do, not what the kernel happens to do):
+  forward: 4*d flop per causal pair, n(n+1)/2 pairs per (batch, head);
+  decode : bytes = K and V caches + cached prefix sums (L-1 slots) + q + log f_new
+           read, O + lse + c_{L-1} written.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 matrix / vector
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "causal FoX attn fwd TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)"
+
+
+def fwd_flops(cfg) -> float:
+    return 4.0 * cfg.d * cfg.N * (cfg.N + 1) / 2 * cfg.B * cfg.H
+
+
+def decode_bytes(cfg) -> dict:
+    sh = cfg.S * cfg.H
+    eb = 2 if cfg.dtype == "bf16" else 4
+    kv = 2 * sh * cfg.L * cfg.d * eb
+    rd = kv + sh * (cfg.L - 1) * 4 + sh * cfg.d * eb + sh * 4
+    wr = sh * cfg.d * eb + sh * 4 + sh * 4
+    return {"total": rd + wr, "read": rd, "kv": kv, "write": wr}
+
+
+def _events_time(torch, fn, k):
+    """Whole-region time (ms) of k back-to-back calls, and the mean of k per-call event pairs (ms)."""
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(k):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    region = e0.elapsed_time(e1)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    for a, b in pairs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    return region, sum(per) / len(per), per[len(per) // 2]
+
+
+def bench_fwd(torch, fox, fi, tag, steps, warmup):
+    cfg = fi.FWD[tag]
+    inp = fi.fwd_inputs(cfg)
+    dev = "cuda"
+    q, k, v, logf = (inp[n].to(dev) for n in ("q", "k", "v", "logf"))
+    o = torch.empty_like(q)
+    lse = torch.empty_like(logf)
+    c = torch.empty_like(logf)
+    fn = lambda: fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
+    for _ in range(warmup):
+        fn()
+    region, mean_launch, med_launch = _events_time(torch, fn, steps)
+    flops = fwd_flops(cfg)
+    ms = region / steps
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops / (mean_launch * 1e-3) / 1e12
+    return {
+        "cfg": cfg, "inp": inp,
+        "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+        "kernel": f"fwd_{cfg.dtype}_kernel<{cfg.d}>", "launch_ms_mean": mean_launch, "launch_ms_median": med_launch,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+        "flop_per_launch": flops,
+    }
+
+
+def bench_decode(torch, fox, fi, tag, steps, warmup):
+    cfg = fi.DECODE[tag]
+    t0 = time.time()
+    inp = fi.decode_inputs(cfg)
+    gen_s = time.time() - t0
+    dev = "cuda"
+    L = cfg.L
+    q = inp["q"].to(dev)
+    kc = inp["k"].to(dev)
+    vc = inp["v"].to(dev)
+    cc = fox.logf_cumsum(inp["logf_all"].to(dev))  # the cache's prefix sums, built by the library's scan
+    lnew = inp["logf_all"][..., L - 1].contiguous().to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.S, cfg.H, device=dev)
+    ws = torch.empty(fox.decode_workspace_bytes(cfg.S, cfg.H, L, cfg.d), device=dev, dtype=torch.uint8)
+    fn = lambda: fox.attn_decode(q, kc, vc, cc, lnew, scale=inp["scale"], out=o, lse=lse, workspace=ws)  # noqa
+    for _ in range(warmup):
+        fn()
+    region, mean_launch, med_launch = _events_time(torch, fn, steps)
+    by = decode_bytes(cfg)
+    ms = region / steps
+    achieved = by["total"] / (mean_launch * 1e-3) / 1e9
+    res = {
+        "workload": cfg.desc, "ms_per_step": round(ms, 4), "value": round(by["total"] / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "bytes_per_step": by["total"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "note": "per call = split kernel + combine kernel; bytes = algorithmic bytes per call"},
+        "input_gen_s": round(gen_s, 1),
+    }
+    del kc, vc
+    return res, inp
+
+
+def _blas_threads() -> int:
+    """Threads the oracle's NumPy BLAS actually uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_fwd(fi, inp, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a sample of whole heads of the same workload."""
+    import numpy as np
+
+    import oracle
+    cores = _blas_threads()
+    cfg = inp["cfg"]
+    q, k, v, lf = (inp[n].double().numpy() for n in ("q", "k", "v", "logf"))
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    done, t0 = 0, time.perf_counter()
+    rows = np.arange(cfg.N)
+    # whole (batch, head) slices, cycling over the workload until the budget is spent
+    while time.perf_counter() - t0 < budget_s:
+        b, h = heads[done % len(heads)]
+        oracle.fwd_head_rows(q[b, h], k[b, h], v[b, h], lf[b, h], inp["scale"], rows)
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = 4.0 * cfg.d * cfg.N * (cfg.N + 1) / 2 * done
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} (batch, head) slices of the same workload ({len(heads)} per batch, cycled), all "
+                      f"{cfg.N} rows each, fp64 NumPy, {dt:.1f} s wall"}
+
+
+def cpu_baseline_decode(inp, cfg, budget_s=8.0):
+    import numpy as np
+
+    import oracle
+    L = cfg.L
+    t0 = time.perf_counter()
+    done = 0
+    for s in range(inp["q"].shape[0]):
+        lf = inp["logf_all"][s:s + 1].double().numpy()
+        cc = oracle.logf_cumsum(lf).astype(np.float32).astype(np.float64)  # an fp32 cache, like the GPU's
+        oracle.attn_decode(inp["q"][s:s + 1].double().numpy(), inp["k"][s:s + 1].double().numpy(),
+                           inp["v"][s:s + 1].double().numpy(), cc, lf[..., L - 1], inp["scale"])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    by = decode_bytes(cfg)["total"] * done / cfg.S
+    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {cfg.S} sequences (all heads), fp64 NumPy, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="measure the selected workload only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import forget_gated_causal_amd as fox
+    import fox_inputs as fi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    print(f"# device: {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded, see fox_inputs.py)"}
+    if args.workload == "c5":
+        dec, dinp = bench_decode(torch, fox, fi, "c5", args.steps, args.warmup)
+        line.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": dec["ms_per_step"], "dtype": "bf16",
+                     "config": {"workload": dec["workload"], "global_batch": 64, "seq_len": 8192,
+                                "parallelism": "single GPU"},
+                     "roofline": dec["roofline"]})
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_decode(dinp, fi.DECODE["c5"])
+        print(json.dumps(line), flush=True)
+        return
+
+    r = bench_fwd(torch, fox, fi, args.workload, args.steps, args.warmup)
+    cfg = r["cfg"]
+    print(f"# {cfg.desc}: {r['ms_per_step']*1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s, "
+          f"kernel mean {r['launch_ms_mean']*1e3:.1f} us", file=sys.stderr, flush=True)
+    line.update({
+        "value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 5),
+        "dtype": cfg.dtype,
+        "config": {"workload": cfg.desc, "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H,
+                   "head_dim": cfg.d, "parallelism": "single GPU"},
+        "roofline": dict(r["roofline"], kernel=r["kernel"], launch_us_mean=round(r["launch_ms_mean"] * 1e3, 2),
+                         flop_per_launch=r["flop_per_launch"]),
+    })
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_fwd(fi, r["inp"])
+    del r
+    if not args.only:
+        others = {}
+        for tag in ("c3", "c4"):
+            x = bench_fwd(torch, fox, fi, tag, max(10, args.steps // 5), max(3, args.warmup // 2))
+            print(f"# {x['cfg'].desc}: {x['ms_per_step']*1e3:.1f} us/step, {x['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            others[tag] = {"workload": x["cfg"].desc, "value": round(x["tflops"], 2), "unit": "TFLOP/s",
+                           "ms_per_step": round(x["ms_per_step"], 4), "roofline": x["roofline"]}
+            del x
+            torch.cuda.empty_cache()
+        dec, _ = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))
+        print(f"# {dec['workload']}: {dec['ms_per_step']*1e3:.1f} us/step, {dec['value']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        others["c5_decode"] = dec
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,117 @@
+"""Causal Forgetting-Transformer (FoX) attention on MI355X: Python binding of libfox.
+
+Every function here only marshals torch tensors (device memory) and the current
+HIP stream into the C ABI of include/fox.h; all arithmetic runs in the HIP
+kernels of libfox.so.  Outputs are allocated with torch when not supplied.
+
+    c            = logf_cumsum(logf)                          # [..., N] fp32
+    o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
+    o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import FOX_BF16, FOX_F32, FoxError, check, lib, status_string  # noqa: F401
+
+__all__ = ["logf_cumsum", "attn_fwd", "attn_decode", "decode_workspace_bytes", "FoxError", "status_string"]
+
+_DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _default_scale(d: int) -> float:
+    return float(torch.tensor(d ** -0.5, dtype=torch.float32))
+
+
+def logf_cumsum(logf: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Inclusive prefix sum of log forget gates along the last axis (fp32 in/out)."""
+    _need(logf, "logf", torch.float32)
+    n = logf.shape[-1]
+    rows = logf.numel() // max(n, 1)
+    c = torch.empty_like(logf) if out is None else out
+    _need(c, "out", torch.float32)
+    check("fox_logf_cumsum", lib().fox_logf_cumsum(_ptr(logf), _ptr(c), rows, n, _stream()))
+    return c
+
+
+def attn_fwd(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=None,
+             want_lse: bool = True, want_c: bool = True):
+    """Causal FoX attention forward. q, k, v: [B,H,N,d] (fp32 or bf16); logf: [B,H,N] fp32.
+
+    Returns (o, lse, c); lse / c are None when not wanted.
+    """
+    B, H, N, d = q.shape
+    dt = _DTYPES.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, H, N, d)}")
+    _need(logf, "logf", torch.float32)
+    if tuple(logf.shape) != (B, H, N):
+        raise ValueError(f"logf shape {tuple(logf.shape)} != {(B, H, N)}")
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    if want_c and c is None:
+        c = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = lib().fox_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse if want_lse else None),
+                            _ptr(c if want_c else None), B, H, N, d, scale, dt, _stream())
+    check("fox_attn_fwd", st)
+    return o, (lse if want_lse else None), (c if want_c else None)
+
+
+def decode_workspace_bytes(s: int, h: int, l: int, d: int) -> int:
+    return int(lib().fox_attn_decode_workspace_bytes(s, h, l, d))
+
+
+def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = None, out=None, lse=None,
+                workspace=None, want_lse: bool = True):
+    """One decode step. q: [S,H,d]; caches [S,H,L,d] with the new token at slot L-1;
+    c_cache [S,H,L] fp32 (slot L-1 is written); logf_new [S,H] fp32.  Returns (o, lse)."""
+    S, H, d = q.shape
+    L = k_cache.shape[2]
+    dt = _DTYPES.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _need(q, "q", q.dtype)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype)
+        if tuple(t.shape) != (S, H, L, d):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(S, H, L, d)}")
+    _need(c_cache, "c_cache", torch.float32)
+    _need(logf_new, "logf_new", torch.float32)
+    if tuple(c_cache.shape) != (S, H, L) or tuple(logf_new.shape) != (S, H):
+        raise ValueError("c_cache must be [S,H,L] and logf_new [S,H]")
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty(S, H, device=q.device, dtype=torch.float32)
+    nbytes = decode_workspace_bytes(S, H, L, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8)
+    st = lib().fox_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(c_cache), _ptr(logf_new), _ptr(o),
+                               _ptr(lse if want_lse else None), _ptr(workspace), workspace.numel() *
+                               workspace.element_size(), S, H, L, d, float(_default_scale(d) if scale is None
+                                                                             else scale), dt, _stream())
+    check("fox_attn_decode", st)
+    return o, (lse if want_lse else None)

@@ -1,0 +1,116 @@
+// fox_api.hip -- the C ABI of libfox (declared in include/fox.h): argument
+// validation on the host, then kernel launches on the caller's stream.
+// Nothing is launched when validation fails; no allocation, no synchronisation.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fox.h"
+#include "fox_internal.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) overlap
+bool overlap(const void* p, size_t bytes, const void* q, size_t qbytes) {
+  if (!p || !q) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + qbytes && b < a + bytes;
+}
+
+bool head_dim_ok(int64_t d) { return d == 32 || d == 64 || d == 128; }
+bool dtype_ok(fox_dtype_t t) { return t == FOX_F32 || t == FOX_BF16; }
+size_t elem_bytes(fox_dtype_t t) { return t == FOX_BF16 ? 2 : 4; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
+
+fox_status_t from_hip(hipError_t e) { return e == hipSuccess ? FOX_OK : FOX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fox_status_string(fox_status_t status) {
+  switch (status) {
+    case FOX_OK: return "ok";
+    case FOX_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size, bad scale, misaligned or aliased buffer)";
+    case FOX_ERR_UNSUPPORTED: return "unsupported head dim (need 32, 64 or 128) or dtype";
+    case FOX_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+    case FOX_ERR_HIP: return "HIP runtime error at kernel launch";
+  }
+  return "unknown status";
+}
+
+fox_status_t fox_logf_cumsum(const float* logf, float* c, int64_t rows, int64_t n, hipStream_t stream) {
+  if (!logf || !c) return FOX_ERR_INVALID_ARG;
+  if (rows <= 0 || n <= 0 || n > FOX_MAX_SEQ || rows > kI32Max) return FOX_ERR_INVALID_ARG;
+  if (!aligned(logf, 4) || !aligned(c, 4)) return FOX_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)rows * (size_t)n * sizeof(float);
+  if (overlap(logf, bytes, c, bytes)) return FOX_ERR_INVALID_ARG;
+  return from_hip(fox::launch_logf_cumsum(logf, c, rows, (int)n, stream));
+}
+
+fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                          float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
+                          hipStream_t stream) {
+  if (!q || !k || !v || !logf || !o) return FOX_ERR_INVALID_ARG;
+  if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
+  if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || !head_dim_ok(d)) return FOX_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
+  if ((n + 127) / 128 > kMaxGridY) return FOX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(logf, 4) || !aligned(lse, 4) || !aligned(c, 4)) return FOX_ERR_INVALID_ARG;
+  const int64_t bh = b * h;
+  const size_t tbytes = (size_t)bh * (size_t)n * (size_t)d * elem_bytes(dtype);
+  const size_t vbytes = (size_t)bh * (size_t)n * sizeof(float);
+  if (overlap(o, tbytes, q, tbytes) || overlap(o, tbytes, k, tbytes) || overlap(o, tbytes, v, tbytes) ||
+      overlap(o, tbytes, logf, vbytes) || overlap(lse, vbytes, logf, vbytes) || overlap(c, vbytes, logf, vbytes) ||
+      overlap(lse, vbytes, c, vbytes) || overlap(lse, vbytes, o, tbytes) || overlap(c, vbytes, o, tbytes) ||
+      overlap(lse, vbytes, q, tbytes) || overlap(lse, vbytes, k, tbytes) || overlap(lse, vbytes, v, tbytes) ||
+      overlap(c, vbytes, q, tbytes) || overlap(c, vbytes, k, tbytes) || overlap(c, vbytes, v, tbytes))
+    return FOX_ERR_INVALID_ARG;
+  return from_hip(
+      fox::launch_attn_fwd(q, k, v, logf, o, lse, c, bh, (int)n, (int)d, scale, dtype == FOX_BF16, stream));
+}
+
+size_t fox_attn_decode_workspace_bytes(int64_t s, int64_t h, int64_t l, int64_t d) {
+  if (s <= 0 || h <= 0 || l <= 0 || l > FOX_MAX_SEQ || !head_dim_ok(d) || s > kI32Max / h) return 0;
+  return fox::decode_workspace_bytes(s * h, (int)l, (int)d);
+}
+
+fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                             const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                             int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
+                             hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !c_cache || !logf_new || !o) return FOX_ERR_INVALID_ARG;
+  if (s <= 0 || h <= 0 || l <= 0 || d <= 0 || l > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
+  if (s > kI32Max / h) return FOX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || !head_dim_ok(d)) return FOX_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+    return FOX_ERR_INVALID_ARG;
+  if (!aligned(c_cache, 4) || !aligned(logf_new, 4) || !aligned(lse, 4)) return FOX_ERR_INVALID_ARG;
+  const int64_t sh = s * h;
+  const int nsplit = fox::decode_num_splits(sh, (int)l, (int)d);
+  if (sh > kI32Max / nsplit) return FOX_ERR_INVALID_ARG;
+  const size_t need = fox::decode_workspace_bytes(sh, (int)l, (int)d);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(dtype);
+  const size_t obytes = (size_t)sh * (size_t)d * eb, cbytes = (size_t)sh * (size_t)l * sizeof(float);
+  const size_t kvbytes = (size_t)sh * (size_t)l * (size_t)d * eb, sbytes = (size_t)sh * sizeof(float);
+  if (overlap(o, obytes, q, obytes) || overlap(o, obytes, k_cache, kvbytes) || overlap(o, obytes, v_cache, kvbytes) ||
+      overlap(o, obytes, c_cache, cbytes) || overlap(lse, sbytes, c_cache, cbytes) ||
+      overlap(lse, sbytes, o, obytes) || overlap(workspace, need, o, obytes) ||
+      overlap(workspace, need, c_cache, cbytes) || overlap(workspace, need, k_cache, kvbytes) ||
+      overlap(workspace, need, v_cache, kvbytes) || overlap(c_cache, cbytes, k_cache, kvbytes) ||
+      overlap(c_cache, cbytes, v_cache, kvbytes) || overlap(c_cache, cbytes, logf_new, sbytes))
+    return FOX_ERR_INVALID_ARG;
+  return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, o, lse,
+                                          static_cast<float*>(workspace), sh, (int)l, (int)d, scale,
+                                          dtype == FOX_BF16, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,519 @@
+// fox_fwd.hip -- K2: fused causal FoX attention forward on gfx950 MFMA.
+//
+// Definition (FoX module page, ForgettingAttention.forward, decoder mode;
+// foxwindow README, opening paragraph):
+//   s_ij = scale * q_i.k_j + sum_{t=j+1..i} log f_t  (j <= i),  softmax over j,  O_i = sum_j p_ij v_j.
+//
+// Work decomposition
+//   * One 256-thread workgroup (4 waves) per (query block of 128 rows, batch*head).
+//     Wave w owns 32 query rows.  Grid x = batch*head (fastest, so the workgroups of one
+//     head land on one XCD when batch*head is a multiple of 8 and share its L2),
+//     grid y = query block, heaviest (last) blocks dispatched first.
+//   * Key tiles of 64 keys are visited from the diagonal tile DOWN to tile 0; tiles
+//     above the diagonal are never touched (their weights are exactly 0).  Walking
+//     backwards makes the first tile a row sees hold its largest gate bias, so the
+//     running max rarely moves and the lazy rescale below almost never fires.
+//   * Gate bias without a prefix-sum buffer: while walking backwards the loader keeps
+//     the fp64 suffix sum R_j = sum_{t=j+1..ref} log f_t (ref = the block's last row).
+//     Then c_i - c_j = R_j - R_i; the per-row constant R_i drops out of the softmax and
+//     is added back to lse only.  Each score costs one FMA: s2 = acc*scale*log2e + R_j*log2e.
+//     The block's own c_i = c_ref - R_i is written as the `c` output.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N), so a lane holds
+//     one query row and 16 keys per 32x32 block: the row max / sum are in-lane plus
+//     one permlane32 swap.  The S^T accumulator registers are, after rounding to bf16,
+//     directly the B operand of O^T = V^T P^T (keys permuted consistently; see vt_pos).
+//   * K is staged row-major in LDS (16-byte row padding), V transposed with the key
+//     order permuted so each lane's 8 keys are one ds_read_b128.  Global loads of the
+//     next tile are issued before the current tile's MFMAs (register prefetch).
+//   * Online softmax in base 2 with lazy rescaling: the running max is only raised when
+//     a row's tile max exceeds it by more than kTau (exact: the final normalisation uses
+//     the same stale max; p stays <= 2^kTau).
+//
+// fp32 inputs use the same schedule with v_mfma_f32_32x32x2f32 and fp32 P; there the
+// bias R_j - R_i is formed per score in fp64 (kept in LDS), so no fp32 rounding of a
+// block-relative gate sum enters the scores.
+#include <math.h>
+
+#include "fox_device.h"
+#include "fox_internal.h"
+
+namespace fox {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBR = 128;      // query rows per workgroup
+constexpr int kBC = 64;       // keys per tile
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr float kNegInf = -INFINITY;
+
+// Key position inside a 16-key group of the transposed V tile: bits 2 and 3 swapped.
+// With it, the 8 keys that one lane feeds to a PV MFMA (keys {0..3, 8..11} + 4*half
+// of a 16-key step) are contiguous.
+__device__ __forceinline__ int vt_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+
+struct GateLds {
+  float r2[kBC];     // R_j * log2(e) for the keys of the current tile
+  double r64[kBC];   // R_j in fp64 (the fp32-input kernel forms R_j - R_i exactly from these)
+  double rowR[kBR];  // R_i for the block's own rows
+  double cref;       // c at the block's reference row (sum of log f over 0..ref)
+};
+
+// Wave 0: gate suffix sums for tile kt.  `lf` is log f of key kt*64+lane (0 beyond ref),
+// `carry` the fp64 sum of log f over (tile end, ref] on entry, updated on exit.
+__device__ __forceinline__ void gate_tile(GateLds& g, int lane, int kt, int row0, int ref, float lf, double& carry) {
+  double s = (double)lf;  // becomes the inclusive suffix sum within the tile
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_down(s, off);
+    if (lane + off < 64) s += y;
+  }
+  double excl = __shfl_down(s, 1);
+  if (lane == 63) excl = 0.0;
+  const double rj = carry + excl;  // sum_{t=j+1..ref} log f_t
+  g.r2[lane] = (float)(rj * kLog2ed);
+  g.r64[lane] = rj;
+  const int j = kt * kBC + lane;
+  if (j >= row0 && j <= ref) g.rowR[j - row0] = rj;
+  carry += __shfl(s, 0);
+  if (kt == 0 && lane == 0) g.cref = carry;
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct Bf16Tile {
+  static constexpr int KS = D + 8;             // K row stride in LDS (bf16 elements)
+  static constexpr int VS = kBC + 8;           // V^T row stride in LDS (bf16 elements)
+  static constexpr int GROUPS = D / 8;         // 16-byte chunks per key row
+  static constexpr int KPT = kBC * GROUPS / kThreads;  // keys per thread in the tile loader
+  static_assert(KPT >= 1 && KPT * kThreads == kBC * GROUPS, "loader mapping");
+  u32x4 k[KPT];
+  u32x4 v[KPT];
+};
+
+template <int D>
+struct Bf16Lds {
+  bf16 k[kBC * Bf16Tile<D>::KS];
+  bf16 vt[D * Bf16Tile<D>::VS];
+  GateLds gate;
+};
+
+template <int D>
+__device__ __forceinline__ void bf16_load_tile(Bf16Tile<D>& t, const bf16* kb, const bf16* vb, int kt, int n,
+                                               int tid) {
+  constexpr int G = Bf16Tile<D>::GROUPS, KPT = Bf16Tile<D>::KPT;
+  const int c = tid % G, a = tid / G;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int key = kt * kBC + a * KPT + i;
+    if (key < n) {
+      t.k[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + 8 * c);
+      t.v[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + 8 * c);
+    } else {
+      t.k[i] = u32x4{0u, 0u, 0u, 0u};
+      t.v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void bf16_store_tile(const Bf16Tile<D>& t, Bf16Lds<D>& s, int tid) {
+  constexpr int G = Bf16Tile<D>::GROUPS, KPT = Bf16Tile<D>::KPT, KS = Bf16Tile<D>::KS, VS = Bf16Tile<D>::VS;
+  const int c = tid % G, a = tid / G;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(&s.k[(a * KPT + i) * KS + 8 * c]) = t.k[i];
+  const int pos = vt_pos(a * KPT);
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) {
+    bf16* dst = &s.vt[(8 * c + dd) * VS + pos];
+    const uint32_t sel = (dd & 1) ? kSelHiHi : kSelLoLo;
+    if constexpr (KPT == 4) {
+      u32x2 w;
+      w[0] = perm_b32(t.v[1][dd >> 1], t.v[0][dd >> 1], sel);
+      w[1] = perm_b32(t.v[3][dd >> 1], t.v[2][dd >> 1], sel);
+      *reinterpret_cast<u32x2*>(dst) = w;
+    } else if constexpr (KPT == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = perm_b32(t.v[1][dd >> 1], t.v[0][dd >> 1], sel);
+    } else {
+      const uint32_t w = t.v[0][dd >> 1];
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((dd & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                           const bf16* __restrict__ v,
+                                                           const float* __restrict__ logf, bf16* __restrict__ o,
+                                                           float* __restrict__ lse, float* __restrict__ c_out, int n,
+                                                           float scale_log2) {
+  constexpr int KS = Bf16Tile<D>::KS, VS = Bf16Tile<D>::VS, KK = D / 16, DB = D / 32;
+  __shared__ Bf16Lds<D> lds;
+
+  const int bh = blockIdx.x;
+  const int qb = gridDim.y - 1 - blockIdx.y;
+  const int row0 = qb * kBR;
+  const int ref = min(row0 + kBR - 1, n - 1);
+  const int kt_hi = ref / kBC;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t base = (size_t)bh * n * D;
+  const bf16* kb = k + base;
+  const bf16* vb = v + base;
+  const float* lfb = logf + (size_t)bh * n;
+
+  const int wrow0 = row0 + wave * 32;
+  const bool active = wrow0 < n;
+  const int kt_first = active ? min(wrow0 + 31, n - 1) / kBC : -1;
+  const int my_row = wrow0 + l32;
+
+  bf16x8 qreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (my_row < n)
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + base + (size_t)my_row * D + 16 * kk + 8 * hi);
+    else
+      qreg[kk] = bf16x8{};
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m = kNegInf, lsum = 0.0f;
+  double carry = 0.0;
+
+  Bf16Tile<D> tile;
+  bf16_load_tile<D>(tile, kb, vb, kt_hi, n, tid);
+  float lf = 0.0f;
+  if (wave == 0) {
+    const int j = kt_hi * kBC + lane;
+    lf = (j <= ref) ? lfb[j] : 0.0f;
+  }
+
+  for (int kt = kt_hi; kt >= 0; --kt) {
+    __syncthreads();  // previous tile fully consumed
+    bf16_store_tile<D>(tile, lds, tid);
+    if (wave == 0) gate_tile(lds.gate, lane, kt, row0, ref, lf, carry);
+    __syncthreads();
+    if (kt > 0) {
+      bf16_load_tile<D>(tile, kb, vb, kt - 1, n, tid);
+      if (wave == 0) lf = lfb[(kt - 1) * kBC + lane];
+    }
+    if (!active || kt > kt_first) continue;
+
+    // ---- S^T = K Q^T: two 32-key blocks -------------------------------------------------
+    f32x16 sacc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      sacc[b] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds.k[(32 * b + l32) * KS + 16 * kk + 8 * hi]);
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[b], 0, 0, 0);
+      }
+    }
+
+    // ---- scale + gate bias (+ causal mask on the diagonal tile), row max ----------------
+    const bool diag = kt * kBC + kBC - 1 > wrow0;
+    float mx = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kl = 32 * b + 8 * g + 4 * hi;
+        const f32x4 r2 = *reinterpret_cast<const f32x4*>(&lds.gate.r2[kl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = fmaf(sacc[b][4 * g + e], scale_log2, r2[e]);
+          if (diag && kt * kBC + kl + e > my_row) s = kNegInf;
+          sacc[b][4 * g + e] = s;
+          mx = fmaxf(mx, s);
+        }
+      }
+    }
+    mx = pair32_max(mx);
+
+    // ---- lazy online-softmax rescale ----------------------------------------------------
+    const float mcand = fmaxf(m, mx);
+    const bool need = mcand > m + kTau;
+    if (wave_any(need)) {
+      const float mn = need ? mcand : m;
+      const float alpha = exp2_hw(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m = mn;
+    }
+    const float msub = (m == kNegInf) ? 0.0f : m;
+
+    // ---- P = exp2(s - m), O^T += V^T P^T ------------------------------------------------
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_hw(sacc[b][8 * u + e] - msub);
+          lsum += p;
+          pb[e] = (bf16)p;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(&lds.vt[(32 * db + l32) * VS + 16 * (2 * b + u) + 8 * hi]);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = acc / l, lse, c ---------------------------------------------------
+  if (!active) return;
+  const float ltot = pair32_sum(lsum);
+  if (my_row >= n) return;
+  const float inv = 1.0f / ltot;
+  bf16* orow = o + base + (size_t)my_row * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+      w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w;
+    }
+  }
+  if (hi == 0) {
+    const double ri = lds.gate.rowR[my_row - row0];
+    const size_t idx = (size_t)bh * n + my_row;
+    if (lse) lse[idx] = (float)(((double)m + (double)log2_hw(ltot)) * kLn2d - ri);
+    if (c_out) c_out[idx] = (float)(lds.gate.cref - ri);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp32
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct F32Tile {
+  static constexpr int KS = D + 1;  // K row stride (floats): odd, so column reads spread over banks
+  static constexpr int VS = D + 8;  // V row stride (floats)
+  static constexpr int GROUPS = D / 4;
+  static constexpr int KPT = kBC * GROUPS / kThreads;
+  static_assert(KPT >= 1 && KPT * kThreads == kBC * GROUPS, "loader mapping");
+  f32x4 k[KPT];
+  f32x4 v[KPT];
+};
+
+template <int D>
+struct F32Lds {
+  float k[kBC * F32Tile<D>::KS];
+  float v[kBC * F32Tile<D>::VS];
+  GateLds gate;
+};
+
+template <int D>
+__device__ __forceinline__ void f32_load_tile(F32Tile<D>& t, const float* kb, const float* vb, int kt, int n,
+                                              int tid) {
+  constexpr int G = F32Tile<D>::GROUPS, KPT = F32Tile<D>::KPT;
+  const int c = tid % G, a = tid / G;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int key = kt * kBC + a * KPT + i;
+    if (key < n) {
+      t.k[i] = *reinterpret_cast<const f32x4*>(kb + (size_t)key * D + 4 * c);
+      t.v[i] = *reinterpret_cast<const f32x4*>(vb + (size_t)key * D + 4 * c);
+    } else {
+      t.k[i] = f32x4{};
+      t.v[i] = f32x4{};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void f32_store_tile(const F32Tile<D>& t, F32Lds<D>& s, int tid) {
+  constexpr int G = F32Tile<D>::GROUPS, KPT = F32Tile<D>::KPT, KS = F32Tile<D>::KS, VS = F32Tile<D>::VS;
+  const int c = tid % G, a = tid / G;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int key = a * KPT + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s.k[key * KS + 4 * c + e] = t.k[i][e];
+    *reinterpret_cast<f32x4*>(&s.v[key * VS + 4 * c]) = t.v[i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          const float* __restrict__ logf, float* __restrict__ o,
+                                                          float* __restrict__ lse, float* __restrict__ c_out, int n,
+                                                          float scale_log2) {
+  constexpr int KS = F32Tile<D>::KS, VS = F32Tile<D>::VS, KK = D / 2, DB = D / 32;
+  __shared__ F32Lds<D> lds;
+
+  const int bh = blockIdx.x;
+  const int qb = gridDim.y - 1 - blockIdx.y;
+  const int row0 = qb * kBR;
+  const int ref = min(row0 + kBR - 1, n - 1);
+  const int kt_hi = ref / kBC;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t base = (size_t)bh * n * D;
+  const float* kb = k + base;
+  const float* vb = v + base;
+  const float* lfb = logf + (size_t)bh * n;
+
+  const int wrow0 = row0 + wave * 32;
+  const bool active = wrow0 < n;
+  const int kt_first = active ? min(wrow0 + 31, n - 1) / kBC : -1;
+  const int my_row = wrow0 + l32;
+
+  float qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = (my_row < n) ? q[base + (size_t)my_row * D + 2 * kk + hi] : 0.0f;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m = kNegInf, lsum = 0.0f;
+  double carry = 0.0, ri_row = 0.0;
+
+  F32Tile<D> tile;
+  f32_load_tile<D>(tile, kb, vb, kt_hi, n, tid);
+  float lf = 0.0f;
+  if (wave == 0) {
+    const int j = kt_hi * kBC + lane;
+    lf = (j <= ref) ? lfb[j] : 0.0f;
+  }
+
+  for (int kt = kt_hi; kt >= 0; --kt) {
+    __syncthreads();
+    f32_store_tile<D>(tile, lds, tid);
+    if (wave == 0) gate_tile(lds.gate, lane, kt, row0, ref, lf, carry);
+    __syncthreads();
+    if (kt > 0) {
+      f32_load_tile<D>(tile, kb, vb, kt - 1, n, tid);
+      if (wave == 0) lf = lfb[(kt - 1) * kBC + lane];
+    }
+    if (!active || kt > kt_first) continue;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      sacc[b] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds.k[(32 * b + l32) * KS + 2 * kk + hi], qf[kk], sacc[b],
+                                                       0, 0, 0);
+    }
+
+    // This row's R_i is in the gate LDS from the wave's first (diagonal) tile on.
+    if (kt == kt_first) ri_row = (my_row < n) ? lds.gate.rowR[my_row - row0] : 0.0;
+    const bool diag = kt * kBC + kBC - 1 > wrow0;
+    float mx = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kl = 32 * b + 8 * g + 4 * hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // full bias sum_{t=j+1..i} log f_t = R_j - R_i, formed in fp64 and rounded once
+          const float bias2 = (float)((lds.gate.r64[kl + e] - ri_row) * kLog2ed);
+          float s = fmaf(sacc[b][4 * g + e], scale_log2, bias2);
+          if (diag && kt * kBC + kl + e > my_row) s = kNegInf;
+          sacc[b][4 * g + e] = s;
+          mx = fmaxf(mx, s);
+        }
+      }
+    }
+    mx = pair32_max(mx);
+
+    const float mcand = fmaxf(m, mx);
+    const bool need = mcand > m + kTau;
+    if (wave_any(need)) {
+      const float mn = need ? mcand : m;
+      const float alpha = exp2_hw(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m = mn;
+    }
+    const float msub = (m == kNegInf) ? 0.0f : m;
+
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(sacc[b][r] - msub);
+        lsum += p;
+        const int key = 32 * b + 8 * (r / 4) + 4 * hi + (r % 4);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds.v[key * VS + 32 * db + l32], p, oacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!active) return;
+  const float ltot = pair32_sum(lsum);
+  if (my_row >= n) return;
+  const float inv = 1.0f / ltot;
+  float* orow = o + base + (size_t)my_row * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
+      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hi) = w;
+    }
+  }
+  if (hi == 0) {
+    const double ri = lds.gate.rowR[my_row - row0];
+    const size_t idx = (size_t)bh * n + my_row;
+    if (lse) lse[idx] = (float)(((double)m + (double)log2f(ltot)) * kLn2d);  // scores already carry -R_i
+    if (c_out) c_out[idx] = (float)(lds.gate.cref - ri);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                        float* c, int64_t bh, int n, float scale_log2, hipStream_t stream) {
+  const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL(fwd_bf16_kernel<D>, grid, dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+  } else {
+    hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, logf, (float*)o, lse, c, n, scale_log2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, hipStream_t stream) {
+  const float scale_log2 = (float)((double)scale * kLog2ed);
+  if (is_bf16) {
+    switch (d) {
+      case 32: return launch_fwd_t<bf16, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+      case 64: return launch_fwd_t<bf16, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+      case 128: return launch_fwd_t<bf16, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+    }
+  } else {
+    switch (d) {
+      case 32: return launch_fwd_t<float, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+      case 64: return launch_fwd_t<float, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+      case 128: return launch_fwd_t<float, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fox

@@ -1,0 +1,26 @@
+// fox_internal.h -- host-side launchers of the libfox kernels (not part of the public ABI).
+// Each launcher assumes its arguments were validated by the C-ABI layer (fox_api.hip)
+// and returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fox {
+
+// Inclusive prefix sums of `rows` independent rows of length n (fp64 accumulate).
+hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream);
+
+// Causal FoX forward; is_bf16 selects the element type of q/k/v/o; d in {32,64,128}.
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, hipStream_t stream);
+
+// Split-K decode: number of key splits used for these sizes, and the workspace it needs.
+int decode_num_splits(int64_t sh, int l, int d);
+size_t decode_workspace_bytes(int64_t sh, int l, int d);
+hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
+                              void* o, float* lse, float* workspace, int64_t sh, int l, int d, float scale,
+                              bool is_bf16, hipStream_t stream);
+
+}  // namespace fox

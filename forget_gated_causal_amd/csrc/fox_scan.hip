@@ -1,0 +1,66 @@
+// fox_scan.hip -- K1: inclusive prefix sum of log forget gates, c_i = sum_{t<=i} log f_t.
+//
+// FoX module page, ForgettingAttention.forward: the cumulative sum of log f
+// along the sequence axis.  One 256-thread workgroup per (batch, head) row walks
+// the row in chunks of 1024 elements: each thread sums 4 consecutive gates, a
+// wave64 shuffle scan and a 4-entry LDS scan give the chunk prefix, and a carry
+// links the chunks.  Accumulation is fp64 (|c| reaches ~10^3 at 8k tokens, where
+// an fp32 running sum would drift); each c is rounded to fp32 once.
+#include "fox_device.h"
+#include "fox_internal.h"
+
+namespace fox {
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanPerThread = 4;
+constexpr int kScanChunk = kScanThreads * kScanPerThread;
+
+__global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* __restrict__ logf,
+                                                                   float* __restrict__ c, int n) {
+  __shared__ double wave_tot[kScanThreads / 64];
+  const size_t row = blockIdx.x;
+  const float* src = logf + row * (size_t)n;
+  float* dst = c + row * (size_t)n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double carry = 0.0;
+  for (int base = 0; base < n; base += kScanChunk) {
+    const int i0 = base + tid * kScanPerThread;
+    double x[kScanPerThread];
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) x[e] = (i0 + e < n) ? (double)src[i0 + e] : 0.0;
+#pragma unroll
+    for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
+    double t = x[kScanPerThread - 1];  // inclusive over this wave's threads after the loop below
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    double excl = __shfl_up(t, 1);
+    if (lane == 0) excl = 0.0;
+    if (lane == 63) wave_tot[wave] = t;
+    __syncthreads();
+    double before = carry, chunk = 0.0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      if (w < wave) before += wave_tot[w];
+      chunk += wave_tot[w];
+    }
+    __syncthreads();  // wave_tot is rewritten by the next chunk
+    const double pre = before + excl;
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e)
+      if (i0 + e < n) dst[i0 + e] = (float)(pre + x[e]);
+    carry += chunk;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(logf_cumsum_kernel, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf, c, n);
+  return hipGetLastError();
+}
+
+}  // namespace fox

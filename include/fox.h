@@ -1,0 +1,130 @@
+/*
+ * fox.h -- C ABI of libfox: causal Forgetting-Transformer (FoX) attention on MI355X (gfx950).
+ *
+ * What is computed.  With l_t = log f_t (the log forget gate of token t of one
+ * (batch, head) sequence) and c_i = sum_{t<=i} l_t:
+ *
+ *     s_ij  = scale * q_i . k_j + (c_i - c_j)          for j <= i   (weight 0 for j > i)
+ *     lse_i = ln sum_j exp(s_ij)                      O_i = sum_j exp(s_ij - lse_i) v_j
+ *
+ * Sources: "Forgetting Transformer (FoX) Attention" module page
+ * (frankenstein-transformer docs), ForgettingAttention.forward -- cumulative
+ * sum of log gates, bias cum[i] - cum[j] added after the scaled q k^T (the bias
+ * is not scaled), decoder-mode mask of the strict upper triangle, softmax over
+ * keys, times v; and the foxwindow README, opening paragraph -- the same score
+ * written as q.k + sum over t = j+1..i of log g_t.  lse is not defined on the
+ * pages; here it is the natural-log log-sum-exp of the full logit row.
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers are DEVICE pointers (hipMalloc'd or equivalent) owned by the
+ *    caller.  The library never allocates, frees or synchronises.
+ *  - Every call is asynchronous on `stream` (0 = the null stream), like a
+ *    kernel launch; results are valid once the stream has been synchronised.
+ *  - The library keeps no mutable global state: calls are reentrant and
+ *    thread-safe.  Calls that write the same buffers race like any kernels.
+ *  - Tensors are dense row-major with the shapes given; Q/K/V/O element type
+ *    is `dtype` (fp32 or bf16), gates / prefix sums / lse are always fp32.
+ *  - Q/K/V/O pointers must be 16-byte aligned; fp32 vectors 4-byte aligned.
+ *  - Argument errors are detected on the host, before anything is launched,
+ *    and returned as a status; no exception or abort crosses the ABI.
+ *  - Preconditions NOT checked (they would need device reads): gate values are
+ *    finite and <= 0 (gates in (0,1)); buffers have the stated sizes.
+ */
+#ifndef FOX_H_
+#define FOX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fox_status {
+  FOX_OK = 0,
+  FOX_ERR_INVALID_ARG = 1, /* null pointer, size <= 0 or too large, bad scale, misaligned pointer */
+  FOX_ERR_UNSUPPORTED = 2, /* head dim not in {32, 64, 128}, unknown dtype */
+  FOX_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than fox_attn_decode_workspace_bytes() */
+  FOX_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} fox_status_t;
+
+typedef enum fox_dtype {
+  FOX_F32 = 0, /* IEEE binary32 */
+  FOX_BF16 = 1 /* bfloat16; products accumulate in fp32, outputs rounded to nearest even */
+} fox_dtype_t;
+
+/* Largest sequence length / cache length accepted (keeps all index arithmetic in range). */
+#define FOX_MAX_SEQ (1 << 22)
+
+/*
+ * fox_logf_cumsum -- inclusive prefix sum of log forget gates along the sequence.
+ *   FoX module page, ForgettingAttention.forward: cumulative sum of log f over
+ *   the sequence axis, per (batch, head).
+ *
+ *   logf : [rows, n] fp32, input (rows = batch * heads).
+ *   c    : [rows, n] fp32, output; c[r, i] = sum_{t<=i} logf[r, t], accumulated
+ *          in fp64 and rounded once to fp32.  May not alias logf.
+ *   rows, n : > 0, n <= FOX_MAX_SEQ.
+ */
+fox_status_t fox_logf_cumsum(const float* logf, float* c, int64_t rows, int64_t n, hipStream_t stream);
+
+/*
+ * fox_attn_fwd -- causal FoX attention forward (prefill) over whole sequences.
+ *   FoX module page, ForgettingAttention.forward (decoder mode), from the
+ *   projected, head-split q, k, v onwards (the output projection is not part
+ *   of it).
+ *
+ *   q, k, v : [b, h, n, d] of `dtype`, inputs.
+ *   logf    : [b, h, n] fp32, input log forget gates.
+ *   o       : [b, h, n, d] of `dtype`, output (bf16: rounded to nearest even).
+ *   lse     : [b, h, n] fp32, output log-sum-exp (natural log) of each logit row, or NULL.
+ *   c       : [b, h, n] fp32, output prefix sums of logf (as fox_logf_cumsum), or NULL;
+ *             these seed a decode cache.
+ *   d       : head dim, one of 32, 64, 128.
+ *   scale   : multiplier of q.k (finite, > 0); the module uses d ** -0.5.
+ *   Outputs must not alias inputs.
+ */
+fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                          float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
+                          hipStream_t stream);
+
+/*
+ * fox_attn_decode_workspace_bytes -- bytes of scratch fox_attn_decode needs for
+ * these sizes (split-K partial results).  Returns 0 for invalid sizes.
+ */
+size_t fox_attn_decode_workspace_bytes(int64_t s, int64_t h, int64_t l, int64_t d);
+
+/*
+ * fox_attn_decode -- one causal FoX decode step per (sequence, head) against a KV cache.
+ *   The last query row of fox_attn_fwd's definition.  The pages define no
+ *   decode; the cache semantics are this library's: the caller has already
+ *   written the new token's k and v at slot l-1, and slots 0..l-2 of c_cache
+ *   hold the prefix sums c_0..c_{l-2} (e.g. from fox_attn_fwd's `c`).
+ *
+ *   q        : [s, h, d] of `dtype`, the new tokens' queries.
+ *   k_cache  : [s, h, l, d] of `dtype`; v_cache likewise.
+ *   c_cache  : [s, h, l] fp32; slots 0..l-2 read, slot l-1 WRITTEN with
+ *              c_{l-1} = c_{l-2} + logf_new (logf_new when l == 1).
+ *   logf_new : [s, h] fp32, the new tokens' log forget gates.
+ *   o        : [s, h, d] of `dtype`, output.
+ *   lse      : [s, h] fp32, output (natural log), or NULL.
+ *   workspace, workspace_bytes : device scratch of at least
+ *              fox_attn_decode_workspace_bytes(s, h, l, d) bytes, 16-byte aligned;
+ *              contents on entry are ignored.
+ *   scale    : multiplier of q.k (finite, > 0).
+ */
+fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                             const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                             int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
+                             hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fox_status_string(fox_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOX_H_ */

@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments with the documented status before launching
+anything (no GPU needed: every call here fails validation)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from forget_gated_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fox.h")
+
+# fake, never dereferenced device addresses (16-byte aligned, far apart)
+A, B, C, D, E, F, G, H = (0x10_0000_0000 * (i + 1) for i in range(8))
+OK, INVALID, UNSUP, WS = _lib.FOX_OK, _lib.FOX_ERR_INVALID_ARG, _lib.FOX_ERR_UNSUPPORTED, _lib.FOX_ERR_WORKSPACE
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fox_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(L):
+    names = declared_functions()
+    assert names == sorted(_lib.SIGNATURES), names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fox_[a-z0-9_]+)", out))
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert getattr(L, n) is not None
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert len(_lib.status_string(s)) > 0
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_decode_workspace_bytes(L):
+    f = L.fox_attn_decode_workspace_bytes
+    assert f(64, 32, 8192, 128) > 0
+    assert f(64, 32, 8192, 128) % (4 * 130) == 0
+    assert f(0, 32, 8192, 128) == 0 and f(1, 1, 0, 128) == 0 and f(1, 1, 10, 48) == 0
+    assert f(1, 1, 1, 32) == 1 * 34 * 4  # one split for a single key
+
+
+def _fwd(L, q=A, k=B, v=C, logf=D, o=E, lse=F, c=G, b=1, h=2, n=128, d=32, scale=0.17, dt=_lib.FOX_F32):
+    return L.fox_attn_fwd(q, k, v, logf, o, lse, c, b, h, n, d, scale, dt, None)
+
+
+def test_fwd_rejects_bad_arguments(L):
+    assert _fwd(L, q=None) == INVALID
+    assert _fwd(L, o=None) == INVALID
+    assert _fwd(L, logf=None) == INVALID
+    assert _fwd(L, n=0) == INVALID
+    assert _fwd(L, b=-1) == INVALID
+    assert _fwd(L, n=(1 << 22) + 1) == INVALID
+    assert _fwd(L, d=48) == UNSUP
+    assert _fwd(L, d=256) == UNSUP
+    assert _fwd(L, dt=7) == UNSUP
+    assert _fwd(L, scale=0.0) == INVALID
+    assert _fwd(L, scale=float("nan")) == INVALID
+    assert _fwd(L, scale=float("inf")) == INVALID
+    assert _fwd(L, q=A + 8) == INVALID  # not 16-byte aligned
+    assert _fwd(L, lse=F + 2) == INVALID  # not 4-byte aligned
+    assert _fwd(L, o=A) == INVALID  # output aliases q
+    assert _fwd(L, c=D) == INVALID  # c aliases logf
+    assert _fwd(L, lse=G) == INVALID  # lse aliases c
+
+
+def test_cumsum_rejects_bad_arguments(L):
+    f = L.fox_logf_cumsum
+    assert f(None, A, 1, 10, None) == INVALID
+    assert f(A, None, 1, 10, None) == INVALID
+    assert f(A, B, 0, 10, None) == INVALID
+    assert f(A, B, 1, 0, None) == INVALID
+    assert f(A, A + 4, 1, 10, None) == INVALID  # overlapping
+    assert f(A + 1, B, 1, 10, None) == INVALID
+
+
+def _dec(L, q=A, k=B, v=C, cc=D, ln=E, o=F, lse=G, ws=H, wsb=1 << 30, s=2, h=2, l=100, d=64, scale=0.1,
+         dt=_lib.FOX_BF16):
+    return L.fox_attn_decode(q, k, v, cc, ln, o, lse, ws, wsb, s, h, l, d, scale, dt, None)
+
+
+def test_decode_rejects_bad_arguments(L):
+    assert _dec(L, q=None) == INVALID
+    assert _dec(L, cc=None) == INVALID
+    assert _dec(L, l=0) == INVALID
+    assert _dec(L, d=96) == UNSUP
+    assert _dec(L, dt=3) == UNSUP
+    assert _dec(L, scale=-1.0) == INVALID
+    assert _dec(L, k=B + 4) == INVALID
+    assert _dec(L, ws=None) == WS
+    assert _dec(L, wsb=16) == WS
+    assert _dec(L, ws=H + 8) == WS
+    assert _dec(L, o=B) == INVALID  # output inside the K cache
+    assert _dec(L, ws=C) == INVALID  # workspace inside the V cache

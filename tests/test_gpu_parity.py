@@ -1,0 +1,198 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (max-abs over every compared element): 1e-5 for fp32 inputs and 2e-2
+for bf16 inputs with fp32 accumulation, on O and lse; the gate prefix sums c
+within one fp32 ulp of max|c| (they are accumulated in fp64 and rounded once).
+The oracle sees exactly the values the GPU sees (bf16 widened exactly, the fp32
+scale widened).  Output buffers are pre-filled with NaN so an unwritten element
+fails.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import forget_gated_causal_amd as fox
+import fox_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def _ulp(x):
+    return float(np.spacing(np.float32(np.max(np.abs(x)) if np.size(x) else 1.0)))
+
+
+def _run_fwd(inp):
+    q, k, v, logf = (inp[n].to(DEV) for n in ("q", "k", "v", "logf"))
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full_like(logf, nan)
+    c = torch.full_like(logf, nan)
+    fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)
+    torch.cuda.synchronize()
+    return o, lse, c
+
+
+def _check_fwd_full(inp, tol):
+    o, lse, c = _run_fwd(inp)
+    o_ref, lse_ref, c_ref = oracle.attn_fwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]),
+                                            inp["scale"])
+    eo, el, ec = np.abs(_np(o) - o_ref).max(), np.abs(_np(lse) - lse_ref).max(), np.abs(_np(c) - c_ref).max()
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc|={ec:.3e} (ulp {_ulp(c_ref):.1e})", flush=True)
+    assert eo <= tol and el <= tol and ec <= _ulp(c_ref)
+    return o, lse, c
+
+
+# ---------------------------------------------------------------------------------- gate scan
+
+@pytest.mark.parametrize("rows,n", [(1, 1), (3, 1000), (2, 1025), (5, 4097), (2048, 8192)])
+def test_logf_cumsum_parity(rows, n):
+    g = torch.Generator().manual_seed(rows * 7919 + n)
+    logf = torch.nn.functional.logsigmoid((torch.randn(rows, n, generator=g) * 2 + 4).double()).float()
+    c = fox.logf_cumsum(logf.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.logf_cumsum(logf.double().numpy())
+    err = np.abs(_np(c) - ref).max()
+    assert err <= _ulp(ref), err
+
+
+# ---------------------------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("tag", ["c1", "c2", "c2_f1", "c2_alibi"])
+def test_fwd_config_full_parity(tag):
+    cfg = fi.FWD[tag]
+    inp = fi.fwd_inputs(cfg)
+    print(f"  {cfg.desc} inputs {fi.digest(inp['q'], inp['k'], inp['v'], inp['logf'])}", flush=True)
+    _check_fwd_full(inp, TOL[cfg.dtype])
+
+
+RAGGED = [(dt, d, n) for dt in ("f32", "bf16") for d in (32, 64, 128) for n in (1, 33, 64, 65, 129, 300)]
+
+
+@pytest.mark.parametrize("dtype,d,n", RAGGED)
+def test_fwd_ragged_parity(dtype, d, n):
+    cfg = fi.FwdConfig(f"ragged_{dtype}_{d}_{n}", 2, 2, n, d, dtype, 1.0, 2.0)
+    _check_fwd_full(fi.fwd_inputs(cfg), TOL[dtype])
+
+
+def _sampled_rows(n):
+    rows = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, n // 2 - 1, n // 2, n - 129, n - 128, n - 65, n - 64,
+            n - 2, n - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+@pytest.mark.parametrize("tag", ["c3", "c4"])
+def test_fwd_full_size_sampled_parity(tag):
+    cfg = fi.FWD[tag]
+    inp = fi.fwd_inputs(cfg)
+    o, lse, c = _run_fwd(inp)
+    rows = _sampled_rows(cfg.N)
+    o_ref, lse_ref = oracle.attn_fwd_rows(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]),
+                                          inp["scale"], rows)
+    eo = np.abs(_np(o[:, :, rows]) - o_ref).max()
+    el = np.abs(_np(lse[:, :, rows]) - lse_ref).max()
+    c_ref = oracle.logf_cumsum(_np(inp["logf"]))
+    ec = np.abs(_np(c) - c_ref).max()
+    print(f"  {cfg.desc}: rows {len(rows)}/head max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc|={ec:.3e}", flush=True)
+    assert eo <= TOL[cfg.dtype] and el <= TOL[cfg.dtype] and ec <= _ulp(c_ref)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_fwd_deterministic():
+    inp = fi.fwd_inputs(fi.FWD["c2"])
+    a = _run_fwd(inp)
+    b = _run_fwd(inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x, y.view(torch.uint8)
+                           if y.dtype == torch.bfloat16 else y)
+
+
+# ---------------------------------------------------------------------------------- decode
+
+def _decode_caches(logf_all):
+    """GPU cache from the library's scan; oracle cache from the oracle's scan (fp32-rounded like a real cache)."""
+    L = logf_all.shape[-1]
+    c_gpu = fox.logf_cumsum(logf_all.to(DEV))
+    c_gpu[..., L - 1] = float("nan")
+    c_ora = oracle.logf_cumsum(logf_all.double().numpy()).astype(np.float32).astype(np.float64)
+    c_ora[..., L - 1] = np.nan
+    return c_gpu, c_ora
+
+
+def _run_decode(inp):
+    L = inp["cfg"].L
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    c_gpu, c_ora = _decode_caches(inp["logf_all"])
+    lnew = inp["logf_all"][..., L - 1].contiguous()
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), device=DEV)
+    fox.attn_decode(q, k, v, c_gpu, lnew.to(DEV), scale=inp["scale"], out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse, c_gpu, c_ora, lnew
+
+
+def _check_decode(inp, tol):
+    L = inp["cfg"].L
+    o, lse, c_gpu, c_ora, lnew = _run_decode(inp)
+    o_ref, lse_ref, cnew_ref = oracle.attn_decode(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), c_ora,
+                                                  lnew.double().numpy(), inp["scale"])
+    eo, el = np.abs(_np(o) - o_ref).max(), np.abs(_np(lse) - lse_ref).max()
+    ec = np.abs(_np(c_gpu[..., L - 1]) - cnew_ref).max()
+    print(f"  max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc_new|={ec:.3e}", flush=True)
+    assert eo <= tol and el <= tol and ec <= _ulp(cnew_ref)
+
+
+DECODE_SMALL = [(dt, d, L) for dt in ("f32", "bf16") for d in (32, 64, 128) for L in (1, 2, 77, 1000, 4097)]
+
+
+@pytest.mark.parametrize("dtype,d,L", DECODE_SMALL)
+def test_decode_small_parity(dtype, d, L):
+    cfg = fi.DecodeConfig(f"dec_{dtype}_{d}_{L}", 2, 3, L, d, dtype, 4.0, 2.0)
+    _check_decode(fi.decode_inputs(cfg), TOL[dtype])
+
+
+def test_decode_full_size_sampled_parity():
+    cfg = fi.DECODE["c5"]
+    full = fi.decode_inputs(cfg)
+    o, lse, c_gpu, _, lnew = _run_decode(full)
+    seqs = [0, 31, 63]
+    sub = fi.decode_inputs(cfg, seqs=seqs)  # regenerated independently from the per-sequence seeds
+    assert torch.equal(sub["k"][2], full["k"][63])
+    c_ora = oracle.logf_cumsum(sub["logf_all"].double().numpy()).astype(np.float32).astype(np.float64)
+    c_ora[..., cfg.L - 1] = np.nan
+    o_ref, lse_ref, cnew_ref = oracle.attn_decode(_np(sub["q"]), _np(sub["k"]), _np(sub["v"]), c_ora,
+                                                  sub["logf_all"][..., cfg.L - 1].double().numpy(), sub["scale"])
+    eo = np.abs(_np(o[seqs]) - o_ref).max()
+    el = np.abs(_np(lse[seqs]) - lse_ref).max()
+    ec = np.abs(_np(c_gpu[seqs, :, cfg.L - 1]) - cnew_ref).max()
+    print(f"  {cfg.desc}: seqs {seqs} max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc_new|={ec:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and ec <= _ulp(cnew_ref)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all() and torch.isfinite(c_gpu).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_equals_prefill_last_row(dtype):
+    """Decode of token L-1 against a cache built by the forward (its c output) equals row L-1 of the forward."""
+    B, H, N, d = 2, 4, 777, 128
+    inp = fi.fwd_inputs(fi.FwdConfig(f"consist_{dtype}", B, H, N, d, dtype, 3.0, 1.5))
+    q, k, v, logf = (inp[n].to(DEV) for n in ("q", "k", "v", "logf"))
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    cache_c = c.clone()
+    cache_c[..., N - 1] = float("nan")
+    od, lsed = fox.attn_decode(q[:, :, N - 1].contiguous(), k, v, cache_c, logf[..., N - 1].contiguous(),
+                               scale=inp["scale"])
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert (od.double() - o[:, :, N - 1].double()).abs().max().item() <= tol
+    assert (lsed - lse[..., N - 1]).abs().max().item() <= 1e-4
+    assert (cache_c[..., N - 1] - c[..., N - 1]).abs().max().item() <= _ulp(_np(c))
