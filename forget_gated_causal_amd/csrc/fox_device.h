@@ -77,3 +77,43 @@ constexpr uint32_t kSelLoLo = 0x05040100u;  // lo16(lo) | lo16(hi) << 16
 constexpr uint32_t kSelHiHi = 0x07060302u;  // hi16(lo) | hi16(hi) << 16
 
 }  // namespace fox
+
+namespace fox {
+
+// Inclusive prefix sum over the 64 lanes of a wave in fp64.  The lane moves are DPP
+// (row shifts inside 16-lane rows, then the two row broadcasts of gfx9) applied to the
+// two dwords of each double, so the moved values are exact; lanes whose row or bank is
+// masked off receive 0.  Only the adds round, as fp64.
+template <int CTRL, int ROW_MASK, int BANK_MASK, bool BOUND>
+__device__ __forceinline__ double dpp_or_zero(double v) {
+  const u32x2 w = __builtin_bit_cast(u32x2, v);
+  u32x2 r;
+  r[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[0], CTRL, ROW_MASK, BANK_MASK, BOUND);
+  r[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[1], CTRL, ROW_MASK, BANK_MASK, BOUND);
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  double y = x + dpp_or_zero<0x111, 0xF, 0xF, true>(x);  // row_shr:1
+  y += dpp_or_zero<0x112, 0xF, 0xF, true>(x);            // row_shr:2
+  y += dpp_or_zero<0x113, 0xF, 0xF, true>(x);            // row_shr:3   -> sums of 4 within the row
+  y += dpp_or_zero<0x114, 0xF, 0xE, true>(y);            // row_shr:4 on banks 1..3
+  y += dpp_or_zero<0x118, 0xF, 0xC, true>(y);            // row_shr:8 on banks 2..3 -> row-local scan
+  y += dpp_or_zero<0x142, 0xA, 0xF, false>(y);           // row_bcast:15 into rows 1 and 3
+  y += dpp_or_zero<0x143, 0xC, 0xF, false>(y);           // row_bcast:31 into rows 2 and 3
+  return y;
+}
+
+// Value of lane l-1 (0 in lane 0): wave_shr:1.
+__device__ __forceinline__ double wave_shr1(double x) { return dpp_or_zero<0x138, 0xF, 0xF, true>(x); }
+
+// Value of lane 63, in every lane.
+__device__ __forceinline__ double wave_last(double x) {
+  const u32x2 w = __builtin_bit_cast(u32x2, x);
+  u32x2 r;
+  r[0] = (uint32_t)__builtin_amdgcn_readlane((int)w[0], 63);
+  r[1] = (uint32_t)__builtin_amdgcn_readlane((int)w[1], 63);
+  return __builtin_bit_cast(double, r);
+}
+
+}  // namespace fox

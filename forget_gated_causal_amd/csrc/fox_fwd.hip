@@ -58,23 +58,23 @@ struct GateLds {
   double cref;       // c at the block's reference row (sum of log f over 0..ref)
 };
 
-// Wave 0: gate suffix sums for tile kt.  `lf` is log f of key kt*64+lane (0 beyond ref),
-// `carry` the fp64 sum of log f over (tile end, ref] on entry, updated on exit.
-__device__ __forceinline__ void gate_tile(GateLds& g, int lane, int kt, int row0, int ref, float lf, double& carry) {
-  double s = (double)lf;  // becomes the inclusive suffix sum within the tile
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_down(s, off);
-    if (lane + off < 64) s += y;
-  }
-  double excl = __shfl_down(s, 1);
-  if (lane == 63) excl = 0.0;
-  const double rj = carry + excl;  // sum_{t=j+1..ref} log f_t
-  g.r2[lane] = (float)(rj * kLog2ed);
-  g.r64[lane] = rj;
-  const int j = kt * kBC + lane;
+// Wave 0: gate sums for tile kt.  Lane t holds log f of key 63-t of the tile (0 beyond
+// ref), so the lane-order exclusive prefix is the key-order exclusive suffix
+// sum_{u > j} log f_u inside the tile.  `carry` (fp64) is the sum of log f over
+// (tile end, ref] and is advanced by the tile total.  Writes R_j = carry + suffix for
+// the tile (fp32 * log2 e and fp64), R_i for the block's own rows and, after tile 0,
+// c at the reference row.  Everything is fp64 until the single rounding to fp32.
+__device__ __forceinline__ void gate_tile(GateLds& g, int lane, int kt, int row0, int ref, float lf_rev,
+                                          double& carry) {
+  const double incl = wave_incl_scan((double)lf_rev);
+  const double excl = wave_shr1(incl);
+  const int jl = 63 - lane;
+  const double rj = carry + excl;
+  g.r2[jl] = (float)(rj * kLog2ed);
+  g.r64[jl] = rj;
+  const int j = kt * kBC + jl;
   if (j >= row0 && j <= ref) g.rowR[j - row0] = rj;
-  carry += __shfl(s, 0);
+  carry += wave_last(incl);
   if (kt == 0 && lane == 0) g.cref = carry;
 }
 
@@ -142,13 +142,83 @@ __device__ __forceinline__ void bf16_store_tile(const Bf16Tile<D>& t, Bf16Lds<D>
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                           const bf16* __restrict__ v,
-                                                           const float* __restrict__ logf, bf16* __restrict__ o,
-                                                           float* __restrict__ lse, float* __restrict__ c_out, int n,
-                                                           float scale_log2) {
+// One 64-key tile for one wave: S^T = K Q^T, bias, (mask), lazy online softmax, O^T += V^T P^T.
+template <int D, bool DIAG>
+__device__ __forceinline__ void bf16_tile_compute(const Bf16Lds<D>& lds, const bf16x8 (&qreg)[D / 16],
+                                                  f32x16 (&oacc)[D / 32], float& m, float& lsum, int key0,
+                                                  int my_row, int l32, int hi, float scale_log2) {
   constexpr int KS = Bf16Tile<D>::KS, VS = Bf16Tile<D>::VS, KK = D / 16, DB = D / 32;
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  const bf16* k0 = &lds.k[l32 * KS + 8 * hi];
+  const bf16* k1 = &lds.k[(32 + l32) * KS + 8 * hi];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(k0 + 16 * kk);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(k1 + 16 * kk);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+  }
+  f32x16 sacc[2] = {s0, s1};
+
+  float mx = kNegInf;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int kl = 32 * b + 8 * g + 4 * hi;
+      const f32x4 r2 = *reinterpret_cast<const f32x4*>(&lds.gate.r2[kl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sv = fmaf(sacc[b][4 * g + e], scale_log2, r2[e]);
+        if constexpr (DIAG) {
+          if (key0 + kl + e > my_row) sv = kNegInf;
+        }
+        sacc[b][4 * g + e] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    }
+  }
+  mx = pair32_max(mx);
+
+  const float mcand = fmaxf(m, mx);
+  const bool need = mcand > m + kTau;
+  if (wave_any(need)) {
+    const float mn = need ? mcand : m;
+    const float alpha = exp2_hw(m - mn);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    m = mn;
+  }
+  const float msub = (m == kNegInf) ? 0.0f : m;
+
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = exp2_hw(sacc[b][8 * u + e] - msub);
+        lsum += pv;
+        pb[e] = (bf16)pv;
+      }
+      const bf16* vrow = &lds.vt[l32 * VS + 16 * (2 * b + u) + 8 * hi];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 32 * db * VS);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
+    float scale_log2) {
+  constexpr int KK = D / 16, DB = D / 32;
   __shared__ Bf16Lds<D> lds;
 
   const int bh = blockIdx.x;
@@ -184,10 +254,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const bf16* __restri
   double carry = 0.0;
 
   Bf16Tile<D> tile;
-  bf16_load_tile<D>(tile, kb, vb, kt_hi, n, tid);
-  float lf = 0.0f;
+  bf16_load_tile<D>(tile, kb, vb, kt_hi, n, tid);  // the only tile that may run past n
+  float lf = 0.0f;                                  // wave 0: log f of key 63-lane of the next tile
   if (wave == 0) {
-    const int j = kt_hi * kBC + lane;
+    const int j = kt_hi * kBC + 63 - lane;
     lf = (j <= ref) ? lfb[j] : 0.0f;
   }
 
@@ -196,77 +266,23 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const bf16* __restri
     bf16_store_tile<D>(tile, lds, tid);
     if (wave == 0) gate_tile(lds.gate, lane, kt, row0, ref, lf, carry);
     __syncthreads();
-    if (kt > 0) {
-      bf16_load_tile<D>(tile, kb, vb, kt - 1, n, tid);
-      if (wave == 0) lf = lfb[(kt - 1) * kBC + lane];
+    if (kt > 0) {  // tiles below the top one are complete: no bounds checks
+      constexpr int G = Bf16Tile<D>::GROUPS, KPT = Bf16Tile<D>::KPT;
+      const int c = tid % G, a = tid / G;
+      const size_t off = (size_t)((kt - 1) * kBC + a * KPT) * D + 8 * c;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        tile.k[i] = *reinterpret_cast<const u32x4*>(kb + off + (size_t)i * D);
+        tile.v[i] = *reinterpret_cast<const u32x4*>(vb + off + (size_t)i * D);
+      }
+      if (wave == 0) lf = lfb[(kt - 1) * kBC + 63 - lane];
     }
     if (!active || kt > kt_first) continue;
-
-    // ---- S^T = K Q^T: two 32-key blocks -------------------------------------------------
-    f32x16 sacc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sacc[b] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds.k[(32 * b + l32) * KS + 16 * kk + 8 * hi]);
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[b], 0, 0, 0);
-      }
-    }
-
-    // ---- scale + gate bias (+ causal mask on the diagonal tile), row max ----------------
-    const bool diag = kt * kBC + kBC - 1 > wrow0;
-    float mx = kNegInf;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kl = 32 * b + 8 * g + 4 * hi;
-        const f32x4 r2 = *reinterpret_cast<const f32x4*>(&lds.gate.r2[kl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = fmaf(sacc[b][4 * g + e], scale_log2, r2[e]);
-          if (diag && kt * kBC + kl + e > my_row) s = kNegInf;
-          sacc[b][4 * g + e] = s;
-          mx = fmaxf(mx, s);
-        }
-      }
-    }
-    mx = pair32_max(mx);
-
-    // ---- lazy online-softmax rescale ----------------------------------------------------
-    const float mcand = fmaxf(m, mx);
-    const bool need = mcand > m + kTau;
-    if (wave_any(need)) {
-      const float mn = need ? mcand : m;
-      const float alpha = exp2_hw(m - mn);
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m = mn;
-    }
-    const float msub = (m == kNegInf) ? 0.0f : m;
-
-    // ---- P = exp2(s - m), O^T += V^T P^T ------------------------------------------------
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2_hw(sacc[b][8 * u + e] - msub);
-          lsum += p;
-          pb[e] = (bf16)p;
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&lds.vt[(32 * db + l32) * VS + 16 * (2 * b + u) + 8 * hi]);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-        }
-      }
-    }
+    const int key0 = kt * kBC;
+    if (key0 + kBC - 1 > wrow0)
+      bf16_tile_compute<D, true>(lds, qreg, oacc, m, lsum, key0, my_row, l32, hi, scale_log2);
+    else
+      bf16_tile_compute<D, false>(lds, qreg, oacc, m, lsum, key0, my_row, l32, hi, scale_log2);
   }
 
   // ---- epilogue: O = acc / l, lse, c ---------------------------------------------------
@@ -383,9 +399,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 
   F32Tile<D> tile;
   f32_load_tile<D>(tile, kb, vb, kt_hi, n, tid);
-  float lf = 0.0f;
+  float lf = 0.0f;  // wave 0: log f of key 63-lane of the next tile
   if (wave == 0) {
-    const int j = kt_hi * kBC + lane;
+    const int j = kt_hi * kBC + 63 - lane;
     lf = (j <= ref) ? lfb[j] : 0.0f;
   }
 
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     __syncthreads();
     if (kt > 0) {
       f32_load_tile<D>(tile, kb, vb, kt - 1, n, tid);
-      if (wave == 0) lf = lfb[(kt - 1) * kBC + lane];
+      if (wave == 0) lf = lfb[(kt - 1) * kBC + 63 - lane];
     }
     if (!active || kt > kt_first) continue;
 
