@@ -21,10 +21,11 @@
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N), so a lane holds
 //     one query row and 16 keys per 32x32 block: the row max / sum are in-lane plus
 //     one permlane32 swap.  The S^T accumulator registers are, after rounding to bf16,
-//     directly the B operand of O^T = V^T P^T (keys permuted consistently; see vt_pos).
-//   * K is staged row-major in LDS (16-byte row padding), V transposed with the key
-//     order permuted so each lane's 8 keys are one ds_read_b128.  Global loads of the
-//     next tile are issued before the current tile's MFMAs (register prefetch).
+//     directly the B operand of O^T = V^T P^T (the V operand follows the same key order).
+//   * K and V are staged row-major in LDS (padded rows).  The PV operand, which needs 8
+//     keys of one dim per lane, comes from gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16), so no transposed stores.  Global loads of the next tile are
+//     issued before the current tile's MFMAs (register prefetch).
 //   * Online softmax in base 2 with lazy rescaling: the running max is only raised when
 //     a row's tile max exceeds it by more than kTau (exact: the final normalisation uses
 //     the same stale max; p stays <= 2^kTau).
@@ -45,11 +46,6 @@ constexpr int kBR = 128;      // query rows per workgroup
 constexpr int kBC = 64;       // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 constexpr float kNegInf = -INFINITY;
-
-// Key position inside a 16-key group of the transposed V tile: bits 2 and 3 swapped.
-// With it, the 8 keys that one lane feeds to a PV MFMA (keys {0..3, 8..11} + 4*half
-// of a 16-key step) are contiguous.
-__device__ __forceinline__ int vt_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
 
 struct GateLds {
   float r2[kBC];     // R_j * log2(e) for the keys of the current tile
@@ -83,9 +79,11 @@ __device__ __forceinline__ void gate_tile(GateLds& g, int lane, int kt, int row0
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct Bf16Tile {
-  static constexpr int KS = D + 8;             // K row stride in LDS (bf16 elements)
-  static constexpr int VS = kBC + 8;           // V^T row stride in LDS (bf16 elements)
-  static constexpr int GROUPS = D / 8;         // 16-byte chunks per key row
+  static constexpr int KS = D + 8;  // K row stride in LDS (bf16): 16-byte pad, b128 row reads hit distinct banks
+  // V row stride in LDS (bf16): the transposed b64 reads of one half-wave touch 4 rows x 64
+  // bytes; a stride of 16 dwords (mod 64 banks) puts those rows on disjoint banks.
+  static constexpr int VS = (D == 32) ? D : D + 32;
+  static constexpr int GROUPS = D / 8;                 // 16-byte chunks per key row
   static constexpr int KPT = kBC * GROUPS / kThreads;  // keys per thread in the tile loader
   static_assert(KPT >= 1 && KPT * kThreads == kBC * GROUPS, "loader mapping");
   u32x4 k[KPT];
@@ -95,7 +93,7 @@ struct Bf16Tile {
 template <int D>
 struct Bf16Lds {
   bf16 k[kBC * Bf16Tile<D>::KS];
-  bf16 vt[D * Bf16Tile<D>::VS];
+  bf16 v[kBC * Bf16Tile<D>::VS];
   GateLds gate;
 };
 
@@ -122,24 +120,17 @@ __device__ __forceinline__ void bf16_store_tile(const Bf16Tile<D>& t, Bf16Lds<D>
   constexpr int G = Bf16Tile<D>::GROUPS, KPT = Bf16Tile<D>::KPT, KS = Bf16Tile<D>::KS, VS = Bf16Tile<D>::VS;
   const int c = tid % G, a = tid / G;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(&s.k[(a * KPT + i) * KS + 8 * c]) = t.k[i];
-  const int pos = vt_pos(a * KPT);
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    bf16* dst = &s.vt[(8 * c + dd) * VS + pos];
-    const uint32_t sel = (dd & 1) ? kSelHiHi : kSelLoLo;
-    if constexpr (KPT == 4) {
-      u32x2 w;
-      w[0] = perm_b32(t.v[1][dd >> 1], t.v[0][dd >> 1], sel);
-      w[1] = perm_b32(t.v[3][dd >> 1], t.v[2][dd >> 1], sel);
-      *reinterpret_cast<u32x2*>(dst) = w;
-    } else if constexpr (KPT == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = perm_b32(t.v[1][dd >> 1], t.v[0][dd >> 1], sel);
-    } else {
-      const uint32_t w = t.v[0][dd >> 1];
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)((dd & 1) ? (w >> 16) : (w & 0xFFFFu));
-    }
+  for (int i = 0; i < KPT; ++i) {
+    *reinterpret_cast<u32x4*>(&s.k[(a * KPT + i) * KS + 8 * c]) = t.k[i];
+    *reinterpret_cast<u32x4*>(&s.v[(a * KPT + i) * VS + 8 * c]) = t.v[i];
   }
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, output lane j element e is element j%4
+// of the 8 bytes addressed by lane 4e + j/4 of the group (transpose of a 16x4 block).
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, bias, (mask), lazy online softmax, O^T += V^T P^T.
@@ -192,6 +183,8 @@ __device__ __forceinline__ void bf16_tile_compute(const Bf16Lds<D>& lds, const b
   }
   const float msub = (m == kNegInf) ? 0.0f : m;
 
+  const int lane = hi * 32 + l32, li = lane & 15;
+  const bf16* vlane = &lds.v[(4 * hi + (li >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (li & 3)];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -203,10 +196,16 @@ __device__ __forceinline__ void bf16_tile_compute(const Bf16Lds<D>& lds, const b
         lsum += pv;
         pb[e] = (bf16)pv;
       }
-      const bf16* vrow = &lds.vt[l32 * VS + 16 * (2 * b + u) + 8 * hi];
+      // A operand of O^T += V^T P^T: lane (l32, hi) needs V[key][32db + l32] for the 8 keys
+      // 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3} of block b (the key order of the S^T
+      // registers in pb).  Two transposed reads of 4 keys each: lane i of a 16-lane group
+      // points at V[key0 + i/4][dim0 + 4(i%4)].
+      const bf16* vrow = vlane + (32 * b + 16 * u) * VS;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 32 * db * VS);
+        const bf16x4 lo = lds_read_tr16(vrow + 32 * db);
+        const bf16x4 hi4 = lds_read_tr16(vrow + 32 * db + 8 * VS);
+        const bf16x8 a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
       }
     }
