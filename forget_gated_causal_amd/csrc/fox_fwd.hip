@@ -35,6 +35,8 @@
 // block-relative gate sum enters the scores.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fox_device.h"
 #include "fox_internal.h"
 
@@ -84,75 +86,136 @@ __device__ __forceinline__ void gate_tile(float* r2, double* r64, GateRows& rows
 // ------------------------------------------------------------------------------------------
 // bf16
 // ------------------------------------------------------------------------------------------
+// Staging geometry of the bf16 kernel.  Key tiles move global -> LDS with direct-to-LDS
+// buffer loads (buffer_load_dwordx4 ... lds): one wave instruction writes 1 KB of LDS, 16
+// bytes per lane, contiguously.  Rows are therefore unpadded, and bank spreading comes from an XOR
+// swizzle of the 16-byte chunks of each row, applied by choosing which global chunk each
+// lane fetches.
 template <int D, int NW>
-struct Bf16Tile {
-  static constexpr int KS = D + 8;  // K row stride in LDS (bf16): 16-byte pad, b128 row reads hit distinct banks
-  // V row stride in LDS (bf16): the transposed b64 reads of one half-wave touch 4 rows x 64
-  // bytes; a stride of 16 dwords (mod 64 banks) puts those rows on disjoint banks.
-  static constexpr int VS = (D == 32) ? D : D + 32;
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int GROUPS = D / 8;                 // 16-byte chunks per key row
-  static constexpr int KPT = kBC * GROUPS / THREADS;   // keys per thread in the tile loader
-  static_assert(KPT >= 1 && KPT * THREADS == kBC * GROUPS, "loader mapping");
-  u32x4 k[KPT];
-  u32x4 v[KPT];
+struct Bf16Geom {
+  static constexpr int BR = 32 * NW;         // query rows per workgroup
+  static constexpr int NS = (NW == 8) ? 3 : 2;  // LDS stages: tiles in flight = NS - 1
+  static constexpr int ROWB = 2 * D;         // bytes per key row
+  static constexpr int CH = D / 8;           // 16-byte chunks per row
+  static constexpr int RPO = 1024 / ROWB;    // key rows per 1 KB wave instruction
+  static constexpr int OPS = kBC * ROWB / 1024 / NW;  // wave instructions per wave for K (and for V)
+  static_assert(OPS >= 1 && OPS * NW * 1024 == kBC * ROWB, "staging mapping");
 };
 
+// Chunk swizzles.  K is read 16 bytes per lane by 16 consecutive rows at one logical
+// chunk: the swizzle gives those rows 16 distinct chunks of the 64 banks.  V is read by
+// the transposed b64 loads, 4 consecutive rows x 64 bytes per half-wave: the swizzle moves
+// the 4 rows onto disjoint 64-byte bank groups.
 template <int D>
-struct Bf16Stage {  // one staged key tile
-  bf16 k[kBC * (D + 8)];
-  bf16 v[kBC * ((D == 32) ? D : D + 32)];
-  float r2[kBC];  // R_j * log2(e)
-};
-
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 15;
+  else if constexpr (D == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
 template <int D>
-struct Bf16Lds {
-  Bf16Stage<D> st[2];  // double buffer: tile t is computed while tile t-1 is staged
-  GateRows rows;
-};
-
-template <int D, int NW>
-__device__ __forceinline__ void bf16_load_tile(Bf16Tile<D, NW>& t, const bf16* kb, const bf16* vb, int kt, int n,
-                                               int tid) {
-  constexpr int G = Bf16Tile<D, NW>::GROUPS, KPT = Bf16Tile<D, NW>::KPT;
-  const int c = tid % G, a = tid / G;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int key = kt * kBC + a * KPT + i;
-    if (key < n) {
-      t.k[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + 8 * c);
-      t.v[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + 8 * c);
-    } else {
-      t.k[i] = u32x4{0u, 0u, 0u, 0u};
-      t.v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return 4 * (row & 3);
+  else if constexpr (D == 64) return 4 * ((row >> 1) & 1);
+  else return 0;
 }
 
-// A complete tile (every key < n): no bounds checks.
-template <int D, int NW>
-__device__ __forceinline__ void bf16_load_full_tile(Bf16Tile<D, NW>& t, const bf16* kb, const bf16* vb, int kt,
-                                                    int tid) {
-  constexpr int G = Bf16Tile<D, NW>::GROUPS, KPT = Bf16Tile<D, NW>::KPT;
-  const int c = tid % G, a = tid / G;
-  const size_t off = (size_t)(kt * kBC + a * KPT) * D + 8 * c;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    t.k[i] = *reinterpret_cast<const u32x4*>(kb + off + (size_t)i * D);
-    t.v[i] = *reinterpret_cast<const u32x4*>(vb + off + (size_t)i * D);
-  }
+template <int D>
+struct alignas(1024) Bf16Stage {  // one staged key tile; 1 KB aligned so swizzled offsets XOR into the address
+  bf16 k[kBC * D];
+  bf16 v[kBC * D];
+  float lf[kBC];  // the tile's log gates, as loaded
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS byte address of a __shared__ object (address space 3 offset).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
 
+// Raw buffer resource (byte offsets, no stride) over num_bytes at p: loads at or past
+// num_bytes return zeros, which is how keys past n in the top tile are zero-filled.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* p, uint32_t num_bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  u32x4 r;
+  r[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = (uint32_t)__builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Direct-to-LDS buffer loads: lane l's bytes land at LDS address m0v + l * size.  Issued
+// through inline assembly so the compiler does not track them: the kernel waits for them
+// itself (s_waitcnt vmcnt with counts derived from its own issue order), which lets the
+// next tiles stay in flight across barriers and LDS reads of other stages.
+__device__ __forceinline__ void lds_dma16(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0v), "v"(voff), "s"(rsrc)
+                   : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0v), "v"(voff), "s"(rsrc)
+                   : "memory", "m0");
+}
+
+// Per-lane byte offsets, inside a tile, of the 16-byte chunks this lane stages for K and V.
 template <int D, int NW>
-__device__ __forceinline__ void bf16_store_tile(const Bf16Tile<D, NW>& t, Bf16Stage<D>& s, int tid) {
-  constexpr int G = Bf16Tile<D, NW>::GROUPS, KPT = Bf16Tile<D, NW>::KPT, KS = Bf16Tile<D, NW>::KS,
-                VS = Bf16Tile<D, NW>::VS;
-  const int c = tid % G, a = tid / G;
+struct StageOffsets {
+  int k[Bf16Geom<D, NW>::OPS];
+  int v[Bf16Geom<D, NW>::OPS];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane) {
+  using G = Bf16Geom<D, NW>;
+  StageOffsets<D, NW> so;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    *reinterpret_cast<u32x4*>(&s.k[(a * KPT + i) * KS + 8 * c]) = t.k[i];
-    *reinterpret_cast<u32x4*>(&s.v[(a * KPT + i) * VS + 8 * c]) = t.v[i];
+  for (int o = 0; o < G::OPS; ++o) {
+    const int g = wave * G::OPS + o;           // 1 KB slice of the tile
+    const int row = g * G::RPO + lane / G::CH;  // key row inside the tile
+    const int pc = lane % G::CH;                // physical chunk this lane fills
+    so.k[o] = (row * D + 8 * (pc ^ swz_k<D>(row))) * (int)sizeof(bf16);
+    so.v[o] = (row * D + 8 * (pc ^ swz_v<D>(row))) * (int)sizeof(bf16);
   }
+  return so;
+}
+
+// Issue this wave's loads of key tile t into stage `s`: 2 * OPS instructions, plus (wave 0)
+// one for the tile's 64 log gates.  Number of instructions issued, per wave, is what the
+// vmcnt waits below count.
+template <int D, int NW>
+__device__ __forceinline__ void bf16_stage_tile(Bf16Stage<D>& s, float* lf, u32x4 rk, u32x4 rv, u32x4 rl,
+                                                const StageOffsets<D, NW>& so, int t, int wave, int lane) {
+  using G = Bf16Geom<D, NW>;
+  const uint32_t tile_off = (uint32_t)(t * kBC * D * (int)sizeof(bf16));
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations are wave-uniform (M0)
+#pragma unroll
+  for (int o = 0; o < G::OPS; ++o) {
+    const int g = wv * G::OPS + o;
+    lds_dma16(lds_addr(&s.k[g * 512]), rk, tile_off + (uint32_t)so.k[o]);
+    lds_dma16(lds_addr(&s.v[g * 512]), rv, tile_off + (uint32_t)so.v[o]);
+  }
+  if (wv == 0) lds_dma4(lds_addr(lf), rl, (uint32_t)((t * kBC + lane) * (int)sizeof(float)));
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that does not drain outstanding global loads (a __syncthreads() would
+// wait for the in-flight prefetches); callers wait for exactly the loads they need first.
+__device__ __forceinline__ void barrier_lds() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0): gate / LDS writes done
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, output lane j element e is element j%4
@@ -162,23 +225,56 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+// Byte-offset access into a stage array, keeping the pointer's provenance (the compiler
+// needs to see which __shared__ object is read to not order it after unrelated loads).
+__device__ __forceinline__ bf16x8 lds_read_b128(const bf16* base, uint32_t byte_off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr16_at(const bf16* base, uint32_t byte_off) {
+  return lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+// Opaque copy: stops the compiler from hoisting per-stage address arithmetic out of the
+// tile loop (three stages' worth of addresses would not fit in registers).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// Per-lane LDS byte offsets inside a stage.  The swizzles only touch bits 5-7 (K) and 6-7
+// (V) of these offsets, so the operand of chunk step kk is at k ^ (kk << 5) and that of dim
+// block db at v ^ (db << 6); row offsets of later blocks / steps are multiples of 512 bytes
+// and are added on top.
+template <int D>
+struct LaneOffsets {
+  uint32_t k;  // K operand, chunk step 0, key row l32
+  uint32_t v;  // V operand, dim block 0, the lane's transposed-read row
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
+  LaneOffsets<D> off;
+  const int l32 = lane & 31, hi = lane >> 5, li = lane & 15, half = (lane >> 4) & 1;
+  off.k = (uint32_t)(2 * (l32 * D + 8 * (hi ^ swz_k<D>(l32))));
+  const int vrow = 4 * hi + (li >> 2);
+  const int dim = 16 * half + 4 * (li & 3);
+  off.v = (uint32_t)(2 * (vrow * D + 8 * ((dim >> 3) ^ swz_v<D>(vrow)) + (dim & 7)));
+  return off;
+}
+
 // Softmax and P.V for one 32-key block b of a tile, given its S^T accumulator: bias,
 // (causal mask), lazy rescale of the running state, p = exp2(s - m), O^T += V^T P^T.
 template <int D, bool DIAG>
-__device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, f32x16 sacc, int b,
+__device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, const float* r2s, uint32_t voff,
+                                                      f32x16 sacc, int b,
                                                       f32x16 (&oacc)[D / 32], float& m, float& lsum, int key0,
                                                       int my_row, int lane, float scale_log2) {
-  constexpr int VS = Bf16Tile<D, 4>::VS, DB = D / 32;
-  const int hi = lane >> 5, li = lane & 15;
-#if FOX_EXP_TREE
-  float gm[4];
-#else
+  constexpr int DB = D / 32;
+  const int hi = lane >> 5;
   float mx = kNegInf;
-#endif
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int kl = 32 * b + 8 * g + 4 * hi;
-    const f32x4 r2 = *reinterpret_cast<const f32x4*>(&st.r2[kl]);
+    const f32x4 r2 = *reinterpret_cast<const f32x4*>(&r2s[kl]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float sv = fmaf(sacc[4 * g + e], scale_log2, r2[e]);
@@ -186,17 +282,9 @@ __device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, f3
         if (key0 + kl + e > my_row) sv = kNegInf;
       }
       sacc[4 * g + e] = sv;
-#if !FOX_EXP_TREE
       mx = fmaxf(mx, sv);
-#endif
     }
-#if FOX_EXP_TREE
-    gm[g] = fmaxf(fmaxf(sacc[4 * g], sacc[4 * g + 1]), fmaxf(sacc[4 * g + 2], sacc[4 * g + 3]));
-#endif
   }
-#if FOX_EXP_TREE
-  float mx = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
-#endif
   mx = pair32_max(mx);
 
   const float mcand = fmaxf(m, mx);
@@ -215,31 +303,20 @@ __device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, f3
   // 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3} of block b (the key order of the S^T registers
   // in pb).  Two transposed reads of 4 keys each: lane i of a 16-lane group points at
   // V[key0 + i/4][dim0 + 4(i%4)].
-  const bf16* vlane = &st.v[(32 * b + 4 * hi + (li >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (li & 3)];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     bf16x8 pb;
-#if FOX_EXP_TREE
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = exp2_hw(sacc[8 * u + e] - msub);
-      pb[e] = (bf16)pv[e];
-    }
-    lsum += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-#else
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pv = exp2_hw(sacc[8 * u + e] - msub);
       lsum += pv;
       pb[e] = (bf16)pv;
     }
-#endif
-    const bf16* vrow = vlane + 16 * u * VS;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x4 lo = lds_read_tr16(vrow + 32 * db);
-      const bf16x4 hi4 = lds_read_tr16(vrow + 32 * db + 8 * VS);
+      const uint32_t va = (voff ^ (uint32_t)(db << 6)) + (uint32_t)(2 * (32 * b + 16 * u) * D);
+      const bf16x4 lo = lds_read_tr16_at(st.v, va);
+      const bf16x4 hi4 = lds_read_tr16_at(st.v, va + 16 * D);
       const bf16x8 a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
     }
@@ -249,38 +326,45 @@ __device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, f3
 // One 64-key tile for one wave: both S^T blocks on MFMA first, then block 0's softmax
 // (overlapping block 1's MFMAs) and P.V, then block 1's.
 template <int D, bool DIAG>
-__device__ __forceinline__ void bf16_tile_compute(const Bf16Stage<D>& st, const bf16x8 (&qreg)[D / 16],
-                                                  f32x16 (&oacc)[D / 32], float& m, float& lsum, int key0,
-                                                  int my_row, int lane, float scale_log2) {
-  constexpr int KS = Bf16Tile<D, 4>::KS, KK = D / 16;
-  const int l32 = lane & 31, hi = lane >> 5;
+__device__ __forceinline__ void bf16_tile_compute(const Bf16Stage<D>& st, const float* r2s, const LaneOffsets<D>& off,
+                                                  const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float& m,
+                                                  float& lsum, int key0, int my_row, int lane, float scale_log2) {
+  constexpr int KK = D / 16;
   f32x16 s0 = f32x16{}, s1 = f32x16{};
-  const bf16* k0 = &st.k[l32 * KS + 8 * hi];
-#if FOX_EXP_PRIO
-  __builtin_amdgcn_s_setprio(1);
-#endif
+  const uint32_t koff = off.k, voff = off.v;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(k0 + 16 * kk), qreg[kk], s0, 0,
-                                                 0, 0);
+  for (int kk = 0; kk < KK; ++kk) {
+    const uint32_t a = koff ^ (uint32_t)(kk << 5);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk], s1, 0, 0, 0);
+  }
+  // Keep only a few K operands in flight (each is 4 VGPRs): 4 LDS reads ahead, then
+  // alternate one MFMA and one read.
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(k0 + 32 * KS + 16 * kk),
-                                                 qreg[kk], s1, 0, 0, 0);
-#if FOX_EXP_PRIO
-  __builtin_amdgcn_s_setprio(0);
-#endif
-  bf16_block_softmax_pv<D, DIAG>(st, s0, 0, oacc, m, lsum, key0, my_row, lane, scale_log2);
-  bf16_block_softmax_pv<D, DIAG>(st, s1, 1, oacc, m, lsum, key0, my_row, lane, scale_log2);
+  for (int i = 0; i < 2 * KK - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  bf16_block_softmax_pv<D, DIAG>(st, r2s, voff, s0, 0, oacc, m, lsum, key0, my_row, lane, scale_log2);
+  bf16_block_softmax_pv<D, DIAG>(st, r2s, voff, s1, 1, oacc, m, lsum, key0, my_row, lane, scale_log2);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
-    float scale_log2) {
-  constexpr int KK = D / 16, DB = D / 32, BR = 32 * NW;
-  __shared__ Bf16Lds<D> lds;
+// Kernel body.  Tile kt is staged in stage (kt_hi - kt) % NS.  Every stage is its own
+// __shared__ object and the tile loop is unrolled by NS, so each LDS read and each
+// direct-to-LDS load names a statically known stage: the compiler then knows a load into
+// the stage being refilled cannot alias the stage being read, and does not drain the
+// prefetch before every read.
+template <int D, int NW, int NS>
+__device__ __forceinline__ void fwd_bf16_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1, Bf16Stage<D>& s2, float* g0,
+                                              float* g1, float* g2, GateRows& rows, const bf16* __restrict__ q,
+                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                              const float* __restrict__ logf, bf16* __restrict__ o,
+                                              float* __restrict__ lse, float* __restrict__ c_out, int n,
+                                              float scale_log2) {
+  using G = Bf16Geom<D, NW>;
+  constexpr int KK = D / 16, DB = D / 32, BR = G::BR;
 
   const int bh = blockIdx.x;
   const int qb = gridDim.y - 1 - blockIdx.y;
@@ -298,6 +382,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool active = wrow0 < n;
   const int kt_first = active ? min(wrow0 + 31, n - 1) / kBC : -1;
   const int my_row = wrow0 + l32;
+  const LaneOffsets<D> off = lane_offsets<D>(lane);
+  const StageOffsets<D, NW> so = stage_offsets<D, NW>(wave, lane);
+  const u32x4 rk = raw_rsrc(kb, (uint32_t)n * D * sizeof(bf16));
+  const u32x4 rv = raw_rsrc(vb, (uint32_t)n * D * sizeof(bf16));
+  const u32x4 rl = raw_rsrc(lfb, (uint32_t)n * sizeof(float));
+
+  auto stage = [&](auto J) -> Bf16Stage<D>& {
+    constexpr int j = decltype(J)::value % NS;
+    if constexpr (j == 0) return s0;
+    else if constexpr (j == 1) return s1;
+    else return s2;
+  };
+  auto gates = [&](auto J) -> float* {
+    constexpr int j = decltype(J)::value % NS;
+    if constexpr (j == 0) return g0;
+    else if constexpr (j == 1) return g1;
+    else return g2;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   bf16x8 qreg[KK];
 #pragma unroll
@@ -308,51 +412,78 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       qreg[kk] = bf16x8{};
   }
 
+  // Prologue: loads of the first NS-1 tiles (tile kt lives in stage (kt_hi - kt) % NS).
+  bf16_stage_tile<D, NW>(stage(I0{}), stage(I0{}).lf, rk, rv, rl, so, kt_hi, wave, lane);
+  if constexpr (NS == 3) {
+    if (kt_hi >= 1) bf16_stage_tile<D, NW>(stage(I1{}), stage(I1{}).lf, rk, rv, rl, so, kt_hi - 1, wave, lane);
+  }
+  wait_vmcnt<0>();  // Q (the only loads the compiler tracks) and the prologue tiles
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m = kNegInf, lsum = 0.0f;
   double carry = 0.0;
+  // Gate log f of key 63-lane of tile t from its stage (0 beyond ref).
+  auto gate_in = [&](const float* lf, int t) {
+    return (t * kBC + 63 - lane <= ref) ? lf[63 - lane] : 0.0f;
+  };
+  if (wave == 0) gate_tile(gates(I0{}), nullptr, rows, lane, kt_hi, row0, ref, gate_in(stage(I0{}).lf, kt_hi), carry);
 
-  // Prologue: stage the top tile (the only one that may run past n) into buffer 0 and
-  // start loading the next one.
-  Bf16Tile<D, NW> tile;
-  bf16_load_tile<D, NW>(tile, kb, vb, kt_hi, n, tid);
-  float lf = 0.0f;  // wave 0: log f of key 63-lane of the tile being staged
-  if (wave == 0) {
-    const int j = kt_hi * kBC + 63 - lane;
-    lf = (j <= ref) ? lfb[j] : 0.0f;
-  }
-  bf16_store_tile<D, NW>(tile, lds.st[0], tid);
-  if (wave == 0) gate_tile(lds.st[0].r2, nullptr, lds.rows, lane, kt_hi, row0, ref, lf, carry);
-  if (kt_hi > 0) {
-    bf16_load_full_tile<D, NW>(tile, kb, vb, kt_hi - 1, tid);
-    if (wave == 0) lf = lfb[(kt_hi - 1) * kBC + 63 - lane];
-  }
-
-  for (int kt = kt_hi; kt >= 0; --kt) {
-    const int cur = (kt_hi - kt) & 1;
-    // One barrier per tile: buffer `cur` is fully staged, and every wave is done with
-    // buffer cur^1 (tile kt+1), which is staged next.
-    __syncthreads();
-    if (kt > 0) {
-      bf16_store_tile<D, NW>(tile, lds.st[cur ^ 1], tid);
-      if (wave == 0) gate_tile(lds.st[cur ^ 1].r2, nullptr, lds.rows, lane, kt - 1, row0, ref, lf, carry);
-      if (kt > 1) {
-        bf16_load_full_tile<D, NW>(tile, kb, vb, kt - 2, tid);
-        if (wave == 0) lf = lfb[(kt - 2) * kBC + 63 - lane];
+  // One tile; J = position of the tile in the unrolled group, i.e. its stage.
+  auto step = [&](auto J, int kt) {
+    constexpr int j = decltype(J)::value;
+    // This wave's loads of tile kt are complete once at most the loads issued after them
+    // are outstanding: those of tile kt-1 when NS == 3 (2*OPS, plus the gate load in wave 0).
+    if constexpr (NS == 3) {
+      if (kt >= 1) {
+        if (wave == 0) wait_vmcnt<2 * G::OPS + 1>();
+        else wait_vmcnt<2 * G::OPS>();
+      } else {
+        wait_vmcnt<0>();
       }
+    } else {
+      wait_vmcnt<0>();
     }
-    if (!active || kt > kt_first) continue;
-    const int key0 = kt * kBC;
-    if (key0 + kBC - 1 > wrow0)
-      bf16_tile_compute<D, true>(lds.st[cur], qreg, oacc, m, lsum, key0, my_row, lane, scale_log2);
-    else
-      bf16_tile_compute<D, false>(lds.st[cur], qreg, oacc, m, lsum, key0, my_row, lane, scale_log2);
+    barrier_lds();  // tile kt staged by every wave; every wave is done with tile kt+1's stage
+    const int tn = kt - (NS - 1);
+    if (tn >= 0) {  // refill the stage of tile kt+1 with tile kt-NS+1
+      using JN = std::integral_constant<int, j + NS - 1>;
+      bf16_stage_tile<D, NW>(stage(JN{}), stage(JN{}).lf, rk, rv, rl, so, tn, wave, lane);
+    }
+    if (active && kt <= kt_first) {
+      const int key0 = kt * kBC;
+      if (key0 + kBC - 1 > wrow0)
+        bf16_tile_compute<D, true>(stage(J), gates(J), off, qreg, oacc, m, lsum, key0, my_row, lane, scale_log2);
+      else
+        bf16_tile_compute<D, false>(stage(J), gates(J), off, qreg, oacc, m, lsum, key0, my_row, lane, scale_log2);
+    }
+    // Wave 0: gate sums of tile kt-1 (read by everyone after the next barrier).  Its gate
+    // load is complete once at most the loads issued after it (tile kt-NS+1's, if any) remain.
+    if (wave == 0 && kt >= 1) {
+      if constexpr (NS == 3) {
+        if (tn >= 0) wait_vmcnt<2 * G::OPS + 1>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      using J1 = std::integral_constant<int, j + 1>;
+      gate_tile(gates(J1{}), nullptr, rows, lane, kt - 1, row0, ref, gate_in(stage(J1{}).lf, kt - 1), carry);
+    }
+  };
+
+  for (int kt = kt_hi; kt >= 0; kt -= NS) {
+    step(I0{}, kt);
+    if (kt - 1 < 0) break;
+    step(I1{}, kt - 1);
+    if constexpr (NS == 3) {
+      if (kt - 2 < 0) break;
+      step(std::integral_constant<int, 2>{}, kt - 2);
+    }
   }
 
   // ---- epilogue: O = acc / l, lse, c ---------------------------------------------------
-  __syncthreads();  // rows / cref written by wave 0 are visible (also when no tile was computed)
+  __syncthreads();  // rows / cref written by wave 0 are visible
   if (!active) return;
   const float ltot = pair32_sum(lsum);
   if (my_row >= n) return;
@@ -369,10 +500,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
   if (hi == 0) {
-    const double ri = lds.rows.rowR[my_row - row0];
+    const double ri = rows.rowR[my_row - row0];
     const size_t idx = (size_t)bh * n + my_row;
     if (lse) lse[idx] = (float)(((double)m + (double)log2_hw(ltot)) * kLn2d - ri);
-    if (c_out) c_out[idx] = (float)(lds.rows.cref - ri);
+    if (c_out) c_out[idx] = (float)(rows.cref - ri);
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
+    float scale_log2) {
+  constexpr int NS = Bf16Geom<D, NW>::NS;
+  __shared__ GateRows rows;
+  if constexpr (NS == 3) {
+    __shared__ Bf16Stage<D> s0, s1, s2;
+    __shared__ float g0[kBC], g1[kBC], g2[kBC];
+    fwd_bf16_body<D, NW, 3>(s0, s1, s2, g0, g1, g2, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
+  } else {
+    __shared__ Bf16Stage<D> s0, s1;
+    __shared__ float g0[kBC], g1[kBC];
+    fwd_bf16_body<D, NW, 2>(s0, s1, s0, g0, g1, g0, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
   }
 }
 
