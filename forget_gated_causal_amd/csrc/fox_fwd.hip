@@ -1,36 +1,41 @@
-// fox_fwd.hip -- K2: fused causal FoX attention forward on gfx950 MFMA.
+// fox_fwd.hip -- fused causal FoX attention forward on gfx950 MFMA.
 //
 // Definition (FoX module page, ForgettingAttention.forward, decoder mode;
 // foxwindow README, opening paragraph):
 //   s_ij = scale * q_i.k_j + sum_{t=j+1..i} log f_t  (j <= i),  softmax over j,  O_i = sum_j p_ij v_j.
 //
-// Work decomposition
-//   * One workgroup of NW waves (4 or 8) per (query block of 32*NW rows, batch*head).
-//     Wave w owns 32 query rows; the 8-wave form halves the K/V staging traffic per flop.  Grid x = batch*head (fastest, so the workgroups of one
-//     head land on one XCD when batch*head is a multiple of 8 and share its L2),
-//     grid y = query block, heaviest (last) blocks dispatched first.
-//   * Key tiles of 64 keys are visited from the diagonal tile DOWN to tile 0; tiles
-//     above the diagonal are never touched (their weights are exactly 0).  Walking
-//     backwards makes the first tile a row sees hold its largest gate bias, so the
-//     running max rarely moves and the lazy rescale below almost never fires.
-//   * Gate bias without a prefix-sum buffer: while walking backwards the loader keeps
-//     the fp64 suffix sum R_j = sum_{t=j+1..ref} log f_t (ref = the block's last row).
-//     Then c_i - c_j = R_j - R_i; the per-row constant R_i drops out of the softmax and
-//     is added back to lse only.  Each score costs one FMA: s2 = acc*scale*log2e + R_j*log2e.
-//     The block's own c_i = c_ref - R_i is written as the `c` output.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N), so a lane holds
-//     one query row and 16 keys per 32x32 block: the row max / sum are in-lane plus
-//     one permlane32 swap.  The S^T accumulator registers are, after rounding to bf16,
-//     directly the B operand of O^T = V^T P^T (the V operand follows the same key order).
-//   * K and V are staged row-major in LDS (padded rows).  The PV operand, which needs 8
-//     keys of one dim per lane, comes from gfx950's transposing LDS read
-//     (ds_read_b64_tr_b16), so no transposed stores.  Global loads of the next tile are
-//     issued before the current tile's MFMAs (register prefetch).
-//   * Online softmax in base 2 with lazy rescaling: the running max is only raised when
-//     a row's tile max exceeds it by more than kTau (exact: the final normalisation uses
-//     the same stale max; p stays <= 2^kTau).
+// Work decomposition (bf16)
+//   * One workgroup of NW waves (4 or 8) per (query block of 32*NW rows, batch*head); wave w
+//     owns 32 query rows.  Grid x = batch*head (fastest, so the workgroups of one head land
+//     on one XCD when batch*head is a multiple of 8 and share its L2), grid y = query block,
+//     heaviest (last) blocks dispatched first.  8-wave blocks stage each K/V tile for twice
+//     the rows; they are used when the grid still has two blocks per CU.
+//   * Key tiles of 64 keys are visited from the diagonal tile DOWN to tile 0; tiles above
+//     the diagonal are never touched (their weights are exactly 0).  Walking backwards makes
+//     the first tile a row sees hold its largest gate bias, so the running max rarely moves
+//     and the lazy rescale below almost never fires.
+//   * Gate bias without a prefix-sum buffer: while walking backwards one wave keeps the fp64
+//     suffix sum R_j = sum_{t=j+1..ref} log f_t (ref = the block's last row).  Then
+//     c_i - c_j = R_j - R_i; the per-row constant R_i drops out of the softmax and is added
+//     back to lse only.  Each score costs one FMA: s2 = acc*scale*log2e + R_j*log2e.  The
+//     block's own c_i = c_ref - R_i is written as the `c` output.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N), so a lane holds one
+//     query row and 16 keys per 32x32 block: the row max / sum are in-lane plus one
+//     permlane32 swap.  The S^T accumulator registers are, after rounding to bf16, directly
+//     the B operand of O^T = V^T P^T (the V operand follows the same key order).
+//   * K and V tiles move global -> LDS with direct-to-LDS buffer loads into a ring of four
+//     stages (XOR-swizzled rows, no padding).  The PV operand, which needs 8 keys of one dim
+//     per lane, comes from gfx950's transposing LDS read (ds_read_b64_tr_b16).
+//   * Each wave software-pipelines its tiles: the MFMAs of S for tile t run beside the
+//     exponentials of tile t+1, the MFMAs of O += V^T P^T for tile t+1 beside the scores and
+//     row max of tile t (MFMA and VALU work overlap only within one wave's instruction
+//     stream on this chip).
+//   * Online softmax in base 2 with lazy rescaling: the running max is only raised when a
+//     row's tile max exceeds it by more than kTau (exact: the final normalisation uses the
+//     same stale max; p stays <= 2^kTau).  The row sum adds the bf16-rounded p, the same
+//     weights the P.V products use.
 //
-// fp32 inputs use the same schedule with v_mfma_f32_32x32x2f32 and fp32 P; there the
+// fp32 inputs use a non-pipelined schedule with v_mfma_f32_32x32x2f32 and fp32 P; there the
 // bias R_j - R_i is formed per score in fp64 (kept in LDS), so no fp32 rounding of a
 // block-relative gate sum enters the scores.
 #include <math.h>
@@ -42,13 +47,6 @@
 
 namespace fox {
 namespace {
-
-#ifndef FOX_EXP_TREE
-#define FOX_EXP_TREE 0
-#endif
-#ifndef FOX_EXP_PRIO
-#define FOX_EXP_PRIO 0
-#endif
 
 constexpr int kThreads = 256;  // fp32 kernel; the bf16 kernel runs 64 * NW threads
 constexpr int kBR = 128;       // query rows per workgroup of the fp32 kernel (32 per wave)
@@ -94,7 +92,6 @@ __device__ __forceinline__ void gate_tile(float* r2, double* r64, GateRows& rows
 template <int D, int NW>
 struct Bf16Geom {
   static constexpr int BR = 32 * NW;         // query rows per workgroup
-  static constexpr int NS = (NW == 8) ? 3 : 2;  // LDS stages: tiles in flight = NS - 1
   static constexpr int ROWB = 2 * D;         // bytes per key row
   static constexpr int CH = D / 8;           // 16-byte chunks per row
   static constexpr int RPO = 1024 / ROWB;    // key rows per 1 KB wave instruction
@@ -233,12 +230,6 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const bf16* base, uint32_t byte_
 __device__ __forceinline__ bf16x4 lds_read_tr16_at(const bf16* base, uint32_t byte_off) {
   return lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off));
 }
-// Opaque copy: stops the compiler from hoisting per-stage address arithmetic out of the
-// tile loop (three stages' worth of addresses would not fit in registers).
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  __asm__ volatile("" : "+v"(x));
-  return x;
-}
 
 // Per-lane LDS byte offsets inside a stage.  The swizzles only touch bits 5-7 (K) and 6-7
 // (V) of these offsets, so the operand of chunk step kk is at k ^ (kk << 5) and that of dim
@@ -261,32 +252,68 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
   return off;
 }
 
-// Softmax and P.V for one 32-key block b of a tile, given its S^T accumulator: bias,
-// (causal mask), lazy rescale of the running state, p = exp2(s - m), O^T += V^T P^T.
-template <int D, bool DIAG>
-__device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, const float* r2s, uint32_t voff,
-                                                      f32x16 sacc, int b,
-                                                      f32x16 (&oacc)[D / 32], float& m, float& lsum, int key0,
-                                                      int my_row, int lane, float scale_log2) {
-  constexpr int DB = D / 32;
-  const int hi = lane >> 5;
+// ------------------------------------------------------------------------------------------
+// bf16, software-pipelined form
+// ------------------------------------------------------------------------------------------
+// On gfx950 an MFMA and VALU work overlap when both come from the same wave and the VALU
+// instructions sit between the MFMAs of its instruction stream; a wave that only issues
+// MFMAs leaves the VALU idle even when the other wave of the SIMD has softmax work.  So each
+// wave runs its own two-stage pipeline over key tiles: while the MFMAs of S(t) = K_t Q^T
+// execute, the wave computes the probabilities of tile t+1 (the previous tile in visiting
+// order); while the MFMAs of O += V_{t+1}^T P^T execute, it forms the biased scores and the
+// row max of tile t.  Four LDS stages hold tile t+1 (V still read), tile t, and the two
+// tiles in flight.
+
+template <int D>
+struct PipeGeom {
+  static constexpr int KK = D / 16;  // MFMA k-steps of S (16 dims each)
+  static constexpr int DB = D / 32;  // 32-dim output blocks of O
+};
+
+// S^T of one tile: s[b] = K[32b .. 32b+31] Q^T (32 keys x 32 queries per block).
+template <int D>
+__device__ __forceinline__ void pipe_qk(const Bf16Stage<D>& st, uint32_t koff, const bf16x8 (&qreg)[D / 16],
+                                        f32x16 (&s)[2]) {
+  constexpr int KK = PipeGeom<D>::KK;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const uint32_t a = koff ^ (uint32_t)(kk << 5);
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk], s[1], 0, 0, 0);
+  }
+}
+
+// Biased base-2 scores of a tile, in place: s = acc * scale * log2 e + R_j * log2 e, with
+// the causal mask on the diagonal tile.  Returns the tile's row max (both lanes of a row).
+template <bool DIAG>
+__device__ __forceinline__ float pipe_scores(f32x16 (&s)[2], const float* r2s, int key0, int my_row, int hi,
+                                             float scale_log2) {
   float mx = kNegInf;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int kl = 32 * b + 8 * g + 4 * hi;
-    const f32x4 r2 = *reinterpret_cast<const f32x4*>(&r2s[kl]);
+  for (int b = 0; b < 2; ++b) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float sv = fmaf(sacc[4 * g + e], scale_log2, r2[e]);
-      if constexpr (DIAG) {
-        if (key0 + kl + e > my_row) sv = kNegInf;
+    for (int g = 0; g < 4; ++g) {
+      const int kl = 32 * b + 8 * g + 4 * hi;
+      const f32x4 r2 = *reinterpret_cast<const f32x4*>(&r2s[kl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sv = fmaf(s[b][4 * g + e], scale_log2, r2[e]);
+        if constexpr (DIAG) {
+          if (key0 + kl + e > my_row) sv = kNegInf;
+        }
+        s[b][4 * g + e] = sv;
+        mx = fmaxf(mx, sv);
       }
-      sacc[4 * g + e] = sv;
-      mx = fmaxf(mx, sv);
     }
   }
-  mx = pair32_max(mx);
+  return pair32_max(mx);
+}
 
+// Lazy rescale: raise the running max only when the tile max exceeds it by more than kTau.
+template <int DB>
+__device__ __forceinline__ void pipe_rescale(float mx, float& m, float& lsum, f32x16 (&oacc)[DB]) {
   const float mcand = fmaxf(m, mx);
   const bool need = mcand > m + kTau;
   if (wave_any(need)) {
@@ -297,72 +324,165 @@ __device__ __forceinline__ void bf16_block_softmax_pv(const Bf16Stage<D>& st, co
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     m = mn;
   }
-  const float msub = (m == kNegInf) ? 0.0f : m;
+}
 
-  // A operand of O^T += V^T P^T: lane (l32, hi) needs V[key][32db + l32] for the 8 keys
-  // 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3} of block b (the key order of the S^T registers
-  // in pb).  Two transposed reads of 4 keys each: lane i of a 16-lane group points at
-  // V[key0 + i/4][dim0 + 4(i%4)].
+// p = exp2(s - m) rounded to bf16, in the key order of the S^T registers: p[2b+u] holds
+// keys 32b + 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3}, the B operand of O^T += V^T P^T.
+__device__ __forceinline__ void pipe_probs(const f32x16 (&s)[2], float m, bf16x8 (&p)[4]) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    bf16x8 pb;
+  for (int b = 0; b < 2; ++b) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pv = exp2_hw(sacc[8 * u + e] - msub);
-      lsum += pv;
-      pb[e] = (bf16)pv;
-    }
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint32_t va = (voff ^ (uint32_t)(db << 6)) + (uint32_t)(2 * (32 * b + 16 * u) * D);
-      const bf16x4 lo = lds_read_tr16_at(st.v, va);
-      const bf16x4 hi4 = lds_read_tr16_at(st.v, va + 16 * D);
-      const bf16x8 a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+      for (int e = 0; e < 8; ++e) p[2 * b + u][e] = (bf16)exp2_hw(s[b][8 * u + e] - m);
     }
   }
 }
 
-// One 64-key tile for one wave: both S^T blocks on MFMA first, then block 0's softmax
-// (overlapping block 1's MFMAs) and P.V, then block 1's.
-template <int D, bool DIAG>
-__device__ __forceinline__ void bf16_tile_compute(const Bf16Stage<D>& st, const float* r2s, const LaneOffsets<D>& off,
-                                                  const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float& m,
-                                                  float& lsum, int key0, int my_row, int lane, float scale_log2) {
-  constexpr int KK = D / 16;
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
-  const uint32_t koff = off.k, voff = off.v;
+// Row-sum of the rounded probabilities (the weights the P.V products actually use).
+__device__ __forceinline__ float pipe_psum(const bf16x8 (&p)[4], float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float a0 = acc, a1 = 0.0f;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const uint32_t a = koff ^ (uint32_t)(kk << 5);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk], s1, 0, 0, 0);
-  }
-  // Keep only a few K operands in flight (each is 4 VGPRs): 4 LDS reads ahead, then
-  // alternate one MFMA and one read.
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-  for (int i = 0; i < 2 * KK - 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 pr = {p[i][2 * w], p[i][2 * w + 1]};
+      if (w & 1) a1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, a1, false);
+      else a0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, a0, false);
+    }
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  bf16_block_softmax_pv<D, DIAG>(st, r2s, voff, s0, 0, oacc, m, lsum, key0, my_row, lane, scale_log2);
-  bf16_block_softmax_pv<D, DIAG>(st, r2s, voff, s1, 1, oacc, m, lsum, key0, my_row, lane, scale_log2);
+  return a0 + a1;
 }
 
-// Kernel body.  Tile kt is staged in stage (kt_hi - kt) % NS.  Every stage is its own
-// __shared__ object and the tile loop is unrolled by NS, so each LDS read and each
-// direct-to-LDS load names a statically known stage: the compiler then knows a load into
-// the stage being refilled cannot alias the stage being read, and does not drain the
-// prefetch before every read.
-template <int D, int NW, int NS>
-__device__ __forceinline__ void fwd_bf16_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1, Bf16Stage<D>& s2, float* g0,
-                                              float* g1, float* g2, GateRows& rows, const bf16* __restrict__ q,
+// O^T += V^T P^T over one tile.  The V operand of lane (l32, hi) is V[key][32db + l32] for
+// the 8 keys of p[2b+u]: two transposed reads of 4 keys each (lane i of a 16-lane group
+// points at V[key0 + i/4][dim0 + 4(i%4)]).
+template <int D>
+__device__ __forceinline__ void pipe_pv(const Bf16Stage<D>& st, uint32_t voff, const bf16x8 (&p)[4],
+                                        f32x16 (&oacc)[D / 32]) {
+  constexpr int DB = PipeGeom<D>::DB;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t va = (voff ^ (uint32_t)(db << 6)) + (uint32_t)(2 * (32 * b + 16 * u) * D);
+        const bf16x4 lo = lds_read_tr16_at(st.v, va);
+        const bf16x4 hi4 = lds_read_tr16_at(st.v, va + 16 * D);
+        const bf16x8 a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[2 * b + u], oacc[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Steady state, one tile: S(cur) = K_cur Q^T and O += V_prev^T P(prev)^T on MFMA, with the
+// softmax of both tiles between them.  The schedule is explicit: each slot holds one MFMA,
+// the LDS reads a few slots ahead of their use, and a share of the VALU work that does
+// not depend on in-flight MFMAs; sched_barrier keeps the compiler from regrouping slots.
+//   S slots (2*KK):  MFMA of S(cur); p = exp2(s - m) for 32/(2*KK) scores of prev.
+//   PV slots (4*DB): MFMA of O += V^T P^T; bf16 packing and row sum of P(prev); biased
+//                    scores and row max of cur (block 0 first: its MFMAs finished earlier).
+template <int D>
+__device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float* r2cur, const Bf16Stage<D>& prev,
+                                            const LaneOffsets<D>& off, const bf16x8 (&qreg)[D / 16],
+                                            f32x16 (&sp)[2], f32x16 (&sc)[2], f32x16 (&oacc)[D / 32],
+                                            float& m, float& lsum, int hi, float scale_log2) {
+  constexpr int KK = PipeGeom<D>::KK, DB = PipeGeom<D>::DB;
+  constexpr int NQ = 2 * KK;   // S MFMAs
+  constexpr int NP = 4 * DB;   // P.V MFMAs
+  constexpr int PFK = NQ >= 6 ? 4 : NQ - 2;  // K operands in flight
+  constexpr int PFV = NP >= 4 ? 4 : NP;      // V operands in flight
+  constexpr int RD = 3;         // slots between loading a gate-bias quad and its first use
+  constexpr int EQ = 32 / NQ;  // exponentials per S slot
+  constexpr int EP = 32 / NP;  // scores per P.V slot
+  static_assert(NQ >= PFK + 2 && NQ >= PFV && NP >= PFV && 32 % NQ == 0 && 32 % NP == 0, "slot shares");
+
+  bf16x8 kop[NQ];
+  bf16x8 vop[NP];
+  f32x4 r2[8];
+  bf16x8 p[4];
+  auto kread = [&](int i) -> bf16x8 {
+    return lds_read_b128(cur.k, (off.k ^ (uint32_t)((i >> 1) << 5)) + (uint32_t)((i & 1) * 64 * D));
+  };
+  auto vread = [&](int i) -> bf16x8 {
+    const int pi = i / DB, db = i % DB, b = pi >> 1, u = pi & 1;
+    const uint32_t va = (off.v ^ (uint32_t)(db << 6)) + (uint32_t)(2 * (32 * b + 16 * u) * D);
+    const bf16x4 lo = lds_read_tr16_at(prev.v, va);
+    const bf16x4 hi4 = lds_read_tr16_at(prev.v, va + 16 * D);
+    return __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto pack = [&](int pi) {
+    const int b = pi >> 1, u = pi & 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[pi][e] = (bf16)sp[b][8 * u + e];
+  };
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float ls0 = lsum, ls1 = 0.0f;
+  float mx0 = kNegInf, mx1 = kNegInf;
+
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < PFK; ++i) kop[i] = kread(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int b = i & 1, kk = i >> 1;
+    if (kk == 0)
+      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], f32x16{}, 0, 0, 0);
+    else
+      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], sc[b], 0, 0, 0);
+    if (i + PFK < NQ) kop[i + PFK] = kread(i + PFK);
+    if (i >= NQ - PFV) vop[i - (NQ - PFV)] = vread(i - (NQ - PFV));  // first V operands of the P.V slots
+#pragma unroll
+    for (int kq = 0; kq < 8; ++kq)  // bias quads needed in the first P.V slots
+      if ((4 * kq) / EP - RD + NQ == i) r2[kq] = *reinterpret_cast<const f32x4*>(&r2cur[8 * kq + 4 * hi]);
+#pragma unroll
+    for (int e = i * EQ; e < (i + 1) * EQ; ++e) sp[e >> 4][e & 15] = exp2_hw(sp[e >> 4][e & 15] - m);
+    if (i == NQ - 1) pack(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pi = i / DB, db = i % DB;
+    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], p[pi], oacc[db], 0, 0, 0);
+    if (i + PFV < NP) vop[i + PFV] = vread(i + PFV);
+#pragma unroll
+    for (int kq = 0; kq < 8; ++kq)
+      if ((4 * kq) / EP - RD == i) r2[kq] = *reinterpret_cast<const f32x4*>(&r2cur[8 * kq + 4 * hi]);
+    if (db == DB - 1 && pi < 3) pack(pi + 1);
+    // row sum: the 4 words of p[pi] over the DB slots of pi
+#pragma unroll
+    for (int w = db * 4 / DB; w < (db + 1) * 4 / DB; ++w) {
+      const bf16x2 pr = {p[pi][2 * w], p[pi][2 * w + 1]};
+      if (w & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls1, false);
+      else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls0, false);
+    }
+#pragma unroll
+    for (int e = i * EP; e < (i + 1) * EP; ++e) {
+      const int b = e >> 4, r = e & 15;
+      const float sv = fmaf(sc[b][r], scale_log2, r2[4 * b + (r >> 2)][r & 3]);
+      sc[b][r] = sv;
+      if (e & 1) mx1 = fmaxf(mx1, sv);
+      else mx0 = fmaxf(mx0, sv);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lsum = ls0 + ls1;
+  pipe_rescale<DB>(pair32_max(fmaxf(mx0, mx1)), m, lsum, oacc);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1, Bf16Stage<D>& s2,
+                                              Bf16Stage<D>& s3, float* g0, float* g1, float* g2, float* g3,
+                                              GateRows& rows, const bf16* __restrict__ q,
                                               const bf16* __restrict__ k, const bf16* __restrict__ v,
                                               const float* __restrict__ logf, bf16* __restrict__ o,
                                               float* __restrict__ lse, float* __restrict__ c_out, int n,
                                               float scale_log2) {
+  constexpr int NS = 4;  // LDS stages: tile t+1 (V still read), tile t, two tiles in flight
   using G = Bf16Geom<D, NW>;
   constexpr int KK = D / 16, DB = D / 32, BR = G::BR;
 
@@ -392,13 +512,15 @@ __device__ __forceinline__ void fwd_bf16_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
     constexpr int j = decltype(J)::value % NS;
     if constexpr (j == 0) return s0;
     else if constexpr (j == 1) return s1;
-    else return s2;
+    else if constexpr (j == 2) return s2;
+    else return s3;
   };
   auto gates = [&](auto J) -> float* {
     constexpr int j = decltype(J)::value % NS;
     if constexpr (j == 0) return g0;
     else if constexpr (j == 1) return g1;
-    else return g2;
+    else if constexpr (j == 2) return g2;
+    else return g3;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -412,62 +534,60 @@ __device__ __forceinline__ void fwd_bf16_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
       qreg[kk] = bf16x8{};
   }
 
-  // Prologue: loads of the first NS-1 tiles (tile kt lives in stage (kt_hi - kt) % NS).
+  // Prologue: tiles kt_hi and kt_hi-1 (tile kt lives in stage (kt_hi - kt) % 4; the tile
+  // loop issues tile kt-2 while computing tile kt).
   bf16_stage_tile<D, NW>(stage(I0{}), stage(I0{}).lf, rk, rv, rl, so, kt_hi, wave, lane);
-  if constexpr (NS == 3) {
-    if (kt_hi >= 1) bf16_stage_tile<D, NW>(stage(I1{}), stage(I1{}).lf, rk, rv, rl, so, kt_hi - 1, wave, lane);
-  }
-  wait_vmcnt<0>();  // Q (the only loads the compiler tracks) and the prologue tiles
+  if (kt_hi >= 1) bf16_stage_tile<D, NW>(stage(I1{}), stage(I1{}).lf, rk, rv, rl, so, kt_hi - 1, wave, lane);
+  wait_vmcnt<0>();
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  f32x16 sa[2], sb[2];  // scores of the tiles at even / odd loop positions
+  sa[0] = sa[1] = sb[0] = sb[1] = f32x16{};
   float m = kNegInf, lsum = 0.0f;
   double carry = 0.0;
-  // Gate log f of key 63-lane of tile t from its stage (0 beyond ref).
   auto gate_in = [&](const float* lf, int t) {
     return (t * kBC + 63 - lane <= ref) ? lf[63 - lane] : 0.0f;
   };
   if (wave == 0) gate_tile(gates(I0{}), nullptr, rows, lane, kt_hi, row0, ref, gate_in(stage(I0{}).lf, kt_hi), carry);
 
-  // One tile; J = position of the tile in the unrolled group, i.e. its stage.
   auto step = [&](auto J, int kt) {
     constexpr int j = decltype(J)::value;
-    // This wave's loads of tile kt are complete once at most the loads issued after them
-    // are outstanding: those of tile kt-1 when NS == 3 (2*OPS, plus the gate load in wave 0).
-    if constexpr (NS == 3) {
-      if (kt >= 1) {
-        if (wave == 0) wait_vmcnt<2 * G::OPS + 1>();
-        else wait_vmcnt<2 * G::OPS>();
-      } else {
-        wait_vmcnt<0>();
-      }
+    using JP = std::integral_constant<int, j + NS - 1>;  // position of tile kt+1
+    using JN = std::integral_constant<int, j + 2>;       // position of tiles kt+2 / kt-2
+    using J1 = std::integral_constant<int, j + 1>;       // position of tile kt-1
+    f32x16(&sc)[2] = (j & 1) ? sb : sa;
+    f32x16(&sp)[2] = (j & 1) ? sa : sb;
+    // Own loads of tile kt are complete once at most those of tile kt-1 remain.
+    if (kt >= 1) {
+      if (wave == 0) wait_vmcnt<2 * G::OPS + 1>();
+      else wait_vmcnt<2 * G::OPS>();
     } else {
       wait_vmcnt<0>();
     }
-    barrier_lds();  // tile kt staged by every wave; every wave is done with tile kt+1's stage
-    const int tn = kt - (NS - 1);
-    if (tn >= 0) {  // refill the stage of tile kt+1 with tile kt-NS+1
-      using JN = std::integral_constant<int, j + NS - 1>;
-      bf16_stage_tile<D, NW>(stage(JN{}), stage(JN{}).lf, rk, rv, rl, so, tn, wave, lane);
-    }
+    barrier_lds();  // tile kt and its gate sums visible; every wave is done with tile kt+2's stage
+    if (kt >= 2) bf16_stage_tile<D, NW>(stage(JN{}), stage(JN{}).lf, rk, rv, rl, so, kt - 2, wave, lane);
     if (active && kt <= kt_first) {
-      const int key0 = kt * kBC;
-      if (key0 + kBC - 1 > wrow0)
-        bf16_tile_compute<D, true>(stage(J), gates(J), off, qreg, oacc, m, lsum, key0, my_row, lane, scale_log2);
-      else
-        bf16_tile_compute<D, false>(stage(J), gates(J), off, qreg, oacc, m, lsum, key0, my_row, lane, scale_log2);
-    }
-    // Wave 0: gate sums of tile kt-1 (read by everyone after the next barrier).  Its gate
-    // load is complete once at most the loads issued after it (tile kt-NS+1's, if any) remain.
-    if (wave == 0 && kt >= 1) {
-      if constexpr (NS == 3) {
-        if (tn >= 0) wait_vmcnt<2 * G::OPS + 1>();
-        else wait_vmcnt<0>();
+      if (kt == kt_first) {  // first tile of this wave: the diagonal tile, nothing to overlap with
+        pipe_qk<D>(stage(J), off.k, qreg, sc);
+        const float mx = pipe_scores<true>(sc, gates(J), kt * kBC, my_row, hi, scale_log2);
+        pipe_rescale<DB>(mx, m, lsum, oacc);
       } else {
-        wait_vmcnt<0>();
+        pipe_steady<D>(stage(J), gates(J), stage(JP{}), off, qreg, sp, sc, oacc, m, lsum, hi, scale_log2);
       }
-      using J1 = std::integral_constant<int, j + 1>;
+      if (kt == 0) {  // drain: probabilities and P.V of tile 0
+        bf16x8 p[4];
+        pipe_probs(sc, m, p);
+        pipe_pv<D>(stage(J), off.v, p, oacc);
+        lsum = pipe_psum(p, lsum);
+      }
+    }
+    // Wave 0: gate sums of tile kt-1 (read after the next barrier).  Its gate load is
+    // complete once at most the loads issued after it (tile kt-2's, if any) remain.
+    if (wave == 0 && kt >= 1) {
+      if (kt >= 2) wait_vmcnt<2 * G::OPS + 1>();
+      else wait_vmcnt<0>();
       gate_tile(gates(J1{}), nullptr, rows, lane, kt - 1, row0, ref, gate_in(stage(J1{}).lf, kt - 1), carry);
     }
   };
@@ -476,10 +596,10 @@ __device__ __forceinline__ void fwd_bf16_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
     step(I0{}, kt);
     if (kt - 1 < 0) break;
     step(I1{}, kt - 1);
-    if constexpr (NS == 3) {
-      if (kt - 2 < 0) break;
-      step(std::integral_constant<int, 2>{}, kt - 2);
-    }
+    if (kt - 2 < 0) break;
+    step(std::integral_constant<int, 2>{}, kt - 2);
+    if (kt - 3 < 0) break;
+    step(std::integral_constant<int, 3>{}, kt - 3);
   }
 
   // ---- epilogue: O = acc / l, lse, c ---------------------------------------------------
@@ -508,21 +628,14 @@ __device__ __forceinline__ void fwd_bf16_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
     float scale_log2) {
-  constexpr int NS = Bf16Geom<D, NW>::NS;
   __shared__ GateRows rows;
-  if constexpr (NS == 3) {
-    __shared__ Bf16Stage<D> s0, s1, s2;
-    __shared__ float g0[kBC], g1[kBC], g2[kBC];
-    fwd_bf16_body<D, NW, 3>(s0, s1, s2, g0, g1, g2, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
-  } else {
-    __shared__ Bf16Stage<D> s0, s1;
-    __shared__ float g0[kBC], g1[kBC];
-    fwd_bf16_body<D, NW, 2>(s0, s1, s0, g0, g1, g0, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
-  }
+  __shared__ Bf16Stage<D> s0, s1, s2, s3;
+  __shared__ float g0[kBC], g1[kBC], g2[kBC], g3[kBC];
+  fwd_pipe_body<D, NW>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -725,20 +838,17 @@ hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t blocks256 = bh * (int64_t)((n + 255) / 256);
-    bool big = false;
     if constexpr (D >= 64) {
       if (blocks256 >= 2 * (int64_t)cus) {
-        big = true;
         const dim3 grid((unsigned)bh, (unsigned)((n + 255) / 256));
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), grid, dim3(512), 0, stream, (const bf16*)q, (const bf16*)k,
+        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8>), grid, dim3(512), 0, stream, (const bf16*)q, (const bf16*)k,
                            (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+        return hipGetLastError();
       }
     }
-    if (!big) {
-      const dim3 grid((unsigned)bh, (unsigned)((n + 127) / 128));
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), grid, dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
-    }
+    const dim3 grid((unsigned)bh, (unsigned)((n + 127) / 128));
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4>), grid, dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
     hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
