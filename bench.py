@@ -10,10 +10,12 @@ The headline workload is the bf16 forward B=4 H=12 N=1024 d=64; the JSON line
 also carries the long forward workloads and the decode workload (the metric
 quotes prefill TFLOP/s and decode GB/s) unless --only is given.
 
-Timing: W untimed warm-up steps, then K steps between two HIP events on the
-stream the library launches on (torch's current stream), bracketed by
-synchronisation.  Per-launch event pairs over the same number of calls give the
-dominant kernel's average launch duration for the roofline object.
+Timing: W untimed warm-up steps, then K back-to-back steps between two HIP events
+on the stream the library launches on (torch's current stream), bracketed by
+synchronisation.  A forward step is exactly one kernel launch, so the region time
+over K is also that kernel's average launch duration, which the roofline object
+uses (per-launch event pairs would add their own overhead to a 25 us kernel); a
+decode step is its split kernel plus the small combine kernel.
 
 Algorithmic work (what the method must do, not what the kernel happens to do):
   forward: 4*d flop per causal pair, n(n+1)/2 pairs per (batch, head);
@@ -52,7 +54,7 @@ def decode_bytes(cfg) -> dict:
 
 
 def _events_time(torch, fn, k):
-    """Whole-region time (ms) of k back-to-back calls, and the mean of k per-call event pairs (ms)."""
+    """Time (ms) of k back-to-back calls between two events on the launch stream."""
     st = torch.cuda.current_stream()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -61,15 +63,16 @@ def _events_time(torch, fn, k):
         fn()
     e1.record(st)
     torch.cuda.synchronize()
-    region = e0.elapsed_time(e1)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
-    for a, b in pairs:
-        a.record(st)
-        fn()
-        b.record(st)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in pairs)
-    return region, sum(per) / len(per), per[len(per) // 2]
+    return e0.elapsed_time(e1)
+
+
+def fwd_kernel_name(torch, cfg) -> str:
+    """The kernel fox_attn_fwd launches for this shape (same rule as the library's dispatch)."""
+    if cfg.dtype != "bf16":
+        return f"fwd_f32_kernel<{cfg.d}>"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nw = 8 if cfg.d >= 64 and cfg.B * cfg.H * ((cfg.N + 255) // 256) >= 2 * cus else 4
+    return f"fwd_bf16_pipe_kernel<{cfg.d},{nw}>"
 
 
 def bench_fwd(torch, fox, fi, tag, steps, warmup):
@@ -83,15 +86,15 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup):
     fn = lambda: fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
     for _ in range(warmup):
         fn()
-    region, mean_launch, med_launch = _events_time(torch, fn, steps)
+    region = _events_time(torch, fn, steps)
     flops = fwd_flops(cfg)
     ms = region / steps
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = flops / (mean_launch * 1e-3) / 1e12
+    achieved = flops / (ms * 1e-3) / 1e12
     return {
         "cfg": cfg, "inp": inp,
         "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-        "kernel": f"fwd_{cfg.dtype}_kernel<{cfg.d}>", "launch_ms_mean": mean_launch, "launch_ms_median": med_launch,
+        "kernel": fwd_kernel_name(torch, cfg), "launch_ms_mean": ms,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None},
         "flop_per_launch": flops,
@@ -116,10 +119,10 @@ def bench_decode(torch, fox, fi, tag, steps, warmup):
     fn = lambda: fox.attn_decode(q, kc, vc, cc, lnew, scale=inp["scale"], out=o, lse=lse, workspace=ws)  # noqa
     for _ in range(warmup):
         fn()
-    region, mean_launch, med_launch = _events_time(torch, fn, steps)
+    region = _events_time(torch, fn, steps)
     by = decode_bytes(cfg)
     ms = region / steps
-    achieved = by["total"] / (mean_launch * 1e-3) / 1e9
+    achieved = by["total"] / (ms * 1e-3) / 1e9
     res = {
         "workload": cfg.desc, "ms_per_step": round(ms, 4), "value": round(by["total"] / (ms * 1e-3) / 1e9, 1),
         "unit": "GB/s", "bytes_per_step": by["total"],
@@ -188,8 +191,8 @@ def cpu_baseline_decode(inp, cfg, budget_s=8.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the selected workload only")
@@ -225,8 +228,8 @@ def main():
 
     r = bench_fwd(torch, fox, fi, args.workload, args.steps, args.warmup)
     cfg = r["cfg"]
-    print(f"# {cfg.desc}: {r['ms_per_step']*1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s, "
-          f"kernel mean {r['launch_ms_mean']*1e3:.1f} us", file=sys.stderr, flush=True)
+    print(f"# {cfg.desc}: {r['ms_per_step']*1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s, {r['kernel']}",
+          file=sys.stderr, flush=True)
     line.update({
         "value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 5),
         "dtype": cfg.dtype,
@@ -245,7 +248,8 @@ def main():
             print(f"# {x['cfg'].desc}: {x['ms_per_step']*1e3:.1f} us/step, {x['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             others[tag] = {"workload": x["cfg"].desc, "value": round(x["tflops"], 2), "unit": "TFLOP/s",
-                           "ms_per_step": round(x["ms_per_step"], 4), "roofline": x["roofline"]}
+                           "ms_per_step": round(x["ms_per_step"], 4),
+                           "roofline": dict(x["roofline"], kernel=x["kernel"])}
             del x
             torch.cuda.empty_cache()
         dec, _ = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))
