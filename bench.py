@@ -71,8 +71,12 @@ def fwd_kernel_name(torch, cfg) -> str:
     if cfg.dtype != "bf16":
         return f"fwd_f32_kernel<{cfg.d}>"
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    nw = 8 if cfg.d >= 64 and cfg.B * cfg.H * ((cfg.N + 255) // 256) >= 2 * cus else 4
-    return f"fwd_bf16_pipe_kernel<{cfg.d},{nw}>"
+    bh = cfg.B * cfg.H
+    if cfg.d >= 64 and bh * ((cfg.N + 255) // 256) >= 2 * cus:
+        return f"fwd_bf16_pipe_kernel<{cfg.d},8,1>"
+    if cfg.d <= 64 and bh * ((cfg.N + 127) // 128) < 2 * cus:
+        return f"fwd_bf16_pipe_kernel<{cfg.d},4,2>"
+    return f"fwd_bf16_pipe_kernel<{cfg.d},4,1>"
 
 
 def bench_fwd(torch, fox, fi, tag, steps, warmup):

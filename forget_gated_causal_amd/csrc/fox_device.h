@@ -58,6 +58,14 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Opaque copy of a per-lane value: address arithmetic derived from it cannot be hoisted out
+// of the loop that makes the copy (a kernel unrolled over four LDS stages would otherwise
+// keep four stages' worth of addresses live in VGPRs).
+__device__ __forceinline__ int opaque_lane(int x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
 // Wave-uniform "any lane" vote.
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 
@@ -93,14 +101,25 @@ __device__ __forceinline__ double dpp_or_zero(double v) {
   return __builtin_bit_cast(double, r);
 }
 
+// Step k (1..7) of the inclusive scan below, on (x, y) = (lane value, partial scan); the
+// steps can be issued separately (interleaved with other work) as long as they stay in order.
+__device__ __forceinline__ void wave_scan_step(int k, double x, double& y) {
+  switch (k) {
+    case 1: y = x + dpp_or_zero<0x111, 0xF, 0xF, true>(x); break;  // row_shr:1
+    case 2: y += dpp_or_zero<0x112, 0xF, 0xF, true>(x); break;     // row_shr:2
+    case 3: y += dpp_or_zero<0x113, 0xF, 0xF, true>(x); break;     // row_shr:3   -> sums of 4 within the row
+    case 4: y += dpp_or_zero<0x114, 0xF, 0xE, true>(y); break;     // row_shr:4 on banks 1..3
+    case 5: y += dpp_or_zero<0x118, 0xF, 0xC, true>(y); break;     // row_shr:8 on banks 2..3 -> row-local scan
+    case 6: y += dpp_or_zero<0x142, 0xA, 0xF, false>(y); break;    // row_bcast:15 into rows 1 and 3
+    case 7: y += dpp_or_zero<0x143, 0xC, 0xF, false>(y); break;    // row_bcast:31 into rows 2 and 3
+    default: break;
+  }
+}
+
 __device__ __forceinline__ double wave_incl_scan(double x) {
-  double y = x + dpp_or_zero<0x111, 0xF, 0xF, true>(x);  // row_shr:1
-  y += dpp_or_zero<0x112, 0xF, 0xF, true>(x);            // row_shr:2
-  y += dpp_or_zero<0x113, 0xF, 0xF, true>(x);            // row_shr:3   -> sums of 4 within the row
-  y += dpp_or_zero<0x114, 0xF, 0xE, true>(y);            // row_shr:4 on banks 1..3
-  y += dpp_or_zero<0x118, 0xF, 0xC, true>(y);            // row_shr:8 on banks 2..3 -> row-local scan
-  y += dpp_or_zero<0x142, 0xA, 0xF, false>(y);           // row_bcast:15 into rows 1 and 3
-  y += dpp_or_zero<0x143, 0xC, 0xF, false>(y);           // row_bcast:31 into rows 2 and 3
+  double y = 0.0;
+#pragma unroll
+  for (int k = 1; k <= 7; ++k) wave_scan_step(k, x, y);
   return y;
 }
 

@@ -55,9 +55,10 @@ constexpr int kBC = 64;       // keys per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 constexpr float kNegInf = -INFINITY;
 
-struct GateRows {      // per workgroup
-  double rowR[kMaxBR]; // R_i for the block's own rows
-  double cref;         // c at the block's reference row (sum of log f over 0..ref)
+struct GateRows {          // per workgroup
+  double rowR[kMaxBR + 1]; // R_i for the block's own rows; the last slot takes discarded writes
+  double cref;             // c at the block's reference row (sum of log f over 0..ref)
+  double cref_discard;     // takes the cref write of tiles other than tile 0
 };
 
 // Wave 0: gate sums for tile kt.  Lane t holds log f of key 63-t of the tile (0 beyond
@@ -67,19 +68,34 @@ struct GateRows {      // per workgroup
 // the tile (r2 = R_j * log2 e in fp32; r64 = R_j, when given), R_i for the block's own
 // rows and, after tile 0, c at the reference row.  Everything is fp64 until the single
 // rounding to fp32.
-__device__ __forceinline__ void gate_tile(float* r2, double* r64, GateRows& rows, int lane, int kt, int row0,
-                                          int ref, float lf_rev, double& carry) {
-  const double incl = wave_incl_scan((double)lf_rev);
+__device__ __forceinline__ void gate_finish(double incl, float* r2, double* r64, GateRows& rows, int lane, int kt,
+                                            int row0, int ref, double& carry) {
   const double excl = wave_shr1(incl);
   const int jl = 63 - lane;
   const double rj = carry + excl;
   r2[jl] = (float)(rj * kLog2ed);
   if (r64) r64[jl] = rj;
+  // Branch-free writes (this code also runs inside the MFMA schedule): rows outside the
+  // block and tiles other than tile 0 write to discard slots.
   const int j = kt * kBC + jl;
-  if (j >= row0 && j <= ref) rows.rowR[j - row0] = rj;
+  rows.rowR[(j >= row0 && j <= ref) ? j - row0 : kMaxBR] = rj;
   carry += wave_last(incl);
-  if (kt == 0 && lane == 0) rows.cref = carry;
+  *(kt == 0 ? &rows.cref : &rows.cref_discard) = carry;
 }
+__device__ __forceinline__ void gate_tile(float* r2, double* r64, GateRows& rows, int lane, int kt, int row0,
+                                          int ref, float lf_rev, double& carry) {
+  gate_finish(wave_incl_scan((double)lf_rev), r2, r64, rows, lane, kt, row0, ref, carry);
+}
+
+// The gate sums of one tile as a job that a wave can spread over its MFMA schedule.
+struct GateJob {
+  const float* lf;  // the tile's staged log gates
+  float* r2;        // its biases R_j * log2 e (out)
+  int kt;           // tile index
+  int row0, ref;
+  GateRows* rows;
+  double* carry;
+};
 
 // ------------------------------------------------------------------------------------------
 // bf16
@@ -181,22 +197,23 @@ __device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane)
   return so;
 }
 
-// Issue this wave's loads of key tile t into stage `s`: 2 * OPS instructions, plus (wave 0)
-// one for the tile's 64 log gates.  Number of instructions issued, per wave, is what the
+// Issue this wave's loads of key tile t into stage `s`: (the gate wave) one for the tile's 64
+// log gates, then 2 * OPS for K and V.  Number of instructions issued, per wave, is what the
 // vmcnt waits below count.
 template <int D, int NW>
 __device__ __forceinline__ void bf16_stage_tile(Bf16Stage<D>& s, float* lf, u32x4 rk, u32x4 rv, u32x4 rl,
-                                                const StageOffsets<D, NW>& so, int t, int wave, int lane) {
+                                                const StageOffsets<D, NW>& so, int t, int wave, int lane,
+                                                bool gate_wave) {
   using G = Bf16Geom<D, NW>;
   const uint32_t tile_off = (uint32_t)(t * kBC * D * (int)sizeof(bf16));
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations are wave-uniform (M0)
+  if (gate_wave) lds_dma4(lds_addr(lf), rl, (uint32_t)((t * kBC + lane) * (int)sizeof(float)));
 #pragma unroll
   for (int o = 0; o < G::OPS; ++o) {
     const int g = wv * G::OPS + o;
     lds_dma16(lds_addr(&s.k[g * 512]), rk, tile_off + (uint32_t)so.k[o]);
     lds_dma16(lds_addr(&s.v[g * 512]), rv, tile_off + (uint32_t)so.v[o]);
   }
-  if (wv == 0) lds_dma4(lds_addr(lf), rl, (uint32_t)((t * kBC + lane) * (int)sizeof(float)));
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited on).
@@ -385,11 +402,14 @@ __device__ __forceinline__ void pipe_pv(const Bf16Stage<D>& st, uint32_t voff, c
 //   S slots (2*KK):  MFMA of S(cur); p = exp2(s - m) for 32/(2*KK) scores of prev.
 //   PV slots (4*DB): MFMA of O += V^T P^T; bf16 packing and row sum of P(prev); biased
 //                    scores and row max of cur (block 0 first: its MFMAs finished earlier).
-template <int D>
+// With GATE the wave also runs the gate scan of the next tile (GateJob) in the P.V slots, so
+// the wave that owns the scan does not hold the others up at the next barrier.
+template <int D, bool GATE>
 __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float* r2cur, const Bf16Stage<D>& prev,
                                             const LaneOffsets<D>& off, const bf16x8 (&qreg)[D / 16],
                                             f32x16 (&sp)[2], f32x16 (&sc)[2], f32x16 (&oacc)[D / 32],
-                                            float& m, float& lsum, int hi, float scale_log2) {
+                                            float& m, float& lsum, int lane, float scale_log2, const GateJob& gj) {
+  const int hi = lane >> 5;
   constexpr int KK = PipeGeom<D>::KK, DB = PipeGeom<D>::DB;
   constexpr int NQ = 2 * KK;   // S MFMAs
   constexpr int NP = 4 * DB;   // P.V MFMAs
@@ -422,6 +442,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
   float ls0 = lsum, ls1 = 0.0f;
   float mx0 = kNegInf, mx1 = kNegInf;
+  double gx = 0.0, gy = 0.0;  // gate value of key 63-lane of the next tile, its running scan
 
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -442,6 +463,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
 #pragma unroll
     for (int e = i * EQ; e < (i + 1) * EQ; ++e) sp[e >> 4][e & 15] = exp2_hw(sp[e >> 4][e & 15] - m);
     if (i == NQ - 1) pack(0);
+    if (GATE && i == 0) gx = (double)((gj.kt * kBC + 63 - lane <= gj.ref) ? gj.lf[63 - lane] : 0.0f);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -468,23 +490,38 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
       if (e & 1) mx1 = fmaxf(mx1, sv);
       else mx0 = fmaxf(mx0, sv);
     }
+    if constexpr (GATE) {  // scan steps 1..7 and the finish, spread evenly over the slots
+#pragma unroll
+      for (int k = 1; k <= 8; ++k) {
+        if ((k - 1) * NP / 8 == i) {
+          if (k <= 7) wave_scan_step(k, gx, gy);
+          else gate_finish(gy, gj.r2, nullptr, *gj.rows, lane, gj.kt, gj.row0, gj.ref, *gj.carry);
+        }
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   lsum = ls0 + ls1;
   pipe_rescale<DB>(pair32_max(fmaxf(mx0, mx1)), m, lsum, oacc);
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1, Bf16Stage<D>& s2,
-                                              Bf16Stage<D>& s3, float* g0, float* g1, float* g2, float* g3,
-                                              GateRows& rows, const bf16* __restrict__ q,
-                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
-                                              const float* __restrict__ logf, bf16* __restrict__ o,
-                                              float* __restrict__ lse, float* __restrict__ c_out, int n,
-                                              float scale_log2) {
+// Kernel body.  NWR waves of 32 rows each share a block of 32*NWR query rows; with SP == 2
+// a second set of NWR waves takes the lower half of the block's key tiles (an in-workgroup
+// key split, for grids too small to fill the chip: it halves the longest chain of tiles) and
+// the two partial softmax states are merged through LDS at the end.  Each split has its own
+// copy of every LDS stage.
+template <int D, int NWR, int SP>
+__device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1, Bf16Stage<D>* s2,
+                                              Bf16Stage<D>* s3, float (*g0)[kBC], float (*g1)[kBC],
+                                              float (*g2)[kBC], float (*g3)[kBC], GateRows& rows,
+                                              const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                              const bf16* __restrict__ v, const float* __restrict__ logf,
+                                              bf16* __restrict__ o, float* __restrict__ lse,
+                                              float* __restrict__ c_out, int n, float scale_log2) {
   constexpr int NS = 4;  // LDS stages: tile t+1 (V still read), tile t, two tiles in flight
-  using G = Bf16Geom<D, NW>;
+  using G = Bf16Geom<D, NWR>;
   constexpr int KK = D / 16, DB = D / 32, BR = G::BR;
+  static_assert(SP == 1 || SP == 2, "key splits");
 
   const int bh = blockIdx.x;
   const int qb = gridDim.y - 1 - blockIdx.y;
@@ -492,23 +529,35 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
   const int ref = min(row0 + BR - 1, n - 1);
   const int kt_hi = ref / kBC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rw = wave % NWR;                                    // row-wave
+  const int sp = __builtin_amdgcn_readfirstlane(wave / NWR);  // key split (wave-uniform: LDS DMA bases)
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t base = (size_t)bh * n * D;
   const bf16* kb = k + base;
   const bf16* vb = v + base;
   const float* lfb = logf + (size_t)bh * n;
 
-  const int wrow0 = row0 + wave * 32;
+  // Key tiles of this wave's split: [bot, top].  Split 0 keeps the diagonal tiles (at least
+  // the top two, which hold every row's diagonal) and the upper half of the rest.
+  const int ntiles = kt_hi + 1;
+  const int n0 = (SP == 1 || ntiles <= 2) ? ntiles : max(2, (ntiles + 1) / 2);
+  const int top = sp == 0 ? kt_hi : kt_hi - n0;
+  const int bot = sp == 0 ? kt_hi - n0 + 1 : 0;
+  const bool lead = rw == sp;  // loads the split's gates and runs its gate scan (on distinct SIMDs)
+
+  const int wrow0 = row0 + rw * 32;
   const bool active = wrow0 < n;
-  const int kt_first = active ? min(wrow0 + 31, n - 1) / kBC : -1;
+  const int kt_first = !active ? -1 : (sp == 0 ? min(wrow0 + 31, n - 1) / kBC : top);
   const int my_row = wrow0 + l32;
-  const LaneOffsets<D> off = lane_offsets<D>(lane);
-  const StageOffsets<D, NW> so = stage_offsets<D, NW>(wave, lane);
+  LaneOffsets<D> off = lane_offsets<D>(lane);
+  off.k += (uint32_t)(sp * sizeof(Bf16Stage<D>));  // 1 KB multiple: the XOR swizzles still apply
+  off.v += (uint32_t)(sp * sizeof(Bf16Stage<D>));
+  const StageOffsets<D, NWR> so = stage_offsets<D, NWR>(rw, lane);
   const u32x4 rk = raw_rsrc(kb, (uint32_t)n * D * sizeof(bf16));
   const u32x4 rv = raw_rsrc(vb, (uint32_t)n * D * sizeof(bf16));
   const u32x4 rl = raw_rsrc(lfb, (uint32_t)n * sizeof(float));
 
-  auto stage = [&](auto J) -> Bf16Stage<D>& {
+  auto stage = [&](auto J) -> Bf16Stage<D>* {
     constexpr int j = decltype(J)::value % NS;
     if constexpr (j == 0) return s0;
     else if constexpr (j == 1) return s1;
@@ -517,10 +566,10 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
   };
   auto gates = [&](auto J) -> float* {
     constexpr int j = decltype(J)::value % NS;
-    if constexpr (j == 0) return g0;
-    else if constexpr (j == 1) return g1;
-    else if constexpr (j == 2) return g2;
-    else return g3;
+    if constexpr (j == 0) return g0[sp];
+    else if constexpr (j == 1) return g1[sp];
+    else if constexpr (j == 2) return g2[sp];
+    else return g3[sp];
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -534,10 +583,19 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
       qreg[kk] = bf16x8{};
   }
 
-  // Prologue: tiles kt_hi and kt_hi-1 (tile kt lives in stage (kt_hi - kt) % 4; the tile
+  // Gate sum above this split's first tile: 0 for split 0 (its first tile holds ref), the
+  // sum of log f over (end of tile top, ref] for split 1.
+  double carry = 0.0;
+  if (SP == 2 && sp == 1 && lead) {
+    double part = 0.0;
+    for (int j = (top + 1) * kBC + lane; j <= ref; j += 64) part += (double)lfb[j];
+    carry = wave_last(wave_incl_scan(part));
+  }
+
+  // Prologue: tiles top and top-1 (the i-th tile of the split lives in stage i % 4; the
   // loop issues tile kt-2 while computing tile kt).
-  bf16_stage_tile<D, NW>(stage(I0{}), stage(I0{}).lf, rk, rv, rl, so, kt_hi, wave, lane);
-  if (kt_hi >= 1) bf16_stage_tile<D, NW>(stage(I1{}), stage(I1{}).lf, rk, rv, rl, so, kt_hi - 1, wave, lane);
+  if (top >= bot) bf16_stage_tile<D, NWR>(stage(I0{})[sp], stage(I0{})[sp].lf, rk, rv, rl, so, top, rw, lane, lead);
+  if (top - 1 >= bot) bf16_stage_tile<D, NWR>(stage(I1{})[sp], stage(I1{})[sp].lf, rk, rv, rl, so, top - 1, rw, lane, lead);
   wait_vmcnt<0>();
 
   f32x16 oacc[DB];
@@ -546,64 +604,100 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
   f32x16 sa[2], sb[2];  // scores of the tiles at even / odd loop positions
   sa[0] = sa[1] = sb[0] = sb[1] = f32x16{};
   float m = kNegInf, lsum = 0.0f;
-  double carry = 0.0;
-  auto gate_in = [&](const float* lf, int t) {
-    return (t * kBC + 63 - lane <= ref) ? lf[63 - lane] : 0.0f;
+  auto gate_in = [&](const float* lf, int t, int ln) {
+    return (t * kBC + 63 - ln <= ref) ? lf[63 - ln] : 0.0f;
   };
-  if (wave == 0) gate_tile(gates(I0{}), nullptr, rows, lane, kt_hi, row0, ref, gate_in(stage(I0{}).lf, kt_hi), carry);
+  if (lead && top >= bot)
+    gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry);
 
-  auto step = [&](auto J, int kt) {
+  // Position i of the split's tile sequence: tile kt = top - i.
+  auto step = [&](auto J, int i) {
     constexpr int j = decltype(J)::value;
     using JP = std::integral_constant<int, j + NS - 1>;  // position of tile kt+1
     using JN = std::integral_constant<int, j + 2>;       // position of tiles kt+2 / kt-2
     using J1 = std::integral_constant<int, j + 1>;       // position of tile kt-1
     f32x16(&sc)[2] = (j & 1) ? sb : sa;
-    f32x16(&sp)[2] = (j & 1) ? sa : sb;
-    // Own loads of tile kt are complete once at most those of tile kt-1 remain.
-    if (kt >= 1) {
-      if (wave == 0) wait_vmcnt<2 * G::OPS + 1>();
-      else wait_vmcnt<2 * G::OPS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    f32x16(&sp_)[2] = (j & 1) ? sa : sb;
+    const int kt = top - i;
+    const int ln = opaque_lane(lane);  // per-tile copy: keeps stage addresses out of the loop-invariant set
+    // Own loads of tile kt, and the gate load of tile kt-1 (issued first for its tile), are
+    // complete once at most the K/V loads of tile kt-1 remain.
+    if (kt - 1 >= bot) wait_vmcnt<2 * G::OPS>();
+    else wait_vmcnt<0>();
     barrier_lds();  // tile kt and its gate sums visible; every wave is done with tile kt+2's stage
-    if (kt >= 2) bf16_stage_tile<D, NW>(stage(JN{}), stage(JN{}).lf, rk, rv, rl, so, kt - 2, wave, lane);
-    if (active && kt <= kt_first) {
-      if (kt == kt_first) {  // first tile of this wave: the diagonal tile, nothing to overlap with
-        pipe_qk<D>(stage(J), off.k, qreg, sc);
-        const float mx = pipe_scores<true>(sc, gates(J), kt * kBC, my_row, hi, scale_log2);
+    if (kt - 2 >= bot) bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl, so, kt - 2, rw, lane, lead);
+    // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
+    const bool gate_job = lead && kt - 1 >= bot;
+    bool gate_done = false;
+    const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, &rows, &carry};
+    if (active && kt >= bot && kt <= kt_first) {
+      if (kt == kt_first) {  // first tile of this wave: nothing to overlap with
+        pipe_qk<D>(stage(J)[0], off.k, qreg, sc);
+        const float mx = sp == 0 ? pipe_scores<true>(sc, gates(J), kt * kBC, my_row, ln >> 5, scale_log2)
+                                 : pipe_scores<false>(sc, gates(J), 0, 0, ln >> 5, scale_log2);
         pipe_rescale<DB>(mx, m, lsum, oacc);
+      } else if (gate_job) {
+        pipe_steady<D, true>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
+                             scale_log2, gj);
+        gate_done = true;
       } else {
-        pipe_steady<D>(stage(J), gates(J), stage(JP{}), off, qreg, sp, sc, oacc, m, lsum, hi, scale_log2);
+        pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
+                              scale_log2, gj);
       }
-      if (kt == 0) {  // drain: probabilities and P.V of tile 0
+      if (kt == bot) {  // drain: probabilities and P.V of the split's last tile
         bf16x8 p[4];
         pipe_probs(sc, m, p);
-        pipe_pv<D>(stage(J), off.v, p, oacc);
+        pipe_pv<D>(stage(J)[0], off.v, p, oacc);
         lsum = pipe_psum(p, lsum);
       }
     }
-    // Wave 0: gate sums of tile kt-1 (read after the next barrier).  Its gate load is
-    // complete once at most the loads issued after it (tile kt-2's, if any) remain.
-    if (wave == 0 && kt >= 1) {
-      if (kt >= 2) wait_vmcnt<2 * G::OPS + 1>();
-      else wait_vmcnt<0>();
-      gate_tile(gates(J1{}), nullptr, rows, lane, kt - 1, row0, ref, gate_in(stage(J1{}).lf, kt - 1), carry);
-    }
+    // Otherwise the lead wave runs it here (read by everyone after the next barrier).
+    if (gate_job && !gate_done)
+      gate_tile(gates(J1{}), nullptr, rows, ln, kt - 1, row0, ref, gate_in(stage(J1{})[sp].lf, kt - 1, ln), carry);
   };
 
-  for (int kt = kt_hi; kt >= 0; kt -= NS) {
-    step(I0{}, kt);
-    if (kt - 1 < 0) break;
-    step(I1{}, kt - 1);
-    if (kt - 2 < 0) break;
-    step(std::integral_constant<int, 2>{}, kt - 2);
-    if (kt - 3 < 0) break;
-    step(std::integral_constant<int, 3>{}, kt - 3);
+  for (int i = 0; i < n0; i += NS) {
+    step(I0{}, i);
+    if (i + 1 >= n0) break;
+    step(I1{}, i + 1);
+    if (i + 2 >= n0) break;
+    step(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 >= n0) break;
+    step(std::integral_constant<int, 3>{}, i + 3);
   }
 
-  // ---- epilogue: O = acc / l, lse, c ---------------------------------------------------
-  __syncthreads();  // rows / cref written by wave 0 are visible
+  // ---- epilogue: merge the splits, O = acc / l, lse, c ---------------------------------
+  __syncthreads();  // rows / cref written by the lead waves are visible; all stages are free
+  if constexpr (SP == 2) {
+    // Split 1 leaves (O, m, l) in LDS in its own lane layout; the split-0 wave of the same
+    // rows reads the same lane's values.  Row-wave r uses the memory of stage r.
+    constexpr int CB = (DB * 16 + 2) * 64;
+    static_assert(CB * sizeof(float) <= sizeof(Bf16Stage<D>) && NWR <= 4, "merge buffer");
+    Bf16Stage<D>* sr = rw == 0 ? s0 : rw == 1 ? s1 : rw == 2 ? s2 : s3;
+    float* cb = reinterpret_cast<float*>(sr);
+    if (sp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb[(db * 16 + r) * 64 + lane] = oacc[db][r];
+      cb[(DB * 16) * 64 + lane] = m;
+      cb[(DB * 16 + 1) * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (sp == 1) return;
+    if (active) {
+      const float m1 = cb[(DB * 16) * 64 + lane];
+      const float l1 = cb[(DB * 16 + 1) * 64 + lane];
+      const float mm = fmaxf(m, m1);
+      const float a0 = exp2_hw(m - mm), a1 = exp2_hw(m1 - mm);
+      lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + cb[(db * 16 + r) * 64 + lane] * a1;
+      m = mm;
+    }
+  }
   if (!active) return;
   const float ltot = pair32_sum(lsum);
   if (my_row >= n) return;
@@ -627,15 +721,15 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>& s0, Bf16Stage<D>& s1
   }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
+template <int D, int NWR, int SP>
+__global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
     float scale_log2) {
   __shared__ GateRows rows;
-  __shared__ Bf16Stage<D> s0, s1, s2, s3;
-  __shared__ float g0[kBC], g1[kBC], g2[kBC], g3[kBC];
-  fwd_pipe_body<D, NW>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
+  __shared__ Bf16Stage<D> s0[SP], s1[SP], s2[SP], s3[SP];
+  __shared__ float g0[SP][kBC], g1[SP][kBC], g2[SP][kBC], g3[SP][kBC];
+  fwd_pipe_body<D, NWR, SP>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -841,13 +935,22 @@ hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float
     if constexpr (D >= 64) {
       if (blocks256 >= 2 * (int64_t)cus) {
         const dim3 grid((unsigned)bh, (unsigned)((n + 255) / 256));
-        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8>), grid, dim3(512), 0, stream, (const bf16*)q, (const bf16*)k,
-                           (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1>), grid, dim3(512), 0, stream, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
         return hipGetLastError();
       }
     }
     const dim3 grid((unsigned)bh, (unsigned)((n + 127) / 128));
-    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4>), grid, dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+    const int64_t blocks128 = bh * (int64_t)((n + 127) / 128);
+    if constexpr (D <= 64) {
+      // Fewer than two 128-row blocks per CU: split each block's key tiles over two wave sets.
+      if (blocks128 < 2 * (int64_t)cus) {
+        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2>), grid, dim3(512), 0, stream, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1>), grid, dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
                        (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
