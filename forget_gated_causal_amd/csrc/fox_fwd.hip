@@ -59,6 +59,7 @@ struct GateRows {          // per workgroup
   double rowR[kMaxBR + 1]; // R_i for the block's own rows; the last slot takes discarded writes
   double cref;             // c at the block's reference row (sum of log f over 0..ref)
   double cref_discard;     // takes the cref write of tiles other than tile 0
+  double csplit;           // key split: sum of log f over split 0's keys (split 1's frame offset)
 };
 
 // Wave 0: gate sums for tile kt.  Lane t holds log f of key 63-t of the tile (0 beyond
@@ -207,7 +208,12 @@ __device__ __forceinline__ void bf16_stage_tile(Bf16Stage<D>& s, float* lf, u32x
   using G = Bf16Geom<D, NW>;
   const uint32_t tile_off = (uint32_t)(t * kBC * D * (int)sizeof(bf16));
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations are wave-uniform (M0)
-  if (gate_wave) lds_dma4(lds_addr(lf), rl, (uint32_t)((t * kBC + lane) * (int)sizeof(float)));
+  if (gate_wave) {
+    // lane index recomputed here (volatile, so not hoisted) rather than kept live across the tile loop
+    uint32_t ln;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    lds_dma4(lds_addr(lf), rl, (uint32_t)(t * kBC * (int)sizeof(float)) + ln * (uint32_t)sizeof(float));
+  }
 #pragma unroll
   for (int o = 0; o < G::OPS; ++o) {
     const int g = wv * G::OPS + o;
@@ -285,25 +291,30 @@ template <int D>
 struct PipeGeom {
   static constexpr int KK = D / 16;  // MFMA k-steps of S (16 dims each)
   static constexpr int DB = D / 32;  // 32-dim output blocks of O
+  // Fold the running max into the S accumulators' initial value (saves one subtraction per
+  // score; costs 16 VGPRs, which the d = 128 schedule does not have to spare).
+  static constexpr bool FOLD = D <= 64;
 };
 
-// S^T of one tile: s[b] = K[32b .. 32b+31] Q^T (32 keys x 32 queries per block).
+// S^T of one tile: s[b] = K[32b .. 32b+31] Q^T + cinit (32 keys x 32 queries per block).
+// cinit holds -m / (scale log2 e) of the lane's row in every register, so the scores come
+// out already relative to the running max m (no subtraction per score before exp2).
 template <int D>
 __device__ __forceinline__ void pipe_qk(const Bf16Stage<D>& st, uint32_t koff, const bf16x8 (&qreg)[D / 16],
-                                        f32x16 (&s)[2]) {
+                                        const f32x16& cinit, f32x16 (&s)[2]) {
   constexpr int KK = PipeGeom<D>::KK;
-  s[0] = f32x16{};
-  s[1] = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const uint32_t a = koff ^ (uint32_t)(kk << 5);
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk], s[1], 0, 0, 0);
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], kk == 0 ? cinit : s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk],
+                                                   kk == 0 ? cinit : s[1], 0, 0, 0);
   }
 }
 
-// Biased base-2 scores of a tile, in place: s = acc * scale * log2 e + R_j * log2 e, with
-// the causal mask on the diagonal tile.  Returns the tile's row max (both lanes of a row).
+// Biased base-2 scores of a tile, in place: s = acc * scale * log2 e + R_j * log2 e (minus the
+// running max, through acc's initial value), with the causal mask on the diagonal tile.
+// Returns the tile's row max (both lanes of a row).
 template <bool DIAG>
 __device__ __forceinline__ float pipe_scores(f32x16 (&s)[2], const float* r2s, int key0, int my_row, int hi,
                                              float scale_log2) {
@@ -328,30 +339,60 @@ __device__ __forceinline__ float pipe_scores(f32x16 (&s)[2], const float* r2s, i
   return pair32_max(mx);
 }
 
-// Lazy rescale: raise the running max only when the tile max exceeds it by more than kTau.
-template <int DB>
-__device__ __forceinline__ void pipe_rescale(float mx, float& m, float& lsum, f32x16 (&oacc)[DB]) {
-  const float mcand = fmaxf(m, mx);
-  const bool need = mcand > m + kTau;
+// Broadcast of -m / (scale log2 e), the initial value of every S accumulator.
+__device__ __forceinline__ f32x16 pipe_cinit(float m, float scale_log2) {
+  const float c = -m / scale_log2;
+  f32x16 r;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) r[e] = c;
+  return r;
+}
+
+// Lazy rescale (mx = the tile's row max): raise m only when the tile max exceeds it by more
+// than kTau, and scale O and l to the new max.  With FOLD the scores are relative to m (and
+// shifted along with it, as is the accumulator offset); otherwise they are absolute.
+template <bool FOLD, int DB>
+__device__ __forceinline__ void pipe_rescale(float mx, float& m, float& lsum, f32x16 (&oacc)[DB], f32x16 (&s)[2],
+                                             f32x16& cinit, float scale_log2) {
+  const float rel = FOLD ? mx : mx - m;
+  const bool need = rel > kTau;
   if (wave_any(need)) {
-    const float mn = need ? mcand : m;
-    const float alpha = exp2_hw(m - mn);
+    const float delta = need ? rel : 0.0f;
+    const float alpha = exp2_hw(-delta);
     lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    m = mn;
+    m += delta;
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) s[b] -= delta;
+      cinit = pipe_cinit(m, scale_log2);
+    }
   }
 }
 
-// p = exp2(s - m) rounded to bf16, in the key order of the S^T registers: p[2b+u] holds
-// keys 32b + 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3}, the B operand of O^T += V^T P^T.
+// First tile of a wave (m is still 0, O and l zero): m becomes the tile's row max.
+template <bool FOLD>
+__device__ __forceinline__ void pipe_first_max(float mx, float& m, f32x16 (&s)[2], f32x16& cinit, float scale_log2) {
+  m = mx;
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) s[b] -= mx;
+    cinit = pipe_cinit(m, scale_log2);
+  }
+}
+
+// p = exp2(s - m) rounded to bf16 (s already relative to m when FOLD), in the key order of
+// the S^T registers: p[2b+u] holds keys 32b + 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3}, the B
+// operand of O^T += V^T P^T.
+template <bool FOLD>
 __device__ __forceinline__ void pipe_probs(const f32x16 (&s)[2], float m, bf16x8 (&p)[4]) {
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[2 * b + u][e] = (bf16)exp2_hw(s[b][8 * u + e] - m);
+      for (int e = 0; e < 8; ++e) p[2 * b + u][e] = (bf16)exp2_hw(FOLD ? s[b][8 * u + e] : s[b][8 * u + e] - m);
     }
   }
 }
@@ -408,7 +449,8 @@ template <int D, bool GATE>
 __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float* r2cur, const Bf16Stage<D>& prev,
                                             const LaneOffsets<D>& off, const bf16x8 (&qreg)[D / 16],
                                             f32x16 (&sp)[2], f32x16 (&sc)[2], f32x16 (&oacc)[D / 32],
-                                            float& m, float& lsum, int lane, float scale_log2, const GateJob& gj) {
+                                            f32x16& cinit, float& m, float& lsum, int lane, float scale_log2,
+                                            const GateJob& gj) {
   const int hi = lane >> 5;
   constexpr int KK = PipeGeom<D>::KK, DB = PipeGeom<D>::DB;
   constexpr int NQ = 2 * KK;   // S MFMAs
@@ -451,8 +493,14 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const int b = i & 1, kk = i >> 1;
+    // The slot's exponentials go ahead of its MFMA: at the start of a tile they run while the
+    // first K operands are still in flight.
+#pragma unroll
+    for (int e = i * EQ; e < (i + 1) * EQ; ++e)
+      sp[e >> 4][e & 15] = exp2_hw(PipeGeom<D>::FOLD ? sp[e >> 4][e & 15] : sp[e >> 4][e & 15] - m);
+    __builtin_amdgcn_sched_barrier(0);
     if (kk == 0)
-      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], f32x16{}, 0, 0, 0);
+      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], cinit, 0, 0, 0);
     else
       sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], sc[b], 0, 0, 0);
     if (i + PFK < NQ) kop[i + PFK] = kread(i + PFK);
@@ -460,8 +508,6 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
 #pragma unroll
     for (int kq = 0; kq < 8; ++kq)  // bias quads needed in the first P.V slots
       if ((4 * kq) / EP - RD + NQ == i) r2[kq] = *reinterpret_cast<const f32x4*>(&r2cur[8 * kq + 4 * hi]);
-#pragma unroll
-    for (int e = i * EQ; e < (i + 1) * EQ; ++e) sp[e >> 4][e & 15] = exp2_hw(sp[e >> 4][e & 15] - m);
     if (i == NQ - 1) pack(0);
     if (GATE && i == 0) gx = (double)((gj.kt * kBC + 63 - lane <= gj.ref) ? gj.lf[63 - lane] : 0.0f);
     __builtin_amdgcn_sched_barrier(0);
@@ -502,7 +548,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
     __builtin_amdgcn_sched_barrier(0);
   }
   lsum = ls0 + ls1;
-  pipe_rescale<DB>(pair32_max(fmaxf(mx0, mx1)), m, lsum, oacc);
+  pipe_rescale<PipeGeom<D>::FOLD, DB>(pair32_max(fmaxf(mx0, mx1)), m, lsum, oacc, sc, cinit, scale_log2);
 }
 
 // Kernel body.  NWR waves of 32 rows each share a block of 32*NWR query rows; with SP == 2
@@ -583,14 +629,10 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       qreg[kk] = bf16x8{};
   }
 
-  // Gate sum above this split's first tile: 0 for split 0 (its first tile holds ref), the
-  // sum of log f over (end of tile top, ref] for split 1.
+  // Gate sums start at 0 above each split's first tile.  For split 0 that tile holds ref, so
+  // its frame is the true one; split 1's sums miss the gates of split 0's keys, a constant
+  // that shifts all of split 1's scores alike and is added back to its max at the merge.
   double carry = 0.0;
-  if (SP == 2 && sp == 1 && lead) {
-    double part = 0.0;
-    for (int j = (top + 1) * kBC + lane; j <= ref; j += 64) part += (double)lfb[j];
-    carry = wave_last(wave_incl_scan(part));
-  }
 
   // Prologue: tiles top and top-1 (the i-th tile of the split lives in stage i % 4; the
   // loop issues tile kt-2 while computing tile kt).
@@ -603,7 +645,8 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   f32x16 sa[2], sb[2];  // scores of the tiles at even / odd loop positions
   sa[0] = sa[1] = sb[0] = sb[1] = f32x16{};
-  float m = kNegInf, lsum = 0.0f;
+  float m = 0.0f, lsum = 0.0f;  // m: running max (base 2); scores are kept relative to it
+  f32x16 cinit = f32x16{};      // -m / (scale log2 e) in every lane register: S accumulators start there
   auto gate_in = [&](const float* lf, int t, int ln) {
     return (t * kBC + 63 - ln <= ref) ? lf[63 - ln] : 0.0f;
   };
@@ -632,21 +675,21 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, &rows, &carry};
     if (active && kt >= bot && kt <= kt_first) {
       if (kt == kt_first) {  // first tile of this wave: nothing to overlap with
-        pipe_qk<D>(stage(J)[0], off.k, qreg, sc);
+        pipe_qk<D>(stage(J)[0], off.k, qreg, cinit, sc);
         const float mx = sp == 0 ? pipe_scores<true>(sc, gates(J), kt * kBC, my_row, ln >> 5, scale_log2)
                                  : pipe_scores<false>(sc, gates(J), 0, 0, ln >> 5, scale_log2);
-        pipe_rescale<DB>(mx, m, lsum, oacc);
+        pipe_first_max<PipeGeom<D>::FOLD>(mx, m, sc, cinit, scale_log2);
       } else if (gate_job) {
-        pipe_steady<D, true>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
+        pipe_steady<D, true>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, cinit, m, lsum, ln,
                              scale_log2, gj);
         gate_done = true;
       } else {
-        pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
-                              scale_log2, gj);
+        pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, cinit, m, lsum,
+                              ln, scale_log2, gj);
       }
       if (kt == bot) {  // drain: probabilities and P.V of the split's last tile
         bf16x8 p[4];
-        pipe_probs(sc, m, p);
+        pipe_probs<PipeGeom<D>::FOLD>(sc, m, p);
         pipe_pv<D>(stage(J)[0], off.v, p, oacc);
         lsum = pipe_psum(p, lsum);
       }
@@ -667,6 +710,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   }
 
   // ---- epilogue: merge the splits, O = acc / l, lse, c ---------------------------------
+  if (SP == 2 && sp == 0 && lead && lane == 0) rows.csplit = carry;  // split 0's gate total
   __syncthreads();  // rows / cref written by the lead waves are visible; all stages are free
   if constexpr (SP == 2) {
     // Split 1 leaves (O, m, l) in LDS in its own lane layout; the split-0 wave of the same
@@ -676,12 +720,16 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     Bf16Stage<D>* sr = rw == 0 ? s0 : rw == 1 ? s1 : rw == 2 ? s2 : s3;
     float* cb = reinterpret_cast<float*>(sr);
     if (sp == 1) {
+      const bool worked = active && top >= bot;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) cb[(db * 16 + r) * 64 + lane] = oacc[db][r];
-      cb[(DB * 16) * 64 + lane] = m;
+      // back to the true frame: split 1's scores were high by -csplit * log2 e
+      cb[(DB * 16) * 64 + lane] = worked ? m + (float)(rows.csplit * kLog2ed) : kNegInf;
       cb[(DB * 16 + 1) * 64 + lane] = lsum;
+      // tile 0 was split 1's: its gate total misses split 0's keys as well
+      if (lead && lane == 0 && top >= bot) rows.cref += rows.csplit;
     }
     __syncthreads();
     if (sp == 1) return;
