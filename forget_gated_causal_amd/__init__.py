@@ -15,7 +15,8 @@ import torch
 
 from ._lib import FOX_BF16, FOX_F32, FoxError, check, lib, status_string  # noqa: F401
 
-__all__ = ["logf_cumsum", "attn_fwd", "attn_decode", "decode_workspace_bytes", "FoxError", "status_string"]
+__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes", "attn_decode",
+           "decode_workspace_bytes", "FoxError", "status_string"]
 
 _DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
 
@@ -78,6 +79,44 @@ def attn_fwd(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=No
     st = lib().fox_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse if want_lse else None),
                             _ptr(c if want_c else None), B, H, N, d, scale, dt, _stream())
     check("fox_attn_fwd", st)
+    return o, (lse if want_lse else None), (c if want_c else None)
+
+
+def attn_fwd_pruned_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
+    return int(lib().fox_attn_fwd_pruned_workspace_bytes(b, h, n, d))
+
+
+def attn_fwd_pruned(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=None, workspace=None,
+                    want_lse: bool = True, want_c: bool = True):
+    """fox_attn_fwd_pruned: attn_fwd with gate-aware tile skipping (equal to fp32 rounding).
+
+    ``workspace``: uint8 device tensor of at least attn_fwd_pruned_workspace_bytes(B, H, N, d)
+    bytes (allocated here when None).
+    """
+    B, H, N, d = q.shape
+    dt = _DTYPES.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, H, N, d)}")
+    _need(logf, "logf", torch.float32)
+    if tuple(logf.shape) != (B, H, N):
+        raise ValueError(f"logf shape {tuple(logf.shape)} != {(B, H, N)}")
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    if want_c and c is None:
+        c = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    wb = attn_fwd_pruned_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(wb, 16), device=q.device, dtype=torch.uint8)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = lib().fox_attn_fwd_pruned(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse if want_lse else None),
+                                   _ptr(c if want_c else None), _ptr(workspace), workspace.numel(), B, H, N, d,
+                                   scale, dt, _stream())
+    check("fox_attn_fwd_pruned", st)
     return o, (lse if want_lse else None), (c if want_c else None)
 
 

@@ -52,9 +52,9 @@ fox_status_t fox_logf_cumsum(const float* logf, float* c, int64_t rows, int64_t 
   return from_hip(fox::launch_logf_cumsum(logf, c, rows, (int)n, stream));
 }
 
-fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                          float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
-                          hipStream_t stream) {
+// Validation shared by the two forward entry points.
+static fox_status_t fwd_args(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                             float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype) {
   if (!q || !k || !v || !logf || !o) return FOX_ERR_INVALID_ARG;
   if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
@@ -72,8 +72,40 @@ fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const flo
       overlap(lse, vbytes, q, tbytes) || overlap(lse, vbytes, k, tbytes) || overlap(lse, vbytes, v, tbytes) ||
       overlap(c, vbytes, q, tbytes) || overlap(c, vbytes, k, tbytes) || overlap(c, vbytes, v, tbytes))
     return FOX_ERR_INVALID_ARG;
+  return FOX_OK;
+}
+
+fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                          float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
+                          hipStream_t stream) {
+  const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
+  if (st != FOX_OK) return st;
   return from_hip(
-      fox::launch_attn_fwd(q, k, v, logf, o, lse, c, bh, (int)n, (int)d, scale, dtype == FOX_BF16, stream));
+      fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b * h, (int)n, (int)d, scale, dtype == FOX_BF16, stream));
+}
+
+size_t fox_attn_fwd_pruned_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d) {
+  if (b <= 0 || h <= 0 || n <= 0 || n > FOX_MAX_SEQ || !head_dim_ok(d) || b > kI32Max / h) return 0;
+  return fox::attn_fwd_pruned_workspace_bytes(b * h, (int)n);
+}
+
+fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, const float* logf, void* o,
+                                 float* lse, float* c, void* workspace, size_t workspace_bytes, int64_t b, int64_t h,
+                                 int64_t n, int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream) {
+  const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
+  if (st != FOX_OK) return st;
+  const int64_t bh = b * h;
+  const size_t need = fox::attn_fwd_pruned_workspace_bytes(bh, (int)n);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
+  const size_t tbytes = (size_t)bh * (size_t)n * (size_t)d * elem_bytes(dtype);
+  const size_t vbytes = (size_t)bh * (size_t)n * sizeof(float);
+  if (overlap(workspace, need, q, tbytes) || overlap(workspace, need, k, tbytes) ||
+      overlap(workspace, need, v, tbytes) || overlap(workspace, need, o, tbytes) ||
+      overlap(workspace, need, logf, vbytes) || overlap(workspace, need, lse, vbytes) ||
+      overlap(workspace, need, c, vbytes))
+    return FOX_ERR_INVALID_ARG;
+  return from_hip(fox::launch_attn_fwd_pruned(q, k, v, logf, o, lse, c, static_cast<float*>(workspace), bh, (int)n,
+                                              (int)d, scale, dtype == FOX_BF16, stream));
 }
 
 size_t fox_attn_decode_workspace_bytes(int64_t s, int64_t h, int64_t l, int64_t d) {

@@ -60,6 +60,9 @@ struct GateRows {          // per workgroup
   double cref;             // c at the block's reference row (sum of log f over 0..ref)
   double cref_discard;     // takes the cref write of tiles other than tile 0
   double csplit;           // key split: sum of log f over split 0's keys (split 1's frame offset)
+  float kmax;              // pruning: largest key norm of the block's key range
+  float prune_t;           // pruning: margin 25 + log2 n (base-2 units)
+  int done_it[16];         // pruning: loop position at which each wave stopped (INT_MAX: still running)
 };
 
 // Wave 0: gate sums for tile kt.  Lane t holds log f of key 63-t of the tile (0 beyond
@@ -556,18 +559,28 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
 // key split, for grids too small to fill the chip: it halves the longest chain of tiles) and
 // the two partial softmax states are merged through LDS at the end.  Each split has its own
 // copy of every LDS stage.
-template <int D, int NWR, int SP>
+//
+// PRUNE (gate-aware tile skipping, SP == 1 only): knorm holds the largest key norm of every
+// 64-key tile.  Walking down from the diagonal, a wave stops once, for each of its rows,
+//   scale * |q_i| * max_j |k_j| * log2 e + R_{j1} * log2 e < m_i - (25 + log2 n),
+// where j1 is the highest key of the tile: every remaining score is then below the running
+// max by more than that, so all remaining keys together weigh less than 2^-24 of the row sum
+// (Cauchy-Schwarz on q.k; R_j grows with j).  The workgroup leaves the loop when all its
+// waves have stopped.  Results then equal the full computation to fp32 rounding.
+template <int D, int NWR, int SP, bool PRUNE>
 __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1, Bf16Stage<D>* s2,
                                               Bf16Stage<D>* s3, float (*g0)[kBC], float (*g1)[kBC],
                                               float (*g2)[kBC], float (*g3)[kBC], GateRows& rows,
                                               const bf16* __restrict__ q, const bf16* __restrict__ k,
                                               const bf16* __restrict__ v, const float* __restrict__ logf,
                                               bf16* __restrict__ o, float* __restrict__ lse,
-                                              float* __restrict__ c_out, int n, float scale_log2) {
+                                              float* __restrict__ c_out, int n, float scale_log2,
+                                              const float* __restrict__ knorm) {
   constexpr int NS = 4;  // LDS stages: tile t+1 (V still read), tile t, two tiles in flight
   using G = Bf16Geom<D, NWR>;
   constexpr int KK = D / 16, DB = D / 32, BR = G::BR;
   static_assert(SP == 1 || SP == 2, "key splits");
+  static_assert(!PRUNE || SP == 1, "pruning runs without the key split");
 
   const int bh = blockIdx.x;
   const int qb = gridDim.y - 1 - blockIdx.y;
@@ -629,6 +642,33 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       qreg[kk] = bf16x8{};
   }
 
+  // Pruning: scale log2 e |q_i| of the lane's row (kept in LDS: the d = 128 schedule has
+  // no VGPR to spare), the largest key norm below the block, the margin, stop markers.
+  __shared__ float qn_lds[PRUNE ? 64 * NWR * SP : 1];
+  if constexpr (PRUNE) {
+    float qn = 0.0f;
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)qreg[kk][e], (float)qreg[kk][e], ss);
+    qn = scale_log2 * sqrtf(pair32_sum(ss));  // scale * log2 e * |q_i|
+    qn_lds[tid] = qn;
+    if (wave == 0) {
+      const int nt = (n + kBC - 1) / kBC;
+      float km = 0.0f;
+      for (int t = lane; t <= kt_hi; t += 64) km = fmaxf(km, knorm[(size_t)bh * nt + t]);
+#pragma unroll
+      for (int o2 = 32; o2 >= 1; o2 >>= 1) km = fmaxf(km, __shfl_xor(km, o2));
+      if (lane == 0) {
+        rows.kmax = km;
+        rows.prune_t = 25.0f + log2_hw((float)n);
+      }
+    }
+    if (tid < 16) rows.done_it[tid] = (tid >= NWR || row0 + 32 * tid >= n) ? -1 : 0x7FFFFFFF;
+  }
+  bool wdone = false;
+
   // Gate sums start at 0 above each split's first tile.  For split 0 that tile holds ref, so
   // its frame is the true one; split 1's sums miss the gates of split 0's keys, a constant
   // that shifts all of split 1's scores alike and is added back to its max at the merge.
@@ -653,6 +693,13 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   if (lead && top >= bot)
     gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry);
 
+  // Pruning test for tile kt (and so every tile below it), wave-uniform.
+  auto prune_stop = [&](int kt, const float* r2t) -> bool {
+    (void)kt;
+    const float bound = qn_lds[tid] * rows.kmax + r2t[kBC - 1] + rows.prune_t;
+    const bool ok = my_row >= n || bound < m;
+    return __ballot(!ok) == 0;
+  };
   // Position i of the split's tile sequence: tile kt = top - i.
   auto step = [&](auto J, int i) {
     constexpr int j = decltype(J)::value;
@@ -668,12 +715,21 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     if (kt - 1 >= bot) wait_vmcnt<2 * G::OPS>();
     else wait_vmcnt<0>();
     barrier_lds();  // tile kt and its gate sums visible; every wave is done with tile kt+2's stage
+    if constexpr (PRUNE) {
+      // Leave when every wave stopped before this position (those marks are all visible now;
+      // a mark set during this position would read as "running" to every wave alike).
+      bool all = true;
+#pragma unroll
+      for (int w = 0; w < NWR; ++w) all = all && rows.done_it[w] < i;
+      if (all) return true;
+    }
     if (kt - 2 >= bot) bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl, so, kt - 2, rw, lane, lead);
     // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
     const bool gate_job = lead && kt - 1 >= bot;
     bool gate_done = false;
     const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, &rows, &carry};
-    if (active && kt >= bot && kt <= kt_first) {
+    const bool stop_here = PRUNE && active && !wdone && kt < kt_first && kt >= bot && prune_stop(kt, gates(J));
+    if (active && kt >= bot && kt <= kt_first && !wdone) {
       if (kt == kt_first) {  // first tile of this wave: nothing to overlap with
         pipe_qk<D>(stage(J)[0], off.k, qreg, cinit, sc);
         const float mx = sp == 0 ? pipe_scores<true>(sc, gates(J), kt * kBC, my_row, ln >> 5, scale_log2)
@@ -687,7 +743,13 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
         pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, cinit, m, lsum,
                               ln, scale_log2, gj);
       }
-      if (kt == bot) {  // drain: probabilities and P.V of the split's last tile
+      // With pruning, a wave whose remaining keys (tile kt and below) are all negligible still
+      // finishes tile kt (same code path) and then stops.
+      if (PRUNE && kt != kt_first && stop_here) {
+        wdone = true;
+        if (lane == 0) rows.done_it[wave] = i;
+      }
+      if (kt == bot || wdone) {  // drain: probabilities and P.V of the split's last tile
         bf16x8 p[4];
         pipe_probs<PipeGeom<D>::FOLD>(sc, m, p);
         pipe_pv<D>(stage(J)[0], off.v, p, oacc);
@@ -697,17 +759,16 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     // Otherwise the lead wave runs it here (read by everyone after the next barrier).
     if (gate_job && !gate_done)
       gate_tile(gates(J1{}), nullptr, rows, ln, kt - 1, row0, ref, gate_in(stage(J1{})[sp].lf, kt - 1, ln), carry);
+    return false;
   };
 
   for (int i = 0; i < n0; i += NS) {
-    step(I0{}, i);
-    if (i + 1 >= n0) break;
-    step(I1{}, i + 1);
-    if (i + 2 >= n0) break;
-    step(std::integral_constant<int, 2>{}, i + 2);
-    if (i + 3 >= n0) break;
-    step(std::integral_constant<int, 3>{}, i + 3);
+    if (step(I0{}, i) || i + 1 >= n0) break;
+    if (step(I1{}, i + 1) || i + 2 >= n0) break;
+    if (step(std::integral_constant<int, 2>{}, i + 2) || i + 3 >= n0) break;
+    if (step(std::integral_constant<int, 3>{}, i + 3)) break;
   }
+  if constexpr (PRUNE) wait_vmcnt<0>();  // an early exit leaves tile loads in flight
 
   // ---- epilogue: merge the splits, O = acc / l, lse, c ---------------------------------
   if (SP == 2 && sp == 0 && lead && lane == 0) rows.csplit = carry;  // split 0's gate total
@@ -769,15 +830,42 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   }
 }
 
-template <int D, int NWR, int SP>
+template <int D, int NWR, int SP, bool PRUNE>
 __global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
-    float scale_log2) {
+    float scale_log2, const float* __restrict__ knorm) {
   __shared__ GateRows rows;
   __shared__ Bf16Stage<D> s0[SP], s1[SP], s2[SP], s3[SP];
   __shared__ float g0[SP][kBC], g1[SP][kBC], g2[SP][kBC], g3[SP][kBC];
-  fwd_pipe_body<D, NWR, SP>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n, scale_log2);
+  fwd_pipe_body<D, NWR, SP, PRUNE>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n, scale_log2,
+                                   knorm);
+}
+
+// Largest L2 norm of the keys of every 64-key tile (pruning bound).  One wave per tile, a
+// lane per key; keys past n count as 0.
+template <int D>
+__global__ __launch_bounds__(256) void key_tile_norm_kernel(const bf16* __restrict__ k, float* __restrict__ kn, int n) {
+  const int nt = (n + kBC - 1) / kBC;
+  const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const size_t bh = blockIdx.y;
+  if (t >= nt) return;
+  const int key = t * kBC + lane;
+  float ss = 0.0f;
+  if (key < n) {
+    const bf16* row = k + (bh * n + key) * D;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)x[e], (float)x[e], ss);
+    }
+  }
+  float nm = sqrtf(ss);
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) nm = fmaxf(nm, __shfl_xor(nm, o2));
+  if (lane == 0) kn[bh * nt + t] = nm;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -972,19 +1060,25 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 
 template <typename T, int D>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                        float* c, int64_t bh, int n, float scale_log2, hipStream_t stream) {
+                        float* c, int64_t bh, int n, float scale_log2, const float* knorm, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
     // 256-row blocks (8 waves) stage each K/V tile for twice the compute of 128-row
     // blocks, halving the L2 -> LDS traffic per flop; used when there are enough blocks
-    // to keep every CU busy for two rounds.
+    // to keep every CU busy for two rounds.  knorm != nullptr selects the pruned kernels.
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t blocks256 = bh * (int64_t)((n + 255) / 256);
+    const bf16 *qq = (const bf16*)q, *kk = (const bf16*)k, *vv = (const bf16*)v;
+    bf16* oo = (bf16*)o;
     if constexpr (D >= 64) {
       if (blocks256 >= 2 * (int64_t)cus) {
         const dim3 grid((unsigned)bh, (unsigned)((n + 255) / 256));
-        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1>), grid, dim3(512), 0, stream, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+        if (knorm)
+          hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, true>), grid, dim3(512), 0, stream, qq, kk, vv, logf, oo,
+                             lse, c, n, scale_log2, knorm);
+        else
+          hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, false>), grid, dim3(512), 0, stream, qq, kk, vv, logf, oo,
+                             lse, c, n, scale_log2, knorm);
         return hipGetLastError();
       }
     }
@@ -992,19 +1086,31 @@ hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float
     const int64_t blocks128 = bh * (int64_t)((n + 127) / 128);
     if constexpr (D <= 64) {
       // Fewer than two 128-row blocks per CU: split each block's key tiles over two wave sets.
-      if (blocks128 < 2 * (int64_t)cus) {
-        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2>), grid, dim3(512), 0, stream, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+      if (!knorm && blocks128 < 2 * (int64_t)cus) {
+        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, false>), grid, dim3(512), 0, stream, qq, kk, vv, logf, oo,
+                           lse, c, n, scale_log2, knorm);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1>), grid, dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, logf, (bf16*)o, lse, c, n, scale_log2);
+    if (knorm)
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1, true>), grid, dim3(256), 0, stream, qq, kk, vv, logf, oo, lse,
+                         c, n, scale_log2, knorm);
+    else
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1, false>), grid, dim3(256), 0, stream, qq, kk, vv, logf, oo, lse,
+                         c, n, scale_log2, knorm);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
     hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, logf, (float*)o, lse, c, n, scale_log2);
   }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_key_norm_t(const void* k, float* kn, int64_t bh, int n, hipStream_t stream) {
+  const int nt = (n + kBC - 1) / kBC;
+  const dim3 grid((unsigned)((nt + 3) / 4), (unsigned)bh);
+  hipLaunchKernelGGL(key_tile_norm_kernel<D>, grid, dim3(256), 0, stream, (const bf16*)k, kn, n);
   return hipGetLastError();
 }
 
@@ -1015,16 +1121,48 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const fl
   const float scale_log2 = (float)((double)scale * kLog2ed);
   if (is_bf16) {
     switch (d) {
-      case 32: return launch_fwd_t<bf16, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
-      case 64: return launch_fwd_t<bf16, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
-      case 128: return launch_fwd_t<bf16, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+      case 32: return launch_fwd_t<bf16, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 64: return launch_fwd_t<bf16, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 128: return launch_fwd_t<bf16, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
     }
   } else {
     switch (d) {
-      case 32: return launch_fwd_t<float, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
-      case 64: return launch_fwd_t<float, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
-      case 128: return launch_fwd_t<float, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, stream);
+      case 32: return launch_fwd_t<float, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 64: return launch_fwd_t<float, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 128: return launch_fwd_t<float, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t attn_fwd_pruned_workspace_bytes(int64_t bh, int n) {
+  return (size_t)bh * (size_t)((n + kBC - 1) / kBC) * sizeof(float);
+}
+
+hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, const float* logf, void* o,
+                                  float* lse, float* c, float* workspace, int64_t bh, int n, int d, float scale,
+                                  bool is_bf16, hipStream_t stream) {
+  if (!is_bf16)  // the fp32 path is not pruned: it computes every causal pair
+    return launch_attn_fwd(q, k, v, logf, o, lse, c, bh, n, d, scale, false, stream);
+  const float scale_log2 = (float)((double)scale * kLog2ed);
+  hipError_t e = hipSuccess;
+  switch (d) {
+    case 32: e = launch_key_norm_t<32>(k, workspace, bh, n, stream); break;
+    case 64: e = launch_key_norm_t<64>(k, workspace, bh, n, stream); break;
+    case 128: e = launch_key_norm_t<128>(k, workspace, bh, n, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  // A pruned workgroup may stop before tile 0, where the kernel would learn c at its last
+  // row; c comes from the prefix-sum kernel instead.
+  if (c) {
+    e = launch_logf_cumsum(logf, c, bh, n, stream);
+    if (e != hipSuccess) return e;
+  }
+  switch (d) {
+    case 32: return launch_fwd_t<bf16, 32>(q, k, v, logf, o, lse, nullptr, bh, n, scale_log2, workspace, stream);
+    case 64: return launch_fwd_t<bf16, 64>(q, k, v, logf, o, lse, nullptr, bh, n, scale_log2, workspace, stream);
+    case 128: return launch_fwd_t<bf16, 128>(q, k, v, logf, o, lse, nullptr, bh, n, scale_log2, workspace, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -16,6 +16,13 @@ hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
                            float* c, int64_t bh, int n, int d, float scale, bool is_bf16, hipStream_t stream);
 
+// Forward with gate-aware tile skipping (results equal to fp32 rounding); the workspace
+// holds one float per (batch*head, 64-key tile).
+size_t attn_fwd_pruned_workspace_bytes(int64_t bh, int n);
+hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, const float* logf, void* o,
+                                  float* lse, float* c, float* workspace, int64_t bh, int n, int d, float scale,
+                                  bool is_bf16, hipStream_t stream);
+
 // Split-K decode: number of key splits used for these sizes, and the workspace it needs.
 int decode_num_splits(int64_t sh, int l, int d);
 size_t decode_workspace_bytes(int64_t sh, int l, int d);

@@ -91,6 +91,34 @@ fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const flo
                           hipStream_t stream);
 
 /*
+ * fox_attn_fwd_pruned_workspace_bytes -- bytes of scratch fox_attn_fwd_pruned needs
+ * (one float per (batch, head, 64-key tile)).  Returns 0 for invalid sizes.
+ */
+size_t fox_attn_fwd_pruned_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
+
+/*
+ * fox_attn_fwd_pruned -- fox_attn_fwd with gate-aware tile skipping.
+ *   foxwindow README, "The window is a first-passage time": the gate bias
+ *   sum_{t=j+1..i} log f_t only falls as the key j moves away from the query i,
+ *   so beyond some distance every key's weight is negligible.  Walking the key
+ *   tiles down from the diagonal, a query block stops once, for each of its rows,
+ *   the bound  scale * |q_i| * max_j |k_j| + (c_i - c_j1)  on every remaining score
+ *   (Cauchy-Schwarz; j1 the highest remaining key) lies more than (25 + log2 n) * ln 2
+ *   below the row's running max: the skipped keys then weigh less than 2^-24 of the
+ *   row sum, so O and lse equal fox_attn_fwd's to fp32 rounding.  Gates near 1
+ *   (long windows) skip little; fp32 inputs are not pruned (full computation).
+ *
+ *   Arguments as fox_attn_fwd, plus
+ *   workspace, workspace_bytes : device scratch of at least
+ *              fox_attn_fwd_pruned_workspace_bytes(b, h, n, d) bytes, 16-byte aligned,
+ *              not overlapping any other argument; contents on entry are ignored.
+ *   c is produced by the prefix-sum kernel (same values as fox_logf_cumsum).
+ */
+fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, const float* logf, void* o,
+                                 float* lse, float* c, void* workspace, size_t workspace_bytes, int64_t b, int64_t h,
+                                 int64_t n, int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream);
+
+/*
  * fox_attn_decode_workspace_bytes -- bytes of scratch fox_attn_decode needs for
  * these sizes (split-K partial results).  Returns 0 for invalid sizes.
  */

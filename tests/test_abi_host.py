@@ -80,6 +80,32 @@ def test_fwd_rejects_bad_arguments(L):
     assert _fwd(L, lse=G) == INVALID  # lse aliases c
 
 
+def _fwdp(L, q=A, k=B, v=C, logf=D, o=E, lse=F, c=G, ws=H, wsb=1 << 20, b=1, h=2, n=128, d=64, scale=0.17,
+          dt=_lib.FOX_BF16):
+    return L.fox_attn_fwd_pruned(q, k, v, logf, o, lse, c, ws, wsb, b, h, n, d, scale, dt, None)
+
+
+def test_fwd_pruned_workspace_bytes(L):
+    f = L.fox_attn_fwd_pruned_workspace_bytes
+    assert f(2, 16, 4096, 128) == 2 * 16 * 64 * 4  # one float per (batch, head, 64-key tile)
+    assert f(1, 1, 65, 64) == 2 * 4
+    assert f(0, 1, 10, 64) == 0 and f(1, 1, 10, 48) == 0 and f(1, 1, 0, 64) == 0
+
+
+def test_fwd_pruned_rejects_bad_arguments(L):
+    # the forward's own checks apply unchanged
+    assert _fwdp(L, q=None) == INVALID
+    assert _fwdp(L, n=0) == INVALID
+    assert _fwdp(L, d=48) == UNSUP
+    assert _fwdp(L, scale=0.0) == INVALID
+    assert _fwdp(L, o=A) == INVALID
+    # workspace: present, 16-byte aligned, large enough, disjoint from the tensors
+    assert _fwdp(L, ws=None) == _lib.FOX_ERR_WORKSPACE
+    assert _fwdp(L, ws=H + 4) == _lib.FOX_ERR_WORKSPACE
+    assert _fwdp(L, wsb=3) == _lib.FOX_ERR_WORKSPACE
+    assert _fwdp(L, ws=D) == INVALID  # overlaps logf
+
+
 def test_cumsum_rejects_bad_arguments(L):
     f = L.fox_logf_cumsum
     assert f(None, A, 1, 10, None) == INVALID

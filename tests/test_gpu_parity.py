@@ -129,6 +129,74 @@ def test_fwd_full_size_sampled_parity(tag):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+# ---------------------------------------------------------------- forward with tile skipping
+
+def _run_fwd_pruned(inp):
+    q, k, v, logf = (inp[n].to(DEV) for n in ("q", "k", "v", "logf"))
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full_like(logf, nan)
+    c = torch.full_like(logf, nan)
+    fox.attn_fwd_pruned(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)
+    torch.cuda.synchronize()
+    return o, lse, c
+
+
+# (d, B, H, n, gate-logit mean, sd): low means forget fast, so most key tiles are skippable;
+# mean 8 keeps every tile.  Small grids run the 4-wave kernel, the 256-head ones the 8-wave kernel.
+PRUNED = [(64, 2, 2, 777, 0.0, 1.0), (128, 1, 2, 1000, 1.0, 2.0), (32, 2, 2, 300, -1.0, 1.0), (64, 2, 2, 65, 0.0, 1.0),
+          (128, 2, 2, 129, 0.0, 1.0), (64, 2, 2, 512, 8.0, 0.5), (128, 2, 128, 1000, 1.0, 1.0),
+          (64, 4, 64, 777, 0.0, 1.0)]
+
+
+@pytest.mark.parametrize("d,B,H,n,mu,sigma", PRUNED)
+def test_fwd_pruned_parity(d, B, H, n, mu, sigma):
+    """The pruned forward against the oracle (the bf16 bound) and against the unpruned kernel:
+    skipped keys weigh < 2^-24 of each row sum, so the two GPU results agree to output rounding."""
+    cfg = fi.FwdConfig(f"pruned_{d}_{B}_{H}_{n}_{mu}", B, H, n, d, "bf16", mu, sigma)
+    inp = fi.fwd_inputs(cfg)
+    o, lse, c = _run_fwd_pruned(inp)
+    o_full, lse_full, _ = _run_fwd(inp)
+    rows = np.arange(n) if B * H <= 4 else _sampled_rows(n)
+    o_ref, lse_ref = oracle.attn_fwd_rows(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]),
+                                          inp["scale"], rows)
+    c_ref = oracle.logf_cumsum(_np(inp["logf"]))
+    eo = np.abs(_np(o[:, :, rows]) - o_ref).max()
+    el = np.abs(_np(lse[:, :, rows]) - lse_ref).max()
+    ec = np.abs(_np(c) - c_ref).max()
+    do = (o.float() - o_full.float()).abs().max().item()
+    dl = (lse - lse_full).abs().max().item()
+    print(f"  {cfg.desc}: max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc|={ec:.3e}; vs unpruned dO={do:.2e} "
+          f"dlse={dl:.2e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and ec <= _ulp(c_ref)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # Both sum the bf16-rounded weights, and for d <= 64 small grids the unpruned path runs the
+    # key-split kernel (another summation order and max reference): they may differ at the level
+    # of that rounding (a couple of bf16 ulps of O, ~2^-9 of a row sum), not more.
+    assert do <= 2.0 ** -6 and dl <= 4e-3
+
+
+def test_fwd_pruned_full_size_c3():
+    cfg = fi.FWD["c3"]
+    inp = fi.fwd_inputs(cfg)
+    o, lse, c = _run_fwd_pruned(inp)
+    rows = _sampled_rows(cfg.N)
+    o_ref, lse_ref = oracle.attn_fwd_rows(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]),
+                                          inp["scale"], rows)
+    eo = np.abs(_np(o[:, :, rows]) - o_ref).max()
+    el = np.abs(_np(lse[:, :, rows]) - lse_ref).max()
+    print(f"  {cfg.desc} pruned: rows {len(rows)}/head max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_fwd_pruned_f32_is_full():
+    inp = fi.fwd_inputs(fi.FWD["c1"])
+    o, lse, _ = _run_fwd_pruned(inp)
+    o_ref, lse_ref, _ = oracle.attn_fwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]), inp["scale"])
+    assert np.abs(_np(o) - o_ref).max() <= TOL["f32"] and np.abs(_np(lse) - lse_ref).max() <= TOL["f32"]
+
+
 def test_fwd_deterministic():
     inp = fi.fwd_inputs(fi.FWD["c2"])
     a = _run_fwd(inp)
