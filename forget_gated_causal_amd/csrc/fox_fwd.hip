@@ -842,30 +842,36 @@ __global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2
                                    knorm);
 }
 
-// Largest L2 norm of the keys of every 64-key tile (pruning bound).  One wave per tile, a
-// lane per key; keys past n count as 0.
+// Largest L2 norm of the keys of every 64-key tile (pruning bound); keys past n count as 0.
 template <int D>
 __global__ __launch_bounds__(256) void key_tile_norm_kernel(const bf16* __restrict__ k, float* __restrict__ kn, int n) {
+  // One wave per 64-key tile.  A wave-wide load covers 64 consecutive 16-byte chunks, i.e.
+  // 64/(D/8) whole keys, so every load instruction reads one contiguous 1 KiB span.
+  constexpr int LPK = D / 8;        // lanes per key
+  constexpr int KPL = 64 / LPK;     // keys per load
   const int nt = (n + kBC - 1) / kBC;
   const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const size_t bh = blockIdx.y;
   if (t >= nt) return;
-  const int key = t * kBC + lane;
-  float ss = 0.0f;
-  if (key < n) {
-    const bf16* row = k + (bh * n + key) * D;
+  const int sub = lane / LPK, chunk = lane % LPK;
+  float nm = 0.0f;
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+  for (int r = 0; r < kBC / KPL; ++r) {
+    const int key = t * kBC + r * KPL + sub;
+    float ss = 0.0f;
+    if (key < n) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + (bh * n + key) * D + 8 * chunk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf((float)x[e], (float)x[e], ss);
     }
-  }
-  float nm = sqrtf(ss);
 #pragma unroll
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) nm = fmaxf(nm, __shfl_xor(nm, o2));
-  if (lane == 0) kn[bh * nt + t] = nm;
+    for (int o2 = LPK / 2; o2 >= 1; o2 >>= 1) ss += __shfl_xor(ss, o2);
+    nm = fmaxf(nm, ss);
+  }
+#pragma unroll
+  for (int o2 = 32; o2 >= LPK; o2 >>= 1) nm = fmaxf(nm, __shfl_xor(nm, o2));
+  if (lane == 0) kn[bh * nt + t] = sqrtf(nm);
 }
 
 // ------------------------------------------------------------------------------------------

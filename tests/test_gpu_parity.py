@@ -283,5 +283,8 @@ def test_decode_equals_prefill_last_row(dtype):
     torch.cuda.synchronize()
     tol = TOL[dtype]
     assert (od.double() - o[:, :, N - 1].double()).abs().max().item() <= tol
-    assert (lsed - lse[..., N - 1]).abs().max().item() <= 1e-4
+    # The bf16 forward sums the bf16-rounded weights (those its P.V product uses), each within
+    # 2^-9 of the fp32 weight the decode sums, so the two row sums differ by at most 2^-9
+    # relative and the two lse by at most about 2^-9 (natural log); fp32 paths agree closely.
+    assert (lsed - lse[..., N - 1]).abs().max().item() <= (2.0 ** -9 + 1e-5 if dtype == "bf16" else 1e-4)
     assert (cache_c[..., N - 1] - c[..., N - 1]).abs().max().item() <= _ulp(_np(c))
