@@ -489,6 +489,12 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
   float mx0 = kNegInf, mx1 = kNegInf;
   double gx = 0.0, gy = 0.0;  // gate value of key 63-lane of the next tile, its running scan
 
+  // The step runs one of two instances of this schedule (with and without the gate job).  Their
+  // exponentials are identical, so the compiler would hoist them above the branch, out of the
+  // S slots they are meant to overlap; an opaque, instance-specific copy of their inputs keeps
+  // them here.
+  if constexpr (GATE) __asm__ volatile("; gate" : "+v"(sp[0]), "+v"(sp[1]));
+  else __asm__ volatile("; nogate" : "+v"(sp[0]), "+v"(sp[1]));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < PFK; ++i) kop[i] = kread(i);
@@ -774,59 +780,69 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   if (SP == 2 && sp == 0 && lead && lane == 0) rows.csplit = carry;  // split 0's gate total
   __syncthreads();  // rows / cref written by the lead waves are visible; all stages are free
   if constexpr (SP == 2) {
-    // Split 1 leaves (O, m, l) in LDS in its own lane layout; the split-0 wave of the same
-    // rows reads the same lane's values.  Row-wave r uses the memory of stage r.
-    constexpr int CB = (DB * 16 + 2) * 64;
-    static_assert(CB * sizeof(float) <= sizeof(Bf16Stage<D>) && NWR <= 4, "merge buffer");
+    // Split 1 leaves (O, m, l) in LDS in its own lane layout, 16 bytes per lane and write; the
+    // split-0 wave of the same rows reads the same lane's values.  Row-wave r uses the memory
+    // of stage r.
+    constexpr int NQD = 4 * DB;  // float4 quads of O per lane; one more holds (m, l)
+    static_assert((NQD + 1) * 64 * sizeof(f32x4) <= sizeof(Bf16Stage<D>) && NWR <= 4, "merge buffer");
     Bf16Stage<D>* sr = rw == 0 ? s0 : rw == 1 ? s1 : rw == 2 ? s2 : s3;
-    float* cb = reinterpret_cast<float*>(sr);
+    f32x4* cb = reinterpret_cast<f32x4*>(sr);
     if (sp == 1) {
       const bool worked = active && top >= bot;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cb[(db * 16 + r) * 64 + lane] = oacc[db][r];
+      for (int qd = 0; qd < NQD; ++qd) {
+        const int db = qd >> 2, r = 4 * (qd & 3);
+        cb[qd * 64 + lane] = f32x4{oacc[db][r], oacc[db][r + 1], oacc[db][r + 2], oacc[db][r + 3]};
+      }
       // back to the true frame: split 1's scores were high by -csplit * log2 e
-      cb[(DB * 16) * 64 + lane] = worked ? m + (float)(rows.csplit * kLog2ed) : kNegInf;
-      cb[(DB * 16 + 1) * 64 + lane] = lsum;
+      cb[NQD * 64 + lane] = f32x4{worked ? m + (float)(rows.csplit * kLog2ed) : kNegInf, lsum, 0.0f, 0.0f};
       // tile 0 was split 1's: its gate total misses split 0's keys as well
       if (lead && lane == 0 && top >= bot) rows.cref += rows.csplit;
     }
     __syncthreads();
     if (sp == 1) return;
     if (active) {
-      const float m1 = cb[(DB * 16) * 64 + lane];
-      const float l1 = cb[(DB * 16 + 1) * 64 + lane];
-      const float mm = fmaxf(m, m1);
-      const float a0 = exp2_hw(m - mm), a1 = exp2_hw(m1 - mm);
-      lsum = lsum * a0 + l1 * a1;
+      const f32x4 ml = cb[NQD * 64 + lane];
+      const float mm = fmaxf(m, ml[0]);
+      const float a0 = exp2_hw(m - mm), a1 = exp2_hw(ml[0] - mm);
+      lsum = lsum * a0 + ml[1] * a1;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int qd = 0; qd < NQD; ++qd) {
+        const f32x4 x = cb[qd * 64 + lane];
+        const int db = qd >> 2, r = 4 * (qd & 3);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + cb[(db * 16 + r) * 64 + lane] * a1;
+        for (int e = 0; e < 4; ++e) oacc[db][r + e] = oacc[db][r + e] * a0 + x[e] * a1;
+      }
       m = mm;
     }
   }
   if (!active) return;
   const float ltot = pair32_sum(lsum);
   if (my_row >= n) return;
+  // The gate sums of the row are read before the output math so their latency overlaps it.
+  const double ri = rows.rowR[my_row - row0];
+  const double cref = rows.cref;
   const float inv = 1.0f / ltot;
-  bf16* orow = o + base + (size_t)my_row * D;
+  // All packed words first, then the stores back to back (no store waits on a register
+  // that the previous store still has to read).
+  u32x2 w[DB * 4];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-      w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-      *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w;
+      w[db * 4 + g][0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+      w[db * 4 + g][1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
     }
   }
+  bf16* orow = o + base + (size_t)my_row * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w[db * 4 + g];
   if (hi == 0) {
-    const double ri = rows.rowR[my_row - row0];
     const size_t idx = (size_t)bh * n + my_row;
     if (lse) lse[idx] = (float)(((double)m + (double)log2_hw(ltot)) * kLn2d - ri);
-    if (c_out) c_out[idx] = (float)(rows.cref - ri);
+    if (c_out) c_out[idx] = (float)(cref - ri);
   }
 }
 
