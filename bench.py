@@ -26,6 +26,9 @@ Algorithmic work (what the method must do, not what the kernel happens to do):
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -51,6 +54,113 @@ def decode_bytes(cfg) -> dict:
     rd = kv + sh * (cfg.L - 1) * 4 + sh * cfg.d * eb + sh * 4
     wr = sh * cfg.d * eb + sh * 4 + sh * 4
     return {"total": rd + wr, "read": rd, "kv": kv, "write": wr}
+
+
+# HBM-side traffic of the dominant kernel comes from rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain device
+# copy of known size.  The summaries live in profiles/*_traffic.txt with a digest of the kernel
+# sources they were taken on; a summary of older sources is not used (traffic reported as null).
+KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_device.h"], "decode": ["fox_decode.hip", "fox_device.h"]}
+COPY_CAL_BYTES = 1 << 30
+DECODE_KERNEL = "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>"
+
+
+def kernel_source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "forget_gated_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _read_summary(path):
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    return kv
+
+
+def stored_traffic(tag: str, kernel: str, kind: str):
+    """Bytes per launch of `kernel` on workload `tag` from a committed counter summary, or None."""
+    digest = kernel_source_digest(kind)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.txt"))):
+        kv = _read_summary(path)
+        if kv.get("workload") == tag and kv.get("kernel") == kernel and kv.get("source_digest") == digest:
+            return float(kv["traffic_bytes_per_launch"])
+    return None
+
+
+def _counter_per_dispatch(path, counter, name_part):
+    """Mean value of `counter` over the dispatches of kernels whose name contains name_part."""
+    tot, ids = 0.0, set()
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                tot += float(r["Counter_Value"])
+                ids.add(r["Dispatch_Id"])
+    if not ids:
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {name_part!r}")
+    return tot / len(ids), len(ids)
+
+
+def write_traffic_summary(args):
+    """Combine four rocprofv3 --pmc CSVs (kernel FETCH/WRITE, copy FETCH/WRITE) into a summary."""
+    fetch, nf = _counter_per_dispatch(args.fetch_csv, "FETCH_SIZE", args.kernel_match)
+    write, nw = _counter_per_dispatch(args.write_csv, "WRITE_SIZE", args.kernel_match)
+    cf, _ = _counter_per_dispatch(args.copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_per_dispatch(args.copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    f_fac, w_fac = COPY_CAL_BYTES / (cf * 1024), COPY_CAL_BYTES / (cw * 1024)
+    rd, wr = fetch * 1024 * f_fac, write * 1024 * w_fac
+    lines = [
+        f"# rocprofv3 counter summary: HBM-side traffic per launch of {args.kernel} on workload {args.workload}",
+        "# commands (one counter per run; <out> is the output directory):",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o p -- python3 bench.py --workload {args.workload} "
+        "--only --no-cpu-baseline --steps 4 --warmup 2",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o p -- python3 bench.py --workload {args.workload} "
+        "--only --no-cpu-baseline --steps 4 --warmup 2",
+        "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/copy_fetch -o p -- python3 bench.py --copy-calibration",
+        "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/copy_write -o p -- python3 bench.py --copy-calibration",
+        "#   python3 bench.py --traffic-summary ... (this file)",
+        "# calibration: a device copy of 1 GiB reads as FETCH_SIZE "
+        f"{cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB, so the factors are {f_fac:.4f} (read) and {w_fac:.4f} (write)",
+        f"workload: {args.workload}",
+        f"kernel: {args.kernel}",
+        f"source_digest: {kernel_source_digest(args.kind)}",
+        f"dispatches: {nf} (FETCH_SIZE run), {nw} (WRITE_SIZE run)",
+        f"fetch_kib_per_dispatch: {fetch:.1f}",
+        f"write_kib_per_dispatch: {write:.1f}",
+        f"read_bytes_per_launch: {rd:.0f}",
+        f"write_bytes_per_launch: {wr:.0f}",
+        f"traffic_bytes_per_launch: {rd + wr:.0f}",
+    ]
+    if args.alg_bytes:
+        lines.append(f"algorithmic_bytes_per_launch: {args.alg_bytes:.0f}")
+        lines.append(f"traffic_over_algorithmic: {(rd + wr) / args.alg_bytes:.3f}")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, three times (counter calibration)."""
+    import torch
+    x = torch.empty(COPY_CAL_BYTES // 4, device="cuda", dtype=torch.float32).fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_CAL_BYTES} bytes x 3", flush=True)
+
+
+def fwd_min_bytes(cfg) -> float:
+    """Bytes the forward must move: q, k, v, log f read; o, lse, c written."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    rows = cfg.B * cfg.H * cfg.N
+    return rows * cfg.d * eb * 4 + rows * 4 * 3
 
 
 def _events_time(torch, fn, k):
@@ -95,12 +205,13 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup):
     ms = region / steps
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (ms * 1e-3) / 1e12
+    kernel = fwd_kernel_name(torch, cfg)
     return {
         "cfg": cfg, "inp": inp,
         "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-        "kernel": fwd_kernel_name(torch, cfg), "launch_ms_mean": ms,
+        "kernel": kernel, "launch_ms_mean": ms,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4), "traffic": stored_traffic(tag, kernel, "fwd")},
         "flop_per_launch": flops,
     }
 
@@ -131,7 +242,8 @@ def bench_decode(torch, fox, fi, tag, steps, warmup):
         "workload": cfg.desc, "ms_per_step": round(ms, 4), "value": round(by["total"] / (ms * 1e-3) / 1e9, 1),
         "unit": "GB/s", "bytes_per_step": by["total"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": stored_traffic(tag, DECODE_KERNEL, "decode"), "kernel": DECODE_KERNEL,
                      "note": "per call = split kernel + combine kernel; bytes = algorithmic bytes per call"},
         "input_gen_s": round(gen_s, 1),
     }
@@ -200,11 +312,25 @@ def main():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the selected workload only")
+    ap.add_argument("--copy-calibration", action="store_true", help="run the 1 GiB device copy for counter scaling")
+    ap.add_argument("--traffic-summary", action="store_true", help="write a traffic summary from counter CSVs")
+    ap.add_argument("--fetch-csv"), ap.add_argument("--write-csv")
+    ap.add_argument("--copy-fetch-csv"), ap.add_argument("--copy-write-csv")
+    ap.add_argument("--kernel", help="kernel label as bench.py reports it"), ap.add_argument("--kernel-match")
+    ap.add_argument("--kind", choices=["fwd", "decode"], default="fwd")
+    ap.add_argument("--alg-bytes", type=float, default=0.0), ap.add_argument("--out")
     args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+              "the multi-GPU sharding is not built", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
