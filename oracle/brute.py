@@ -1,4 +1,4 @@
-"""Scalar brute-force enumeration of causal FoX attention for tiny inputs.
+"""Scalar brute-force enumeration of FoX attention for tiny inputs.
 
 TEST INFRASTRUCTURE (same rule as the rest of ``oracle/``).
 
@@ -14,22 +14,30 @@ from __future__ import annotations
 import math
 
 
-def brute_fwd_head(q, k, v, logf, scale):
-    """q, k, v: lists [N][d] of floats; logf: list [N]. Returns (O [N][d], lse [N])."""
+def brute_fwd_head(q, k, v, logf, scale, causal=True):
+    """q, k, v: lists [N][d] of floats; logf: list [N]. Returns (O [N][d], lse [N]).
+
+    causal=False (the module's unmasked mode) enumerates every key; a key after the
+    query gets the bias -(sum of log f_t over t = i+1 .. j), summed directly.
+    """
     n = len(q)
     d = len(v[0]) if n else 0
     out, lse = [], []
     for i in range(n):
+        keys = range(i + 1) if causal else range(n)
         logits = []
-        for j in range(i + 1):
+        for j in keys:
             dot = math.fsum(q[i][e] * k[j][e] for e in range(len(q[i])))
-            bias = math.fsum(logf[t] for t in range(j + 1, i + 1))
+            if j <= i:
+                bias = math.fsum(logf[t] for t in range(j + 1, i + 1))
+            else:
+                bias = -math.fsum(logf[t] for t in range(i + 1, j + 1))
             logits.append(scale * dot + bias)
         top = max(logits)
         z = math.fsum(math.exp(s - top) for s in logits)
         row_lse = top + math.log(z)
         w = [math.exp(s - row_lse) for s in logits]
-        out.append([math.fsum(w[j] * v[j][e] for j in range(i + 1)) for e in range(d)])
+        out.append([math.fsum(w[a] * v[j][e] for a, j in enumerate(keys)) for e in range(d)])
         lse.append(row_lse)
     return out, lse
 

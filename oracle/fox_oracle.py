@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for causal Forgetting-Transformer (FoX) attention.
+"""Plain fp64 CPU oracle for Forgetting-Transformer (FoX) attention.
 
 TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
 leg of the benchmark may import this module. The product path (the HIP
@@ -23,6 +23,10 @@ softmax, no split-K):
 * Softmax over keys and the weighted sum of values -- same ``forward``.
   ``lse_i`` is the natural-log log-sum-exp of the full logits row (scale and
   bias included); the pages do not define it, this is the plainest reading.
+* Unmasked mode -- the module's default (not decoder) mode applies no mask: every
+  key j = 0 .. N-1 enters the softmax with the same bias ``c_i - c_j``, which for a
+  key after the query equals ``-(sum_{t=i+1..j} log f_t)`` (>= 0).  Source: the same
+  ``forward``, whose triangle mask is applied in decoder mode only.
 * Decode -- the single query row i = L-1 of a sequence whose key/value cache
   holds slots 0..L-1 (the new token's k, v already at slot L-1) and whose
   cached prefix sums hold slots 0..L-2; the new prefix sum is
@@ -61,15 +65,16 @@ def logf_cumsum(logf) -> np.ndarray:
     return np.cumsum(_f64(logf), axis=-1)
 
 
-def fwd_head_rows(q, k, v, logf, scale, rows, chunk: int = 256):
-    """Definition of causal FoX attention for one head, for selected rows.
+def fwd_head_rows(q, k, v, logf, scale, rows, chunk: int = 256, causal: bool = True):
+    """Definition of FoX attention for one head, for selected rows.
 
     q, k, v: [N, d]; logf: [N]; rows: 1-D integer array of query indices.
     Returns (O[rows] [len(rows), d], lse[rows] [len(rows)]).
 
-    FoX module page, ``ForgettingAttention.forward`` (decoder mode):
-    logits = scale * q k^T + (c_i - c_j), strict upper triangle set to -inf,
-    softmax over keys, times v.  ``lse`` is log sum_j exp(logit_ij).
+    FoX module page, ``ForgettingAttention.forward``:
+    logits = scale * q k^T + (c_i - c_j); in decoder mode (``causal``) the
+    strict upper triangle is set to -inf, in the default mode nothing is
+    masked; softmax over keys, times v.  ``lse`` is log sum_j exp(logit_ij).
     Each row is computed from the definition independently; ``chunk`` only
     bounds how many rows are held in memory at once.
     """
@@ -82,10 +87,11 @@ def fwd_head_rows(q, k, v, logf, scale, rows, chunk: int = 256):
     lse = np.empty(rows.size, dtype=np.float64)
     for lo in range(0, rows.size, chunk):
         r = rows[lo:lo + chunk]
-        kmax = int(r.max()) + 1 if r.size else 0
-        # logits over keys 0..kmax-1 (keys beyond every selected row are masked anyway)
+        # causal: logits over keys 0..kmax-1 (keys beyond every selected row are masked anyway)
+        kmax = (int(r.max()) + 1 if r.size else 0) if causal else n
         s = scale * (q[r] @ k[:kmax].T) + (c[r][:, None] - c[None, :kmax])
-        s = np.where(keys[None, :kmax] > r[:, None], -np.inf, s)
+        if causal:
+            s = np.where(keys[None, :kmax] > r[:, None], -np.inf, s)
         m = s.max(axis=1)
         z = np.exp(s - m[:, None]).sum(axis=1)
         row_lse = m + np.log(z)
@@ -95,7 +101,7 @@ def fwd_head_rows(q, k, v, logf, scale, rows, chunk: int = 256):
     return out, lse
 
 
-def attn_fwd_rows(q, k, v, logf, scale, rows):
+def attn_fwd_rows(q, k, v, logf, scale, rows, causal: bool = True):
     """Rows ``rows`` of every (batch, head): q,k,v [B,H,N,d], logf [B,H,N].
 
     Returns (O [B,H,len(rows),d], lse [B,H,len(rows)]).
@@ -107,17 +113,18 @@ def attn_fwd_rows(q, k, v, logf, scale, rows):
     lse = np.empty((bsz, nh, rows.size), dtype=np.float64)
     for b in range(bsz):
         for h in range(nh):
-            out[b, h], lse[b, h] = fwd_head_rows(q[b, h], k[b, h], v[b, h], logf[b, h], scale, rows)
+            out[b, h], lse[b, h] = fwd_head_rows(q[b, h], k[b, h], v[b, h], logf[b, h], scale, rows,
+                                                 causal=causal)
     return out, lse
 
 
-def attn_fwd(q, k, v, logf, scale):
-    """Full causal FoX attention: q,k,v [B,H,N,d], logf [B,H,N].
+def attn_fwd(q, k, v, logf, scale, causal: bool = True):
+    """Full FoX attention (causal, or unmasked with causal=False): q,k,v [B,H,N,d], logf [B,H,N].
 
     Returns (O [B,H,N,d], lse [B,H,N], c [B,H,N]) in float64.
     """
     n = np.asarray(q).shape[2]
-    out, lse = attn_fwd_rows(q, k, v, logf, scale, np.arange(n))
+    out, lse = attn_fwd_rows(q, k, v, logf, scale, np.arange(n), causal=causal)
     return out, lse, logf_cumsum(logf)
 
 

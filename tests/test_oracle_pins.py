@@ -332,3 +332,174 @@ def test_planted_mistake_is_caught(kind):
             except (AssertionError, ValueError, IndexError):
                 failed.append(pin.__name__)
     assert failed, f"mutant {kind} passed every pin"
+
+
+# ----------------------------------------------------------------------------------------------
+# unmasked (default, non-decoder) mode: every key enters, bias c_i - c_j for all pairs
+# ----------------------------------------------------------------------------------------------
+# FoX module page, ForgettingAttention.forward: the triangle mask belongs to decoder mode only;
+# without it the same scaled q k^T + (cum[i] - cum[j]) is softmaxed over all keys.
+
+def _nc(fwd):
+    """The routine under test in unmasked mode, with the fwd_head_rows signature."""
+    return lambda q, k, v, logf, scale, rows: fwd(q, k, v, logf, scale, rows, causal=False)
+
+
+def npin_unit_gate_is_softmax(fwd):
+    """log f = 0: no bias and no mask, plain softmax attention."""
+    q, k, v, _ = _rand_head(31, 96, 16)
+    scale = 16 ** -0.5
+    o, lse = _all_rows(fwd, q, k, v, np.zeros(96), scale)
+    o_ref, lse_ref = _sdpa(q, k, v, scale, causal=False)
+    assert np.abs(o - o_ref).max() < TOL and np.abs(lse - lse_ref).max() < TOL
+
+
+def npin_constant_gate_is_two_sided_slope(fwd):
+    """log f = -m: bias -m (i - j) for every pair, +m per step for keys after the query."""
+    n, d = 72, 8
+    q, k, v, _ = _rand_head(32, n, d)
+    scale = 0.37
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    for m in (0.05, 0.3):
+        o, lse = _all_rows(fwd, q, k, v, np.full(n, -m), scale)
+        o_ref, lse_ref = _sdpa(q, k, v, scale, mask=-m * (i - j).astype(np.float64))
+        assert np.abs(o - o_ref).max() < TOL and np.abs(lse - lse_ref).max() < TOL
+
+
+def npin_general_bias_by_signed_indicator_sum(fwd):
+    """Random gates: bias_ij = sum_t ([j < t <= i] - [i < t <= j]) log f_t, no prefix sums."""
+    n, d = 40, 12
+    q, k, v, logf = _rand_head(33, n, d, mu=0.5, sigma=1.5)
+    scale = d ** -0.5
+    t = np.arange(n)
+    fwd_ind = (t[None, None, :] > t[None, :, None]) & (t[None, None, :] <= t[:, None, None])  # j < t <= i
+    bwd_ind = (t[None, None, :] > t[:, None, None]) & (t[None, None, :] <= t[None, :, None])  # i < t <= j
+    bias = (fwd_ind.astype(np.float64) - bwd_ind.astype(np.float64)) @ logf
+    o, lse = _all_rows(fwd, q, k, v, logf, scale)
+    o_ref, lse_ref = _sdpa(q, k, v, scale, mask=bias)
+    assert np.abs(o - o_ref).max() < TOL and np.abs(lse - lse_ref).max() < TOL
+
+
+def npin_zero_query_closed_form(fwd):
+    """q = 0: the bias c_i - c_j is rank one, so every row has the same weights, proportional to
+    exp(-c_j): O_i = sum_j e^{-c_j} v_j / sum_j e^{-c_j} and lse_i = c_i + ln sum_j e^{-c_j}."""
+    n, d = 64, 5
+    _, k, v, logf = _rand_head(34, n, d, mu=1.0, sigma=2.0)
+    c = np.array([math.fsum(logf[: i + 1]) for i in range(n)])
+    w = np.exp(-(c - c.max()))  # shifted for range; the shift cancels in the ratio
+    o_ref = (w[:, None] * v).sum(0) / w.sum()
+    lse_ref = c - c.max() + math.log(math.fsum(w))
+    o, lse = _all_rows(fwd, np.zeros((n, d)), k, v, logf, 1.0)
+    assert np.abs(o - o_ref[None, :]).max() < 1e-11 and np.abs(lse - lse_ref).max() < 1e-11
+
+
+def npin_rows_normalised(fwd):
+    q, k, _, logf = _rand_head(35, 50, 8)
+    o, _ = _all_rows(fwd, q, k, np.ones((50, 3)), logf, 0.9)
+    assert np.abs(o - 1.0).max() < TOL
+
+
+def npin_gate_origin_irrelevant(fwd):
+    q, k, v, logf = _rand_head(36, 45, 6)
+    o1, l1 = _all_rows(fwd, q, k, v, logf, 0.4)
+    logf2 = logf.copy()
+    logf2[0] = -7.5
+    o2, l2 = _all_rows(fwd, q, k, v, logf2, 0.4)
+    assert np.abs(o1 - o2).max() < 1e-13 and np.abs(l1 - l2).max() < 1e-13
+
+
+def npin_brute_force(fwd):
+    """Scalar enumeration over every key, biases summed directly in both directions, N <= 8."""
+    for seed, (n, d) in enumerate([(1, 1), (2, 3), (5, 4), (8, 8), (7, 2)]):
+        q, k, v, logf = _rand_head(200 + seed, n, d, mu=0.3, sigma=2.0)
+        scale = d ** -0.5
+        o_b, l_b = brute_fwd_head(q.tolist(), k.tolist(), v.tolist(), logf.tolist(), scale, causal=False)
+        o, lse = _all_rows(fwd, q, k, v, logf, scale)
+        assert np.abs(o - np.array(o_b)).max() < TOL and np.abs(lse - np.array(l_b)).max() < TOL
+
+
+NPINS = [
+    npin_unit_gate_is_softmax,
+    npin_constant_gate_is_two_sided_slope,
+    npin_general_bias_by_signed_indicator_sum,
+    npin_zero_query_closed_form,
+    npin_rows_normalised,
+    npin_gate_origin_irrelevant,
+    npin_brute_force,
+]
+
+
+@pytest.mark.parametrize("pin", NPINS, ids=[p.__name__ for p in NPINS])
+def test_oracle_pin_unmasked(pin):
+    pin(_nc(fwd_head_rows))
+
+
+def test_unmasked_wrapper_matches_heads():
+    r = _rng(37)
+    B, H, N, d = 2, 2, 19, 4
+    q, k, v = (r.standard_normal((B, H, N, d)) for _ in range(3))
+    logf = _logsigmoid(r.normal(2, 1, (B, H, N)))
+    o, lse, _ = attn_fwd(q, k, v, logf, 0.5, causal=False)
+    for b in range(B):
+        for h in range(H):
+            oh, lh = fwd_head_rows(q[b, h], k[b, h], v[b, h], logf[b, h], 0.5, np.arange(N), causal=False)
+            assert np.array_equal(oh, o[b, h]) and np.array_equal(lh, lse[b, h])
+    # the last row sees every key in both modes
+    oc, lc, _ = attn_fwd(q, k, v, logf, 0.5)
+    assert np.abs(oc[:, :, -1] - o[:, :, -1]).max() < 1e-13 and np.abs(lc[:, :, -1] - lse[:, :, -1]).max() < 1e-13
+
+
+def _mutant_unmasked(kind):
+    def fwd(q, k, v, logf, scale, rows):
+        q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+        logf = np.asarray(logf, np.float64)
+        c = np.cumsum(logf)
+        if kind == "exclusive_scan":
+            c = c - logf
+        n = q.shape[0]
+        rows = np.asarray(rows)
+        keys = np.arange(n)
+        qq, kk = (k, q) if kind == "swap_qk" else (q, k)
+        bias = c[rows][:, None] - c[None, :]
+        if kind == "bias_sign":
+            bias = -bias
+        if kind == "future_bias_dropped":  # bias applied below the diagonal only
+            bias = np.where(keys[None, :] > rows[:, None], 0.0, bias)
+        if kind == "future_bias_mirrored":  # |i - j| distance decay in both directions
+            bias = np.where(keys[None, :] > rows[:, None], -bias, bias)
+        s = scale * (qq[rows] @ kk.T + bias) if kind == "scaled_bias" else scale * (qq[rows] @ kk.T) + bias
+        if kind == "drop_bias":
+            s = scale * (qq[rows] @ kk.T)
+        if kind == "causal_mask":
+            s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+        m = s.max(1)
+        lse = m + np.log(np.exp(s - m[:, None]).sum(1))
+        if kind == "lse_base2":
+            lse = lse / math.log(2)
+            p = np.exp((s - m[:, None])) / np.exp(s - m[:, None]).sum(1)[:, None]
+        else:
+            p = np.exp(s - lse[:, None])
+        vv = v[::-1] if kind == "reversed_values" else v
+        return p @ vv, lse
+    return fwd
+
+
+MUTANTS_UNMASKED = ["exclusive_scan", "swap_qk", "bias_sign", "future_bias_dropped", "future_bias_mirrored",
+                    "scaled_bias", "drop_bias", "causal_mask", "lse_base2", "reversed_values"]
+
+
+def test_unmasked_reference_mutant_passes():
+    for pin in NPINS:
+        pin(_mutant_unmasked("none"))
+
+
+@pytest.mark.parametrize("kind", MUTANTS_UNMASKED)
+def test_unmasked_planted_mistake_is_caught(kind):
+    failed = []
+    with np.errstate(all="ignore"):
+        for pin in NPINS:
+            try:
+                pin(_mutant_unmasked(kind))
+            except (AssertionError, ValueError, IndexError):
+                failed.append(pin.__name__)
+    assert failed, f"mutant {kind} passed every unmasked-mode pin"
