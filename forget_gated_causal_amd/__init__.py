@@ -6,6 +6,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
 
     c            = logf_cumsum(logf)                          # [..., N] fp32
     o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
+    o, lse, c    = attn_fwd_noncausal(q, k, v, logf)          # every key, no mask
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
 """
 
@@ -15,7 +16,7 @@ import torch
 
 from ._lib import FOX_BF16, FOX_F32, FoxError, check, lib, status_string  # noqa: F401
 
-__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes", "attn_decode",
+__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes", "attn_decode",
            "decode_workspace_bytes", "FoxError", "status_string"]
 
 _DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
@@ -53,12 +54,8 @@ def logf_cumsum(logf: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     return c
 
 
-def attn_fwd(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=None,
-             want_lse: bool = True, want_c: bool = True):
-    """Causal FoX attention forward. q, k, v: [B,H,N,d] (fp32 or bf16); logf: [B,H,N] fp32.
-
-    Returns (o, lse, c); lse / c are None when not wanted.
-    """
+def _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c):
+    """Checks the forward inputs and returns (dtype code, o, lse, c), allocating missing outputs."""
     B, H, N, d = q.shape
     dt = _DTYPES.get(q.dtype)
     if dt is None:
@@ -75,11 +72,34 @@ def attn_fwd(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=No
         lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
     if want_c and c is None:
         c = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    return dt, o, (lse if want_lse else None), (c if want_c else None)
+
+
+def attn_fwd(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=None,
+             want_lse: bool = True, want_c: bool = True):
+    """Causal FoX attention forward. q, k, v: [B,H,N,d] (fp32 or bf16); logf: [B,H,N] fp32.
+
+    Returns (o, lse, c); lse / c are None when not wanted.
+    """
+    B, H, N, d = q.shape
+    dt, o, lse, c = _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c)
     scale = _default_scale(d) if scale is None else float(scale)
-    st = lib().fox_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse if want_lse else None),
-                            _ptr(c if want_c else None), B, H, N, d, scale, dt, _stream())
+    st = lib().fox_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse), _ptr(c), B, H, N, d, scale,
+                            dt, _stream())
     check("fox_attn_fwd", st)
-    return o, (lse if want_lse else None), (c if want_c else None)
+    return o, lse, c
+
+
+def attn_fwd_noncausal(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=None,
+                       want_lse: bool = True, want_c: bool = True):
+    """FoX attention forward over every key (no causal mask); arguments and results as attn_fwd."""
+    B, H, N, d = q.shape
+    dt, o, lse, c = _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = lib().fox_attn_fwd_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse), _ptr(c), B, H, N, d,
+                                      scale, dt, _stream())
+    check("fox_attn_fwd_noncausal", st)
+    return o, lse, c
 
 
 def attn_fwd_pruned_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
@@ -94,30 +114,15 @@ def attn_fwd_pruned(q, k, v, logf, scale: float | None = None, out=None, lse=Non
     bytes (allocated here when None).
     """
     B, H, N, d = q.shape
-    dt = _DTYPES.get(q.dtype)
-    if dt is None:
-        raise ValueError(f"unsupported dtype {q.dtype}")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, q.dtype)
-        if tuple(t.shape) != (B, H, N, d):
-            raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, H, N, d)}")
-    _need(logf, "logf", torch.float32)
-    if tuple(logf.shape) != (B, H, N):
-        raise ValueError(f"logf shape {tuple(logf.shape)} != {(B, H, N)}")
-    o = torch.empty_like(q) if out is None else out
-    if want_lse and lse is None:
-        lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
-    if want_c and c is None:
-        c = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    dt, o, lse, c = _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c)
     wb = attn_fwd_pruned_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(wb, 16), device=q.device, dtype=torch.uint8)
     scale = _default_scale(d) if scale is None else float(scale)
-    st = lib().fox_attn_fwd_pruned(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse if want_lse else None),
-                                   _ptr(c if want_c else None), _ptr(workspace), workspace.numel(), B, H, N, d,
-                                   scale, dt, _stream())
+    st = lib().fox_attn_fwd_pruned(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse), _ptr(c),
+                                   _ptr(workspace), workspace.numel(), B, H, N, d, scale, dt, _stream())
     check("fox_attn_fwd_pruned", st)
-    return o, (lse if want_lse else None), (c if want_c else None)
+    return o, lse, c
 
 
 def decode_workspace_bytes(s: int, h: int, l: int, d: int) -> int:

@@ -27,6 +27,8 @@ SIGNATURES = {
     "fox_logf_cumsum": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "fox_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                     ctypes.c_int, _P]),
+    "fox_attn_fwd_noncausal": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                              ctypes.c_int, _P]),
     "fox_attn_fwd_pruned_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "fox_attn_fwd_pruned": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _I64, _I64,
                                            ctypes.c_float, ctypes.c_int, _P]),

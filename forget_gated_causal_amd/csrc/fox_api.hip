@@ -52,7 +52,7 @@ fox_status_t fox_logf_cumsum(const float* logf, float* c, int64_t rows, int64_t 
   return from_hip(fox::launch_logf_cumsum(logf, c, rows, (int)n, stream));
 }
 
-// Validation shared by the two forward entry points.
+// Validation shared by the forward entry points.
 static fox_status_t fwd_args(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
                              float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype) {
   if (!q || !k || !v || !logf || !o) return FOX_ERR_INVALID_ARG;
@@ -80,8 +80,17 @@ fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const flo
                           hipStream_t stream) {
   const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
   if (st != FOX_OK) return st;
-  return from_hip(
-      fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b * h, (int)n, (int)d, scale, dtype == FOX_BF16, stream));
+  return from_hip(fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b * h, (int)n, (int)d, scale, dtype == FOX_BF16,
+                                       true, stream));
+}
+
+fox_status_t fox_attn_fwd_noncausal(const void* q, const void* k, const void* v, const float* logf, void* o,
+                                    float* lse, float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale,
+                                    fox_dtype_t dtype, hipStream_t stream) {
+  const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
+  if (st != FOX_OK) return st;
+  return from_hip(fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b * h, (int)n, (int)d, scale, dtype == FOX_BF16,
+                                       false, stream));
 }
 
 size_t fox_attn_fwd_pruned_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d) {

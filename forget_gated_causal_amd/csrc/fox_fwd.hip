@@ -57,7 +57,7 @@ constexpr float kNegInf = -INFINITY;
 
 struct GateRows {          // per workgroup
   double rowR[kMaxBR + 1]; // R_i for the block's own rows; the last slot takes discarded writes
-  double cref;             // c at the block's reference row (sum of log f over 0..ref)
+  double cref;             // c at the frame row of the gate sums (sum of log f up to it)
   double cref_discard;     // takes the cref write of tiles other than tile 0
   double csplit;           // key split: sum of log f over split 0's keys (split 1's frame offset)
   float kmax;              // pruning: largest key norm of the block's key range
@@ -96,7 +96,8 @@ struct GateJob {
   const float* lf;  // the tile's staged log gates
   float* r2;        // its biases R_j * log2 e (out)
   int kt;           // tile index
-  int row0, ref;
+  int row0, ref;    // the block's first and last rows (R_i of these rows is kept)
+  int fref;         // frame row: gates past it do not enter the sums
   GateRows* rows;
   double* carry;
 };
@@ -518,7 +519,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
     for (int kq = 0; kq < 8; ++kq)  // bias quads needed in the first P.V slots
       if ((4 * kq) / EP - RD + NQ == i) r2[kq] = *reinterpret_cast<const f32x4*>(&r2cur[8 * kq + 4 * hi]);
     if (i == NQ - 1) pack(0);
-    if (GATE && i == 0) gx = (double)((gj.kt * kBC + 63 - lane <= gj.ref) ? gj.lf[63 - lane] : 0.0f);
+    if (GATE && i == 0) gx = (double)((gj.kt * kBC + 63 - lane <= gj.fref) ? gj.lf[63 - lane] : 0.0f);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -573,7 +574,12 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
 // max by more than that, so all remaining keys together weigh less than 2^-24 of the row sum
 // (Cauchy-Schwarz on q.k; R_j grows with j).  The workgroup leaves the loop when all its
 // waves have stopped.  Results then equal the full computation to fp32 rounding.
-template <int D, int NWR, int SP, bool PRUNE>
+//
+// CAUSAL == false (the module's default, unmasked mode): every row attends to every key; the
+// gate sums are taken relative to the last row of the sequence (R_j = sum_{t=j+1..n-1} log f_t,
+// so c_i - c_j = R_j - R_i still holds, with R_j >= 0 past the row), the walk starts at the
+// last key tile, where each row's largest bias lies, and only keys past n are masked.
+template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL>
 __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1, Bf16Stage<D>* s2,
                                               Bf16Stage<D>* s3, float (*g0)[kBC], float (*g1)[kBC],
                                               float (*g2)[kBC], float (*g3)[kBC], GateRows& rows,
@@ -587,12 +593,14 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   constexpr int KK = D / 16, DB = D / 32, BR = G::BR;
   static_assert(SP == 1 || SP == 2, "key splits");
   static_assert(!PRUNE || SP == 1, "pruning runs without the key split");
+  static_assert(!PRUNE || CAUSAL, "pruning bounds the keys below the diagonal");
 
   const int bh = blockIdx.x;
   const int qb = gridDim.y - 1 - blockIdx.y;
   const int row0 = qb * BR;
-  const int ref = min(row0 + BR - 1, n - 1);
-  const int kt_hi = ref / kBC;
+  const int ref = min(row0 + BR - 1, n - 1);  // the block's last row
+  const int fref = CAUSAL ? ref : n - 1;      // frame row of the gate sums
+  const int kt_hi = fref / kBC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rw = wave % NWR;                                    // row-wave
   const int sp = __builtin_amdgcn_readfirstlane(wave / NWR);  // key split (wave-uniform: LDS DMA bases)
@@ -612,7 +620,10 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
 
   const int wrow0 = row0 + rw * 32;
   const bool active = wrow0 < n;
-  const int kt_first = !active ? -1 : (sp == 0 ? min(wrow0 + 31, n - 1) / kBC : top);
+  int kt_first = !active ? -1 : (sp == 0 && CAUSAL ? min(wrow0 + 31, n - 1) / kBC : top);
+  // Opaque to the optimiser: with every wave starting at the split's top tile (unmasked mode)
+  // it would otherwise specialise the first unrolled step and run out of registers.
+  __asm__ volatile("" : "+v"(kt_first));
   const int my_row = wrow0 + l32;
   LaneOffsets<D> off = lane_offsets<D>(lane);
   off.k += (uint32_t)(sp * sizeof(Bf16Stage<D>));  // 1 KB multiple: the XOR swizzles still apply
@@ -694,7 +705,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   float m = 0.0f, lsum = 0.0f;  // m: running max (base 2); scores are kept relative to it
   f32x16 cinit = f32x16{};      // -m / (scale log2 e) in every lane register: S accumulators start there
   auto gate_in = [&](const float* lf, int t, int ln) {
-    return (t * kBC + 63 - ln <= ref) ? lf[63 - ln] : 0.0f;
+    return (t * kBC + 63 - ln <= fref) ? lf[63 - ln] : 0.0f;
   };
   if (lead && top >= bot)
     gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry);
@@ -733,12 +744,14 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
     const bool gate_job = lead && kt - 1 >= bot;
     bool gate_done = false;
-    const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, &rows, &carry};
+    const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, fref, &rows, &carry};
     const bool stop_here = PRUNE && active && !wdone && kt < kt_first && kt >= bot && prune_stop(kt, gates(J));
     if (active && kt >= bot && kt <= kt_first && !wdone) {
       if (kt == kt_first) {  // first tile of this wave: nothing to overlap with
         pipe_qk<D>(stage(J)[0], off.k, qreg, cinit, sc);
-        const float mx = sp == 0 ? pipe_scores<true>(sc, gates(J), kt * kBC, my_row, ln >> 5, scale_log2)
+        // split 0's first tile holds the row's diagonal (causal) or the end of the sequence
+        const float mx = sp == 0 ? pipe_scores<true>(sc, gates(J), kt * kBC, CAUSAL ? my_row : n - 1, ln >> 5,
+                                                     scale_log2)
                                  : pipe_scores<false>(sc, gates(J), 0, 0, ln >> 5, scale_log2);
         pipe_first_max<PipeGeom<D>::FOLD>(mx, m, sc, cinit, scale_log2);
       } else if (gate_job) {
@@ -820,7 +833,10 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   const float ltot = pair32_sum(lsum);
   if (my_row >= n) return;
   // The gate sums of the row are read before the output math so their latency overlaps it.
-  const double ri = rows.rowR[my_row - row0];
+  // Rows in split 1's key range (unmasked mode only) got R_i in split 1's frame, which misses
+  // the gates of split 0's keys.
+  double ri = rows.rowR[my_row - row0];
+  if (SP == 2 && !CAUSAL && my_row / kBC <= kt_hi - n0) ri += rows.csplit;
   const double cref = rows.cref;
   const float inv = 1.0f / ltot;
   // All packed words first, then the stores back to back (no store waits on a register
@@ -846,7 +862,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   }
 }
 
-template <int D, int NWR, int SP, bool PRUNE>
+template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL>
 __global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
@@ -854,8 +870,8 @@ __global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2
   __shared__ GateRows rows;
   __shared__ Bf16Stage<D> s0[SP], s1[SP], s2[SP], s3[SP];
   __shared__ float g0[SP][kBC], g1[SP][kBC], g2[SP][kBC], g3[SP][kBC];
-  fwd_pipe_body<D, NWR, SP, PRUNE>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n, scale_log2,
-                                   knorm);
+  fwd_pipe_body<D, NWR, SP, PRUNE, CAUSAL>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n,
+                                           scale_log2, knorm);
 }
 
 // Largest L2 norm of the keys of every 64-key tile (pruning bound); keys past n count as 0.
@@ -944,7 +960,7 @@ __device__ __forceinline__ void f32_store_tile(const F32Tile<D>& t, F32Lds<D>& s
   }
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                           const float* __restrict__ v,
                                                           const float* __restrict__ logf, float* __restrict__ o,
@@ -956,8 +972,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const int bh = blockIdx.x;
   const int qb = gridDim.y - 1 - blockIdx.y;
   const int row0 = qb * kBR;
-  const int ref = min(row0 + kBR - 1, n - 1);
-  const int kt_hi = ref / kBC;
+  const int ref = min(row0 + kBR - 1, n - 1);  // the block's last row
+  const int fref = CAUSAL ? ref : n - 1;       // frame row of the gate sums
+  const int kt_hi = fref / kBC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t base = (size_t)bh * n * D;
@@ -967,7 +984,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 
   const int wrow0 = row0 + wave * 32;
   const bool active = wrow0 < n;
-  const int kt_first = active ? min(wrow0 + 31, n - 1) / kBC : -1;
+  const int kt_first = !active ? -1 : (CAUSAL ? min(wrow0 + 31, n - 1) / kBC : kt_hi);
   const int my_row = wrow0 + l32;
 
   float qf[KK];
@@ -979,13 +996,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m = kNegInf, lsum = 0.0f;
   double carry = 0.0, ri_row = 0.0;
-
+  // Unmasked mode: the biases stay relative to the frame row n-1 (R_j - 0), where every row's
+  // heaviest keys lie, so those scores are small and exactly rounded; R_i comes off in lse.
   F32Tile<D> tile;
   f32_load_tile<D>(tile, kb, vb, kt_hi, n, tid);
   float lf = 0.0f;  // wave 0: log f of key 63-lane of the next tile
   if (wave == 0) {
     const int j = kt_hi * kBC + 63 - lane;
-    lf = (j <= ref) ? lfb[j] : 0.0f;
+    lf = (j <= fref) ? lfb[j] : 0.0f;
   }
 
   for (int kt = kt_hi; kt >= 0; --kt) {
@@ -1010,8 +1028,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     }
 
     // This row's R_i is in the gate LDS from the wave's first (diagonal) tile on.
-    if (kt == kt_first) ri_row = (my_row < n) ? lds.rows.rowR[my_row - row0] : 0.0;
-    const bool diag = kt * kBC + kBC - 1 > wrow0;
+    if (CAUSAL && kt == kt_first) ri_row = (my_row < n) ? lds.rows.rowR[my_row - row0] : 0.0;
+    // causal: keys past the row; otherwise only keys past the end of the sequence
+    const int last_key = CAUSAL ? my_row : n - 1;
+    const bool diag = CAUSAL ? kt * kBC + kBC - 1 > wrow0 : kt * kBC + kBC > n;
     float mx = kNegInf;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -1023,7 +1043,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
           // full bias sum_{t=j+1..i} log f_t = R_j - R_i, formed in fp64 and rounded once
           const float bias2 = (float)((lds.r64[kl + e] - ri_row) * kLog2ed);
           float s = fmaf(sacc[b][4 * g + e], scale_log2, bias2);
-          if (diag && kt * kBC + kl + e > my_row) s = kNegInf;
+          if (diag && kt * kBC + kl + e > last_key) s = kNegInf;
           sacc[b][4 * g + e] = s;
           mx = fmaxf(mx, s);
         }
@@ -1075,57 +1095,73 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   if (hi == 0) {
     const double ri = lds.rows.rowR[my_row - row0];
     const size_t idx = (size_t)bh * n + my_row;
-    if (lse) lse[idx] = (float)(((double)m + (double)log2f(ltot)) * kLn2d);  // scores already carry -R_i
+    // causal scores already carry -R_i
+    if (lse) lse[idx] = (float)(((double)m + (double)log2f(ltot)) * kLn2d - (CAUSAL ? 0.0 : ri));
     if (c_out) c_out[idx] = (float)(lds.rows.cref - ri);
   }
 }
 
-template <typename T, int D>
+// Kernel choice for the bf16 forward (knorm != nullptr selects the pruned, causal kernels):
+//  * 256-row blocks (8 waves) stage each K/V tile for twice the compute of 128-row blocks,
+//    halving the L2 -> LDS traffic per flop; used when there are enough blocks to keep every
+//    CU busy for two rounds;
+//  * d <= 64 with fewer than two 128-row blocks per CU: 128-row blocks whose key tiles are
+//    split over two wave sets;
+//  * otherwise 128-row blocks of 4 waves.
+template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
                         float* c, int64_t bh, int n, float scale_log2, const float* knorm, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    // 256-row blocks (8 waves) stage each K/V tile for twice the compute of 128-row
-    // blocks, halving the L2 -> LDS traffic per flop; used when there are enough blocks
-    // to keep every CU busy for two rounds.  knorm != nullptr selects the pruned kernels.
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t blocks256 = bh * (int64_t)((n + 255) / 256);
+    const int64_t blocks128 = bh * (int64_t)((n + 127) / 128);
     const bf16 *qq = (const bf16*)q, *kk = (const bf16*)k, *vv = (const bf16*)v;
     bf16* oo = (bf16*)o;
+    auto go = [&](auto kernel, int rows, int threads) {
+      const dim3 grid((unsigned)bh, (unsigned)((n + rows - 1) / rows));
+      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, qq, kk, vv, logf, oo, lse, c, n, scale_log2, knorm);
+      return hipGetLastError();
+    };
     if constexpr (D >= 64) {
       if (blocks256 >= 2 * (int64_t)cus) {
-        const dim3 grid((unsigned)bh, (unsigned)((n + 255) / 256));
-        if (knorm)
-          hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, true>), grid, dim3(512), 0, stream, qq, kk, vv, logf, oo,
-                             lse, c, n, scale_log2, knorm);
-        else
-          hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, false>), grid, dim3(512), 0, stream, qq, kk, vv, logf, oo,
-                             lse, c, n, scale_log2, knorm);
-        return hipGetLastError();
+        if constexpr (CAUSAL)
+          if (knorm) return go(fwd_bf16_pipe_kernel<D, 8, 1, true, true>, 256, 512);
+        return go(fwd_bf16_pipe_kernel<D, 8, 1, false, CAUSAL>, 256, 512);
       }
     }
-    const dim3 grid((unsigned)bh, (unsigned)((n + 127) / 128));
-    const int64_t blocks128 = bh * (int64_t)((n + 127) / 128);
     if constexpr (D <= 64) {
-      // Fewer than two 128-row blocks per CU: split each block's key tiles over two wave sets.
-      if (!knorm && blocks128 < 2 * (int64_t)cus) {
-        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, false>), grid, dim3(512), 0, stream, qq, kk, vv, logf, oo,
-                           lse, c, n, scale_log2, knorm);
-        return hipGetLastError();
-      }
+      if (!knorm && blocks128 < 2 * (int64_t)cus) return go(fwd_bf16_pipe_kernel<D, 4, 2, false, CAUSAL>, 128, 512);
     }
-    if (knorm)
-      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1, true>), grid, dim3(256), 0, stream, qq, kk, vv, logf, oo, lse,
-                         c, n, scale_log2, knorm);
-    else
-      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1, false>), grid, dim3(256), 0, stream, qq, kk, vv, logf, oo, lse,
-                         c, n, scale_log2, knorm);
+    if constexpr (CAUSAL)
+      if (knorm) return go(fwd_bf16_pipe_kernel<D, 4, 1, true, true>, 128, 256);
+    return go(fwd_bf16_pipe_kernel<D, 4, 1, false, CAUSAL>, 128, 256);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
-    hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, logf, (float*)o, lse, c, n, scale_log2);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+}
+
+template <bool CAUSAL>
+hipError_t launch_fwd_d(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse, float* c,
+                        int64_t bh, int n, int d, float scale, bool is_bf16, const float* knorm, hipStream_t stream) {
+  const float scale_log2 = (float)((double)scale * kLog2ed);
+  if (is_bf16) {
+    switch (d) {
+      case 32: return launch_fwd_t<bf16, 32, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, stream);
+      case 64: return launch_fwd_t<bf16, 64, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, stream);
+      case 128: return launch_fwd_t<bf16, 128, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, stream);
+    }
+  } else {
+    switch (d) {
+      case 32: return launch_fwd_t<float, 32, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 64: return launch_fwd_t<float, 64, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 128: return launch_fwd_t<float, 128, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -1139,22 +1175,10 @@ hipError_t launch_key_norm_t(const void* k, float* kn, int64_t bh, int n, hipStr
 }  // namespace
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, hipStream_t stream) {
-  const float scale_log2 = (float)((double)scale * kLog2ed);
-  if (is_bf16) {
-    switch (d) {
-      case 32: return launch_fwd_t<bf16, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-      case 64: return launch_fwd_t<bf16, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-      case 128: return launch_fwd_t<bf16, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-    }
-  } else {
-    switch (d) {
-      case 32: return launch_fwd_t<float, 32>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-      case 64: return launch_fwd_t<float, 64>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-      case 128: return launch_fwd_t<float, 128>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-    }
-  }
-  return hipErrorInvalidValue;
+                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, bool causal,
+                           hipStream_t stream) {
+  return causal ? launch_fwd_d<true>(q, k, v, logf, o, lse, c, bh, n, d, scale, is_bf16, nullptr, stream)
+                : launch_fwd_d<false>(q, k, v, logf, o, lse, c, bh, n, d, scale, is_bf16, nullptr, stream);
 }
 
 size_t attn_fwd_pruned_workspace_bytes(int64_t bh, int n) {
@@ -1165,8 +1189,7 @@ hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, c
                                   float* lse, float* c, float* workspace, int64_t bh, int n, int d, float scale,
                                   bool is_bf16, hipStream_t stream) {
   if (!is_bf16)  // the fp32 path is not pruned: it computes every causal pair
-    return launch_attn_fwd(q, k, v, logf, o, lse, c, bh, n, d, scale, false, stream);
-  const float scale_log2 = (float)((double)scale * kLog2ed);
+    return launch_attn_fwd(q, k, v, logf, o, lse, c, bh, n, d, scale, false, true, stream);
   hipError_t e = hipSuccess;
   switch (d) {
     case 32: e = launch_key_norm_t<32>(k, workspace, bh, n, stream); break;
@@ -1181,12 +1204,7 @@ hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, c
     e = launch_logf_cumsum(logf, c, bh, n, stream);
     if (e != hipSuccess) return e;
   }
-  switch (d) {
-    case 32: return launch_fwd_t<bf16, 32>(q, k, v, logf, o, lse, nullptr, bh, n, scale_log2, workspace, stream);
-    case 64: return launch_fwd_t<bf16, 64>(q, k, v, logf, o, lse, nullptr, bh, n, scale_log2, workspace, stream);
-    case 128: return launch_fwd_t<bf16, 128>(q, k, v, logf, o, lse, nullptr, bh, n, scale_log2, workspace, stream);
-  }
-  return hipErrorInvalidValue;
+  return launch_fwd_d<true>(q, k, v, logf, o, lse, nullptr, bh, n, d, scale, true, workspace, stream);
 }
 
 }  // namespace fox

@@ -12,9 +12,11 @@ namespace fox {
 // Inclusive prefix sums of `rows` independent rows of length n (fp64 accumulate).
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream);
 
-// Causal FoX forward; is_bf16 selects the element type of q/k/v/o; d in {32,64,128}.
+// FoX forward, causal (decoder mode) or over every key; is_bf16 selects the element type of
+// q/k/v/o; d in {32,64,128}.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, hipStream_t stream);
+                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, bool causal,
+                           hipStream_t stream);
 
 // Forward with gate-aware tile skipping (results equal to fp32 rounding); the workspace
 // holds one float per (batch*head, 64-key tile).

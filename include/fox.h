@@ -91,6 +91,20 @@ fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const flo
                           hipStream_t stream);
 
 /*
+ * fox_attn_fwd_noncausal -- FoX attention forward without the causal mask.
+ *   FoX module page, ForgettingAttention.forward in its default (not decoder)
+ *   mode: the same scaled q k^T plus bias cum[i] - cum[j], softmax over every
+ *   key of the sequence.  For a key after the query (j > i) the bias is
+ *   c_i - c_j = -(sum_{t=i+1..j} log f_t) >= 0, so later keys are weighted up.
+ *
+ *   Arguments, layouts, outputs and errors exactly as fox_attn_fwd; lse is the
+ *   log-sum-exp over all n keys of each row.
+ */
+fox_status_t fox_attn_fwd_noncausal(const void* q, const void* k, const void* v, const float* logf, void* o,
+                                    float* lse, float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale,
+                                    fox_dtype_t dtype, hipStream_t stream);
+
+/*
  * fox_attn_fwd_pruned_workspace_bytes -- bytes of scratch fox_attn_fwd_pruned needs
  * (one float per (batch, head, 64-key tile)).  Returns 0 for invalid sizes.
  */

@@ -4,6 +4,8 @@ anything (no GPU needed: every call here fails validation)."""
 
 from __future__ import annotations
 
+import functools
+
 import ctypes
 import os
 import re
@@ -56,11 +58,14 @@ def test_decode_workspace_bytes(L):
     assert f(1, 1, 1, 32) == 1 * 34 * 4  # one split for a single key
 
 
-def _fwd(L, q=A, k=B, v=C, logf=D, o=E, lse=F, c=G, b=1, h=2, n=128, d=32, scale=0.17, dt=_lib.FOX_F32):
-    return L.fox_attn_fwd(q, k, v, logf, o, lse, c, b, h, n, d, scale, dt, None)
+def _fwd(L, q=A, k=B, v=C, logf=D, o=E, lse=F, c=G, b=1, h=2, n=128, d=32, scale=0.17, dt=_lib.FOX_F32,
+         fn="fox_attn_fwd"):
+    return getattr(L, fn)(q, k, v, logf, o, lse, c, b, h, n, d, scale, dt, None)
 
 
-def test_fwd_rejects_bad_arguments(L):
+@pytest.mark.parametrize("fn", ["fox_attn_fwd", "fox_attn_fwd_noncausal"])
+def test_fwd_rejects_bad_arguments(L, fn):
+    _fwd = functools.partial(globals()["_fwd"], fn=fn)
     assert _fwd(L, q=None) == INVALID
     assert _fwd(L, o=None) == INVALID
     assert _fwd(L, logf=None) == INVALID

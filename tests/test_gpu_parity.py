@@ -129,6 +129,63 @@ def test_fwd_full_size_sampled_parity(tag):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+# ---------------------------------------------------------------- forward without the causal mask
+
+def _run_fwd_nc(inp):
+    q, k, v, logf = (inp[n].to(DEV) for n in ("q", "k", "v", "logf"))
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full_like(logf, nan)
+    c = torch.full_like(logf, nan)
+    fox.attn_fwd_noncausal(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)
+    torch.cuda.synchronize()
+    return o, lse, c
+
+
+def _check_fwd_nc(inp, tol, rows=None):
+    o, lse, c = _run_fwd_nc(inp)
+    n = inp["q"].shape[2]
+    rows = np.arange(n) if rows is None else rows
+    o_ref, lse_ref = oracle.attn_fwd_rows(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]),
+                                          inp["scale"], rows, causal=False)
+    c_ref = oracle.logf_cumsum(_np(inp["logf"]))
+    eo = np.abs(_np(o[:, :, rows]) - o_ref).max()
+    el = np.abs(_np(lse[:, :, rows]) - lse_ref).max()
+    ec = np.abs(_np(c) - c_ref).max()
+    print(f"  unmasked: max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc|={ec:.3e}", flush=True)
+    assert eo <= tol and el <= tol and ec <= _ulp(c_ref)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("tag", ["c1", "c2", "c2_f1", "c2_alibi"])
+def test_fwd_noncausal_config_parity(tag):
+    cfg = fi.FWD[tag]
+    _check_fwd_nc(fi.fwd_inputs(cfg), TOL[cfg.dtype])
+
+
+@pytest.mark.parametrize("dtype,d,n", [(dt, d, n) for dt in ("f32", "bf16") for d in (32, 64, 128)
+                                       for n in (1, 33, 65, 129, 300)])
+def test_fwd_noncausal_ragged_parity(dtype, d, n):
+    cfg = fi.FwdConfig(f"nc_{dtype}_{d}_{n}", 2, 2, n, d, dtype, 1.0, 2.0)
+    _check_fwd_nc(fi.fwd_inputs(cfg), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,d,B,H,n", WIDE)
+def test_fwd_noncausal_wide_grid_parity(dtype, d, B, H, n):
+    cfg = fi.FwdConfig(f"ncwide_{d}_{B}_{H}_{n}", B, H, n, d, dtype, 2.0, 2.0)
+    _check_fwd_nc(fi.fwd_inputs(cfg), TOL[dtype], rows=_sampled_rows(n))
+
+
+def test_fwd_noncausal_last_row_equals_causal():
+    """The last row sees every key in both modes."""
+    inp = fi.fwd_inputs(fi.FwdConfig("nc_last", 2, 3, 777, 64, "bf16", 3.0, 1.5))
+    o_nc, l_nc, c_nc = _run_fwd_nc(inp)
+    o_c, l_c, c_c = _run_fwd(inp)
+    assert (o_nc[:, :, -1].float() - o_c[:, :, -1].float()).abs().max().item() <= 2.0 ** -7
+    assert (l_nc[:, :, -1] - l_c[:, :, -1]).abs().max().item() <= 2.0 ** -9 + 1e-5
+    assert torch.equal(c_nc, c_c)
+
+
 # ---------------------------------------------------------------- forward with tile skipping
 
 def _run_fwd_pruned(inp):
