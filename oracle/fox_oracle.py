@@ -49,6 +49,7 @@ __all__ = [
     "attn_fwd",
     "attn_fwd_rows",
     "attn_decode",
+    "attn_decode_ragged",
 ]
 
 
@@ -152,4 +153,25 @@ def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale):
     lse = m + np.log(z)
     p = np.exp(s - lse[..., None])
     out = np.einsum("shl,shld->shd", p, vc)
+    return out, lse, c_new
+
+
+def attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, lens, scale):
+    """Decode against caches of per-sequence length: sequence s uses slots 0..lens[s]-1 of
+    caches with capacity L (k_cache, v_cache [S,H,L,d], c_cache [S,H,L]), its new token at
+    slot lens[s]-1.  Each sequence is exactly ``attn_decode`` on its own first lens[s] slots.
+
+    Returns (O [S,H,d], lse [S,H], c_new [S,H]).
+    """
+    q, kc, vc, cc = _f64(q), _f64(k_cache), _f64(v_cache), _f64(c_cache)
+    ln = _f64(logf_new)
+    S, H, d = q.shape
+    out = np.empty((S, H, d))
+    lse = np.empty((S, H))
+    c_new = np.empty((S, H))
+    for s in range(S):
+        L = int(lens[s])
+        o_s, l_s, c_s = attn_decode(q[s:s + 1], kc[s:s + 1, :, :L], vc[s:s + 1, :, :L], cc[s:s + 1, :, :L],
+                                    ln[s:s + 1], scale)
+        out[s], lse[s], c_new[s] = o_s[0], l_s[0], c_s[0]
     return out, lse, c_new

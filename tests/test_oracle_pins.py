@@ -24,7 +24,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_decode, attn_fwd, brute_decode_head, brute_fwd_head, fwd_head_rows, logf_cumsum
+from oracle import attn_decode, attn_decode_ragged, attn_fwd, brute_decode_head, brute_fwd_head, fwd_head_rows, logf_cumsum
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TOL = 1e-12
@@ -258,6 +258,25 @@ def test_decode_matches_brute_force(L):
                                        logf_all[s, h].tolist(), scale)
             assert np.abs(o[s, h] - np.array(ob)).max() < TOL and abs(lse[s, h] - lb) < TOL
             assert abs(c_new[s, h] - math.fsum(logf_all[s, h])) < 1e-12
+
+
+def test_ragged_decode_matches_brute_force():
+    """Per-sequence cache lengths: each sequence against the scalar enumeration of its own slots."""
+    S, H, L, d = 4, 2, 9, 3
+    q, kc, vc, logf_all, _ = _decode_case(30, S, H, L, d)
+    lens = [1, 9, 4, 2]
+    cc = np.cumsum(logf_all, -1)
+    ln = np.empty((S, H))
+    for s, Ls in enumerate(lens):
+        ln[s] = logf_all[s, :, Ls - 1]
+        cc[s, :, Ls - 1:] = np.nan  # the slot the step computes, and the unused tail
+    o, lse, c_new = attn_decode_ragged(q, kc, vc, cc, ln, lens, 0.45)
+    for s, Ls in enumerate(lens):
+        for h in range(H):
+            ob, lb = brute_decode_head(q[s, h].tolist(), kc[s, h, :Ls].tolist(), vc[s, h, :Ls].tolist(),
+                                       logf_all[s, h, :Ls].tolist(), 0.45)
+            assert np.abs(o[s, h] - np.array(ob)).max() < TOL and abs(lse[s, h] - lb) < TOL
+            assert abs(c_new[s, h] - math.fsum(logf_all[s, h, :Ls])) < 1e-12
 
 
 def test_decode_is_last_row_of_forward():
