@@ -189,7 +189,10 @@ def fwd_kernel_name(torch, cfg) -> str:
     return f"fwd_bf16_pipe_kernel<{cfg.d},4,1>"
 
 
-def bench_fwd(torch, fox, fi, tag, steps, warmup):
+def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
+    """mode: "causal" (fox_attn_fwd), "unmasked" (fox_attn_fwd_noncausal, 4*d flop for every
+    (query, key) pair) or "pruned" (fox_attn_fwd_pruned, timed whole with its key-norm and
+    prefix-sum kernels; its rate is the causal work over that time, an effective rate)."""
     cfg = fi.FWD[tag]
     inp = fi.fwd_inputs(cfg)
     dev = "cuda"
@@ -197,15 +200,23 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty_like(logf)
     c = torch.empty_like(logf)
-    fn = lambda: fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
+    if mode == "unmasked":
+        fn = lambda: fox.attn_fwd_noncausal(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
+    elif mode == "pruned":
+        ws = torch.empty(max(16, fox.attn_fwd_pruned_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d)), device=dev,
+                         dtype=torch.uint8)
+        fn = lambda: fox.attn_fwd_pruned(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c,  # noqa: E731
+                                         workspace=ws)
+    else:
+        fn = lambda: fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
     for _ in range(warmup):
         fn()
     region = _events_time(torch, fn, steps)
-    flops = fwd_flops(cfg)
+    flops = 4.0 * cfg.d * cfg.N * cfg.N * cfg.B * cfg.H if mode == "unmasked" else fwd_flops(cfg)
     ms = region / steps
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (ms * 1e-3) / 1e12
-    kernel = fwd_kernel_name(torch, cfg)
+    kernel = fwd_kernel_name(torch, cfg) + ({"unmasked": " unmasked", "pruned": " pruned"}.get(mode, ""))
     return {
         "cfg": cfg, "inp": inp,
         "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
@@ -380,6 +391,18 @@ def main():
             others[tag] = {"workload": x["cfg"].desc, "value": round(x["tflops"], 2), "unit": "TFLOP/s",
                            "ms_per_step": round(x["ms_per_step"], 4),
                            "roofline": dict(x["roofline"], kernel=x["kernel"])}
+            del x
+            torch.cuda.empty_cache()
+        for tag, mode in (("c2", "unmasked"), ("c3", "pruned")):
+            x = bench_fwd(torch, fox, fi, tag, max(10, args.steps // 5), max(3, args.warmup // 2), mode=mode)
+            print(f"# {x['cfg'].desc}, {mode}: {x['ms_per_step']*1e3:.1f} us/step, {x['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            note = ("4*d flop for every (query, key) pair" if mode == "unmasked" else
+                    "effective rate: the causal work over the time of the pruned call (key-norm, prefix-sum and "
+                    "forward kernels); skipped keys weigh < 2^-24 of each row sum")
+            others[f"{tag}_{mode}"] = {"workload": x["cfg"].desc + f", {mode}", "value": round(x["tflops"], 2),
+                                       "unit": "TFLOP/s", "ms_per_step": round(x["ms_per_step"], 4),
+                                       "note": note, "roofline": dict(x["roofline"], kernel=x["kernel"])}
             del x
             torch.cuda.empty_cache()
         dec, _ = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))

@@ -8,6 +8,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
     o, lse, c    = attn_fwd_noncausal(q, k, v, logf)          # every key, no mask
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
+    o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
 """
 
 from __future__ import annotations
@@ -16,7 +17,8 @@ import torch
 
 from ._lib import FOX_BF16, FOX_F32, FoxError, check, lib, status_string  # noqa: F401
 
-__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes", "attn_decode",
+__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes",
+           "attn_decode", "attn_decode_ragged",
            "decode_workspace_bytes", "FoxError", "status_string"]
 
 _DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
@@ -129,10 +131,7 @@ def decode_workspace_bytes(s: int, h: int, l: int, d: int) -> int:
     return int(lib().fox_attn_decode_workspace_bytes(s, h, l, d))
 
 
-def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = None, out=None, lse=None,
-                workspace=None, want_lse: bool = True):
-    """One decode step. q: [S,H,d]; caches [S,H,L,d] with the new token at slot L-1;
-    c_cache [S,H,L] fp32 (slot L-1 is written); logf_new [S,H] fp32.  Returns (o, lse)."""
+def _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, workspace, want_lse):
     S, H, d = q.shape
     L = k_cache.shape[2]
     dt = _DTYPES.get(q.dtype)
@@ -153,9 +152,31 @@ def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = No
     nbytes = decode_workspace_bytes(S, H, L, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8)
+    return S, H, L, d, dt, o, (lse if want_lse else None), workspace
+
+
+def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = None, out=None, lse=None,
+                workspace=None, want_lse: bool = True):
+    """One decode step. q: [S,H,d]; caches [S,H,L,d] with the new token at slot L-1;
+    c_cache [S,H,L] fp32 (slot L-1 is written); logf_new [S,H] fp32.  Returns (o, lse)."""
+    S, H, L, d, dt, o, lse, ws = _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, workspace, want_lse)
     st = lib().fox_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(c_cache), _ptr(logf_new), _ptr(o),
-                               _ptr(lse if want_lse else None), _ptr(workspace), workspace.numel() *
-                               workspace.element_size(), S, H, L, d, float(_default_scale(d) if scale is None
-                                                                             else scale), dt, _stream())
+                               _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), S, H, L, d,
+                               float(_default_scale(d) if scale is None else scale), dt, _stream())
     check("fox_attn_decode", st)
-    return o, (lse if want_lse else None)
+    return o, lse
+
+
+def attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens, scale: float | None = None, out=None,
+                       lse=None, workspace=None, want_lse: bool = True):
+    """attn_decode where sequence s uses the first cache_lens[s] slots (int32 device tensor [S])
+    of caches allocated for L slots; its new token sits at slot cache_lens[s]-1."""
+    S, H, L, d, dt, o, lse, ws = _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, workspace, want_lse)
+    _need(cache_lens, "cache_lens", torch.int32)
+    if tuple(cache_lens.shape) != (S,):
+        raise ValueError(f"cache_lens shape {tuple(cache_lens.shape)} != {(S,)}")
+    st = lib().fox_attn_decode_ragged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(c_cache), _ptr(logf_new),
+                                      _ptr(cache_lens), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                      S, H, L, d, float(_default_scale(d) if scale is None else scale), dt, _stream())
+    check("fox_attn_decode_ragged", st)
+    return o, lse

@@ -122,10 +122,10 @@ size_t fox_attn_decode_workspace_bytes(int64_t s, int64_t h, int64_t l, int64_t 
   return fox::decode_workspace_bytes(s * h, (int)l, (int)d);
 }
 
-fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
-                             const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                             int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
-                             hipStream_t stream) {
+// Validation shared by the decode entry points.
+static fox_status_t decode_args(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                                const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype) {
   if (!q || !k_cache || !v_cache || !c_cache || !logf_new || !o) return FOX_ERR_INVALID_ARG;
   if (s <= 0 || h <= 0 || l <= 0 || d <= 0 || l > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (s > kI32Max / h) return FOX_ERR_INVALID_ARG;
@@ -149,8 +149,38 @@ fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_c
       overlap(workspace, need, v_cache, kvbytes) || overlap(c_cache, cbytes, k_cache, kvbytes) ||
       overlap(c_cache, cbytes, v_cache, kvbytes) || overlap(c_cache, cbytes, logf_new, sbytes))
     return FOX_ERR_INVALID_ARG;
-  return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, o, lse,
-                                          static_cast<float*>(workspace), sh, (int)l, (int)d, scale,
+  return FOX_OK;
+}
+
+fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                             const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                             int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
+                             hipStream_t stream) {
+  const fox_status_t st =
+      decode_args(q, k_cache, v_cache, c_cache, logf_new, o, lse, workspace, workspace_bytes, s, h, l, d, scale, dtype);
+  if (st != FOX_OK) return st;
+  return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, nullptr, (int)h, o, lse,
+                                          static_cast<float*>(workspace), s * h, (int)l, (int)d, scale,
+                                          dtype == FOX_BF16, stream));
+}
+
+fox_status_t fox_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                                    const float* logf_new, const int32_t* cache_lens, void* o, float* lse,
+                                    void* workspace, size_t workspace_bytes, int64_t s, int64_t h, int64_t l,
+                                    int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream) {
+  const fox_status_t st =
+      decode_args(q, k_cache, v_cache, c_cache, logf_new, o, lse, workspace, workspace_bytes, s, h, l, d, scale, dtype);
+  if (st != FOX_OK) return st;
+  if (!cache_lens || !aligned(cache_lens, 4)) return FOX_ERR_INVALID_ARG;
+  const size_t lbytes = (size_t)s * sizeof(int32_t);
+  const size_t need = fox::decode_workspace_bytes(s * h, (int)l, (int)d);
+  const size_t cbytes = (size_t)s * (size_t)h * (size_t)l * sizeof(float);
+  if (overlap(cache_lens, lbytes, c_cache, cbytes) || overlap(cache_lens, lbytes, workspace, need) ||
+      overlap(cache_lens, lbytes, o, (size_t)s * (size_t)h * (size_t)d * elem_bytes(dtype)) ||
+      overlap(cache_lens, lbytes, lse, (size_t)s * (size_t)h * sizeof(float)))
+    return FOX_ERR_INVALID_ARG;
+  return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, cache_lens, (int)h, o, lse,
+                                          static_cast<float*>(workspace), s * h, (int)l, (int)d, scale,
                                           dtype == FOX_BF16, stream));
 }
 

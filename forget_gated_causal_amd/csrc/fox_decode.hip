@@ -18,6 +18,10 @@
 //   (max, sum, acc[d]) over lane groups and waves and writes one partial record.
 // K4 (decode_combine_kernel): merges the records of one (sequence, head) by the
 //   log-sum-exp rule, writes O, lse and the new prefix sum into cache slot L-1.
+//
+// Ragged caches: with `lens` given, sequence s uses only its first lens[s] slots (clamped to
+// [1, L]) of caches allocated for L, and its new token sits at slot lens[s]-1.  The split
+// grid still covers L slots; splits past a sequence's length leave empty records.
 #include <math.h>
 
 #include <algorithm>
@@ -81,7 +85,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
                                                                   const T* __restrict__ vc,
                                                                   const float* __restrict__ cc,
                                                                   const float* __restrict__ logf_new,
-                                                                  float* __restrict__ part, int L, int nsplit,
+                                                                  float* __restrict__ part, int Lcap,
+                                                                  const int* __restrict__ lens, int nh, int nsplit,
                                                                   int chunk, float scale_log2) {
   using C = DecCfg<T, D>;
   constexpr int EPL = C::EPL, G = C::G, KPW = C::KPW, KPB = C::KPB;
@@ -90,15 +95,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
 
   const int wg = blockIdx.x;
   const int sh = wg / nsplit, split = wg - sh * nsplit;
+  const int L = lens ? min(max(lens[sh / nh], 1), Lcap) : Lcap;  // this sequence's slots
   const int start = split * chunk;
   const int end = min(L, start + chunk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G;
   const int slot = lane / G + KPW * wave;
-  const size_t kvbase = (size_t)sh * L * D;
+  const size_t kvbase = (size_t)sh * Lcap * D;
   const T* kp = kc + kvbase + g * EPL;
   const T* vp = vc + kvbase + g * EPL;
-  const float* ccr = cc + (size_t)sh * L;
+  const float* ccr = cc + (size_t)sh * Lcap;
 
   float qv[EPL];
 #pragma unroll
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 
-  const int nsteps = (end - start + KPB - 1) / KPB;
+  const int nsteps = end > start ? (end - start + KPB - 1) / KPB : 0;
   for (int s0 = nsteps - 1; s0 >= 0; s0 -= kDecU) {
     Vec16<T> kr[kDecU], vr[kDecU];
     float cj[kDecU];
@@ -216,7 +222,8 @@ __device__ __forceinline__ void store_out<float>(float* p, float x) {
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part, T* __restrict__ o,
                                                            float* __restrict__ lse, float* __restrict__ cc,
-                                                           const float* __restrict__ logf_new, int L, int nsplit) {
+                                                           const float* __restrict__ logf_new, int Lcap,
+                                                           const int* __restrict__ lens, int nh, int nsplit) {
   constexpr int REC = D + 2;
   const int sh = blockIdx.x;
   const int lane = threadIdx.x;
@@ -248,25 +255,27 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   }
   if (lane == 0) {
     if (lse) lse[sh] = (float)(((double)M + (double)log2f(lt)) * kLn2d);
-    const float* ccr = cc + (size_t)sh * L;
+    const int L = lens ? min(max(lens[sh / nh], 1), Lcap) : Lcap;
+    float* ccr = cc + (size_t)sh * Lcap;
     const float cprev = (L >= 2) ? ccr[L - 2] : 0.0f;
-    cc[(size_t)sh * L + (L - 1)] = cprev + logf_new[sh];
+    ccr[L - 1] = cprev + logf_new[sh];
   }
 }
 
 template <typename T, int D>
-hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new, void* o,
-                           float* lse, float* ws, int64_t sh, int l, float scale, hipStream_t stream) {
+hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
+                           const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, float scale,
+                           hipStream_t stream) {
   const int nsplit = decode_num_splits(sh, l, D);
   const int chunk = (l + nsplit - 1) / nsplit;
   const float scale_log2 = (float)((double)scale * kLog2ed);
   hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)(sh * nsplit)), dim3(kDecThreads), 0, stream,
-                     (const T*)q, (const T*)kc, (const T*)vc, (const float*)cc, logf_new, ws, l, nsplit, chunk,
-                     scale_log2);
+                     (const T*)q, (const T*)kc, (const T*)vc, (const float*)cc, logf_new, ws, l, lens, nh, nsplit,
+                     chunk, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)sh), dim3(64), 0, stream, (const float*)ws,
-                     (T*)o, lse, cc, logf_new, l, nsplit);
+                     (T*)o, lse, cc, logf_new, l, lens, nh, nsplit);
   return hipGetLastError();
 }
 
@@ -288,19 +297,19 @@ size_t decode_workspace_bytes(int64_t sh, int l, int d) {
 }
 
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
-                              void* o, float* lse, float* ws, int64_t sh, int l, int d, float scale, bool is_bf16,
-                              hipStream_t stream) {
+                              const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, int d,
+                              float scale, bool is_bf16, hipStream_t stream) {
   if (is_bf16) {
     switch (d) {
-      case 32: return launch_decode_t<bf16, 32>(q, kc, vc, cc, logf_new, o, lse, ws, sh, l, scale, stream);
-      case 64: return launch_decode_t<bf16, 64>(q, kc, vc, cc, logf_new, o, lse, ws, sh, l, scale, stream);
-      case 128: return launch_decode_t<bf16, 128>(q, kc, vc, cc, logf_new, o, lse, ws, sh, l, scale, stream);
+      case 32: return launch_decode_t<bf16, 32>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
+      case 64: return launch_decode_t<bf16, 64>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
+      case 128: return launch_decode_t<bf16, 128>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
     }
   } else {
     switch (d) {
-      case 32: return launch_decode_t<float, 32>(q, kc, vc, cc, logf_new, o, lse, ws, sh, l, scale, stream);
-      case 64: return launch_decode_t<float, 64>(q, kc, vc, cc, logf_new, o, lse, ws, sh, l, scale, stream);
-      case 128: return launch_decode_t<float, 128>(q, kc, vc, cc, logf_new, o, lse, ws, sh, l, scale, stream);
+      case 32: return launch_decode_t<float, 32>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
+      case 64: return launch_decode_t<float, 64>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
+      case 128: return launch_decode_t<float, 128>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
     }
   }
   return hipErrorInvalidValue;

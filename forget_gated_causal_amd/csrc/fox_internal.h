@@ -28,8 +28,10 @@ hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, c
 // Split-K decode: number of key splits used for these sizes, and the workspace it needs.
 int decode_num_splits(int64_t sh, int l, int d);
 size_t decode_workspace_bytes(int64_t sh, int l, int d);
+// lens (device, one int per sequence, or nullptr): per-sequence cache lengths, clamped to
+// [1, l]; nh = heads per sequence (sequence of (s, h) row sh is sh / nh).
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
-                              void* o, float* lse, float* workspace, int64_t sh, int l, int d, float scale,
-                              bool is_bf16, hipStream_t stream);
+                              const int* lens, int nh, void* o, float* lse, float* workspace, int64_t sh, int l,
+                              int d, float scale, bool is_bf16, hipStream_t stream);
 
 }  // namespace fox

@@ -162,6 +162,25 @@ fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_c
                              int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
                              hipStream_t stream);
 
+/*
+ * fox_attn_decode_ragged -- fox_attn_decode for a batch of sequences of different lengths.
+ *   Same step and cache convention per sequence, with sequence s using only the first
+ *   cache_lens[s] slots of caches allocated for l slots: its new token's k, v sit at slot
+ *   cache_lens[s]-1 and that slot of c_cache is written.  Slots past cache_lens[s] are
+ *   neither read nor written.
+ *
+ *   cache_lens : [s] int32 DEVICE array, 4-byte aligned, values in [1, l] (read by the
+ *                kernels; values outside are clamped to [1, l], never used to address
+ *                memory outside the caches).
+ *   l          : the caches' slot capacity (the third dimension of k_cache / v_cache / c_cache).
+ *   Every other argument, the workspace size (fox_attn_decode_workspace_bytes(s, h, l, d))
+ *   and the errors as fox_attn_decode.
+ */
+fox_status_t fox_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                                    const float* logf_new, const int32_t* cache_lens, void* o, float* lse,
+                                    void* workspace, size_t workspace_bytes, int64_t s, int64_t h, int64_t l,
+                                    int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fox_status_string(fox_status_t status);
 

@@ -139,3 +139,23 @@ def test_decode_rejects_bad_arguments(L):
     assert _dec(L, ws=H + 8) == WS
     assert _dec(L, o=B) == INVALID  # output inside the K cache
     assert _dec(L, ws=C) == INVALID  # workspace inside the V cache
+
+
+def _decr(L, lens=0x90_0000_0000, **kw):
+    args = dict(q=A, k=B, v=C, cc=D, lnew=E, o=F, lse=G, ws=H, wsb=1 << 24, s=2, h=3, l=100, d=64, scale=0.125,
+                dt=_lib.FOX_BF16)
+    args.update(kw)
+    a = args
+    return L.fox_attn_decode_ragged(a["q"], a["k"], a["v"], a["cc"], a["lnew"], lens, a["o"], a["lse"], a["ws"],
+                                    a["wsb"], a["s"], a["h"], a["l"], a["d"], a["scale"], a["dt"], None)
+
+
+def test_decode_ragged_rejects_bad_arguments(L):
+    assert _decr(L, lens=None) == INVALID
+    assert _decr(L, lens=0x90_0000_0002) == INVALID  # not 4-byte aligned
+    assert _decr(L, lens=D) == INVALID  # lengths inside the prefix-sum cache
+    assert _decr(L, q=None) == INVALID
+    assert _decr(L, l=0) == INVALID
+    assert _decr(L, d=96) == UNSUP
+    assert _decr(L, ws=None) == WS
+    assert _decr(L, o=B) == INVALID

@@ -345,3 +345,73 @@ def test_decode_equals_prefill_last_row(dtype):
     # relative and the two lse by at most about 2^-9 (natural log); fp32 paths agree closely.
     assert (lsed - lse[..., N - 1]).abs().max().item() <= (2.0 ** -9 + 1e-5 if dtype == "bf16" else 1e-4)
     assert (cache_c[..., N - 1] - c[..., N - 1]).abs().max().item() <= _ulp(_np(c))
+
+
+# ---------------------------------------------------------------------------------- ragged decode
+
+def _ragged_lens(S, L, seed):
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(1, L + 1, (S,), generator=g, dtype=torch.int32)
+    lens[0] = 1
+    lens[-1] = L
+    return lens
+
+
+def _check_decode_ragged(inp, lens, tol, seqs=None):
+    L = inp["cfg"].L
+    S = inp["q"].shape[0]
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    la = inp["logf_all"]
+    c_gpu = fox.logf_cumsum(la.to(DEV))
+    c_ora = oracle.logf_cumsum(la.double().numpy()).astype(np.float32).astype(np.float64)
+    lnew = torch.empty(S, la.shape[1])
+    for s in range(S):
+        Ls = int(lens[s])
+        lnew[s] = la[s, :, Ls - 1]
+        c_gpu[s, :, Ls - 1:] = float("nan")  # the slot the step writes, and the unused tail
+        c_ora[s, :, Ls - 1:] = np.nan
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), device=DEV)
+    fox.attn_decode_ragged(q, k, v, c_gpu, lnew.to(DEV), lens.to(DEV), scale=inp["scale"], out=o, lse=lse)
+    torch.cuda.synchronize()
+    seqs = list(range(S)) if seqs is None else seqs
+    o_ref, lse_ref, cnew_ref = oracle.attn_decode_ragged(_np(inp["q"])[seqs], _np(inp["k"])[seqs],
+                                                         _np(inp["v"])[seqs], c_ora[seqs],
+                                                         lnew.double().numpy()[seqs], lens.numpy()[seqs],
+                                                         inp["scale"])
+    eo = np.abs(_np(o)[seqs] - o_ref).max()
+    el = np.abs(_np(lse)[seqs] - lse_ref).max()
+    cg = _np(c_gpu)
+    ec = max(abs(cg[s, :, int(lens[s]) - 1] - cnew_ref[i]).max() for i, s in enumerate(seqs))
+    tails_untouched = all(np.isnan(cg[s, :, int(lens[s]):]).all() for s in seqs)
+    print(f"  ragged lens {lens.tolist()[:8]}...: max|dO|={eo:.3e} max|dlse|={el:.3e} max|dc_new|={ec:.3e}",
+          flush=True)
+    assert eo <= tol and el <= tol and ec <= _ulp(cnew_ref)
+    assert tails_untouched
+
+
+@pytest.mark.parametrize("dtype,d,L", [(dt, d, L) for dt in ("f32", "bf16") for d in (32, 64, 128)
+                                       for L in (1, 77, 1000, 4097)])
+def test_decode_ragged_parity(dtype, d, L):
+    cfg = fi.DecodeConfig(f"ragged_dec_{dtype}_{d}_{L}", 5, 3, L, d, dtype, 4.0, 2.0)
+    _check_decode_ragged(fi.decode_inputs(cfg), _ragged_lens(5, L, L + d), TOL[dtype])
+
+
+def test_decode_ragged_full_size_sampled():
+    cfg = fi.DECODE["c5"]
+    inp = fi.decode_inputs(cfg)
+    lens = _ragged_lens(cfg.S, cfg.L, 5)
+    _check_decode_ragged(inp, lens, TOL["bf16"], seqs=[0, 1, 17, 40, 63])
+
+
+def test_decode_ragged_full_length_equals_decode():
+    """With every length equal to the capacity the ragged step is the plain step, bit for bit."""
+    cfg = fi.DecodeConfig("ragged_eq", 3, 4, 1500, 128, "bf16", 4.0, 2.0)
+    inp = fi.decode_inputs(cfg)
+    o1, lse1, c1, _, lnew = _run_decode(inp)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    c2, _ = _decode_caches(inp["logf_all"])
+    lens = torch.full((cfg.S,), cfg.L, dtype=torch.int32, device=DEV)
+    o2, lse2 = fox.attn_decode_ragged(q, k, v, c2, lnew.to(DEV), lens, scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2) and torch.equal(c1, c2)
