@@ -7,6 +7,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     c            = logf_cumsum(logf)                          # [..., N] fp32
     o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
     o, lse, c    = attn_fwd_noncausal(q, k, v, logf)          # every key, no mask
+    o, lse, c    = attn_fwd_ex(q, k, v, logf, causal, layout)  # layout "head" [B,H,N,d] / "token" [B,N,H,d]
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
     o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
 """
@@ -15,9 +16,9 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import FOX_BF16, FOX_F32, FoxError, check, lib, status_string  # noqa: F401
+from ._lib import FOX_BF16, FOX_F32, FOX_HEAD_MAJOR, FOX_TOKEN_MAJOR, FoxError, check, lib, status_string  # noqa: F401
 
-__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes",
+__all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_ex", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes",
            "attn_decode", "attn_decode_ragged",
            "decode_workspace_bytes", "FoxError", "status_string"]
 
@@ -101,6 +102,46 @@ def attn_fwd_noncausal(q, k, v, logf, scale: float | None = None, out=None, lse=
     st = lib().fox_attn_fwd_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse), _ptr(c), B, H, N, d,
                                       scale, dt, _stream())
     check("fox_attn_fwd_noncausal", st)
+    return o, lse, c
+
+
+def attn_fwd_ex(q, k, v, logf, causal: bool = True, layout: str = "head", scale: float | None = None, out=None,
+                lse=None, c=None, want_lse: bool = True, want_c: bool = True):
+    """fox_attn_fwd_ex: the forward in either mode and layout.
+
+    layout "head": q, k, v [B,H,N,d], logf / lse / c [B,H,N] (as attn_fwd);
+    layout "token": q, k, v [B,N,H,d], logf / lse / c [B,N,H] (the projections' layout before
+    the head permute).  Outputs are written in the inputs' layout.
+    """
+    if layout not in ("head", "token"):
+        raise ValueError(f"layout must be 'head' or 'token', got {layout!r}")
+    if layout == "token":
+        B, N, H, d = q.shape
+        dt = _DTYPES.get(q.dtype)
+        if dt is None:
+            raise ValueError(f"unsupported dtype {q.dtype}")
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, name, q.dtype)
+            if tuple(t.shape) != (B, N, H, d):
+                raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, N, H, d)}")
+        _need(logf, "logf", torch.float32)
+        if tuple(logf.shape) != (B, N, H):
+            raise ValueError(f"logf shape {tuple(logf.shape)} != {(B, N, H)}")
+        o = torch.empty_like(q) if out is None else out
+        if want_lse and lse is None:
+            lse = torch.empty(B, N, H, device=q.device, dtype=torch.float32)
+        if want_c and c is None:
+            c = torch.empty(B, N, H, device=q.device, dtype=torch.float32)
+        lse, c = (lse if want_lse else None), (c if want_c else None)
+        code = FOX_TOKEN_MAJOR
+    else:
+        B, H, N, d = q.shape
+        dt, o, lse, c = _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c)
+        code = FOX_HEAD_MAJOR
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = lib().fox_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse), _ptr(c), B, H, N, d, scale,
+                               dt, 1 if causal else 0, code, _stream())
+    check("fox_attn_fwd_ex", st)
     return o, lse, c
 
 

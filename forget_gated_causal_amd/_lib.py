@@ -19,6 +19,8 @@ FOX_ERR_WORKSPACE = 3
 FOX_ERR_HIP = 4
 FOX_F32 = 0
 FOX_BF16 = 1
+FOX_HEAD_MAJOR = 0
+FOX_TOKEN_MAJOR = 1
 
 # exported symbol -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -27,6 +29,8 @@ SIGNATURES = {
     "fox_logf_cumsum": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "fox_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                     ctypes.c_int, _P]),
+    "fox_attn_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
     "fox_attn_fwd_noncausal": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
                                               ctypes.c_int, _P]),
     "fox_attn_fwd_pruned_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),

@@ -75,22 +75,28 @@ static fox_status_t fwd_args(const void* q, const void* k, const void* v, const 
   return FOX_OK;
 }
 
+fox_status_t fox_attn_fwd_ex(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                             float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
+                             int causal, fox_layout_t layout, hipStream_t stream) {
+  const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
+  if (st != FOX_OK) return st;
+  if (layout != FOX_HEAD_MAJOR && layout != FOX_TOKEN_MAJOR) return FOX_ERR_UNSUPPORTED;
+  // token-major: one head's rows span (n-1)*h*d + d elements, addressed with 32-bit byte offsets
+  if (layout == FOX_TOKEN_MAJOR && (n + 64) * h * d * (int64_t)elem_bytes(dtype) > kI32Max) return FOX_ERR_UNSUPPORTED;
+  return from_hip(fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b, h, (int)n, (int)d, scale, dtype == FOX_BF16,
+                                       causal != 0, layout == FOX_TOKEN_MAJOR, stream));
+}
+
 fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
                           float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
                           hipStream_t stream) {
-  const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
-  if (st != FOX_OK) return st;
-  return from_hip(fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b * h, (int)n, (int)d, scale, dtype == FOX_BF16,
-                                       true, stream));
+  return fox_attn_fwd_ex(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype, 1, FOX_HEAD_MAJOR, stream);
 }
 
 fox_status_t fox_attn_fwd_noncausal(const void* q, const void* k, const void* v, const float* logf, void* o,
                                     float* lse, float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale,
                                     fox_dtype_t dtype, hipStream_t stream) {
-  const fox_status_t st = fwd_args(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype);
-  if (st != FOX_OK) return st;
-  return from_hip(fox::launch_attn_fwd(q, k, v, logf, o, lse, c, b * h, (int)n, (int)d, scale, dtype == FOX_BF16,
-                                       false, stream));
+  return fox_attn_fwd_ex(q, k, v, logf, o, lse, c, b, h, n, d, scale, dtype, 0, FOX_HEAD_MAJOR, stream);
 }
 
 size_t fox_attn_fwd_pruned_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d) {

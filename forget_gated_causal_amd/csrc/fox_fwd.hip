@@ -102,6 +102,17 @@ struct GateJob {
   double* carry;
 };
 
+// Element strides of one forward call.  Head-major: q/k/v/o [B,H,N,d], gates / lse / c [B,H,N]
+// (rows d apart).  Token-major: q/k/v/o [B,N,H,d], gates / lse / c [B,N,H] (rows h*d apart),
+// the layout the projections produce before the head permute.
+struct FwdLayout {
+  int64_t bs, hs;    // q/k/v/o: batch and head strides
+  int rs;            // q/k/v/o: row (token) stride
+  int64_t gbs, ghs;  // gates, lse, c: batch and head strides
+  int gs;            // gates, lse, c: row stride
+  int nh;            // heads per batch entry
+};
+
 // ------------------------------------------------------------------------------------------
 // bf16
 // ------------------------------------------------------------------------------------------
@@ -188,7 +199,7 @@ struct StageOffsets {
 };
 
 template <int D, int NW>
-__device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane) {
+__device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane, int rs) {
   using G = Bf16Geom<D, NW>;
   StageOffsets<D, NW> so;
 #pragma unroll
@@ -196,8 +207,8 @@ __device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane)
     const int g = wave * G::OPS + o;           // 1 KB slice of the tile
     const int row = g * G::RPO + lane / G::CH;  // key row inside the tile
     const int pc = lane % G::CH;                // physical chunk this lane fills
-    so.k[o] = (row * D + 8 * (pc ^ swz_k<D>(row))) * (int)sizeof(bf16);
-    so.v[o] = (row * D + 8 * (pc ^ swz_v<D>(row))) * (int)sizeof(bf16);
+    so.k[o] = (row * rs + 8 * (pc ^ swz_k<D>(row))) * (int)sizeof(bf16);
+    so.v[o] = (row * rs + 8 * (pc ^ swz_v<D>(row))) * (int)sizeof(bf16);
   }
   return so;
 }
@@ -208,15 +219,15 @@ __device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane)
 template <int D, int NW>
 __device__ __forceinline__ void bf16_stage_tile(Bf16Stage<D>& s, float* lf, u32x4 rk, u32x4 rv, u32x4 rl,
                                                 const StageOffsets<D, NW>& so, int t, int wave, int lane,
-                                                bool gate_wave) {
+                                                bool gate_wave, int rs, int gs) {
   using G = Bf16Geom<D, NW>;
-  const uint32_t tile_off = (uint32_t)(t * kBC * D * (int)sizeof(bf16));
+  const uint32_t tile_off = (uint32_t)t * (uint32_t)(kBC * rs * (int)sizeof(bf16));
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations are wave-uniform (M0)
   if (gate_wave) {
     // lane index recomputed here (volatile, so not hoisted) rather than kept live across the tile loop
     uint32_t ln;
     __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    lds_dma4(lds_addr(lf), rl, (uint32_t)(t * kBC * (int)sizeof(float)) + ln * (uint32_t)sizeof(float));
+    lds_dma4(lds_addr(lf), rl, ((uint32_t)(t * kBC) + ln) * (uint32_t)(gs * (int)sizeof(float)));
   }
 #pragma unroll
   for (int o = 0; o < G::OPS; ++o) {
@@ -579,7 +590,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
 // gate sums are taken relative to the last row of the sequence (R_j = sum_{t=j+1..n-1} log f_t,
 // so c_i - c_j = R_j - R_i still holds, with R_j >= 0 past the row), the walk starts at the
 // last key tile, where each row's largest bias lies, and only keys past n are masked.
-template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL>
+template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL, bool TM>
 __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1, Bf16Stage<D>* s2,
                                               Bf16Stage<D>* s3, float (*g0)[kBC], float (*g1)[kBC],
                                               float (*g2)[kBC], float (*g3)[kBC], GateRows& rows,
@@ -587,7 +598,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
                                               const bf16* __restrict__ v, const float* __restrict__ logf,
                                               bf16* __restrict__ o, float* __restrict__ lse,
                                               float* __restrict__ c_out, int n, float scale_log2,
-                                              const float* __restrict__ knorm) {
+                                              const float* __restrict__ knorm, const FwdLayout& lay) {
   constexpr int NS = 4;  // LDS stages: tile t+1 (V still read), tile t, two tiles in flight
   using G = Bf16Geom<D, NWR>;
   constexpr int KK = D / 16, DB = D / 32, BR = G::BR;
@@ -605,10 +616,14 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   const int rw = wave % NWR;                                    // row-wave
   const int sp = __builtin_amdgcn_readfirstlane(wave / NWR);  // key split (wave-uniform: LDS DMA bases)
   const int l32 = lane & 31, hi = lane >> 5;
-  const size_t base = (size_t)bh * n * D;
+  // TM: token-major strides from `lay`; otherwise the head-major ones as compile-time constants
+  const int bb = bh / lay.nh, hh = bh - bb * lay.nh;
+  const size_t base = TM ? (size_t)bb * lay.bs + (size_t)hh * lay.hs : (size_t)bh * n * D;  // q/k/v/o
+  const size_t gbase = TM ? (size_t)bb * lay.gbs + (size_t)hh * lay.ghs : (size_t)bh * n;  // gates/lse/c
+  const int rs = TM ? lay.rs : D, gs = TM ? lay.gs : 1;
   const bf16* kb = k + base;
   const bf16* vb = v + base;
-  const float* lfb = logf + (size_t)bh * n;
+  const float* lfb = logf + gbase;
 
   // Key tiles of this wave's split: [bot, top].  Split 0 keeps the diagonal tiles (at least
   // the top two, which hold every row's diagonal) and the upper half of the rest.
@@ -628,10 +643,12 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   LaneOffsets<D> off = lane_offsets<D>(lane);
   off.k += (uint32_t)(sp * sizeof(Bf16Stage<D>));  // 1 KB multiple: the XOR swizzles still apply
   off.v += (uint32_t)(sp * sizeof(Bf16Stage<D>));
-  const StageOffsets<D, NWR> so = stage_offsets<D, NWR>(rw, lane);
-  const u32x4 rk = raw_rsrc(kb, (uint32_t)n * D * sizeof(bf16));
-  const u32x4 rv = raw_rsrc(vb, (uint32_t)n * D * sizeof(bf16));
-  const u32x4 rl = raw_rsrc(lfb, (uint32_t)n * sizeof(float));
+  const StageOffsets<D, NWR> so = stage_offsets<D, NWR>(rw, lane, rs);
+  // The resources end at the last row's last byte: rows at or past n read as zeros.
+  const uint32_t kv_bytes = (uint32_t)(((size_t)(n - 1) * rs + D) * sizeof(bf16));
+  const u32x4 rk = raw_rsrc(kb, kv_bytes);
+  const u32x4 rv = raw_rsrc(vb, kv_bytes);
+  const u32x4 rl = raw_rsrc(lfb, (uint32_t)(((size_t)(n - 1) * gs + 1) * sizeof(float)));
 
   auto stage = [&](auto J) -> Bf16Stage<D>* {
     constexpr int j = decltype(J)::value % NS;
@@ -654,7 +671,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (my_row < n)
-      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + base + (size_t)my_row * D + 16 * kk + 8 * hi);
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + base + (size_t)my_row * rs + 16 * kk + 8 * hi);
     else
       qreg[kk] = bf16x8{};
   }
@@ -693,8 +710,10 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
 
   // Prologue: tiles top and top-1 (the i-th tile of the split lives in stage i % 4; the
   // loop issues tile kt-2 while computing tile kt).
-  if (top >= bot) bf16_stage_tile<D, NWR>(stage(I0{})[sp], stage(I0{})[sp].lf, rk, rv, rl, so, top, rw, lane, lead);
-  if (top - 1 >= bot) bf16_stage_tile<D, NWR>(stage(I1{})[sp], stage(I1{})[sp].lf, rk, rv, rl, so, top - 1, rw, lane, lead);
+  if (top >= bot)
+    bf16_stage_tile<D, NWR>(stage(I0{})[sp], stage(I0{})[sp].lf, rk, rv, rl, so, top, rw, lane, lead, rs, gs);
+  if (top - 1 >= bot)
+    bf16_stage_tile<D, NWR>(stage(I1{})[sp], stage(I1{})[sp].lf, rk, rv, rl, so, top - 1, rw, lane, lead, rs, gs);
   wait_vmcnt<0>();
 
   f32x16 oacc[DB];
@@ -740,7 +759,8 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       for (int w = 0; w < NWR; ++w) all = all && rows.done_it[w] < i;
       if (all) return true;
     }
-    if (kt - 2 >= bot) bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl, so, kt - 2, rw, lane, lead);
+    if (kt - 2 >= bot)
+      bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl, so, kt - 2, rw, lane, lead, rs, gs);
     // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
     const bool gate_job = lead && kt - 1 >= bot;
     bool gate_done = false;
@@ -850,28 +870,28 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       w[db * 4 + g][1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
     }
   }
-  bf16* orow = o + base + (size_t)my_row * D;
+  bf16* orow = o + base + (size_t)my_row * rs;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w[db * 4 + g];
   if (hi == 0) {
-    const size_t idx = (size_t)bh * n + my_row;
+    const size_t idx = gbase + (size_t)my_row * gs;
     if (lse) lse[idx] = (float)(((double)m + (double)log2_hw(ltot)) * kLn2d - ri);
     if (c_out) c_out[idx] = (float)(cref - ri);
   }
 }
 
-template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL>
+template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL, bool TM>
 __global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
-    float scale_log2, const float* __restrict__ knorm) {
+    float scale_log2, const float* __restrict__ knorm, const FwdLayout lay) {
   __shared__ GateRows rows;
   __shared__ Bf16Stage<D> s0[SP], s1[SP], s2[SP], s3[SP];
   __shared__ float g0[SP][kBC], g1[SP][kBC], g2[SP][kBC], g3[SP][kBC];
-  fwd_pipe_body<D, NWR, SP, PRUNE, CAUSAL>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out, n,
-                                           scale_log2, knorm);
+  fwd_pipe_body<D, NWR, SP, PRUNE, CAUSAL, TM>(s0, s1, s2, s3, g0, g1, g2, g3, rows, q, k, v, logf, o, lse, c_out,
+                                               n, scale_log2, knorm, lay);
 }
 
 // Largest L2 norm of the keys of every 64-key tile (pruning bound); keys past n count as 0.
@@ -931,15 +951,15 @@ struct F32Lds {
 
 template <int D>
 __device__ __forceinline__ void f32_load_tile(F32Tile<D>& t, const float* kb, const float* vb, int kt, int n,
-                                              int tid) {
+                                              int tid, int rs) {
   constexpr int G = F32Tile<D>::GROUPS, KPT = F32Tile<D>::KPT;
   const int c = tid % G, a = tid / G;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int key = kt * kBC + a * KPT + i;
     if (key < n) {
-      t.k[i] = *reinterpret_cast<const f32x4*>(kb + (size_t)key * D + 4 * c);
-      t.v[i] = *reinterpret_cast<const f32x4*>(vb + (size_t)key * D + 4 * c);
+      t.k[i] = *reinterpret_cast<const f32x4*>(kb + (size_t)key * rs + 4 * c);
+      t.v[i] = *reinterpret_cast<const f32x4*>(vb + (size_t)key * rs + 4 * c);
     } else {
       t.k[i] = f32x4{};
       t.v[i] = f32x4{};
@@ -960,12 +980,12 @@ __device__ __forceinline__ void f32_store_tile(const F32Tile<D>& t, F32Lds<D>& s
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool TM>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                           const float* __restrict__ v,
                                                           const float* __restrict__ logf, float* __restrict__ o,
                                                           float* __restrict__ lse, float* __restrict__ c_out, int n,
-                                                          float scale_log2) {
+                                                          float scale_log2, const FwdLayout lay) {
   constexpr int KS = F32Tile<D>::KS, VS = F32Tile<D>::VS, KK = D / 2, DB = D / 32;
   __shared__ F32Lds<D> lds;
 
@@ -977,10 +997,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const int kt_hi = fref / kBC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const size_t base = (size_t)bh * n * D;
+  const int bb = bh / lay.nh, hh = bh - bb * lay.nh;
+  const size_t base = TM ? (size_t)bb * lay.bs + (size_t)hh * lay.hs : (size_t)bh * n * D;  // q/k/v/o
+  const size_t gbase = TM ? (size_t)bb * lay.gbs + (size_t)hh * lay.ghs : (size_t)bh * n;  // gates/lse/c
+  const int rs = TM ? lay.rs : D, gs = TM ? lay.gs : 1;
   const float* kb = k + base;
   const float* vb = v + base;
-  const float* lfb = logf + (size_t)bh * n;
+  const float* lfb = logf + gbase;
 
   const int wrow0 = row0 + wave * 32;
   const bool active = wrow0 < n;
@@ -989,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 
   float qf[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qf[kk] = (my_row < n) ? q[base + (size_t)my_row * D + 2 * kk + hi] : 0.0f;
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = (my_row < n) ? q[base + (size_t)my_row * rs + 2 * kk + hi] : 0.0f;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -999,11 +1022,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   // Unmasked mode: the biases stay relative to the frame row n-1 (R_j - 0), where every row's
   // heaviest keys lie, so those scores are small and exactly rounded; R_i comes off in lse.
   F32Tile<D> tile;
-  f32_load_tile<D>(tile, kb, vb, kt_hi, n, tid);
+  f32_load_tile<D>(tile, kb, vb, kt_hi, n, tid, rs);
   float lf = 0.0f;  // wave 0: log f of key 63-lane of the next tile
   if (wave == 0) {
     const int j = kt_hi * kBC + 63 - lane;
-    lf = (j <= fref) ? lfb[j] : 0.0f;
+    lf = (j <= fref) ? lfb[(size_t)j * gs] : 0.0f;
   }
 
   for (int kt = kt_hi; kt >= 0; --kt) {
@@ -1012,8 +1035,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     if (wave == 0) gate_tile(lds.r2, lds.r64, lds.rows, lane, kt, row0, ref, lf, carry);
     __syncthreads();
     if (kt > 0) {
-      f32_load_tile<D>(tile, kb, vb, kt - 1, n, tid);
-      if (wave == 0) lf = lfb[(kt - 1) * kBC + 63 - lane];
+      f32_load_tile<D>(tile, kb, vb, kt - 1, n, tid, rs);
+      if (wave == 0) lf = lfb[(size_t)((kt - 1) * kBC + 63 - lane) * gs];
     }
     if (!active || kt > kt_first) continue;
 
@@ -1081,7 +1104,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const float ltot = pair32_sum(lsum);
   if (my_row >= n) return;
   const float inv = 1.0f / ltot;
-  float* orow = o + base + (size_t)my_row * D;
+  float* orow = o + base + (size_t)my_row * rs;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -1094,7 +1117,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   }
   if (hi == 0) {
     const double ri = lds.rows.rowR[my_row - row0];
-    const size_t idx = (size_t)bh * n + my_row;
+    const size_t idx = gbase + (size_t)my_row * gs;
     // causal scores already carry -R_i
     if (lse) lse[idx] = (float)(((double)m + (double)log2f(ltot)) * kLn2d - (CAUSAL ? 0.0 : ri));
     if (c_out) c_out[idx] = (float)(lds.rows.cref - ri);
@@ -1108,9 +1131,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 //  * d <= 64 with fewer than two 128-row blocks per CU: 128-row blocks whose key tiles are
 //    split over two wave sets;
 //  * otherwise 128-row blocks of 4 waves.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool TM>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                        float* c, int64_t bh, int n, float scale_log2, const float* knorm, hipStream_t stream) {
+                        float* c, int64_t bh, int n, float scale_log2, const float* knorm, const FwdLayout& lay,
+                        hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1120,48 +1144,68 @@ hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float
     bf16* oo = (bf16*)o;
     auto go = [&](auto kernel, int rows, int threads) {
       const dim3 grid((unsigned)bh, (unsigned)((n + rows - 1) / rows));
-      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, qq, kk, vv, logf, oo, lse, c, n, scale_log2, knorm);
+      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, qq, kk, vv, logf, oo, lse, c, n, scale_log2, knorm,
+                         lay);
       return hipGetLastError();
     };
+    constexpr bool CAN_PRUNE = CAUSAL && !TM;
     if constexpr (D >= 64) {
       if (blocks256 >= 2 * (int64_t)cus) {
-        if constexpr (CAUSAL)
-          if (knorm) return go(fwd_bf16_pipe_kernel<D, 8, 1, true, true>, 256, 512);
-        return go(fwd_bf16_pipe_kernel<D, 8, 1, false, CAUSAL>, 256, 512);
+        if constexpr (CAN_PRUNE)
+          if (knorm) return go(fwd_bf16_pipe_kernel<D, 8, 1, true, true, false>, 256, 512);
+        return go(fwd_bf16_pipe_kernel<D, 8, 1, false, CAUSAL, TM>, 256, 512);
       }
     }
     if constexpr (D <= 64) {
-      if (!knorm && blocks128 < 2 * (int64_t)cus) return go(fwd_bf16_pipe_kernel<D, 4, 2, false, CAUSAL>, 128, 512);
+      if (!knorm && blocks128 < 2 * (int64_t)cus)
+        return go(fwd_bf16_pipe_kernel<D, 4, 2, false, CAUSAL, TM>, 128, 512);
     }
-    if constexpr (CAUSAL)
-      if (knorm) return go(fwd_bf16_pipe_kernel<D, 4, 1, true, true>, 128, 256);
-    return go(fwd_bf16_pipe_kernel<D, 4, 1, false, CAUSAL>, 128, 256);
+    if constexpr (CAN_PRUNE)
+      if (knorm) return go(fwd_bf16_pipe_kernel<D, 4, 1, true, true, false>, 128, 256);
+    return go(fwd_bf16_pipe_kernel<D, 4, 1, false, CAUSAL, TM>, 128, 256);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
-                       (const float*)v, logf, (float*)o, lse, c, n, scale_log2);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TM>), grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, logf, (float*)o, lse, c, n, scale_log2, lay);
     return hipGetLastError();
   }
 }
 
-template <bool CAUSAL>
-hipError_t launch_fwd_d(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse, float* c,
-                        int64_t bh, int n, int d, float scale, bool is_bf16, const float* knorm, hipStream_t stream) {
-  const float scale_log2 = (float)((double)scale * kLog2ed);
+template <bool CAUSAL, bool TM>
+hipError_t launch_fwd_l(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse, float* c,
+                        int64_t bh, int n, int d, float scale_log2, bool is_bf16, const FwdLayout& lay,
+                        const float* knorm, hipStream_t stream) {
   if (is_bf16) {
     switch (d) {
-      case 32: return launch_fwd_t<bf16, 32, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, stream);
-      case 64: return launch_fwd_t<bf16, 64, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, stream);
-      case 128: return launch_fwd_t<bf16, 128, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, stream);
+      case 32: return launch_fwd_t<bf16, 32, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
+      case 64: return launch_fwd_t<bf16, 64, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
+      case 128:
+        return launch_fwd_t<bf16, 128, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
     }
   } else {
     switch (d) {
-      case 32: return launch_fwd_t<float, 32, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-      case 64: return launch_fwd_t<float, 64, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
-      case 128: return launch_fwd_t<float, 128, CAUSAL>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, stream);
+      case 32: return launch_fwd_t<float, 32, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, lay, stream);
+      case 64: return launch_fwd_t<float, 64, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, lay, stream);
+      case 128:
+        return launch_fwd_t<float, 128, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, lay, stream);
     }
   }
   return hipErrorInvalidValue;
+}
+
+template <bool CAUSAL>
+hipError_t launch_fwd_d(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse, float* c,
+                        int64_t b, int64_t h, int n, int d, float scale, bool is_bf16, bool token_major,
+                        const float* knorm, hipStream_t stream) {
+  const float scale_log2 = (float)((double)scale * kLog2ed);
+  const int64_t bh = b * h;
+  // {bs, hs, rs, gbs, ghs, gs, nh}
+  const FwdLayout lay = token_major
+                            ? FwdLayout{(int64_t)n * h * d, (int64_t)d, (int)(h * d), (int64_t)n * h, 1, (int)h, (int)h}
+                            : FwdLayout{h * n * (int64_t)d, (int64_t)n * d, d, h * (int64_t)n, (int64_t)n, 1, (int)h};
+  return token_major
+             ? launch_fwd_l<CAUSAL, true>(q, k, v, logf, o, lse, c, bh, n, d, scale_log2, is_bf16, lay, knorm, stream)
+             : launch_fwd_l<CAUSAL, false>(q, k, v, logf, o, lse, c, bh, n, d, scale_log2, is_bf16, lay, knorm, stream);
 }
 
 template <int D>
@@ -1175,10 +1219,11 @@ hipError_t launch_key_norm_t(const void* k, float* kn, int64_t bh, int n, hipStr
 }  // namespace
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, bool causal,
-                           hipStream_t stream) {
-  return causal ? launch_fwd_d<true>(q, k, v, logf, o, lse, c, bh, n, d, scale, is_bf16, nullptr, stream)
-                : launch_fwd_d<false>(q, k, v, logf, o, lse, c, bh, n, d, scale, is_bf16, nullptr, stream);
+                           float* c, int64_t b, int64_t h, int n, int d, float scale, bool is_bf16, bool causal,
+                           bool token_major, hipStream_t stream) {
+  return causal ? launch_fwd_d<true>(q, k, v, logf, o, lse, c, b, h, n, d, scale, is_bf16, token_major, nullptr, stream)
+                : launch_fwd_d<false>(q, k, v, logf, o, lse, c, b, h, n, d, scale, is_bf16, token_major, nullptr,
+                                      stream);
 }
 
 size_t attn_fwd_pruned_workspace_bytes(int64_t bh, int n) {
@@ -1189,7 +1234,7 @@ hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, c
                                   float* lse, float* c, float* workspace, int64_t bh, int n, int d, float scale,
                                   bool is_bf16, hipStream_t stream) {
   if (!is_bf16)  // the fp32 path is not pruned: it computes every causal pair
-    return launch_attn_fwd(q, k, v, logf, o, lse, c, bh, n, d, scale, false, true, stream);
+    return launch_attn_fwd(q, k, v, logf, o, lse, c, bh, 1, n, d, scale, false, true, false, stream);
   hipError_t e = hipSuccess;
   switch (d) {
     case 32: e = launch_key_norm_t<32>(k, workspace, bh, n, stream); break;
@@ -1204,7 +1249,8 @@ hipError_t launch_attn_fwd_pruned(const void* q, const void* k, const void* v, c
     e = launch_logf_cumsum(logf, c, bh, n, stream);
     if (e != hipSuccess) return e;
   }
-  return launch_fwd_d<true>(q, k, v, logf, o, lse, nullptr, bh, n, d, scale, true, workspace, stream);
+  // (batch*head, 1 head): the head-major layout of b*h independent heads
+  return launch_fwd_d<true>(q, k, v, logf, o, lse, nullptr, bh, 1, n, d, scale, true, false, workspace, stream);
 }
 
 }  // namespace fox

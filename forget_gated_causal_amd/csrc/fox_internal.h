@@ -13,10 +13,11 @@ namespace fox {
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream);
 
 // FoX forward, causal (decoder mode) or over every key; is_bf16 selects the element type of
-// q/k/v/o; d in {32,64,128}.
+// q/k/v/o; d in {32,64,128}; token_major selects [B,N,H,d] tensors with [B,N,H] gates / lse /
+// c instead of [B,H,N,d] and [B,H,N].
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
-                           float* c, int64_t bh, int n, int d, float scale, bool is_bf16, bool causal,
-                           hipStream_t stream);
+                           float* c, int64_t b, int64_t h, int n, int d, float scale, bool is_bf16, bool causal,
+                           bool token_major, hipStream_t stream);
 
 // Forward with gate-aware tile skipping (results equal to fp32 rounding); the workspace
 // holds one float per (batch*head, 64-key tile).

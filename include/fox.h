@@ -55,6 +55,11 @@ typedef enum fox_dtype {
   FOX_BF16 = 1 /* bfloat16; products accumulate in fp32, outputs rounded to nearest even */
 } fox_dtype_t;
 
+typedef enum fox_layout {
+  FOX_HEAD_MAJOR = 0, /* q/k/v/o [b, h, n, d]; logf / lse / c [b, h, n] */
+  FOX_TOKEN_MAJOR = 1 /* q/k/v/o [b, n, h, d]; logf / lse / c [b, n, h] */
+} fox_layout_t;
+
 /* Largest sequence length / cache length accepted (keeps all index arithmetic in range). */
 #define FOX_MAX_SEQ (1 << 22)
 
@@ -103,6 +108,23 @@ fox_status_t fox_attn_fwd(const void* q, const void* k, const void* v, const flo
 fox_status_t fox_attn_fwd_noncausal(const void* q, const void* k, const void* v, const float* logf, void* o,
                                     float* lse, float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale,
                                     fox_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fox_attn_fwd_ex -- fox_attn_fwd / fox_attn_fwd_noncausal with the tensor layout chosen.
+ *   FoX module page, ForgettingAttention.forward: the q, k, v projections are formed as
+ *   [batch, seq, heads, head_dim] and permuted to [batch, heads, seq, head_dim] before the
+ *   attention; FOX_TOKEN_MAJOR takes the tensors before that permute (no copy needed), the
+ *   gates likewise as [batch, seq, heads], and writes o, lse and c in the same layout.
+ *
+ *   causal : nonzero for decoder mode (fox_attn_fwd), zero for the unmasked mode.
+ *   layout : FOX_HEAD_MAJOR or FOX_TOKEN_MAJOR (else FOX_ERR_UNSUPPORTED); with
+ *            FOX_TOKEN_MAJOR, (n + 64) * h * d * sizeof(element) must not exceed 2^31 - 1
+ *            (else FOX_ERR_UNSUPPORTED).
+ *   Every other argument, the results and the errors as fox_attn_fwd.
+ */
+fox_status_t fox_attn_fwd_ex(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
+                             float* c, int64_t b, int64_t h, int64_t n, int64_t d, float scale, fox_dtype_t dtype,
+                             int causal, fox_layout_t layout, hipStream_t stream);
 
 /*
  * fox_attn_fwd_pruned_workspace_bytes -- bytes of scratch fox_attn_fwd_pruned needs

@@ -159,3 +159,13 @@ def test_decode_ragged_rejects_bad_arguments(L):
     assert _decr(L, d=96) == UNSUP
     assert _decr(L, ws=None) == WS
     assert _decr(L, o=B) == INVALID
+
+
+def test_fwd_ex_layout_checks(L):
+    def ex(layout, n=128, h=2, d=32, causal=1):
+        return L.fox_attn_fwd_ex(A, B, C, D, E, F, G, 1, h, n, d, 0.17, _lib.FOX_F32, causal, layout, None)
+    assert ex(7) == UNSUP
+    assert ex(-1) == UNSUP
+    # token-major rows are h*d apart: one head's span must fit 32-bit byte offsets
+    assert ex(_lib.FOX_TOKEN_MAJOR, n=1 << 20, h=64, d=128) == UNSUP
+    assert ex(_lib.FOX_HEAD_MAJOR, n=0) == INVALID
