@@ -95,16 +95,19 @@ def stored_traffic(tag: str, kernel: str, kind: str):
 
 
 def _counter_per_dispatch(path, counter, name_part):
-    """Mean value of `counter` over the dispatches of kernels whose name contains name_part."""
-    tot, ids = 0.0, set()
+    """Mean value of `counter` per dispatch of each kernel whose name contains name_part, summed
+    over those kernels (one call of an entry point that launches several kernels); and the
+    number of dispatches of the first of them."""
+    tot, ids = {}, {}
     with open(path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
-                tot += float(r["Counter_Value"])
-                ids.add(r["Dispatch_Id"])
-    if not ids:
+                k = r["Kernel_Name"]
+                tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+                ids.setdefault(k, set()).add(r["Dispatch_Id"])
+    if not tot:
         raise SystemExit(f"{path}: no {counter} rows for kernels matching {name_part!r}")
-    return tot / len(ids), len(ids)
+    return sum(tot[k] / len(ids[k]) for k in tot), min(len(v) for v in ids.values())
 
 
 def write_traffic_summary(args):
@@ -163,6 +166,20 @@ def fwd_min_bytes(cfg) -> float:
     return rows * cfg.d * eb * 4 + rows * 4 * 3
 
 
+def _warm(torch, fn, warmup, min_s=0.05):
+    """W untimed calls, then more until at least min_s of wall time has passed on the device
+    (clocks ramp up under load; a short workload measured after an idle host phase would
+    otherwise be timed partly at a lower clock)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _events_time(torch, fn, k):
     """Time (ms) of k back-to-back calls between two events on the launch stream."""
     st = torch.cuda.current_stream()
@@ -209,8 +226,7 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
                                          workspace=ws)
     else:
         fn = lambda: fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
-    for _ in range(warmup):
-        fn()
+    _warm(torch, fn, warmup)
     region = _events_time(torch, fn, steps)
     flops = 4.0 * cfg.d * cfg.N * cfg.N * cfg.B * cfg.H if mode == "unmasked" else fwd_flops(cfg)
     ms = region / steps
@@ -243,8 +259,7 @@ def bench_decode(torch, fox, fi, tag, steps, warmup):
     lse = torch.empty(cfg.S, cfg.H, device=dev)
     ws = torch.empty(fox.decode_workspace_bytes(cfg.S, cfg.H, L, cfg.d), device=dev, dtype=torch.uint8)
     fn = lambda: fox.attn_decode(q, kc, vc, cc, lnew, scale=inp["scale"], out=o, lse=lse, workspace=ws)  # noqa
-    for _ in range(warmup):
-        fn()
+    _warm(torch, fn, warmup)
     region = _events_time(torch, fn, steps)
     by = decode_bytes(cfg)
     ms = region / steps
