@@ -27,6 +27,8 @@ softmax, no split-K):
   key j = 0 .. N-1 enters the softmax with the same bias ``c_i - c_j``, which for a
   key after the query equals ``-(sum_{t=i+1..j} log f_t)`` (>= 0).  Source: the same
   ``forward``, whose triangle mask is applied in decoder mode only.
+* Backward -- gradients of a loss through O with respect to q, k, v and the log
+  gates, by the chain rule through the definition (``fwd_bwd_head``).
 * Decode -- the single query row i = L-1 of a sequence whose key/value cache
   holds slots 0..L-1 (the new token's k, v already at slot L-1) and whose
   cached prefix sums hold slots 0..L-2; the new prefix sum is
@@ -50,6 +52,8 @@ __all__ = [
     "attn_fwd_rows",
     "attn_decode",
     "attn_decode_ragged",
+    "fwd_bwd_head",
+    "attn_bwd",
 ]
 
 
@@ -175,3 +179,51 @@ def attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, lens, scale):
                                     ln[s:s + 1], scale)
         out[s], lse[s], c_new[s] = o_s[0], l_s[0], c_s[0]
     return out, lse, c_new
+
+
+def fwd_bwd_head(q, k, v, logf, scale, do, causal: bool = True):
+    """Gradients of FoX attention for one head (fp64), from the definition by the chain rule.
+
+    q, k, v: [N, d]; logf: [N]; do: [N, d] (the gradient of a loss with respect to O).
+    Returns (dq, dk, dv, dlogf).  The pages derive no backward pass; this differentiates the
+    forward above (FoX module page, ``ForgettingAttention.forward``) step by step:
+
+      S = scale q k^T + (c_i - c_j) (masked),  P = softmax_rows(S),  O = P v
+      dv = P^T do;   dP = do v^T;   dS = P * (dP - rowsum(dP * P))   (softmax Jacobian)
+      dq = scale dS k;   dk = scale dS^T q
+      dc_i = sum_j dS_ij - sum_i' dS_i'i   (S_ij depends on c_i with +1 and on c_j with -1)
+      dlogf_t = sum_{i >= t} dc_i           (c_i = sum_{t <= i} logf_t)
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    c = logf_cumsum(logf)
+    n = q.shape[0]
+    s = scale * (q @ k.T) + (c[:, None] - c[None, :])
+    if causal:
+        s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    dc = ds.sum(axis=1) - ds.sum(axis=0)
+    dlogf = np.cumsum(dc[::-1])[::-1]
+    return dq, dk, dv, dlogf
+
+
+def attn_bwd(q, k, v, logf, scale, do, causal: bool = True):
+    """Gradients for every (batch, head): q, k, v, do [B,H,N,d], logf [B,H,N].
+
+    Returns (dq, dk, dv [B,H,N,d], dlogf [B,H,N]) in float64.
+    """
+    q = _f64(q)
+    bsz, nh, n, d = q.shape
+    dq, dk, dv = (np.empty((bsz, nh, n, d)) for _ in range(3))
+    dl = np.empty((bsz, nh, n))
+    for b in range(bsz):
+        for h in range(nh):
+            dq[b, h], dk[b, h], dv[b, h], dl[b, h] = fwd_bwd_head(q[b, h], k[b, h], v[b, h], logf[b, h], scale,
+                                                                 do[b, h], causal=causal)
+    return dq, dk, dv, dl
