@@ -8,6 +8,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
     o, lse, c    = attn_fwd_noncausal(q, k, v, logf)          # every key, no mask
     o, lse, c    = attn_fwd_ex(q, k, v, logf, causal, layout)  # layout "head" [B,H,N,d] / "token" [B,N,H,d]
+    dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, c)   # gradients (bf16)
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
     o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
 """
@@ -19,7 +20,7 @@ import torch
 from ._lib import FOX_BF16, FOX_F32, FOX_HEAD_MAJOR, FOX_TOKEN_MAJOR, FoxError, check, lib, status_string  # noqa: F401
 
 __all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_ex", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes",
-           "attn_decode", "attn_decode_ragged",
+           "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_ragged",
            "decode_workspace_bytes", "FoxError", "status_string"]
 
 _DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
@@ -166,6 +167,40 @@ def attn_fwd_pruned(q, k, v, logf, scale: float | None = None, out=None, lse=Non
                                    _ptr(workspace), workspace.numel(), B, H, N, d, scale, dt, _stream())
     check("fox_attn_fwd_pruned", st)
     return o, lse, c
+
+
+def attn_bwd_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
+    return int(lib().fox_attn_bwd_workspace_bytes(b, h, n, d))
+
+
+def attn_bwd(q, k, v, o, dout, lse, c, causal: bool = True, scale: float | None = None, dq=None, dk=None, dv=None,
+             dlogf=None, workspace=None):
+    """Gradients of FoX attention. q, k, v, o, dout: [B,H,N,d] bf16 (o, lse [B,H,N] and c [B,H,N]
+    as attn_fwd / attn_fwd_noncausal returned them).  Returns (dq, dk, dv, dlogf)."""
+    B, H, N, d = q.shape
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attn_bwd takes bf16 tensors")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, H, N, d)}")
+    for name, t in (("lse", lse), ("c", c)):
+        _need(t, name, torch.float32)
+        if tuple(t.shape) != (B, H, N):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, H, N)}")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dlogf = torch.empty_like(lse) if dlogf is None else dlogf
+    wb = attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(wb, 16), device=q.device, dtype=torch.uint8)
+    scale = _default_scale(d) if scale is None else float(scale)
+    st = lib().fox_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(c), _ptr(dq), _ptr(dk),
+                            _ptr(dv), _ptr(dlogf), _ptr(workspace), workspace.numel() * workspace.element_size(), B,
+                            H, N, d, scale, FOX_BF16, 1 if causal else 0, _stream())
+    check("fox_attn_bwd", st)
+    return dq, dk, dv, dlogf
 
 
 def decode_workspace_bytes(s: int, h: int, l: int, d: int) -> int:

@@ -128,6 +128,42 @@ size_t fox_attn_decode_workspace_bytes(int64_t s, int64_t h, int64_t l, int64_t 
   return fox::decode_workspace_bytes(s * h, (int)l, (int)d);
 }
 
+size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d) {
+  if (b <= 0 || h <= 0 || n <= 0 || n > FOX_MAX_SEQ || !head_dim_ok(d) || b > kI32Max / h) return 0;
+  return fox::attn_bwd_workspace_bytes(b * h, (int)n, (int)d);
+}
+
+fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                          void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
+                          float scale, fox_dtype_t dtype, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !c || !dq || !dk || !dv || !dlogf) return FOX_ERR_INVALID_ARG;
+  if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
+  if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || !head_dim_ok(d)) return FOX_ERR_UNSUPPORTED;
+  if (dtype != FOX_BF16) return FOX_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
+  if ((n + 127) / 128 > kMaxGridY) return FOX_ERR_INVALID_ARG;
+  const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : t16)
+    if (!aligned(p, 16)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(lse, 4) || !aligned(c, 4) || !aligned(dlogf, 4)) return FOX_ERR_INVALID_ARG;
+  const int64_t bh = b * h;
+  const size_t need = fox::attn_bwd_workspace_bytes(bh, (int)n, (int)d);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
+  const size_t tb = (size_t)bh * (size_t)n * (size_t)d * elem_bytes(dtype), vb = (size_t)bh * (size_t)n * sizeof(float);
+  // every output (and the workspace) apart from every other buffer
+  const void* outs[] = {dq, dk, dv, dlogf, workspace};
+  const size_t osz[] = {tb, tb, tb, vb, need};
+  const void* all[] = {q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace};
+  const size_t asz[] = {tb, tb, tb, tb, tb, vb, vb, tb, tb, tb, vb, need};
+  for (int i = 0; i < 5; ++i)
+    for (int j = 0; j < 12; ++j)
+      if (all[j] != outs[i] && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
+  return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, static_cast<float*>(workspace),
+                                       bh, (int)n, (int)d, scale, causal != 0, stream));
+}
+
 // Validation shared by the decode entry points.
 static fox_status_t decode_args(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
                                 const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,

@@ -11,6 +11,8 @@ namespace fox {
 
 // Inclusive prefix sums of `rows` independent rows of length n (fp64 accumulate).
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream);
+// Suffix sums out_t = sum_{i>=t} x_i of `rows` rows of length n (fp64 accumulate).
+hipError_t launch_suffix_sum(const float* x, float* out, int64_t rows, int n, hipStream_t stream);
 
 // FoX forward, causal (decoder mode) or over every key; is_bf16 selects the element type of
 // q/k/v/o; d in {32,64,128}; token_major selects [B,N,H,d] tensors with [B,N,H] gates / lse /
@@ -34,5 +36,12 @@ size_t decode_workspace_bytes(int64_t sh, int l, int d);
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
                               const int* lens, int nh, void* o, float* lse, float* workspace, int64_t sh, int l,
                               int d, float scale, bool is_bf16, hipStream_t stream);
+
+// Backward pass (bf16): dq, dk, dv and dlog f from q, k, v, the forward's o, lse and c, and dO.
+// The workspace holds bh*n*(d + 2) floats (dq accumulator, dO.O per row, dc per key).
+size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                           float* workspace, int64_t bh, int n, int d, float scale, bool causal, hipStream_t stream);
 
 }  // namespace fox

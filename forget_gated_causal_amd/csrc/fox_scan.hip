@@ -16,6 +16,8 @@ constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = 4;
 constexpr int kScanChunk = kScanThreads * kScanPerThread;
 
+// REV: the suffix sums out_t = sum_{i>=t} in_i instead (the same scan over the reversed row).
+template <bool REV>
 __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* __restrict__ logf,
                                                                    float* __restrict__ c, int n) {
   __shared__ double wave_tot[kScanThreads / 64];
@@ -28,7 +30,8 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
     const int i0 = base + tid * kScanPerThread;
     double x[kScanPerThread];
 #pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e) x[e] = (i0 + e < n) ? (double)src[i0 + e] : 0.0;
+    for (int e = 0; e < kScanPerThread; ++e)
+      x[e] = (i0 + e < n) ? (double)src[REV ? n - 1 - (i0 + e) : i0 + e] : 0.0;
 #pragma unroll
     for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
     double t = x[kScanPerThread - 1];  // inclusive over this wave's threads after the loop below
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
     const double pre = before + excl;
 #pragma unroll
     for (int e = 0; e < kScanPerThread; ++e)
-      if (i0 + e < n) dst[i0 + e] = (float)(pre + x[e]);
+      if (i0 + e < n) dst[REV ? n - 1 - (i0 + e) : i0 + e] = (float)(pre + x[e]);
     carry += chunk;
   }
 }
@@ -59,7 +62,12 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
 }  // namespace
 
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(logf_cumsum_kernel, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf, c, n);
+  hipLaunchKernelGGL(logf_cumsum_kernel<false>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf, c, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_suffix_sum(const float* x, float* out, int64_t rows, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(logf_cumsum_kernel<true>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, x, out, n);
   return hipGetLastError();
 }
 

@@ -155,6 +155,39 @@ fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, co
                                  int64_t n, int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream);
 
 /*
+ * fox_attn_bwd_workspace_bytes -- bytes of scratch fox_attn_bwd needs: b*h*n*(d + 2) floats.
+ * Returns 0 for invalid sizes.
+ */
+size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
+
+/*
+ * fox_attn_bwd -- gradients of FoX attention (decoder or unmasked mode), head-major, bf16.
+ *   The pages derive no backward pass.  This is the chain rule through fox_attn_fwd's
+ *   definition (FoX module page, ForgettingAttention.forward), for a loss whose gradient
+ *   with respect to O is dout:
+ *     P = softmax(S), dv = P^T dout, dS = P * (dout v^T - rowsum(dout * O)),
+ *     dq = scale dS k, dk = scale dS^T q, and for the gates, with c_i - c_j in every score,
+ *     dlogf_t = sum over i >= t of (rowsum(dS)_i - colsum(dS)_i)
+ *   (the row sums of dS vanish identically; the kernels use -colsum).
+ *
+ *   q, k, v, o, dout : [b, h, n, d] bf16, inputs; o, lse and c as fox_attn_fwd (same mode) wrote
+ *                      them for these q, k, v, logf and scale.
+ *   lse, c   : [b, h, n] fp32, inputs (fox_attn_fwd's outputs).
+ *   dq, dk, dv : [b, h, n, d] bf16, outputs (rounded to nearest even).
+ *   dlogf    : [b, h, n] fp32, output: the gradient with respect to logf.
+ *   workspace, workspace_bytes : device scratch of at least fox_attn_bwd_workspace_bytes(b, h, n, d)
+ *              bytes, 16-byte aligned; contents on entry are ignored.
+ *   causal   : nonzero for decoder mode, zero for the unmasked mode.
+ *   Errors as fox_attn_fwd; fp32 tensors give FOX_ERR_UNSUPPORTED; every output and the workspace
+ *   must not overlap any other buffer (FOX_ERR_INVALID_ARG).
+ */
+fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                          void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
+                          float scale, fox_dtype_t dtype, int causal, hipStream_t stream);
+
+/*
+ * fox_attn_decode_workspace_bytes/*
  * fox_attn_decode_workspace_bytes -- bytes of scratch fox_attn_decode needs for
  * these sizes (split-K partial results).  Returns 0 for invalid sizes.
  */

@@ -446,3 +446,40 @@ def test_decode_ragged_full_length_equals_decode():
     o2, lse2 = fox.attn_decode_ragged(q, k, v, c2, lnew.to(DEV), lens, scale=inp["scale"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(lse1, lse2) and torch.equal(c1, c2)
+
+
+# ---------------------------------------------------------------------------------- backward
+
+# (d, B, H, n, causal, gate-logit mean, sd)
+BWD = [(32, 1, 2, 65, True, 2.0, 1.0), (64, 2, 2, 300, True, 2.0, 2.0), (128, 1, 2, 257, True, 3.0, 1.5),
+       (64, 2, 3, 129, False, 2.0, 1.0), (128, 2, 2, 200, False, 1.0, 2.0), (32, 3, 2, 1000, True, 4.0, 2.0),
+       (64, 4, 12, 1024, True, 3.0, 1.5)]
+
+
+@pytest.mark.parametrize("d,B,H,n,causal,mu,sigma", BWD)
+def test_bwd_parity(d, B, H, n, causal, mu, sigma):
+    """fox_attn_bwd against the fp64 oracle's chain-rule gradients on the same bf16 inputs.
+
+    Bound: bf16 rounds P and dS before the products (2^-9 relative each), the forward's O and
+    lse enter through D_i and P, and the outputs are rounded to bf16; every gradient element
+    is a sum of such terms, so the error is a small multiple of 2^-9 of the tensor's scale.
+    Checked as max|gpu - ref| <= 2e-2 * max(1, max|ref|) per gradient tensor."""
+    cfg = fi.FwdConfig(f"bwd_{d}_{B}_{H}_{n}_{causal}", B, H, n, d, "bf16", mu, sigma)
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(n * 31 + d)
+    dout = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16)
+    fwd = fox.attn_fwd if causal else fox.attn_fwd_noncausal
+    o, lse, c = fwd(q, k, v, logf, scale=inp["scale"])
+    dq, dk, dv, dl = fox.attn_bwd(q, k, v, o, dout.to(DEV), lse, c, causal=causal, scale=inp["scale"])
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]), inp["scale"], _np(dout),
+                          causal=causal)
+    msg = []
+    for name, got, r in zip(("dq", "dk", "dv", "dlogf"), (dq, dk, dv, dl), ref):
+        err = np.abs(_np(got) - r).max()
+        bound = 2e-2 * max(1.0, np.abs(r).max())
+        msg.append(f"{name} {err:.2e} (max|ref| {np.abs(r).max():.2e})")
+        assert torch.isfinite(got).all(), name
+        assert err <= bound, (name, err, bound)
+    print("  " + cfg.desc + ": " + ", ".join(msg), flush=True)
