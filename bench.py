@@ -243,6 +243,35 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
     }
 
 
+def bench_bwd(torch, fox, fi, tag, steps, warmup):
+    """fox_attn_bwd on the forward workload `tag`: 10*d flop per causal pair (the recomputed
+    q.k, and dP, dV, dK, dQ), timed whole (pre, main, conversion and scan kernels)."""
+    cfg = fi.FWD[tag]
+    inp = fi.fwd_inputs(cfg)
+    dev = "cuda"
+    q, k, v, logf = (inp[n].to(dev) for n in ("q", "k", "v", "logf"))
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    g = torch.Generator().manual_seed(1)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dl = torch.empty_like(logf)
+    ws = torch.empty(fox.attn_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), device=dev, dtype=torch.uint8)
+    fn = lambda: fox.attn_bwd(q, k, v, o, dout, lse, c, scale=inp["scale"], dq=dq, dk=dk, dv=dv,  # noqa: E731
+                              dlogf=dl, workspace=ws)
+    _warm(torch, fn, warmup)
+    region = _events_time(torch, fn, steps)
+    ms = region / steps
+    flops = 2.5 * fwd_flops(cfg)
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"workload": cfg.desc + ", backward", "value": round(achieved, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms, 4),
+            "note": "10*d flop per causal pair; one call = pre, main (bwd_main_kernel), dq conversion and "
+                    "gate suffix-sum kernels",
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "kernel": f"bwd_main_kernel<{cfg.d},causal> + 3 small kernels"}}
+
+
 def bench_decode(torch, fox, fi, tag, steps, warmup):
     cfg = fi.DECODE[tag]
     t0 = time.time()
@@ -336,6 +365,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
+    ap.add_argument("--backward", action="store_true", help="with --only: time fox_attn_bwd on the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the selected workload only")
     ap.add_argument("--copy-calibration", action="store_true", help="run the 1 GiB device copy for counter scaling")
@@ -382,6 +412,14 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    if args.backward:
+        x = bench_bwd(torch, fox, fi, args.workload, args.steps, args.warmup)
+        print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+        line.update({"value": x["value"], "unit": "TFLOP/s", "ms_per_step": x["ms_per_step"], "dtype": "bf16",
+                     "config": {"workload": x["workload"]}, "roofline": x["roofline"]})
+        print(json.dumps(line), flush=True)
+        return
     r = bench_fwd(torch, fox, fi, args.workload, args.steps, args.warmup)
     cfg = r["cfg"]
     print(f"# {cfg.desc}: {r['ms_per_step']*1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s, {r['kernel']}",
@@ -419,6 +457,12 @@ def main():
                                        "unit": "TFLOP/s", "ms_per_step": round(x["ms_per_step"], 4),
                                        "note": note, "roofline": dict(x["roofline"], kernel=x["kernel"])}
             del x
+            torch.cuda.empty_cache()
+        for tag in ("c2", "c3"):
+            x = bench_bwd(torch, fox, fi, tag, max(10, args.steps // 5), max(3, args.warmup // 2))
+            print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+            others[f"{tag}_backward"] = x
             torch.cuda.empty_cache()
         dec, _ = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))
         print(f"# {dec['workload']}: {dec['ms_per_step']*1e3:.1f} us/step, {dec['value']:.0f} GB/s",
