@@ -155,19 +155,49 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   for (int db = 0; db < DB; ++db) dkt[db] = dvt[db] = f32x16{};
   float colsum = 0.0f;
 
+  // The next query tile's q / dO rows, (c - lse) log2 e and D_i are loaded into registers while
+  // the current tile computes, and written to LDS at the top of the next iteration.
+  constexpr int CH = D / 8, NCH = kBQ * CH;
+  constexpr int PF = (NCH + kBwdThreads - 1) / kBwdThreads;
+  bf16x8 nq[PF], nd[PF];
+  float na = kNegInfB, ndr = 0.0f;
+  auto fetch = [&](int q0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int i = tid + j * kBwdThreads, r = i / CH, ch = i - r * CH;
+      nq[j] = nd[j] = bf16x8{};
+      if ((NCH % kBwdThreads == 0 || i < NCH) && q0 + r < n) {
+        nq[j] = *reinterpret_cast<const bf16x8*>(q + (base + q0 + r) * D + 8 * ch);
+        nd[j] = *reinterpret_cast<const bf16x8*>(dout + (base + q0 + r) * D + 8 * ch);
+      }
+    }
+    if (tid < kBQ) {
+      const int i = q0 + tid;
+      na = i < n ? (c[base + i] - lse[base + i]) * kLog2e : kNegInfB;
+      ndr = i < n ? dvec[base + i] : 0.0f;
+    }
+  };
+
   const int nqt = (n + kBQ - 1) / kBQ;
   const int qt0 = CAUSAL ? key0 / kBQ : 0;  // earlier query tiles see none of these keys
+  if (qt0 < nqt) fetch(qt0 * kBQ);
   for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * kBQ;
     __syncthreads();  // the previous tile's q / dO / dS^T are no longer read
-    stage_rows<D>(lds.q, q + (base + q0) * D, kBQ, n - q0, tid);
-    stage_rows<D>(lds.dout, dout + (base + q0) * D, kBQ, n - q0, tid);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int i = tid + j * kBwdThreads, r = i / CH, ch = i - r * CH;
+      if (NCH % kBwdThreads == 0 || i < NCH) {
+        *reinterpret_cast<bf16x8*>(lds.q + r * RS + 8 * ch) = nq[j];
+        *reinterpret_cast<bf16x8*>(lds.dout + r * RS + 8 * ch) = nd[j];
+      }
+    }
     if (tid < kBQ) {
-      const int i = q0 + tid;
-      lds.arow[tid] = i < n ? (c[base + i] - lse[base + i]) * kLog2e : kNegInfB;
-      lds.drow[tid] = i < n ? dvec[base + i] : 0.0f;
+      lds.arow[tid] = na;
+      lds.drow[tid] = ndr;
     }
     __syncthreads();
+    if (qt + 1 < nqt) fetch(q0 + kBQ);
 
     // S = Q K^T and dP = dO V^T for this wave's 32 keys
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -217,8 +247,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
       *reinterpret_cast<bf16x4*>(&lds.dst[(32 * wave + l32) * QS + 8 * g + 4 * hi]) = w4;
     }
     __syncthreads();
-    // dQ^T (dims x queries) = K^T dS^T over the block's keys; DB output blocks shared by the
-    // 4 waves (a wave takes block wave % DB and its share of the 8 key steps)
+    // dQ (queries x dims) = dS K over the block's keys; DB output blocks of 32 dims shared by
+    // the 4 waves (a wave takes block wave % DB and its share of the 8 key steps)
     {
       constexpr int PER = 4 / DB;  // waves per output block
       constexpr int KS = 8 / PER;  // key steps per wave
@@ -229,19 +259,26 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const int ks = part * KS + j;
-        const bf16x8 bop = transposed_operand(lds.dst, QS, 16 * ks, 0, lane);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(transposed_operand(lds.k, RS, 16 * ks, 32 * db, lane), bop, acc,
+        const bf16x8 aop = transposed_operand(lds.dst, QS, 16 * ks, 0, lane);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, transposed_operand(lds.k, RS, 16 * ks, 32 * db, lane), acc,
                                                       0, 0, 0);
-        if (db == 0) rsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bop, rsum, 0, 0, 0);
+        if (db == 0) rsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, ones, rsum, 0, 0, 0);
       }
-      // lane: query q0 + l32, dims 32db + 8(r/4) + 4hi + r%4; every register of rsum holds the
-      // query's row sum over this wave's key steps
-      const int qi = q0 + l32;
-      if (qi < n) {
-        float* dst = dq_acc + (base + qi) * D + 32 * db + 4 * hi;
+      // lane: dim 32db + l32; register r: query q0 + 8(r/4) + 4hi + r%4.  One atomic instruction
+      // covers 32 consecutive dims of two queries (two full 128-byte lines).
+      float* dst = dq_acc + (base + q0 + 4 * hi) * D + 32 * db + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) atomicAdd(dst + 8 * (r >> 2) + (r & 3), acc[r] * scale);
-        if (db == 0 && hi == 0) atomicAdd(dc + base + qi, rsum[0]);
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + (r & 3);
+        if (q0 + 4 * hi + m < n) atomicAdd(dst + (size_t)m * D, acc[r] * scale);
+      }
+      // every lane of rsum holds the row sums of its 16 queries; lane l32 < 16 adds register l32
+      if (db == 0) {
+        float rs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rs = l32 == r ? rsum[r] : rs;
+        const int qi = q0 + 8 * (l32 >> 2) + 4 * hi + (l32 & 3);
+        if (l32 < 16 && qi < n) atomicAdd(dc + base + qi, rs);
       }
     }
   }
