@@ -155,7 +155,8 @@ fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, co
                                  int64_t n, int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream);
 
 /*
- * fox_attn_bwd_workspace_bytes -- bytes of scratch fox_attn_bwd needs: b*h*n*(d + 2) floats.
+ * fox_attn_bwd_workspace_bytes -- bytes of scratch fox_attn_bwd needs:
+ * b*h*(n*(d + 1) + 2*npad) floats, npad = n rounded up to a multiple of 32.
  * Returns 0 for invalid sizes.
  */
 size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
@@ -168,7 +169,8 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
  *     P = softmax(S), dv = P^T dout, dS = P * (dout v^T - rowsum(dout * O)),
  *     dq = scale dS k, dk = scale dS^T q, and for the gates, with c_i - c_j in every score,
  *     dlogf_t = sum over i >= t of (rowsum(dS)_i - colsum(dS)_i)
- *   (the row sums of dS vanish identically; the kernels use -colsum).
+ *   (the row sums of dS vanish in exact arithmetic; the kernels keep them, with both sums
+ *   taken over the same bf16-rounded dS, so that their rounding cancels in dlogf).
  *
  *   q, k, v, o, dout : [b, h, n, d] bf16, inputs; o, lse and c as fox_attn_fwd (same mode) wrote
  *                      them for these q, k, v, logf and scale.

@@ -453,7 +453,11 @@ def test_decode_ragged_full_length_equals_decode():
 # (d, B, H, n, causal, gate-logit mean, sd)
 BWD = [(32, 1, 2, 65, True, 2.0, 1.0), (64, 2, 2, 300, True, 2.0, 2.0), (128, 1, 2, 257, True, 3.0, 1.5),
        (64, 2, 3, 129, False, 2.0, 1.0), (128, 2, 2, 200, False, 1.0, 2.0), (32, 3, 2, 1000, True, 4.0, 2.0),
-       (64, 4, 12, 1024, True, 3.0, 1.5)]
+       (64, 4, 12, 1024, True, 3.0, 1.5),
+       # edges: one row; less than, exactly and one past a 32-query tile; exactly one 128-key block
+       (64, 1, 1, 1, True, 2.0, 1.0), (128, 1, 1, 1, False, 2.0, 1.0), (128, 1, 2, 31, True, 2.0, 1.0),
+       (32, 1, 1, 32, True, 2.0, 1.0), (64, 1, 1, 33, False, 2.0, 1.0), (64, 1, 2, 128, True, 2.0, 1.0),
+       (128, 1, 1, 129, True, 2.0, 1.0)]
 
 
 @pytest.mark.parametrize("d,B,H,n,causal,mu,sigma", BWD)
@@ -483,3 +487,28 @@ def test_bwd_parity(d, B, H, n, causal, mu, sigma):
         assert torch.isfinite(got).all(), name
         assert err <= bound, (name, err, bound)
     print("  " + cfg.desc + ": " + ", ".join(msg), flush=True)
+
+
+def test_bwd_c3_full_size_sampled_heads():
+    """The backward at c3's full size (B=2 H=16 N=4096 d=128) in the bench's launch configuration;
+    two whole heads (first and last) against the fp64 oracle, the rest checked finite."""
+    cfg = fi.FWD["c3"]
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(1)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    dq, dk, dv, dl = fox.attn_bwd(q, k, v, o, dout.to(DEV), lse, c, scale=inp["scale"])
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dl):
+        assert torch.isfinite(t).all()
+    for b, h in ((0, 0), (cfg.B - 1, cfg.H - 1)):
+        ref = oracle.fwd_bwd_head(_np(inp["q"][b, h]), _np(inp["k"][b, h]), _np(inp["v"][b, h]),
+                                  _np(inp["logf"][b, h]), inp["scale"], _np(dout[b, h]))
+        msg = []
+        for name, got, r in zip(("dq", "dk", "dv", "dlogf"), (dq, dk, dv, dl), ref):
+            err = np.abs(_np(got[b, h]) - r).max()
+            bound = 2e-2 * max(1.0, np.abs(r).max())
+            msg.append(f"{name} {err:.2e} (max|ref| {np.abs(r).max():.2e})")
+            assert err <= bound, (b, h, name, err, bound)
+        print(f"  c3 head ({b},{h}): " + ", ".join(msg), flush=True)
