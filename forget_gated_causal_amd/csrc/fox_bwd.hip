@@ -12,25 +12,23 @@
 // cancel and dlog f_t reduces to the cross block (i >= t > j) as it does exactly.  The
 // forward's lse and c (its outputs) give P without a second softmax.
 //
-// Kernels (one call of fox_attn_bwd runs them in this order on the caller's stream):
-//  * bwd_pre_kernel: D_i = dO_i . O_i per row, and zeroes the fp32 dq and dc accumulators.
-//  * bwd_main_kernel<D, CAUSAL>: one workgroup of 4 waves per (128-key block, batch*head); wave w
-//    owns keys 32w..32w+31 of the block.  K and V of the block stay in LDS; 32-query tiles of q
-//    and dO stream through LDS.  Per tile, on v_mfma_f32_32x32x16_bf16 with queries as M and
-//    keys as N (so every accumulator lane holds one key and 16 queries):
-//      S = Q K^T, dP = dO V^T (A = row-major q / dO, B = row-major K / V),
-//      P and dS elementwise in registers,
-//      dV^T += dO^T P and dK^T += Q^T dS (A = transposed LDS reads of dO / q, B = the bf16 P /
-//      dS registers, whose query order the transposed reads follow, as in the forward's P.V),
-//      dS^T goes to LDS, and dQ^T = K^T dS^T over the block's 128 keys is added to a global
-//      fp32 accumulator with atomics (each query tile is shared by every key block); the same
-//      B operands against an all-ones A give the row sums of dS, added to dc with atomics.
-//    dK, dV and -colsum(dS) (into dc) are written once per key after the last tile.
-//  * bwd_post_kernel: dq = fp32 accumulator rounded to bf16;
-//  * the suffix-sum scan (fox_scan.hip): dlog f from dc.
+// Two main kernels split the work so that every output has one writer (no atomics, and the
+// results are the same from run to run):
+//  * bwd_kv_kernel<D, CAUSAL>: key-stationary.  One workgroup of 4 waves per (128-key block,
+//    head); wave w owns keys 32w..32w+31.  32-query tiles of q and dO stream through LDS.  Per
+//    tile, on v_mfma_f32_32x32x16_bf16 with queries as M and keys as N (every accumulator lane
+//    holds one key and 16 queries): S = Q K^T, dP = dO V^T; P and dS in registers; dV^T += dO^T P
+//    and dK^T += Q^T dS (A = transposed LDS reads of dO / q, B = the bf16 P / dS registers).
+//    Writes dk, dv and the column sums of dS.
+//  * bwd_dq_kernel<D, CAUSAL>: query-stationary.  One workgroup of 4 waves per (128-query block,
+//    head); wave w owns queries 32w..32w+31, whose q and dO rows stay in registers.  64-key tiles
+//    of K, V and c stream through LDS.  Per 32-key block, with keys as M and queries as N (every
+//    lane holds one query): S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, and
+//    dQ += dS K with the dS^T accumulators as the A operand (queries as M) and K read transposed.
+//    Writes dq and the row sums of dS.
+//  * bwd_pre_kernel before them: D_i, and per head the padded row vectors both main kernels load;
+//    the reversed prefix scan (fox_scan.hip) after them: dlog f from row sums - column sums.
 #include <math.h>
-
-#include <algorithm>
 
 #include "fox_device.h"
 #include "fox_internal.h"
@@ -38,15 +36,14 @@
 namespace fox {
 namespace {
 
-constexpr int kBK = 128;  // keys per workgroup
-constexpr int kBQ = 32;   // queries per tile
+constexpr int kBK = 128;  // keys per workgroup of the key-stationary kernel
+constexpr int kBQ = 32;   // queries per tile of the key-stationary kernel
+constexpr int kQB = 128;  // queries per workgroup of the query-stationary kernel
+constexpr int kKT = 64;   // keys per tile of the query-stationary kernel
 constexpr int kBwdThreads = 256;
+constexpr int kPad = 64;  // per-head row vectors are padded to a multiple of this
 constexpr float kNegInfB = -INFINITY;
 constexpr int kRawBufferCfg = 0x00020000;  // dword 3 of a raw (unswizzled, byte-offset) buffer resource
-// vector-memory instructions every wave issues between a tile's direct-to-LDS loads and the
-// wait for them (from the second tile on): the 16 dQ atomics of the tile before (wave 0 may
-// issue one more, which only makes the wait stronger)
-constexpr int kAtomicsPerTile = 16;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
@@ -101,7 +98,8 @@ __device__ __forceinline__ int sw_off(int r, int e) {
   return r * W + 8 * ((e >> 3) ^ swz<W>(r)) + (e & 7);
 }
 
-// K and V rows as register-resident B operands (else read from LDS on every query tile)
+// K and V rows as register-resident B operands of the key-stationary kernel (else read from
+// LDS on every query tile)
 template <int D>
 constexpr bool kv_in_regs() {
 #ifdef FOX_BWD_KVREG_MIN_D
@@ -112,14 +110,19 @@ constexpr bool kv_in_regs() {
 }
 
 template <int D>
-struct alignas(16) BwdLds {
-  bf16 k[kBK * D];  // the block's keys (swizzled rows); read transposed for dQ
+struct alignas(16) KvLds {
+  bf16 k[kv_in_regs<D>() ? 8 : kBK * D];  // the block's keys and values (swizzled rows)
   bf16 v[kv_in_regs<D>() ? 8 : kBK * D];
-  bf16 q[2][kBQ * D];     // query tiles, double-buffered, filled by direct-to-LDS loads
-  bf16 dout[2][kBQ * D];  // dO tiles, likewise
-  bf16 dst[2][kBK * kBQ];  // dS^T [key][query], double-buffered (written for tile t, read for it one tile later)
+  bf16 q[2][kBQ * D];      // query tiles, double-buffered, filled by direct-to-LDS loads
+  bf16 dout[2][kBQ * D];   // dO tiles, likewise
   float rowv[2][2 * kBQ];  // per buffer: a_i = (c_i - lse_i) log2 e of the tile's queries, then D_i
-  float rpart[2][4][kBQ];  // per tile parity and wave: partial row sums of dS over its two key steps
+};
+
+template <int D>
+struct alignas(16) DqLds {
+  bf16 k[2][kKT * D];  // key tiles, double-buffered, filled by direct-to-LDS loads
+  bf16 v[2][kKT * D];  // value tiles, likewise
+  float cl[2][kKT];    // c_j log2 e of the tile's keys (+inf past n)
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
@@ -168,15 +171,14 @@ __device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows,
   }
 }
 
-// Per query row: zero its dq accumulator row and dc entry; per head, the row vector block
-// [a_0 .. a_{npad-1} | D_0 .. D_{npad-1}] with a_i = (c_i - lse_i) log2 e and D_i = dO_i . O_i,
-// padded past n with a = -inf (no key weight) and D = 0.  Grid: one thread group of D/8 lanes per
+// Per head, the row-vector block [a | D | cl] of 3 * npad floats (npad = n rounded up to kPad):
+// a_i = (c_i - lse_i) log2 e, D_i = dO_i . O_i, cl_i = c_i log2 e, padded past n with a = -inf,
+// D = 0, cl = +inf, so padded queries and keys carry no weight.  One group of D/8 lanes per
 // (head, padded row).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ c,
-                                                      float* __restrict__ rowv, float* __restrict__ dq_acc,
-                                                      float* __restrict__ dc, int64_t bh_count, int n, int npad) {
+                                                      float* __restrict__ rowv, int64_t bh_count, int n, int npad) {
   constexpr int G = D / 8;  // lanes per row, 8 elements each
   const int64_t prow = (int64_t)blockIdx.x * (kBwdThreads / G) + threadIdx.x / G;
   const int g = threadIdx.x % G;
@@ -190,26 +192,52 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
     const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * D + 8 * g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
-    float4* z = reinterpret_cast<float4*>(dq_acc + row * D + 8 * g);
-    z[0] = float4{0.0f, 0.0f, 0.0f, 0.0f};
-    z[1] = float4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 #pragma unroll
   for (int off = G / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
   if (bh < bh_count && g == 0) {
-    float* blk = rowv + bh * 2 * npad;
+    float* blk = rowv + bh * 3 * npad;
     blk[i] = live ? (c[row] - lse[row]) * kLog2e : kNegInfB;
     blk[npad + i] = live ? s : 0.0f;
-    if (live) dc[row] = 0.0f;
+    blk[2 * npad + i] = live ? c[row] * kLog2e : INFINITY;
   }
 }
 
+// Direct-to-LDS loads of a tile of ROWS rows of D bf16 (global rows from `row0` of the head) into
+// a swizzled LDS tile: 64 chunks of 16 bytes per wave instruction; LDS chunk P = r * CH + pc holds
+// global chunk (r, pc ^ swz(r)), which realises the swizzle with linear LDS writes.  The NI =
+// ROWS * CH / 64 instructions are spread over the 4 waves (instruction g = wave * IPW + j; with
+// fewer than 4, waves 0 .. NI-1 issue one each); toff holds a lane's byte offsets.
+template <int D, int ROWS>
+struct TileLoader {
+  static constexpr int CH = D / 8, NI = ROWS * CH / 64, IPW = NI >= 4 ? NI / 4 : 1;
+  static_assert(NI >= 1 && (NI < 4 || NI % 4 == 0), "tile instructions per wave");
+  uint32_t toff[IPW];
+  __device__ __forceinline__ TileLoader(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int P = 64 * ((wave * IPW + j) % NI) + lane, r = P / CH, pc = P % CH;
+      toff[j] = (uint32_t)((r * D + 8 * (pc ^ swz<D>(r))) * 2);
+    }
+  }
+  __device__ __forceinline__ void load(bf16* tile, u32x4 rsrc, int row0, int wave) const {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int g = wave * IPW + j;  // wave-uniform
+      if (NI >= 4 || g < NI) {
+        const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(tile + 64 * 8 * g));
+        lds_load16(m0v, rsrc, toff[j] + (uint32_t)(row0 * D * 2));
+      }
+    }
+  }
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_main_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_kv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
-    const float* __restrict__ rowv, float* __restrict__ dq_acc, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    const float* __restrict__ c, float* __restrict__ dc, int n, int npad, float scale) {
-  using L = BwdLds<D>;
+    const float* __restrict__ rowv, bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ colsum_out,
+    int n, int npad, float scale) {
+  using L = KvLds<D>;
   constexpr int KK = D / 16, DB = D / 32;
   __shared__ L lds;
 
@@ -222,17 +250,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   const int key = key0 + 32 * wave + l32;  // this lane's key (accumulator column)
   const size_t base = bh * (size_t)n;
   const float scale_log2 = scale * kLog2e;
+  const float* blk = rowv + bh * 3 * npad;
 
-  // Buffer resources over this head's rows: loads past row n return zeros and atomics past it
-  // are dropped, so the ragged last query tile needs no branches.
+  // buffer resources over this head's rows: loads past row n return zeros
   const u32x4 rq = sgpr_rsrc(q + base * D, (uint32_t)(n * D * 2));
   const u32x4 rdo = sgpr_rsrc(dout + base * D, (uint32_t)(n * D * 2));
-  const u32x4 rrow = sgpr_rsrc(rowv + bh * 2 * npad, (uint32_t)(2 * npad * 4));
-  const auto rdq = __builtin_amdgcn_make_buffer_rsrc((void*)(dq_acc + base * D), 0, n * D * 4, kRawBufferCfg);
-  const auto rdc = __builtin_amdgcn_make_buffer_rsrc((void*)(dc + base), 0, n * 4, kRawBufferCfg);
+  const u32x4 rrow = sgpr_rsrc(blk, (uint32_t)(2 * npad * 4));
 
-  stage_rows<D>(lds.k, k + (base + key0) * D, kBK, n - key0, tid);
-  if constexpr (!kv_in_regs<D>()) stage_rows<D>(lds.v, v + (base + key0) * D, kBK, n - key0, tid);
+  if constexpr (!kv_in_regs<D>()) {
+    stage_rows<D>(lds.k, k + (base + key0) * D, kBK, n - key0, tid);
+    stage_rows<D>(lds.v, v + (base + key0) * D, kBK, n - key0, tid);
+  }
   // this lane's key row of K and V as the B operands of S = Q K^T and dP = dO V^T (k-elements
   // 16kk + 8hi .. +7), held in registers for the whole query loop where they fit
   constexpr int KR = kv_in_regs<D>() ? KK : 1;
@@ -245,72 +273,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
       vreg[kk] = *reinterpret_cast<const bf16x8*>(v + (base + key) * D + 16 * kk + 8 * hi);
     }
   }
-  // keys past n: +inf here makes every score -inf, so P and dS are 0 for them
-  const float bkey = key < n ? c[base + key] * kLog2e : INFINITY;
+  // c_j log2 e (+inf past n: every score of the key is then -inf, so P and dS are 0)
+  const float bkey = key < n ? blk[2 * npad + key] : INFINITY;
 
-  // Direct-to-LDS loads of one query tile: the q and dO tiles are 2 * 32 * D / 8 chunks of 16
-  // bytes, IPW wave instructions of 64 chunks per wave; instruction g of the tile fills LDS chunks
-  // 64(g % TB) .. +63 of tile g / TB (q, then dO).  LDS chunk P = r * CH + pc holds global chunk
-  // (r, pc ^ swz(r)), which realises the swizzled layout with linear LDS writes.  Wave 0 also
-  // loads the tile's 32 a_i (lanes 0..31) and 32 D_i (lanes 32..63).
-  constexpr int CH = D / 8, TB = kBQ * CH / 64, IPW = 2 * TB / 4;
-  static_assert(2 * TB % 4 == 0, "tile instructions per wave");
-  uint32_t toff[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int g = wave * IPW + j, P = 64 * (g % TB) + lane, r = P / CH, pc = P % CH;
-    toff[j] = (uint32_t)((r * D + 8 * (pc ^ swz<D>(r))) * 2);
-  }
+  // q and dO tiles (and the tile's 32 a_i, lanes 0..31 of wave 0, and 32 D_i, lanes 32..63)
+  const TileLoader<D, kBQ> tl(wave, lane);
   const uint32_t roff = (uint32_t)((hi ? npad : 0) + l32) * 4u;
   auto load_tile = [&](int q0, int buf) {
-#pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int g = wave * IPW + j;
-      const bool is_q = g < TB;  // wave-uniform
-      const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane(
-          (int)lds_addr(is_q ? &lds.q[buf][64 * 8 * (g % TB)] : &lds.dout[buf][64 * 8 * (g % TB)]));
-      lds_load16(m0v, is_q ? rq : rdo, toff[j] + (uint32_t)(q0 * D * 2));
-    }
+    tl.load(lds.q[buf], rq, q0, wave);
+    tl.load(lds.dout[buf], rdo, q0, wave);
     if (wave == 0)
       lds_load4((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&lds.rowv[buf][0])), rrow,
                 roff + (uint32_t)q0 * 4u);
-  };
-
-  // wave 0: dc[q0 + l] += the four waves' partial row sums of query tile q0 (lanes 0..31)
-  auto add_row_sums = [&](int q0, int par) {
-    const float t = lds.rpart[par][0][l32] + lds.rpart[par][1][l32] + lds.rpart[par][2][l32] + lds.rpart[par][3][l32];
-    if (hi == 0) __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(t, rdc, (q0 + l32) * 4, 0, 0);
-  };
-  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
-  const bf16x8 ones = __builtin_shufflevector(one2, one2, 0, 1, 0, 1, 0, 1, 0, 1);
-  // dQ (queries x dims) = dS K over the block's keys for query tile q0, from dS^T in LDS; DB
-  // output blocks of 32 dims shared by the 4 waves (a wave takes block wave % DB and its share of
-  // the 8 key steps).  Also this wave's partial row sums of dS, into rpart[par].
-  auto dq_tile = [&](int q0, const bf16* dsrc, int par) {
-    constexpr int PER = 4 / DB;  // waves per output block
-    constexpr int KS = 8 / PER;  // key steps per wave
-    const int db = wave % DB, part = wave / DB;
-    f32x16 acc = f32x16{}, rsum = f32x16{};
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      const int ks = part * KS + j;
-      const bf16x8 aop = transposed_operand<kBQ>(dsrc, 16 * ks, 0, lane);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, transposed_operand<D>(lds.k, 16 * ks, 32 * db, lane), acc, 0, 0,
-                                                    0);
-    }
-    // row sums over key steps 2 wave, 2 wave + 1: an all-ones A against dS as B (N = queries)
-    // leaves query l32's partial sum in every register of lane l32
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      rsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, transposed_operand<kBQ>(dsrc, 16 * (2 * wave + j), 0, lane),
-                                                     rsum, 0, 0, 0);
-    if (hi == 0) lds.rpart[par][wave][l32] = rsum[0];
-    // lane: dim 32db + l32; register r: query q0 + 8(r/4) + 4hi + r%4.  One atomic instruction
-    // covers 32 consecutive dims of two queries (two full 128-byte lines).
-    const int off = ((q0 + 4 * hi) * D + 32 * db + l32) * 4;
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * scale, rdq, off + (8 * (r >> 2) + (r & 3)) * D * 4, 0, 0);
   };
 
   f32x16 dkt[DB], dvt[DB];  // dK^T, dV^T: lane = key, 16 dims per 32-dim block
@@ -321,23 +295,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   const int nqt = (n + kBQ - 1) / kBQ;
   const int qt0 = CAUSAL ? key0 / kBQ : 0;  // earlier query tiles see none of these keys
   load_tile(qt0 * kBQ, 0);
-  wait_vmem<0>();  // K, V and the first tile
-  // Iteration t: S, dP, P, dS, dV^T and dK^T of query tile t (dS^T into dst[t & 1]), and dQ of
-  // tile t - 1 from dst[(t - 1) & 1]: one barrier per tile, and the dQ atomics of a tile are
-  // issued a whole iteration before the loads queued behind them are waited for.
   for (int qt = qt0; qt < nqt; ++qt) {
-    const int q0 = qt * kBQ, it = qt - qt0, buf = it & 1;
-    // this wave's loads of tile qt were issued before the dQ atomics of tile qt - 2; after the
-    // barrier every wave's loads are visible, dS^T of tile qt - 1 is complete, and the reads of
-    // tile qt - 1's q / dO buffer and of tile qt - 2's dS^T buffer are done
-    if (it == 1)
-      wait_vmem<0>();
-    else if (it > 1)
-      wait_vmem<kAtomicsPerTile>();
+    const int q0 = qt * kBQ, buf = (qt - qt0) & 1;
+    // this wave's loads of tile qt are the only vector-memory instructions in flight; after the
+    // barrier every wave's loads are visible and the reads of the other buffer are done
+    wait_vmem<0>();
     __syncthreads();
     if (qt + 1 < nqt) load_tile(q0 + kBQ, buf ^ 1);
-    if (it >= 2 && wave == 0) add_row_sums(q0 - 2 * kBQ, buf);
-    if (it >= 1) dq_tile(q0 - kBQ, lds.dst[buf ^ 1], buf ^ 1);
     const bf16* tq = lds.q[buf];
     const bf16* tdo = lds.dout[buf];
     const float* arow = &lds.rowv[buf][0];
@@ -369,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
         const int r = 4 * g + e;
         float p = exp2_hw(fmaf(s[r], scale_log2, a4[e]) - bkey);
         if (CAUSAL && key > q0 + 8 * g + 4 * hi + e) p = 0.0f;
-        // dS as the bf16 value the products and the row sums use
+        // dS as the bf16 value the products and the column sums use
         const float dsv = (float)(bf16)(p * (dp[r] - d4[e]));
         s[r] = p;
         dp[r] = dsv;
@@ -388,25 +352,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
                                                           0, 0, 0);
       }
     }
-    // dS^T to LDS: four runs of 4 consecutive queries per lane, 8 bytes each
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 w4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w4[e] = (bf16)dp[4 * g + e];
-      *reinterpret_cast<bf16x4*>(&lds.dst[buf][sw_off<kBQ>(32 * wave + l32, 8 * g + 4 * hi)]) = w4;
-    }
   }
-  // the last tile's dQ, and the row sums of the last two tiles
-  {
-    const int nt = nqt - qt0, lb = (nt - 1) & 1;
-    __syncthreads();
-    if (nt >= 2 && wave == 0) add_row_sums((nqt - 2) * kBQ, lb ^ 1);
-    dq_tile((nqt - 1) * kBQ, lds.dst[lb], lb);
-    __syncthreads();
-    if (wave == 0) add_row_sums((nqt - 1) * kBQ, lb);
-  }
-
 
   // dK = scale dK^T, dV = dV^T: lane = key, dims 32db + 8(r/4) + 4hi + r%4 (runs of 4)
   colsum = pair32_sum(colsum);
@@ -427,56 +373,161 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
         *reinterpret_cast<bf16x4*>(dvr + 32 * db + 8 * g + 4 * hi) = b;
       }
     }
-    if (hi == 0) atomicAdd(dc + base + key, -colsum);
+    if (hi == 0) colsum_out[base + key] = colsum;
   }
 }
 
-__global__ __launch_bounds__(256) void bwd_post_kernel(const float* __restrict__ dq_acc, bf16* __restrict__ dq,
-                                                       int64_t count) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256)
-    dq[i] = (bf16)dq_acc[i];
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    const float* __restrict__ rowv, bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
+    float scale) {
+  using L = DqLds<D>;
+  constexpr int KK = D / 16, DB = D / 32;
+  __shared__ L lds;
+
+  const size_t bh = blockIdx.x;  // heads fastest: the query blocks of one head share its K / V in L2
+  const int qb = (int)(gridDim.y - 1 - blockIdx.y);  // the longest causal blocks start first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qw0 = qb * kQB + 32 * wave;  // this wave's first query
+  const int qi = qw0 + l32;               // this lane's query (accumulator column of S^T)
+  const size_t base = bh * (size_t)n;
+  const float scale_log2 = scale * kLog2e;
+  const float* blk = rowv + bh * 3 * npad;
+
+  const u32x4 rk = sgpr_rsrc(k + base * D, (uint32_t)(n * D * 2));
+  const u32x4 rv = sgpr_rsrc(v + base * D, (uint32_t)(n * D * 2));
+  const u32x4 rcl = sgpr_rsrc(blk + 2 * npad, (uint32_t)(npad * 4));
+
+  // this lane's q and dO rows as the B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8 qreg[KK], dreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qreg[kk] = dreg[kk] = bf16x8{};
+    if (qi < n) {
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + (base + qi) * D + 16 * kk + 8 * hi);
+      dreg[kk] = *reinterpret_cast<const bf16x8*>(dout + (base + qi) * D + 16 * kk + 8 * hi);
+    }
+  }
+  const float aq = qi < n ? blk[qi] : kNegInfB;     // (c_i - lse_i) log2 e; no weight past n
+  const float dq_i = qi < n ? blk[npad + qi] : 0.0f;  // D_i
+
+  const TileLoader<D, kKT> tl(wave, lane);
+  auto load_tile = [&](int k0, int buf) {
+    tl.load(lds.k[buf], rk, k0, wave);
+    tl.load(lds.v[buf], rv, k0, wave);
+    if (wave == 0)
+      lds_load4((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&lds.cl[buf][0])), rcl,
+                (uint32_t)(k0 + lane) * 4u);
+  };
+
+  f32x16 acc[DB];  // dQ: lane = dim 32db + l32, register r = query 8(r/4) + 4hi + r%4
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float rsum = 0.0f;
+
+  const int kend = CAUSAL ? min(n, (qb + 1) * kQB) : n;  // keys this block sees
+  const int nkt = (kend + kKT - 1) / kKT;
+  load_tile(0, 0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    wait_vmem<0>();
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile((kt + 1) * kKT, buf ^ 1);
+    const bf16* tk = lds.k[buf];
+    const bf16* tv = lds.v[buf];
+#pragma unroll
+    for (int kblk = 0; kblk < kKT / 32; ++kblk) {
+      const int key0 = kt * kKT + 32 * kblk;
+      if (CAUSAL && key0 > qw0 + 31) continue;  // wave-uniform: the block is above all its queries
+      // S^T = K Q^T and dP^T = V dO^T: register r holds key key0 + 8(r/4) + 4hi + r%4
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int col = 16 * kk + 8 * hi;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(tk, 32 * kblk + l32, col), qreg[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(tv, 32 * kblk + l32, col), dreg[kk], dp, 0, 0, 0);
+      }
+      const bool diag = CAUSAL && key0 + 31 > qw0;  // wave-uniform
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&lds.cl[buf][32 * kblk + 8 * g + 4 * hi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = exp2_hw(fmaf(s[r], scale_log2, aq) - c4[e]);
+          if (diag && key0 + 8 * g + 4 * hi + e > qi) p = 0.0f;
+          const float dsv = (float)(bf16)(p * (dp[r] - dq_i));
+          s[r] = dsv;
+          rsum += dsv;
+        }
+      }
+      // dQ += dS K: A = dS^T registers (queries as M, keys as K), B = K read transposed
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 a = acc_operand(s, u);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, transposed_operand<D>(tk, 32 * kblk + 16 * u, 32 * db, lane),
+                                                            acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // dq = scale dQ: lane = dim 32db + l32, register r = query qw0 + 8(r/4) + 4hi + r%4
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = qw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (qr < n) dq[(base + qr) * D + 32 * db + l32] = (bf16)(acc[db][r] * scale);
+    }
+  }
+  rsum = pair32_sum(rsum);  // the two lane halves hold the two halves of each 32-key block
+  if (hi == 0 && qi < n) rowsum_out[base + qi] = rsum;
 }
 
-int bwd_npad(int n) { return (n + kBQ - 1) / kBQ * kBQ; }
+int bwd_npad(int n) { return (n + kPad - 1) / kPad * kPad; }
 
 template <int D>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf, float* ws,
                         int64_t bh, int n, float scale, bool causal, hipStream_t stream) {
-  const int64_t rows = bh * n;
   const int npad = bwd_npad(n);
-  // workspace: dq accumulator [bh][n][D], row vectors [bh][2][npad], dc [bh][n] (fp32)
-  float* dq_acc = ws;
-  float* rowv = dq_acc + rows * D;
-  float* dc = rowv + bh * 2 * npad;
+  // workspace: row vectors [bh][3][npad], row sums [bh][n], column sums [bh][n] (fp32)
+  float* rowv = ws;
+  float* rs = rowv + bh * 3 * npad;
+  float* cs = rs + bh * n;
   constexpr int RPB = kBwdThreads / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((bh * npad + RPB - 1) / RPB)), dim3(kBwdThreads), 0, stream,
-                     (const bf16*)o, (const bf16*)dout, lse, c, rowv, dq_acc, dc, bh, n, npad);
+                     (const bf16*)o, (const bf16*)dout, lse, c, rowv, bh, n, npad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)bh, (unsigned)((n + kBK - 1) / kBK));
-  if (causal)
-    hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, dq_acc, (bf16*)dk, (bf16*)dv, c, dc, n,
-                       npad, scale);
-  else
-    hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, dq_acc, (bf16*)dk,
-                       (bf16*)dv, c, dc, n, npad, scale);
+  const dim3 gkv((unsigned)bh, (unsigned)((n + kBK - 1) / kBK));
+  const dim3 gdq((unsigned)bh, (unsigned)((n + kQB - 1) / kQB));
+  if (causal) {
+    hipLaunchKernelGGL((bwd_kv_kernel<D, true>), gkv, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv, cs, n, npad, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), gdq, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad, scale);
+  } else {
+    hipLaunchKernelGGL((bwd_kv_kernel<D, false>), gkv, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv, cs, n, npad, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), gdq, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad, scale);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t cnt = rows * D;
-  const unsigned pg = (unsigned)std::min<int64_t>((cnt + 255) / 256, 65536);
-  hipLaunchKernelGGL(bwd_post_kernel, dim3(pg), dim3(256), 0, stream, (const float*)dq_acc, (bf16*)dq, cnt);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_suffix_sum(dc, dlogf, bh, n, stream);
+  return launch_suffix_sum(rs, cs, dlogf, bh, n, stream);  // dlog f_t = sum_{i >= t} (rs_i - cs_i)
 }
 
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d) {
-  return (size_t)bh * ((size_t)n * ((size_t)d + 1) + 2 * (size_t)bwd_npad(n)) * sizeof(float);
+  (void)d;
+  return (size_t)bh * (3 * (size_t)bwd_npad(n) + 2 * (size_t)n) * sizeof(float);
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

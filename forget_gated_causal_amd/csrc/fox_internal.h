@@ -11,8 +11,9 @@ namespace fox {
 
 // Inclusive prefix sums of `rows` independent rows of length n (fp64 accumulate).
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream);
-// Suffix sums out_t = sum_{i>=t} x_i of `rows` rows of length n (fp64 accumulate).
-hipError_t launch_suffix_sum(const float* x, float* out, int64_t rows, int n, hipStream_t stream);
+// Suffix sums out_t = sum_{i>=t} (x_i - sub_i) of `rows` rows of length n (sub may be null; fp64
+// accumulate).
+hipError_t launch_suffix_sum(const float* x, const float* sub, float* out, int64_t rows, int n, hipStream_t stream);
 
 // FoX forward, causal (decoder mode) or over every key; is_bf16 selects the element type of
 // q/k/v/o; d in {32,64,128}; token_major selects [B,N,H,d] tensors with [B,N,H] gates / lse /

@@ -16,13 +16,16 @@ constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = 4;
 constexpr int kScanChunk = kScanThreads * kScanPerThread;
 
-// REV: the suffix sums out_t = sum_{i>=t} in_i instead (the same scan over the reversed row).
+// REV: the suffix sums out_t = sum_{i>=t} (in_i - sub_i) instead (the same scan over the reversed
+// row; sub may be null).
 template <bool REV>
 __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* __restrict__ logf,
+                                                                   const float* __restrict__ sub,
                                                                    float* __restrict__ c, int n) {
   __shared__ double wave_tot[kScanThreads / 64];
   const size_t row = blockIdx.x;
   const float* src = logf + row * (size_t)n;
+  const float* sb = sub ? sub + row * (size_t)n : nullptr;
   float* dst = c + row * (size_t)n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   double carry = 0.0;
@@ -31,7 +34,12 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
     double x[kScanPerThread];
 #pragma unroll
     for (int e = 0; e < kScanPerThread; ++e)
-      x[e] = (i0 + e < n) ? (double)src[REV ? n - 1 - (i0 + e) : i0 + e] : 0.0;
+      if (i0 + e < n) {
+        const int j = REV ? n - 1 - (i0 + e) : i0 + e;
+        x[e] = (double)src[j] - (sb ? (double)sb[j] : 0.0);
+      } else {
+        x[e] = 0.0;
+      }
 #pragma unroll
     for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
     double t = x[kScanPerThread - 1];  // inclusive over this wave's threads after the loop below
@@ -62,12 +70,13 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
 }  // namespace
 
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(logf_cumsum_kernel<false>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf, c, n);
+  hipLaunchKernelGGL(logf_cumsum_kernel<false>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf,
+                     (const float*)nullptr, c, n);
   return hipGetLastError();
 }
 
-hipError_t launch_suffix_sum(const float* x, float* out, int64_t rows, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(logf_cumsum_kernel<true>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, x, out, n);
+hipError_t launch_suffix_sum(const float* x, const float* sub, float* out, int64_t rows, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(logf_cumsum_kernel<true>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, x, sub, out, n);
   return hipGetLastError();
 }
 

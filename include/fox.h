@@ -156,7 +156,7 @@ fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, co
 
 /*
  * fox_attn_bwd_workspace_bytes -- bytes of scratch fox_attn_bwd needs:
- * b*h*(n*(d + 1) + 2*npad) floats, npad = n rounded up to a multiple of 32.
+ * b*h*(3*npad + 2*n) floats, npad = n rounded up to a multiple of 64.
  * Returns 0 for invalid sizes.
  */
 size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
@@ -182,6 +182,7 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
  *   causal   : nonzero for decoder mode, zero for the unmasked mode.
  *   Errors as fox_attn_fwd; fp32 tensors give FOX_ERR_UNSUPPORTED; every output and the workspace
  *   must not overlap any other buffer (FOX_ERR_INVALID_ARG).
+ *   Every output element has one writer (no atomics): repeated calls give identical results.
  */
 fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                           const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,

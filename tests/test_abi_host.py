@@ -99,10 +99,10 @@ def test_fwd_pruned_workspace_bytes(L):
 
 def test_bwd_workspace_bytes(L):
     f = L.fox_attn_bwd_workspace_bytes
-    # dQ accumulator [bh, n, d], row vectors a_i and D_i padded to a multiple of 32, dc [bh, n] (fp32)
-    assert f(2, 16, 4096, 128) == 32 * (4096 * 129 + 2 * 4096) * 4
-    assert f(1, 3, 65, 64) == 3 * (65 * 65 + 2 * 96) * 4
-    assert f(1, 1, 1, 32) == (33 + 2 * 32) * 4
+    # row vectors a_i, D_i, c_i log2 e padded to a multiple of 64, row sums and column sums (fp32)
+    assert f(2, 16, 4096, 128) == 32 * (3 * 4096 + 2 * 4096) * 4
+    assert f(1, 3, 65, 64) == 3 * (3 * 128 + 2 * 65) * 4
+    assert f(1, 1, 1, 32) == (3 * 64 + 2) * 4
     assert f(0, 1, 10, 64) == 0 and f(1, 1, 10, 48) == 0 and f(1, 1, 0, 64) == 0
 
 

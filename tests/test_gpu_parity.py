@@ -512,3 +512,18 @@ def test_bwd_c3_full_size_sampled_heads():
             msg.append(f"{name} {err:.2e} (max|ref| {np.abs(r).max():.2e})")
             assert err <= bound, (b, h, name, err, bound)
         print(f"  c3 head ({b},{h}): " + ", ".join(msg), flush=True)
+
+
+def test_bwd_repeatable():
+    """Every backward output has one writer: two calls give bit-identical gradients."""
+    cfg = fi.FwdConfig("bwd_rep", 2, 3, 700, 64, "bf16", 2.0, 1.0)
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(5)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    a = fox.attn_bwd(q, k, v, o, dout, lse, c, scale=inp["scale"])
+    b = fox.attn_bwd(q, k, v, o, dout, lse, c, scale=inp["scale"])
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
