@@ -30,6 +30,8 @@
 //    the reversed prefix scan (fox_scan.hip) after them: dlog f from row sums - column sums.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fox_device.h"
 #include "fox_internal.h"
 
@@ -113,9 +115,9 @@ template <int D>
 struct alignas(16) KvLds {
   bf16 k[kv_in_regs<D>() ? 8 : kBK * D];  // the block's keys and values (swizzled rows)
   bf16 v[kv_in_regs<D>() ? 8 : kBK * D];
-  bf16 q[2][kBQ * D];      // query tiles, double-buffered, filled by direct-to-LDS loads
-  bf16 dout[2][kBQ * D];   // dO tiles, likewise
-  float rowv[2][2 * kBQ];  // per buffer: a_i = (c_i - lse_i) log2 e of the tile's queries, then D_i
+  bf16 q[3][kBQ * D];      // query tiles, three buffers, filled by direct-to-LDS loads
+  bf16 dout[3][kBQ * D];   // dO tiles, likewise
+  float rowv[3][2 * kBQ];  // per buffer: a_i = (c_i - lse_i) log2 e of the tile's queries, then D_i
 };
 
 template <int D>
@@ -292,23 +294,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   for (int db = 0; db < DB; ++db) dkt[db] = dvt[db] = f32x16{};
   float colsum = 0.0f;
 
-  const int nqt = (n + kBQ - 1) / kBQ;
-  const int qt0 = CAUSAL ? key0 / kBQ : 0;  // earlier query tiles see none of these keys
-  load_tile(qt0 * kBQ, 0);
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int q0 = qt * kBQ, buf = (qt - qt0) & 1;
-    // this wave's loads of tile qt are the only vector-memory instructions in flight; after the
-    // barrier every wave's loads are visible and the reads of the other buffer are done
-    wait_vmem<0>();
-    __syncthreads();
-    if (qt + 1 < nqt) load_tile(q0 + kBQ, buf ^ 1);
+  // S = Q K^T and dP = dO V^T of one query tile for this wave's 32 keys
+  auto scores = [&](int buf, f32x16& s, f32x16& dp) {
     const bf16* tq = lds.q[buf];
     const bf16* tdo = lds.dout[buf];
-    const float* arow = &lds.rowv[buf][0];
-    const float* drow = &lds.rowv[buf][kBQ];
-
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys
-    f32x16 s = f32x16{}, dp = f32x16{};
+    s = dp = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int col = 16 * kk + 8 * hi;
@@ -323,36 +313,154 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(tq, l32, col), kb, s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(tdo, l32, col), vb, dp, 0, 0, 0);
     }
-    // P and dS: register r holds query m = 8(r/4) + 4hi + r%4 of the tile
+  };
+
+  // Software pipeline over the query tiles: step t issues the score MFMAs of tile t + 1 and does
+  // the elementwise work and the dV^T / dK^T MFMAs of tile t.  Three LDS buffers: tile t (read
+  // transposed), t + 1 (scores), t + 2 (loading).  The schedule is explicit, as in the forward:
+  // each slot holds one MFMA and a share of the VALU work that does not depend on it, with the
+  // LDS operands read a few slots ahead; sched_barrier keeps the compiler from regrouping slots.
+  constexpr int NQ = 2 * KK;   // score MFMAs per tile (S and dP alternate)
+  constexpr int EQ = 16 / NQ;  // accumulator elements of the previous tile per score slot
+  constexpr int PFQ = NQ >= 8 ? 4 : NQ;  // score operands in flight
+  constexpr int NP = 4 * DB;   // dV^T / dK^T MFMAs per tile
+  constexpr int PFP = NP >= 8 ? 4 : NP;  // their operands in flight
+  static_assert(16 % NQ == 0, "elements per slot");
+  const int nqt = (n + kBQ - 1) / kBQ;
+  const int qt0 = CAUSAL ? key0 / kBQ : 0;  // earlier query tiles see none of these keys
+  const int nt = nqt - qt0;
+
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+  float colsum1 = 0.0f;
+  // One step.  HN: there is a next tile; MASK: the tile may hold keys past its queries (causal);
+  // BC: the tile's LDS buffer when known at compile time (t % 3), else -1.
+  auto step = [&](auto hn, auto mk, auto bc, int t, f32x16& s, f32x16& dp) {
+    constexpr bool HN = decltype(hn)::value, MASK = CAUSAL && decltype(mk)::value;
+    constexpr int BC = decltype(bc)::value;
+    const int q0 = (qt0 + t) * kBQ;
+    const int buf = BC >= 0 ? BC : t % 3, nb = BC >= 0 ? (BC + 1) % 3 : (t + 1) % 3;
+    if constexpr (HN) {
+      // this wave's loads of tile t + 1 are the only vector-memory instructions in flight; after
+      // the barrier every wave's loads are visible and tile t - 1's buffer is no longer read
+      wait_vmem<0>();
+      __syncthreads();
+      if (t + 2 < nt) load_tile(q0 + 2 * kBQ, BC >= 0 ? (BC + 2) % 3 : (t + 2) % 3);
+    }
+    const bf16* tq = lds.q[buf];
+    const bf16* tdo = lds.dout[buf];
+    const float* arow = &lds.rowv[buf][0];
+    const float* drow = &lds.rowv[buf][kBQ];
+    // score operands of tile t + 1: slot i is S (i even) or dP (i odd) for k-step i / 2
+    auto qread = [&](int i) -> bf16x8 {
+      return row_operand<D>(i & 1 ? lds.dout[nb] : lds.q[nb], l32, 16 * (i >> 1) + 8 * hi);
+    };
+    auto kvread = [&](int i) -> bf16x8 {
+      if constexpr (kv_in_regs<D>()) return i & 1 ? vreg[i >> 1] : kreg[i >> 1];
+      else return row_operand<D>(i & 1 ? lds.v : lds.k, 32 * wave + l32, 16 * (i >> 1) + 8 * hi);
+    };
+    bf16x8 aop[NQ], bop[NQ];
+    f32x4 a4[4], d4[4];
+    f32x16 s2 = f32x16{}, dp2 = f32x16{};
+    a4[0] = *reinterpret_cast<const f32x4*>(&arow[4 * hi]);
+    d4[0] = *reinterpret_cast<const f32x4*>(&drow[4 * hi]);
+    if constexpr (HN) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&arow[8 * g + 4 * hi]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&drow[8 * g + 4 * hi]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float p = exp2_hw(fmaf(s[r], scale_log2, a4[e]) - bkey);
-        if (CAUSAL && key > q0 + 8 * g + 4 * hi + e) p = 0.0f;
-        // dS as the bf16 value the products and the column sums use
-        const float dsv = (float)(bf16)(p * (dp[r] - d4[e]));
-        s[r] = p;
-        dp[r] = dsv;
-        colsum += dsv;
+      for (int i = 0; i < PFQ; ++i) {
+        aop[i] = qread(i);
+        bop[i] = kvread(i);
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (K of these MFMAs runs over the tile's 32 queries)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      // the row vectors of query group g, two slots before their first use
+#pragma unroll
+      for (int g = 1; g < 4; ++g) {
+        if (i == (4 * g / EQ >= 2 ? 4 * g / EQ - 2 : 0)) {
+          a4[g] = *reinterpret_cast<const f32x4*>(&arow[8 * g + 4 * hi]);
+          d4[g] = *reinterpret_cast<const f32x4*>(&drow[8 * g + 4 * hi]);
+        }
+      }
+      // P and dS of tile t (fp32; rounded to bf16 once, as MFMA operands): register r holds
+      // query m = 8(r/4) + 4hi + r%4
+#pragma unroll
+      for (int r = i * EQ; r < (i + 1) * EQ; ++r) {
+        const int g = r >> 2, e = r & 3;
+        float p = exp2_hw(fmaf(s[r], scale_log2, a4[g][e]) - bkey);
+        if (MASK && key > q0 + 8 * g + 4 * hi + e) p = 0.0f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[g][e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HN) {
+        if (i & 1) dp2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop[i], dp2, 0, 0, 0);
+        else s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop[i], s2, 0, 0, 0);
+        if (i + PFQ < NQ) {
+          aop[i + PFQ] = qread(i + PFQ);
+          bop[i + PFQ] = kvread(i + PFQ);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (K of these MFMAs runs over the tile's 32 queries); slot j:
+    // query half u = j / (2 DB), dim block db, dV (even) or dK (odd).  The column sums of dS are
+    // taken over the same bf16 values the MFMAs use.
+    const bf16x8 pb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
+    const bf16x8 sb[2] = {acc_operand(dp, 0), acc_operand(dp, 1)};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const bf16x8 pb = acc_operand(s, u), sb = acc_operand(dp, u);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(transposed_operand<D>(tdo, 16 * u, 32 * db, lane), pb, dvt[db],
-                                                          0, 0, 0);
-        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(transposed_operand<D>(tq, 16 * u, 32 * db, lane), sb, dkt[db],
-                                                          0, 0, 0);
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 pr = {sb[u][2 * w], sb[u][2 * w + 1]};
+        if (w & 1) colsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, colsum1, false);
+        else colsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, colsum, false);
       }
     }
+    auto tread = [&](int j) -> bf16x8 {
+      const int u = j / (2 * DB), db = (j >> 1) % DB;
+      return transposed_operand<D>(j & 1 ? tq : tdo, 16 * u, 32 * db, lane);
+    };
+    bf16x8 top[NP];
+#pragma unroll
+    for (int j = 0; j < PFP; ++j) top[j] = tread(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int u = j / (2 * DB), db = (j >> 1) % DB;
+      if (j & 1) dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[j], sb[u], dkt[db], 0, 0, 0);
+      else dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[j], pb[u], dvt[db], 0, 0, 0);
+      if (j + PFP < NP) top[j + PFP] = tread(j + PFP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s = s2;
+    dp = dp2;
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  using DYN = std::integral_constant<int, -1>;
+
+  load_tile(qt0 * kBQ, 0);
+  if (nt > 1) load_tile((qt0 + 1) * kBQ, 1);
+  wait_vmem<0>();
+  __syncthreads();
+  f32x16 s, dp;
+  scores(0, s, dp);
+  // the first 6 tiles (the 4 that hold the block's diagonal, rounded up to a multiple of 3) with
+  // the mask; then groups of 3 with the LDS buffers known at compile time; the rest, and the last
+  // tile (no next), with the mask (harmless where every key precedes every query)
+  const int nm = CAUSAL ? min(nt - 1, 6) : 0;
+  int t = 0;
+  for (; t < nm; ++t) step(T_{}, T_{}, DYN{}, t, s, dp);
+  if (t % 3 == 0) {
+    for (; t + 3 < nt; t += 3) {
+      step(T_{}, F_{}, std::integral_constant<int, 0>{}, t, s, dp);
+      step(T_{}, F_{}, std::integral_constant<int, 1>{}, t + 1, s, dp);
+      step(T_{}, F_{}, std::integral_constant<int, 2>{}, t + 2, s, dp);
+    }
   }
+  for (; t + 1 < nt; ++t) step(T_{}, T_{}, DYN{}, t, s, dp);
+  step(F_{}, T_{}, DYN{}, nt - 1, s, dp);
+  colsum += colsum1;
 
   // dK = scale dK^T, dV = dV^T: lane = key, dims 32db + 8(r/4) + 4hi + r%4 (runs of 4)
   colsum = pair32_sum(colsum);
