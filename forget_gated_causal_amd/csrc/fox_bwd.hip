@@ -122,9 +122,9 @@ struct alignas(16) KvLds {
 
 template <int D>
 struct alignas(16) DqLds {
-  bf16 k[2][kKT * D];  // key tiles, double-buffered, filled by direct-to-LDS loads
-  bf16 v[2][kKT * D];  // value tiles, likewise
-  float cl[2][kKT];    // c_j log2 e of the tile's keys (+inf past n)
+  bf16 k[3][kKT * D];  // key tiles, three buffers, filled by direct-to-LDS loads
+  bf16 v[3][kKT * D];  // value tiles, likewise
+  float cl[3][kKT];    // c_j log2 e of the tile's keys (+inf past n)
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
@@ -534,55 +534,138 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   f32x16 acc[DB];  // dQ: lane = dim 32db + l32, register r = query 8(r/4) + 4hi + r%4
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float rsum = 0.0f;
+  float rsum0 = 0.0f, rsum1 = 0.0f;
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
   const int kend = CAUSAL ? min(n, (qb + 1) * kQB) : n;  // keys this block sees
   const int nkt = (kend + kKT - 1) / kKT;
-  load_tile(0, 0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    wait_vmem<0>();
-    __syncthreads();
-    if (kt + 1 < nkt) load_tile((kt + 1) * kKT, buf ^ 1);
-    const bf16* tk = lds.k[buf];
-    const bf16* tv = lds.v[buf];
+  const int nblk = 2 * nkt;  // 32-key blocks (the last may lie past kend: zero weight)
+
+  // S^T = K Q^T and dP^T = V dO^T of one 32-key block: register r holds key 8(r/4) + 4hi + r%4
+  constexpr int NQ = 2 * KK;   // score MFMAs per block (S and dP alternate)
+  constexpr int EQ = 16 / NQ;  // accumulator elements of the previous block per score slot
+  constexpr int PFQ = NQ >= 8 ? 4 : NQ;
+  constexpr int NP = 2 * DB;   // dQ MFMAs per block
+  constexpr int PFP = NP >= 4 ? 4 : NP;
+  auto kvrow = [&](int buf, int kb, int i) -> bf16x8 {
+    return row_operand<D>(i & 1 ? lds.v[buf] : lds.k[buf], 32 * kb + l32, 16 * (i >> 1) + 8 * hi);
+  };
+  auto scores = [&](int buf, int kb, f32x16& s, f32x16& dp) {
+    s = dp = f32x16{};
 #pragma unroll
-    for (int kblk = 0; kblk < kKT / 32; ++kblk) {
-      const int key0 = kt * kKT + 32 * kblk;
-      if (CAUSAL && key0 > qw0 + 31) continue;  // wave-uniform: the block is above all its queries
-      // S^T = K Q^T and dP^T = V dO^T: register r holds key key0 + 8(r/4) + 4hi + r%4
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int col = 16 * kk + 8 * hi;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(tk, 32 * kblk + l32, col), qreg[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(tv, 32 * kblk + l32, col), dreg[kk], dp, 0, 0, 0);
-      }
-      const bool diag = CAUSAL && key0 + 31 > qw0;  // wave-uniform
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&lds.cl[buf][32 * kblk + 8 * g + 4 * hi]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = exp2_hw(fmaf(s[r], scale_log2, aq) - c4[e]);
-          if (diag && key0 + 8 * g + 4 * hi + e > qi) p = 0.0f;
-          const float dsv = (float)(bf16)(p * (dp[r] - dq_i));
-          s[r] = dsv;
-          rsum += dsv;
-        }
-      }
-      // dQ += dS K: A = dS^T registers (queries as M, keys as K), B = K read transposed
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 a = acc_operand(s, u);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, transposed_operand<D>(tk, 32 * kblk + 16 * u, 32 * db, lane),
-                                                            acc[db], 0, 0, 0);
+    for (int i = 0; i < NQ; ++i) {
+      if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kvrow(buf, kb, i), dreg[i >> 1], dp, 0, 0, 0);
+      else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kvrow(buf, kb, i), qreg[i >> 1], s, 0, 0, 0);
+    }
+  };
+
+  // One step per 32-key block b (tile b / 2, half b % 2), pipelined like the key-stationary
+  // kernel: the score MFMAs of block b + 1 share slots with the elementwise work of block b, then
+  // dQ += dS K for block b.  Three LDS buffers: the tile of block b, the next, and one loading.
+  // HN: a next block exists; MASK: causal mask needed (the block may hold keys past queries);
+  // BC: block b's index modulo 6 when known at compile time (its buffer (b / 2) % 3), else -1.
+  auto step = [&](auto hn, auto mk, auto bc, int b, f32x16& s, f32x16& dp) {
+    constexpr bool HN = decltype(hn)::value, MASK = CAUSAL && decltype(mk)::value;
+    constexpr int BC = decltype(bc)::value;
+    const int kt = b >> 1, kb = BC >= 0 ? (BC & 1) : (b & 1);
+    const int buf = BC >= 0 ? (BC >> 1) : kt % 3;
+    const int nbuf = BC >= 0 ? (((BC + 1) % 6) >> 1) : ((b + 1) >> 1) % 3, nkb = kb ^ 1;
+    if constexpr (HN) {
+      if (kb == 1) {
+        // block b + 1 opens tile kt + 1: this wave's loads of it are the only vector-memory
+        // instructions in flight; after the barrier every wave's loads are visible and tile
+        // kt - 1's buffer is no longer read
+        wait_vmem<0>();
+        __syncthreads();
+        if (kt + 2 < nkt) load_tile((kt + 2) * kKT, BC >= 0 ? ((BC >> 1) + 2) % 3 : (kt + 2) % 3);
       }
     }
+    const int key0 = b * 32;
+    const float* clb = &lds.cl[buf][32 * kb];
+    bf16x8 aop[NQ];
+    f32x4 c4[4];
+    f32x16 s2 = f32x16{}, dp2 = f32x16{};
+    c4[0] = *reinterpret_cast<const f32x4*>(&clb[4 * hi]);
+    if constexpr (HN) {
+#pragma unroll
+      for (int i = 0; i < PFQ; ++i) aop[i] = kvrow(nbuf, nkb, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+      for (int g = 1; g < 4; ++g)
+        if (i == (4 * g / EQ >= 2 ? 4 * g / EQ - 2 : 0)) c4[g] = *reinterpret_cast<const f32x4*>(&clb[8 * g + 4 * hi]);
+      // P^T and dS^T of block b (fp32; rounded to bf16 once, as the dQ operand)
+#pragma unroll
+      for (int r = i * EQ; r < (i + 1) * EQ; ++r) {
+        const int g = r >> 2, e = r & 3;
+        float p = exp2_hw(fmaf(s[r], scale_log2, aq) - c4[g][e]);
+        if (MASK && key0 + 8 * g + 4 * hi + e > qi) p = 0.0f;
+        s[r] = p * (dp[r] - dq_i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HN) {
+        if (i & 1) dp2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], dreg[i >> 1], dp2, 0, 0, 0);
+        else s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], qreg[i >> 1], s2, 0, 0, 0);
+        if (i + PFQ < NQ) aop[i + PFQ] = kvrow(nbuf, nkb, i + PFQ);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dQ += dS K: A = dS^T (queries as M, keys as K), B = K read transposed; the row sums of dS
+    // are taken over the same bf16 values
+    const bf16x8 sb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 pr = {sb[u][2 * w], sb[u][2 * w + 1]};
+        if (w & 1) rsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum1, false);
+        else rsum0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum0, false);
+      }
+    }
+    const bf16* tk = lds.k[buf];
+    auto tread = [&](int j) -> bf16x8 {
+      return transposed_operand<D>(tk, 32 * kb + 16 * (j / DB), 32 * (j % DB), lane);
+    };
+    bf16x8 top[NP];
+#pragma unroll
+    for (int j = 0; j < PFP; ++j) top[j] = tread(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[j / DB], top[j], acc[j % DB], 0, 0, 0);
+      if (j + PFP < NP) top[j + PFP] = tread(j + PFP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s = s2;
+    dp = dp2;
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  using DYN = std::integral_constant<int, -1>;
+
+  load_tile(0, 0);
+  if (nkt > 1) load_tile(kKT, 1);
+  wait_vmem<0>();
+  __syncthreads();
+  f32x16 s, dp;
+  scores(0, 0, s, dp);
+  // groups of 6 blocks (3 tiles) with the buffers known at compile time, unmasked; then the
+  // rest one by one, with the causal mask on the blocks of the last tile... all blocks from
+  // nblk - 4 on (the 128 keys of the diagonal)
+  const int nfree = CAUSAL ? nblk - 4 : nblk - 1;  // blocks before the masked tail (with a next)
+  int b = 0;
+  for (; b + 6 <= nfree; b += 6) {
+    step(T_{}, F_{}, std::integral_constant<int, 0>{}, b, s, dp);
+    step(T_{}, F_{}, std::integral_constant<int, 1>{}, b + 1, s, dp);
+    step(T_{}, F_{}, std::integral_constant<int, 2>{}, b + 2, s, dp);
+    step(T_{}, F_{}, std::integral_constant<int, 3>{}, b + 3, s, dp);
+    step(T_{}, F_{}, std::integral_constant<int, 4>{}, b + 4, s, dp);
+    step(T_{}, F_{}, std::integral_constant<int, 5>{}, b + 5, s, dp);
   }
+  for (; b + 1 < nblk; ++b) step(T_{}, T_{}, DYN{}, b, s, dp);
+  step(F_{}, T_{}, DYN{}, nblk - 1, s, dp);
 
   // dq = scale dQ: lane = dim 32db + l32, register r = query qw0 + 8(r/4) + 4hi + r%4
 #pragma unroll
@@ -593,7 +676,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
       if (qr < n) dq[(base + qr) * D + 32 * db + l32] = (bf16)(acc[db][r] * scale);
     }
   }
-  rsum = pair32_sum(rsum);  // the two lane halves hold the two halves of each 32-key block
+  // the two lane halves hold the two halves of each 32-key block
+  const float rsum = pair32_sum(rsum0 + rsum1);
   if (hi == 0 && qi < n) rowsum_out[base + qi] = rsum;
 }
 
