@@ -265,11 +265,11 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     achieved = flops / (ms * 1e-3) / 1e12
     return {"workload": cfg.desc + ", backward", "value": round(achieved, 2), "unit": "TFLOP/s",
             "ms_per_step": round(ms, 4),
-            "note": "10*d flop per causal pair; one call = pre, main (bwd_main_kernel), dq conversion and "
-                    "gate suffix-sum kernels",
+            "note": "10*d flop per causal pair (the dq kernel's recomputation of S and dP, 4*d more, is not "
+                    "counted); one call = bwd_pre, bwd_kv, bwd_dq and the gate suffix-sum kernels",
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                         "kernel": f"bwd_main_kernel<{cfg.d},causal> + 3 small kernels"}}
+                         "kernel": f"bwd_kv_kernel<{cfg.d},causal> + bwd_dq_kernel<{cfg.d},causal> + 2 small kernels"}}
 
 
 def bench_decode(torch, fox, fi, tag, steps, warmup):
