@@ -44,6 +44,7 @@ constexpr int kQB = 128;  // queries per workgroup of the query-stationary kerne
 constexpr int kKT = 64;   // keys per tile of the query-stationary kernel
 constexpr int kBwdThreads = 256;
 constexpr int kPad = 64;  // per-head row vectors are padded to a multiple of this
+constexpr int64_t kFuseMaxBlocks = 1024;  // grids up to this many blocks run both parts in one launch
 constexpr float kNegInfB = -INFINITY;
 constexpr int kRawBufferCfg = 0x00020000;  // dword 3 of a raw (unswizzled, byte-offset) buffer resource
 
@@ -234,17 +235,14 @@ struct TileLoader {
   }
 };
 
+// Key-stationary part (dK, dV, column sums of dS) for key block kb of head bh.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_kv_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
-    const float* __restrict__ rowv, bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ colsum_out,
-    int n, int npad, float scale) {
-  using L = KvLds<D>;
+__device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, const bf16* __restrict__ q,
+                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                             const bf16* __restrict__ dout, const float* __restrict__ rowv,
+                                             bf16* __restrict__ dk, bf16* __restrict__ dv,
+                                             float* __restrict__ colsum_out, int n, int npad, float scale) {
   constexpr int KK = D / 16, DB = D / 32;
-  __shared__ L lds;
-
-  const size_t bh = blockIdx.x;  // heads fastest: the key blocks of one head share its q / dO in L2
-  const int kb = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -485,17 +483,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   }
 }
 
+// Query-stationary part (dQ, row sums of dS) for query block qb of head bh.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
-    const float* __restrict__ rowv, bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
-    float scale) {
-  using L = DqLds<D>;
+__device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, const bf16* __restrict__ q,
+                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                             const bf16* __restrict__ dout, const float* __restrict__ rowv,
+                                             bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
+                                             float scale) {
   constexpr int KK = D / 16, DB = D / 32;
-  __shared__ L lds;
-
-  const size_t bh = blockIdx.x;  // heads fastest: the query blocks of one head share its K / V in L2
-  const int qb = (int)(gridDim.y - 1 - blockIdx.y);  // the longest causal blocks start first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -681,6 +676,50 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   if (hi == 0 && qi < n) rowsum_out[base + qi] = rsum;
 }
 
+// The two parts as kernels of their own (large grids) ...
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_kv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    const float* __restrict__ rowv, bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ colsum_out,
+    int n, int npad, float scale) {
+  __shared__ KvLds<D> lds;
+  // heads fastest: the key blocks of one head share its q / dO in L2; causal work falls with kb
+  bwd_kv_block<D, CAUSAL>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    const float* __restrict__ rowv, bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
+    float scale) {
+  __shared__ DqLds<D> lds;
+  // the longest causal blocks (the last queries) start first
+  bwd_dq_block<D, CAUSAL>(lds, blockIdx.x, (int)(gridDim.y - 1 - blockIdx.y), q, k, v, dout, rowv, dq, rowsum_out, n,
+                          npad, scale);
+}
+
+// ... and both in one launch for small grids, where each fills the other's tail.  blockIdx.x is the head (the
+// blocks of one head are adjacent and share its tensors in L2); blockIdx.y = 2j is key block j and
+// 2j + 1 is query block nb - 1 - j, so both kinds are issued heaviest first (causal work falls
+// with the key block and grows with the query block).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_main_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    const float* __restrict__ rowv, bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
+    float* __restrict__ rowsum_out, float* __restrict__ colsum_out, int n, int npad, float scale) {
+  __shared__ union {
+    KvLds<D> kv;
+    DqLds<D> dq;
+  } lds;
+  const size_t bh = blockIdx.x;
+  const int j = (int)(blockIdx.y >> 1);
+  if ((blockIdx.y & 1) == 0)
+    bwd_kv_block<D, CAUSAL>(lds.kv, bh, j, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale);
+  else
+    bwd_dq_block<D, CAUSAL>(lds.dq, bh, (int)(gridDim.y >> 1) - 1 - j, q, k, v, dout, rowv, dq, rowsum_out, n, npad,
+                            scale);
+}
+
 int bwd_npad(int n) { return (n + kPad - 1) / kPad * kPad; }
 
 template <int D>
@@ -697,18 +736,34 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                      (const bf16*)o, (const bf16*)dout, lse, c, rowv, bh, n, npad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gkv((unsigned)bh, (unsigned)((n + kBK - 1) / kBK));
-  const dim3 gdq((unsigned)bh, (unsigned)((n + kQB - 1) / kQB));
-  if (causal) {
-    hipLaunchKernelGGL((bwd_kv_kernel<D, true>), gkv, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv, cs, n, npad, scale);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), gdq, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad, scale);
+  static_assert(kBK == kQB, "one key block and one query block per block pair");
+  const int nb = (n + kBK - 1) / kBK;
+  if (2 * bh * nb <= kFuseMaxBlocks) {
+    const dim3 grid((unsigned)bh, (unsigned)(2 * nb));
+    if (causal)
+      hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, (bf16*)dk,
+                         (bf16*)dv, rs, cs, n, npad, scale);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, (bf16*)dk,
+                         (bf16*)dv, rs, cs, n, npad, scale);
   } else {
-    hipLaunchKernelGGL((bwd_kv_kernel<D, false>), gkv, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv, cs, n, npad, scale);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), gdq, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad, scale);
+    const dim3 grid((unsigned)bh, (unsigned)nb);
+    if (causal) {
+      hipLaunchKernelGGL((bwd_kv_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv, cs, n, npad,
+                         scale);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad, scale);
+    } else {
+      hipLaunchKernelGGL((bwd_kv_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv,
+                         cs, n, npad, scale);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad,
+                         scale);
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

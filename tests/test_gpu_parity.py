@@ -457,7 +457,9 @@ BWD = [(32, 1, 2, 65, True, 2.0, 1.0), (64, 2, 2, 300, True, 2.0, 2.0), (128, 1,
        # edges: one row; less than, exactly and one past a 32-query tile; exactly one 128-key block
        (64, 1, 1, 1, True, 2.0, 1.0), (128, 1, 1, 1, False, 2.0, 1.0), (128, 1, 2, 31, True, 2.0, 1.0),
        (32, 1, 1, 32, True, 2.0, 1.0), (64, 1, 1, 33, False, 2.0, 1.0), (64, 1, 2, 128, True, 2.0, 1.0),
-       (128, 1, 1, 129, True, 2.0, 1.0)]
+       (128, 1, 1, 129, True, 2.0, 1.0),
+       # grids above the single-launch limit (2 * heads * 128-blocks > 1024): the two-kernel path
+       (32, 2, 16, 2100, False, 2.0, 1.0), (128, 2, 16, 2100, True, 3.0, 1.5)]
 
 
 @pytest.mark.parametrize("d,B,H,n,causal,mu,sigma", BWD)
