@@ -12,15 +12,17 @@
 // cancel and dlog f_t reduces to the cross block (i >= t > j) as it does exactly.  The
 // forward's lse and c (its outputs) give P without a second softmax.
 //
-// Two main kernels split the work so that every output has one writer (no atomics, and the
-// results are the same from run to run):
-//  * bwd_kv_kernel<D, CAUSAL>: key-stationary.  One workgroup of 4 waves per (128-key block,
+// Two parts split the work so that every output has one writer (no atomics, and the results are
+// the same from run to run).  Large grids run them as two kernels, small grids as one
+// (bwd_main_kernel, which alternates key and query blocks); both use an explicit slot schedule
+// that overlaps the next tile's score MFMAs with the current tile's elementwise work:
+//  * bwd_kv_block / bwd_kv_kernel<D, CAUSAL>: key-stationary.  One workgroup of 4 waves per (128-key block,
 //    head); wave w owns keys 32w..32w+31.  32-query tiles of q and dO stream through LDS.  Per
 //    tile, on v_mfma_f32_32x32x16_bf16 with queries as M and keys as N (every accumulator lane
 //    holds one key and 16 queries): S = Q K^T, dP = dO V^T; P and dS in registers; dV^T += dO^T P
 //    and dK^T += Q^T dS (A = transposed LDS reads of dO / q, B = the bf16 P / dS registers).
 //    Writes dk, dv and the column sums of dS.
-//  * bwd_dq_kernel<D, CAUSAL>: query-stationary.  One workgroup of 4 waves per (128-query block,
+//  * bwd_dq_block / bwd_dq_kernel<D, CAUSAL>: query-stationary.  One workgroup of 4 waves per (128-query block,
 //    head); wave w owns queries 32w..32w+31, whose q and dO rows stay in registers.  64-key tiles
 //    of K, V and c stream through LDS.  Per 32-key block, with keys as M and queries as N (every
 //    lane holds one query): S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, and
@@ -51,10 +53,8 @@ constexpr int kRawBufferCfg = 0x00020000;  // dword 3 of a raw (unswizzled, byte
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
-// Direct-to-LDS buffer loads (lane l's bytes land at LDS byte address m0v + l * size).  Issued
-// through inline assembly, so the compiler does not wait for them; the kernel waits itself.
-// Raw buffer resource in SGPRs for the assembly below (the same fields the compiler builds for
-// __builtin_amdgcn_make_buffer_rsrc).
+// Raw buffer resource in SGPRs for the direct-to-LDS loads below: loads at or past num_bytes
+// return zeros.
 __device__ __forceinline__ u32x4 sgpr_rsrc(const void* p, uint32_t num_bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)p;
   u32x4 r;
@@ -64,6 +64,8 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* p, uint32_t num_bytes) {
   r[3] = (uint32_t)kRawBufferCfg;
   return r;
 }
+// Direct-to-LDS buffer loads (lane l's bytes land at LDS byte address m0v + l * size).  Issued
+// through inline assembly, so the compiler does not wait for them; the kernel waits itself.
 __device__ __forceinline__ void lds_load16(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
   __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :
