@@ -190,7 +190,6 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
                           float scale, fox_dtype_t dtype, int causal, hipStream_t stream);
 
 /*
- * fox_attn_decode_workspace_bytes/*
  * fox_attn_decode_workspace_bytes -- bytes of scratch fox_attn_decode needs for
  * these sizes (split-K partial results).  Returns 0 for invalid sizes.
  */

@@ -181,6 +181,34 @@ def attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, lens, scale):
     return out, lse, c_new
 
 
+def attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, lens, logf_new, scale):
+    """Decode against caches held in pages: logical slot j of sequence s is row j % P of page
+    block_table[s, j // P] (P = page size) in k_pages, v_pages [num_pages, H, P, d] and c_pages
+    [num_pages, H, P].  Each sequence's first lens[s] slots are gathered into a plain cache and
+    decoded as ``attn_decode`` (the new token at slot lens[s]-1).
+
+    Returns (O [S,H,d], lse [S,H], c_new [S,H]).
+    """
+    q = _f64(q)
+    kp, vp, cp = np.asarray(k_pages), np.asarray(v_pages), np.asarray(c_pages)
+    ln = _f64(logf_new)
+    S, H, d = q.shape
+    P = kp.shape[2]
+    out = np.empty((S, H, d))
+    lse = np.empty((S, H))
+    c_new = np.empty((S, H))
+    for s in range(S):
+        L = int(lens[s])
+        pages = [int(block_table[s, j // P]) for j in range(L)]
+        rows = [j % P for j in range(L)]
+        kc = np.stack([kp[pg, :, r] for pg, r in zip(pages, rows)], axis=1)  # [H, L, d]
+        vc = np.stack([vp[pg, :, r] for pg, r in zip(pages, rows)], axis=1)
+        cc = np.stack([cp[pg, :, r] for pg, r in zip(pages, rows)], axis=1)  # [H, L]
+        o_s, l_s, c_s = attn_decode(q[s:s + 1], kc[None], vc[None], cc[None], ln[s:s + 1], scale)
+        out[s], lse[s], c_new[s] = o_s[0], l_s[0], c_s[0]
+    return out, lse, c_new
+
+
 def fwd_bwd_head(q, k, v, logf, scale, do, causal: bool = True):
     """Gradients of FoX attention for one head (fp64), from the definition by the chain rule.
 

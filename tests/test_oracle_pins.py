@@ -24,7 +24,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_decode, attn_decode_ragged, attn_fwd, brute_decode_head, brute_fwd_head, fwd_head_rows, logf_cumsum
+from oracle import attn_decode, attn_decode_paged, attn_decode_ragged, attn_fwd, brute_decode_head, brute_fwd_head, fwd_head_rows, logf_cumsum
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TOL = 1e-12
@@ -271,6 +271,38 @@ def test_ragged_decode_matches_brute_force():
         ln[s] = logf_all[s, :, Ls - 1]
         cc[s, :, Ls - 1:] = np.nan  # the slot the step computes, and the unused tail
     o, lse, c_new = attn_decode_ragged(q, kc, vc, cc, ln, lens, 0.45)
+    for s, Ls in enumerate(lens):
+        for h in range(H):
+            ob, lb = brute_decode_head(q[s, h].tolist(), kc[s, h, :Ls].tolist(), vc[s, h, :Ls].tolist(),
+                                       logf_all[s, h, :Ls].tolist(), 0.45)
+            assert np.abs(o[s, h] - np.array(ob)).max() < TOL and abs(lse[s, h] - lb) < TOL
+            assert abs(c_new[s, h] - math.fsum(logf_all[s, h, :Ls])) < 1e-12
+
+
+def test_paged_decode_matches_brute_force():
+    """Paged caches: sequences of several lengths scattered over shuffled pages of 4 slots (the
+    last page partly used, unused pages and slots NaN), each against the scalar enumeration of its
+    own tokens."""
+    S, H, L, d, P = 4, 2, 11, 3, 4
+    q, kc, vc, logf_all, _ = _decode_case(31, S, H, L, d)
+    lens = [1, 11, 5, 8]
+    maxp = (L + P - 1) // P
+    rng = np.random.default_rng(7)
+    npages = S * maxp + 3
+    perm = rng.permutation(npages)
+    table = perm[: S * maxp].reshape(S, maxp)
+    kp = np.full((npages, H, P, d), np.nan)
+    vp = np.full((npages, H, P, d), np.nan)
+    cp = np.full((npages, H, P), np.nan)
+    cc = np.cumsum(logf_all, -1)
+    ln = np.empty((S, H))
+    for s, Ls in enumerate(lens):
+        ln[s] = logf_all[s, :, Ls - 1]
+        for j in range(Ls):
+            pg, r = table[s, j // P], j % P
+            kp[pg, :, r], vp[pg, :, r] = kc[s, :, j], vc[s, :, j]
+            cp[pg, :, r] = cc[s, :, j] if j < Ls - 1 else np.nan  # the slot the step computes
+    o, lse, c_new = attn_decode_paged(q, kp, vp, cp, table, lens, ln, 0.45)
     for s, Ls in enumerate(lens):
         for h in range(H):
             ob, lb = brute_decode_head(q[s, h].tolist(), kc[s, h, :Ls].tolist(), vc[s, h, :Ls].tolist(),
