@@ -256,3 +256,42 @@ def attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens, scale
                                       S, H, L, d, float(_default_scale(d) if scale is None else scale), dt, _stream())
     check("fox_attn_decode_ragged", st)
     return o, lse
+
+
+def attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, cache_lens, logf_new, scale: float | None = None,
+                      out=None, lse=None, workspace=None, want_lse: bool = True):
+    """attn_decode_ragged with the caches in pages: k_pages, v_pages [num_pages, H, P, d],
+    c_pages [num_pages, H, P] fp32, block_table [S, max_pages] int32 (logical slot j of sequence s
+    is row j % P of page block_table[s, j // P]), cache_lens [S] int32.  Returns (o, lse)."""
+    S, H, d = q.shape
+    NP, H2, P, d2 = k_pages.shape
+    dt = _DTYPES.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if (H2, d2) != (H, d):
+        raise ValueError(f"k_pages shape {tuple(k_pages.shape)} does not match q {tuple(q.shape)}")
+    _need(q, "q", q.dtype)
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        _need(t, name, q.dtype)
+        if tuple(t.shape) != (NP, H, P, d):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(NP, H, P, d)}")
+    _need(c_pages, "c_pages", torch.float32)
+    _need(logf_new, "logf_new", torch.float32)
+    _need(block_table, "block_table", torch.int32)
+    _need(cache_lens, "cache_lens", torch.int32)
+    if tuple(c_pages.shape) != (NP, H, P) or tuple(logf_new.shape) != (S, H):
+        raise ValueError("c_pages must be [num_pages,H,P] and logf_new [S,H]")
+    if block_table.dim() != 2 or block_table.shape[0] != S or tuple(cache_lens.shape) != (S,):
+        raise ValueError("block_table must be [S, max_pages] and cache_lens [S]")
+    maxp = block_table.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty(S, H, device=q.device, dtype=torch.float32)
+    nbytes = decode_workspace_bytes(S, H, maxp * P, d)
+    ws = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8) if workspace is None else workspace
+    st = lib().fox_attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(c_pages), _ptr(block_table),
+                                     _ptr(cache_lens), _ptr(logf_new), _ptr(o), _ptr(lse if want_lse else None),
+                                     _ptr(ws), ws.numel() * ws.element_size(), S, H, NP, P, maxp, d,
+                                     float(_default_scale(d) if scale is None else scale), dt, _stream())
+    check("fox_attn_decode_paged", st)
+    return o, (lse if want_lse else None)

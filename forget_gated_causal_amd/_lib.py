@@ -41,6 +41,8 @@ SIGNATURES = {
                                        ctypes.c_float, ctypes.c_int, _P]),
     "fox_attn_decode_ragged": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _I64,
                                               _I64, ctypes.c_float, ctypes.c_int, _P]),
+    "fox_attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64,
+                                             _I64, _I64, _I64, _I64, ctypes.c_float, ctypes.c_int, _P]),
     "fox_attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "fox_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _I64,
                                     _I64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _P]),

@@ -157,9 +157,9 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
   const size_t osz[] = {tb, tb, tb, vb, need};
   const void* all[] = {q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace};
   const size_t asz[] = {tb, tb, tb, tb, tb, vb, vb, tb, tb, tb, vb, need};
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 5; ++i)  // outs[i] is all[7 + i]
     for (int j = 0; j < 12; ++j)
-      if (all[j] != outs[i] && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
+      if (j != 7 + i && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
   return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, static_cast<float*>(workspace),
                                        bh, (int)n, (int)d, scale, causal != 0, stream));
 }
@@ -224,6 +224,48 @@ fox_status_t fox_attn_decode_ragged(const void* q, const void* k_cache, const vo
   return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, cache_lens, (int)h, o, lse,
                                           static_cast<float*>(workspace), s * h, (int)l, (int)d, scale,
                                           dtype == FOX_BF16, stream));
+}
+
+fox_status_t fox_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, float* c_pages,
+                                   const int32_t* block_table, const int32_t* cache_lens, const float* logf_new,
+                                   void* o, float* lse, void* workspace, size_t workspace_bytes, int64_t s,
+                                   int64_t h, int64_t num_pages, int64_t page_size, int64_t max_pages, int64_t d,
+                                   float scale, fox_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k_pages || !v_pages || !c_pages || !block_table || !cache_lens || !logf_new || !o)
+    return FOX_ERR_INVALID_ARG;
+  if (s <= 0 || h <= 0 || num_pages <= 0 || max_pages <= 0 || d <= 0) return FOX_ERR_INVALID_ARG;
+  if (page_size < 16 || page_size > 4096 || (page_size & (page_size - 1)) != 0) return FOX_ERR_INVALID_ARG;
+  if (max_pages > FOX_MAX_SEQ / page_size || num_pages > kI32Max || s > kI32Max / h) return FOX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || !head_dim_ok(d)) return FOX_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(c_pages, 4) || !aligned(block_table, 4) || !aligned(cache_lens, 4) || !aligned(logf_new, 4) ||
+      !aligned(lse, 4))
+    return FOX_ERR_INVALID_ARG;
+  const int64_t sh = s * h, l = max_pages * page_size;
+  const int nsplit = fox::decode_num_splits(sh, (int)l, (int)d);
+  if (sh > kI32Max / nsplit) return FOX_ERR_INVALID_ARG;
+  const size_t need = fox::decode_workspace_bytes(sh, (int)l, (int)d);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(dtype), slots = (size_t)num_pages * (size_t)h * (size_t)page_size;
+  const size_t obytes = (size_t)sh * (size_t)d * eb, sbytes = (size_t)sh * sizeof(float);
+  const size_t kvbytes = slots * (size_t)d * eb, cbytes = slots * sizeof(float);
+  const size_t tbytes = (size_t)s * (size_t)max_pages * sizeof(int32_t), lbytes = (size_t)s * sizeof(int32_t);
+  // every buffer written (o, lse, c_pages, workspace) apart from every other buffer
+  const void* outs[] = {o, lse, c_pages, workspace};
+  const size_t osz[] = {obytes, sbytes, cbytes, need};
+  const void* all[] = {q, k_pages, v_pages, c_pages, block_table, cache_lens, logf_new, o, lse, workspace};
+  const size_t asz[] = {obytes, kvbytes, kvbytes, cbytes, tbytes, lbytes, sbytes, obytes, sbytes, need};
+  const int self[] = {7, 8, 3, 9};  // outs[i] is all[self[i]]
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (j != self[i] && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
+  int shift = 0;
+  while ((int64_t{1} << shift) < page_size) ++shift;
+  return from_hip(fox::launch_attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, (int)max_pages, shift,
+                                                (int)num_pages, logf_new, cache_lens, (int)h, o, lse,
+                                                static_cast<float*>(workspace), sh, (int)d, scale, dtype == FOX_BF16,
+                                                stream));
 }
 
 }  // extern "C"

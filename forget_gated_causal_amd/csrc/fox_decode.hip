@@ -22,6 +22,9 @@
 // Ragged caches: with `lens` given, sequence s uses only its first lens[s] slots (clamped to
 // [1, L]) of caches allocated for L, and its new token sits at slot lens[s]-1.  The split
 // grid still covers L slots; splits past a sequence's length leave empty records.
+// Paged caches (PAGED): logical slot j of sequence s is row j & (P-1) of physical page
+// table[s][j >> log2 P] in pools [pages][heads][P][d] (c: [pages][heads][P]); the capacity L is
+// max_pages * P.  Everything else is the ragged step.
 #include <math.h>
 
 #include <algorithm>
@@ -67,6 +70,26 @@ struct Vec16<float> {
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
+// Where a (sequence, head)'s logical cache slot lives: the row index into the K / V caches (times d
+// for the element offset) and the index into the c cache.
+struct PageMap {
+  const int* table;  // [sequences][max_pages] physical page numbers, or null (contiguous caches)
+  int max_pages;
+  int shift;   // log2 of the page size
+  int npages;  // pages in the pools (table entries are clamped to [0, npages))
+};
+template <bool PAGED>
+__device__ __forceinline__ size_t cache_row(const PageMap& pm, int sh, int nh, int Lcap, int slot) {
+  if constexpr (PAGED) {
+    const int s = sh / nh, h = sh - s * nh;
+    int pg = pm.table[(size_t)s * pm.max_pages + (slot >> pm.shift)];
+    pg = min(max(pg, 0), pm.npages - 1);
+    return (((size_t)pg * nh + h) << pm.shift) + (size_t)(slot & ((1 << pm.shift) - 1));
+  } else {
+    return (size_t)sh * Lcap + slot;
+  }
+}
+
 // Merge running softmax state (m, l, acc) with another in base 2; either may be empty (m = -inf).
 template <int N>
 __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N], float mo, float lo,
@@ -80,14 +103,14 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N],
   m = mn;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
                                                                   const T* __restrict__ vc,
                                                                   const float* __restrict__ cc,
                                                                   const float* __restrict__ logf_new,
                                                                   float* __restrict__ part, int Lcap,
                                                                   const int* __restrict__ lens, int nh, int nsplit,
-                                                                  int chunk, float scale_log2) {
+                                                                  int chunk, float scale_log2, PageMap pm) {
   using C = DecCfg<T, D>;
   constexpr int EPL = C::EPL, G = C::G, KPW = C::KPW, KPB = C::KPB;
   __shared__ float s_m[kDecWaves], s_l[kDecWaves];
@@ -101,16 +124,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G;
   const int slot = lane / G + KPW * wave;
-  const size_t kvbase = (size_t)sh * Lcap * D;
-  const T* kp = kc + kvbase + g * EPL;
-  const T* vp = vc + kvbase + g * EPL;
-  const float* ccr = cc + (size_t)sh * Lcap;
+  const T* kp = kc + g * EPL;
+  const T* vp = vc + g * EPL;
 
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = to_f32(q[(size_t)sh * D + g * EPL + e]) * scale_log2;
   const float lnew = logf_new[sh];
-  const float cprev = (L >= 2) ? ccr[L - 2] : 0.0f;
+  const float cprev = (L >= 2) ? cc[cache_row<PAGED>(pm, sh, nh, Lcap, L - 2)] : 0.0f;
 
   float m = kNegInf, l = 0.0f, acc[EPL];
 #pragma unroll
@@ -126,9 +147,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
       key[u] = start + (s0 - u) * KPB + slot;
       const bool ok = (s0 - u >= 0) && key[u] < end;
       if (ok) {
-        kr[u].load(kp + (size_t)key[u] * D);
-        vr[u].load(vp + (size_t)key[u] * D);
-        cj[u] = (key[u] < L - 1) ? ccr[key[u]] : cprev;
+        const size_t row = cache_row<PAGED>(pm, sh, nh, Lcap, key[u]);
+        kr[u].load(kp + row * D);
+        vr[u].load(vp + row * D);
+        cj[u] = (key[u] < L - 1) ? cc[row] : cprev;
       } else {
         kr[u].zero();
         vr[u].zero();
@@ -219,11 +241,12 @@ __device__ __forceinline__ void store_out<float>(float* p, float x) {
   *p = x;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part, T* __restrict__ o,
                                                            float* __restrict__ lse, float* __restrict__ cc,
                                                            const float* __restrict__ logf_new, int Lcap,
-                                                           const int* __restrict__ lens, int nh, int nsplit) {
+                                                           const int* __restrict__ lens, int nh, int nsplit,
+                                                           PageMap pm) {
   constexpr int REC = D + 2;
   const int sh = blockIdx.x;
   const int lane = threadIdx.x;
@@ -256,27 +279,34 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   if (lane == 0) {
     if (lse) lse[sh] = (float)(((double)M + (double)log2f(lt)) * kLn2d);
     const int L = lens ? min(max(lens[sh / nh], 1), Lcap) : Lcap;
-    float* ccr = cc + (size_t)sh * Lcap;
-    const float cprev = (L >= 2) ? ccr[L - 2] : 0.0f;
-    ccr[L - 1] = cprev + logf_new[sh];
+    const float cprev = (L >= 2) ? cc[cache_row<PAGED>(pm, sh, nh, Lcap, L - 2)] : 0.0f;
+    cc[cache_row<PAGED>(pm, sh, nh, Lcap, L - 1)] = cprev + logf_new[sh];
   }
+}
+
+template <typename T, int D, bool PAGED>
+hipError_t launch_decode_p(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
+                           const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, float scale,
+                           const PageMap& pm, hipStream_t stream) {
+  const int nsplit = decode_num_splits(sh, l, D);
+  const int chunk = (l + nsplit - 1) / nsplit;
+  const float scale_log2 = (float)((double)scale * kLog2ed);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, PAGED>), dim3((unsigned)(sh * nsplit)), dim3(kDecThreads), 0, stream,
+                     (const T*)q, (const T*)kc, (const T*)vc, (const float*)cc, logf_new, ws, l, lens, nh, nsplit,
+                     chunk, scale_log2, pm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, PAGED>), dim3((unsigned)sh), dim3(64), 0, stream, (const float*)ws,
+                     (T*)o, lse, cc, logf_new, l, lens, nh, nsplit, pm);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
                            const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, float scale,
-                           hipStream_t stream) {
-  const int nsplit = decode_num_splits(sh, l, D);
-  const int chunk = (l + nsplit - 1) / nsplit;
-  const float scale_log2 = (float)((double)scale * kLog2ed);
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)(sh * nsplit)), dim3(kDecThreads), 0, stream,
-                     (const T*)q, (const T*)kc, (const T*)vc, (const float*)cc, logf_new, ws, l, lens, nh, nsplit,
-                     chunk, scale_log2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)sh), dim3(64), 0, stream, (const float*)ws,
-                     (T*)o, lse, cc, logf_new, l, lens, nh, nsplit);
-  return hipGetLastError();
+                           const PageMap& pm, hipStream_t stream) {
+  if (pm.table) return launch_decode_p<T, D, true>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
+  return launch_decode_p<T, D, false>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
 }
 
 }  // namespace
@@ -296,23 +326,45 @@ size_t decode_workspace_bytes(int64_t sh, int l, int d) {
   return (size_t)sh * (size_t)decode_num_splits(sh, l, d) * (size_t)(d + 2) * sizeof(float);
 }
 
-hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
-                              const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, int d,
-                              float scale, bool is_bf16, hipStream_t stream) {
+namespace {
+
+hipError_t launch_decode_any(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
+                             const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, int d,
+                             float scale, bool is_bf16, const PageMap& pm, hipStream_t stream) {
   if (is_bf16) {
     switch (d) {
-      case 32: return launch_decode_t<bf16, 32>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
-      case 64: return launch_decode_t<bf16, 64>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
-      case 128: return launch_decode_t<bf16, 128>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
+      case 32: return launch_decode_t<bf16, 32>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
+      case 64: return launch_decode_t<bf16, 64>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
+      case 128:
+        return launch_decode_t<bf16, 128>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
     }
   } else {
     switch (d) {
-      case 32: return launch_decode_t<float, 32>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
-      case 64: return launch_decode_t<float, 64>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
-      case 128: return launch_decode_t<float, 128>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, stream);
+      case 32: return launch_decode_t<float, 32>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
+      case 64: return launch_decode_t<float, 64>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
+      case 128:
+        return launch_decode_t<float, 128>(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, scale, pm, stream);
     }
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
+                              const int* lens, int nh, void* o, float* lse, float* ws, int64_t sh, int l, int d,
+                              float scale, bool is_bf16, hipStream_t stream) {
+  const PageMap pm{nullptr, 0, 0, 0};
+  return launch_decode_any(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, d, scale, is_bf16, pm, stream);
+}
+
+hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* vp, float* cp, const int* table,
+                                    int max_pages, int page_shift, int npages, const float* logf_new, const int* lens,
+                                    int nh, void* o, float* lse, float* ws, int64_t sh, int d, float scale,
+                                    bool is_bf16, hipStream_t stream) {
+  const PageMap pm{table, max_pages, page_shift, npages};
+  return launch_decode_any(q, kp, vp, cp, logf_new, lens, nh, o, lse, ws, sh, max_pages << page_shift, d, scale,
+                           is_bf16, pm, stream);
 }
 
 }  // namespace fox

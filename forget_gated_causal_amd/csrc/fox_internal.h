@@ -37,6 +37,12 @@ size_t decode_workspace_bytes(int64_t sh, int l, int d);
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
                               const int* lens, int nh, void* o, float* lse, float* workspace, int64_t sh, int l,
                               int d, float scale, bool is_bf16, hipStream_t stream);
+// The same step against paged caches: pools k/v [npages][nh][1 << page_shift][d], c [npages][nh][P],
+// table [sequences][max_pages] (entries clamped to [0, npages)), lens required.
+hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* vp, float* cp, const int* table,
+                                    int max_pages, int page_shift, int npages, const float* logf_new, const int* lens,
+                                    int nh, void* o, float* lse, float* ws, int64_t sh, int d, float scale,
+                                    bool is_bf16, hipStream_t stream);
 
 // Backward pass (bf16): dq, dk, dv and dlog f from q, k, v, the forward's o, lse and c, and dO.
 // The workspace holds bh*n*(d + 2) floats (dq accumulator, dO.O per row, dc per key).

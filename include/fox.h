@@ -238,6 +238,35 @@ fox_status_t fox_attn_decode_ragged(const void* q, const void* k_cache, const vo
                                     void* workspace, size_t workspace_bytes, int64_t s, int64_t h, int64_t l,
                                     int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream);
 
+/*
+ * fox_attn_decode_paged -- fox_attn_decode_ragged with the caches held in fixed-size pages.
+ *   The pages define no cache; this is the ragged step with each sequence's slots reached
+ *   through a page table, the layout that lets serving engines grow caches without copying.
+ *   Logical slot j of sequence s (j < cache_lens[s]) lives at row j % page_size of physical
+ *   page block_table[s * max_pages + j / page_size]; the new token's k, v sit at slot
+ *   cache_lens[s]-1 and that slot of c_pages is written.
+ *
+ *   q        : [s, h, d] of `dtype`, the new tokens' queries.
+ *   k_pages, v_pages : [num_pages, h, page_size, d] of `dtype`: page p holds page_size
+ *              consecutive slots of every head.
+ *   c_pages  : [num_pages, h, page_size] fp32, the prefix sums at the same positions; slots
+ *              0 .. cache_lens[s]-2 read, slot cache_lens[s]-1 WRITTEN (as fox_attn_decode).
+ *   block_table : [s, max_pages] int32 DEVICE array; entries in [0, num_pages) (clamped on
+ *              the device, so a bad entry never addresses memory outside the pools).
+ *   cache_lens  : [s] int32 DEVICE array; values in [1, max_pages * page_size] (clamped).
+ *   logf_new, o, lse, scale, dtype : as fox_attn_decode.
+ *   page_size : a power of two in [16, 4096]; max_pages * page_size <= FOX_MAX_SEQ.
+ *   workspace, workspace_bytes : at least
+ *              fox_attn_decode_workspace_bytes(s, h, max_pages * page_size, d) bytes.
+ *   Pages may be shared between sequences for reading; two sequences whose new tokens map to
+ *   the same page slot race on its c write.  Errors as fox_attn_decode_ragged.
+ */
+fox_status_t fox_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, float* c_pages,
+                                   const int32_t* block_table, const int32_t* cache_lens, const float* logf_new,
+                                   void* o, float* lse, void* workspace, size_t workspace_bytes, int64_t s,
+                                   int64_t h, int64_t num_pages, int64_t page_size, int64_t max_pages, int64_t d,
+                                   float scale, fox_dtype_t dtype, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fox_status_string(fox_status_t status);
 

@@ -170,6 +170,62 @@ def test_decode_ragged_rejects_bad_arguments(L):
     assert _decr(L, o=B) == INVALID
 
 
+def _decp(L, **kw):
+    args = dict(q=A, k=B, v=C, cc=D, table=0x90_0000_0000, lens=0x91_0000_0000, lnew=E, o=F, lse=G, ws=H,
+                wsb=1 << 24, s=2, h=3, npages=40, page=64, maxp=8, d=64, scale=0.125, dt=_lib.FOX_BF16)
+    args.update(kw)
+    a = args
+    return L.fox_attn_decode_paged(a["q"], a["k"], a["v"], a["cc"], a["table"], a["lens"], a["lnew"], a["o"],
+                                   a["lse"], a["ws"], a["wsb"], a["s"], a["h"], a["npages"], a["page"], a["maxp"],
+                                   a["d"], a["scale"], a["dt"], None)
+
+
+def test_decode_paged_rejects_bad_arguments(L):
+    assert _decp(L, table=None) == INVALID
+    assert _decp(L, lens=None) == INVALID
+    assert _decp(L, table=0x90_0000_0002) == INVALID  # not 4-byte aligned
+    for page in (0, 8, 48, 8192):  # a power of two in [16, 4096]
+        assert _decp(L, page=page) == INVALID
+    assert _decp(L, npages=0) == INVALID
+    assert _decp(L, maxp=0) == INVALID
+    assert _decp(L, maxp=(1 << 22) // 64 + 1) == INVALID  # capacity above FOX_MAX_SEQ
+    assert _decp(L, d=96) == UNSUP
+    assert _decp(L, scale=0.0) == INVALID
+    assert _decp(L, ws=None) == WS
+    assert _decp(L, wsb=16) == WS
+    assert _decp(L, o=B) == INVALID  # output inside the K pages
+    assert _decp(L, cc=C) == INVALID  # written c pages inside the V pages
+    assert _decp(L, ws=0x90_0000_0000) == INVALID  # workspace over the page table
+
+
+def _bwd(L, **kw):
+    I, J, K, M = (0x10_0000_0000 * (i + 9) for i in range(4))
+    args = dict(q=A, k=B, v=C, o=D, dout=E, lse=F, c=G, dq=H, dk=I, dv=J, dl=K, ws=M, wsb=1 << 30, b=1, h=2, n=300,
+                d=64, scale=0.125, dt=_lib.FOX_BF16, causal=1)
+    args.update(kw)
+    a = args
+    return L.fox_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["c"], a["dq"], a["dk"], a["dv"],
+                          a["dl"], a["ws"], a["wsb"], a["b"], a["h"], a["n"], a["d"], a["scale"], a["dt"], a["causal"],
+                          None)
+
+
+def test_bwd_rejects_bad_arguments(L):
+    assert _bwd(L, dout=None) == INVALID
+    assert _bwd(L, dl=None) == INVALID
+    assert _bwd(L, n=0) == INVALID
+    assert _bwd(L, d=96) == UNSUP
+    assert _bwd(L, dt=_lib.FOX_F32) == UNSUP  # bf16 only
+    assert _bwd(L, scale=float("nan")) == INVALID
+    assert _bwd(L, q=A + 8) == INVALID  # 16-byte alignment
+    assert _bwd(L, ws=None) == WS
+    assert _bwd(L, wsb=64) == WS
+    # outputs may not alias an input or each other, also when the pointers are equal
+    assert _bwd(L, dq=A) == INVALID
+    assert _bwd(L, dv=0x10_0000_0000 * 9) == INVALID  # dv == dk
+    assert _bwd(L, dl=F) == INVALID  # dlogf == lse
+    assert _bwd(L, ws=H) == INVALID  # workspace == dq
+
+
 def test_fwd_ex_layout_checks(L):
     def ex(layout, n=128, h=2, d=32, causal=1):
         return L.fox_attn_fwd_ex(A, B, C, D, E, F, G, 1, h, n, d, 0.17, _lib.FOX_F32, causal, layout, None)
