@@ -448,6 +448,85 @@ def test_decode_ragged_full_length_equals_decode():
     assert torch.equal(o1, o2) and torch.equal(lse1, lse2) and torch.equal(c1, c2)
 
 
+# ------------------------------------------------------------------------------ paged decode
+
+def _paged_case(inp, lens, P, seed):
+    """Ragged caches of capacity L (a multiple of P) scattered over shuffled pages of P slots, with
+    3 spare pages; unused slots hold NaN.  Returns GPU and oracle views plus the ragged GPU caches."""
+    S, H, L, d = inp["k"].shape
+    maxp = L // P
+    npages = S * maxp + 3
+    g = torch.Generator().manual_seed(seed)
+    table = torch.randperm(npages, generator=g)[: S * maxp].reshape(S, maxp).to(torch.int32)
+    la = inp["logf_all"]
+    c_dense = fox.logf_cumsum(la.to(DEV)).cpu()
+    lnew = torch.empty(S, H)
+    kp = torch.full((npages, H, P, d), float("nan"), dtype=inp["k"].dtype)
+    vp = torch.full((npages, H, P, d), float("nan"), dtype=inp["v"].dtype)
+    cp = torch.full((npages, H, P), float("nan"))
+    for s in range(S):
+        Ls = int(lens[s])
+        lnew[s] = la[s, :, Ls - 1]
+        c_dense[s, :, Ls - 1:] = float("nan")  # the slot the step writes, and the unused tail
+        for i in range((Ls + P - 1) // P):
+            pg, n0 = int(table[s, i]), i * P
+            cnt = min(P, Ls - n0)
+            kp[pg, :, :cnt] = inp["k"][s, :, n0:n0 + cnt]
+            vp[pg, :, :cnt] = inp["v"][s, :, n0:n0 + cnt]
+            cp[pg, :, :cnt] = c_dense[s, :, n0:n0 + cnt]
+    return table, kp, vp, cp, c_dense, lnew
+
+
+PAGED = [("bf16", 128, 64, 1024), ("bf16", 64, 16, 512), ("f32", 32, 256, 1024), ("bf16", 32, 4096, 8192)]
+
+
+@pytest.mark.parametrize("dtype,d,P,L", PAGED)
+def test_decode_paged_parity_and_equals_ragged(dtype, d, P, L):
+    """Paged caches against the oracle's page gather, and bit-equal to the ragged step on the
+    same logical caches (the same arithmetic with other addresses); unused page slots (NaN) are
+    never read and the written c lands in the right page slot."""
+    cfg = fi.DecodeConfig(f"paged_{dtype}_{d}_{P}_{L}", 5, 3, L, d, dtype, 4.0, 2.0)
+    inp = fi.decode_inputs(cfg)
+    lens = _ragged_lens(5, L, P + d)
+    table, kp, vp, cp, c_dense, lnew = _paged_case(inp, lens, P, P + L)
+    q = inp["q"].to(DEV)
+    cp_gpu = cp.to(DEV)
+    o, lse = fox.attn_decode_paged(q, kp.to(DEV), vp.to(DEV), cp_gpu, table.to(DEV), lens.to(DEV), lnew.to(DEV),
+                                   scale=inp["scale"])
+    c_r = c_dense.to(DEV)
+    o_r, lse_r = fox.attn_decode_ragged(q, inp["k"].to(DEV), inp["v"].to(DEV), c_r, lnew.to(DEV), lens.to(DEV),
+                                        scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_r) and torch.equal(lse, lse_r)
+    cpg, crg = cp_gpu.cpu(), c_r.cpu()
+    for s in range(cfg.S):
+        j = int(lens[s]) - 1
+        assert torch.equal(cpg[int(table[s, j // P]), :, j % P], crg[s, :, j])
+    o_ref, lse_ref, cnew_ref = oracle.attn_decode_paged(_np(inp["q"]), _np(kp), _np(vp), _np(cp), table.numpy(),
+                                                        lens.numpy(), lnew.double().numpy(), inp["scale"])
+    eo, el = np.abs(_np(o) - o_ref).max(), np.abs(_np(lse) - lse_ref).max()
+    print(f"  paged P={P} lens {lens.tolist()}: max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL[dtype] and el <= TOL[dtype]
+    assert np.isfinite(_np(o)).all()
+
+
+def test_decode_paged_full_size_equals_ragged():
+    """c5's shape (S=64 H=32 L=8192 d=128) with 256-slot pages in a shuffled pool: bit-equal to the
+    ragged step, which the full-size ragged test checks against the oracle."""
+    cfg = fi.DECODE["c5"]
+    inp = fi.decode_inputs(cfg)
+    lens = _ragged_lens(cfg.S, cfg.L, 11)
+    table, kp, vp, cp, c_dense, lnew = _paged_case(inp, lens, 256, 12)
+    q = inp["q"].to(DEV)
+    o, lse = fox.attn_decode_paged(q, kp.to(DEV), vp.to(DEV), cp.to(DEV), table.to(DEV), lens.to(DEV),
+                                   lnew.to(DEV), scale=inp["scale"])
+    del kp, vp
+    o_r, lse_r = fox.attn_decode_ragged(q, inp["k"].to(DEV), inp["v"].to(DEV), c_dense.to(DEV), lnew.to(DEV),
+                                        lens.to(DEV), scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_r) and torch.equal(lse, lse_r)
+
+
 # ---------------------------------------------------------------------------------- backward
 
 # (d, B, H, n, causal, gate-logit mean, sd)
