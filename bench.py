@@ -47,11 +47,13 @@ def fwd_flops(cfg) -> float:
     return 4.0 * cfg.d * cfg.N * (cfg.N + 1) / 2 * cfg.B * cfg.H
 
 
-def decode_bytes(cfg) -> dict:
-    sh = cfg.S * cfg.H
+def decode_bytes(cfg, lens=None) -> dict:
+    """Algorithmic bytes of one decode call; with per-sequence lengths, only the slots in use."""
     eb = 2 if cfg.dtype == "bf16" else 4
-    kv = 2 * sh * cfg.L * cfg.d * eb
-    rd = kv + sh * (cfg.L - 1) * 4 + sh * cfg.d * eb + sh * 4
+    slots = cfg.S * cfg.L if lens is None else int(sum(int(x) for x in lens))
+    sh = cfg.S * cfg.H
+    kv = 2 * cfg.H * slots * cfg.d * eb
+    rd = kv + cfg.H * (slots - cfg.S) * 4 + sh * cfg.d * eb + sh * 4
     wr = sh * cfg.d * eb + sh * 4 + sh * 4
     return {"total": rd + wr, "read": rd, "kv": kv, "write": wr}
 
@@ -208,8 +210,9 @@ def fwd_kernel_name(torch, cfg) -> str:
 
 def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
     """mode: "causal" (fox_attn_fwd), "unmasked" (fox_attn_fwd_noncausal, 4*d flop for every
-    (query, key) pair) or "pruned" (fox_attn_fwd_pruned, timed whole with its key-norm and
-    prefix-sum kernels; its rate is the causal work over that time, an effective rate)."""
+    (query, key) pair), "pruned" (fox_attn_fwd_pruned, timed whole with its key-norm and
+    prefix-sum kernels; its rate is the causal work over that time, an effective rate) or
+    "token" (fox_attn_fwd_ex on [B,N,H,d] tensors, causal)."""
     cfg = fi.FWD[tag]
     inp = fi.fwd_inputs(cfg)
     dev = "cuda"
@@ -224,6 +227,12 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
                          dtype=torch.uint8)
         fn = lambda: fox.attn_fwd_pruned(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c,  # noqa: E731
                                          workspace=ws)
+    elif mode == "token":
+        tm = lambda t: t.permute(0, 2, 1, 3).contiguous()  # noqa: E731
+        q, k, v, logf = tm(q), tm(k), tm(v), logf.permute(0, 2, 1).contiguous()
+        o, lse, c = torch.empty_like(q), torch.empty_like(logf), torch.empty_like(logf)
+        fn = lambda: fox.attn_fwd_ex(q, k, v, logf, causal=True, layout="token", scale=inp["scale"],  # noqa: E731
+                                     out=o, lse=lse, c=c)
     else:
         fn = lambda: fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)  # noqa: E731
     _warm(torch, fn, warmup)
@@ -232,7 +241,8 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
     ms = region / steps
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (ms * 1e-3) / 1e12
-    kernel = fwd_kernel_name(torch, cfg) + ({"unmasked": " unmasked", "pruned": " pruned"}.get(mode, ""))
+    kernel = fwd_kernel_name(torch, cfg) + ({"unmasked": " unmasked", "pruned": " pruned",
+                                             "token": " token-major"}.get(mode, ""))
     return {
         "cfg": cfg, "inp": inp,
         "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
@@ -272,10 +282,19 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
                          "kernel": f"bwd_kv_kernel<{cfg.d},causal> + bwd_dq_kernel<{cfg.d},causal> + 2 small kernels"}}
 
 
-def bench_decode(torch, fox, fi, tag, steps, warmup):
+_DECODE_INPUTS = {}
+
+
+def bench_decode(torch, fox, fi, tag, steps, warmup, cache="plain"):
+    """cache: "plain" (fox_attn_decode), "ragged" (fox_attn_decode_ragged, seeded lengths in
+    [1, L]; bytes of the slots in use) or "paged" (fox_attn_decode_paged, every sequence at full
+    length in 256-slot pages scattered over a shuffled pool; the same bytes as "plain")."""
     cfg = fi.DECODE[tag]
     t0 = time.time()
-    inp = fi.decode_inputs(cfg)
+    if tag not in _DECODE_INPUTS:  # the host inputs are reused by the cache variants
+        _DECODE_INPUTS.clear()
+        _DECODE_INPUTS[tag] = fi.decode_inputs(cfg)
+    inp = _DECODE_INPUTS[tag]
     gen_s = time.time() - t0
     dev = "cuda"
     L = cfg.L
@@ -287,18 +306,46 @@ def bench_decode(torch, fox, fi, tag, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty(cfg.S, cfg.H, device=dev)
     ws = torch.empty(fox.decode_workspace_bytes(cfg.S, cfg.H, L, cfg.d), device=dev, dtype=torch.uint8)
-    fn = lambda: fox.attn_decode(q, kc, vc, cc, lnew, scale=inp["scale"], out=o, lse=lse, workspace=ws)  # noqa
+    lens = None
+    if cache == "ragged":
+        g = torch.Generator().manual_seed(3)
+        lens = torch.randint(1, L + 1, (cfg.S,), generator=g, dtype=torch.int32)
+        ld = lens.to(dev)
+        fn = lambda: fox.attn_decode_ragged(q, kc, vc, cc, lnew, ld, scale=inp["scale"], out=o, lse=lse,  # noqa
+                                            workspace=ws)
+    elif cache == "paged":
+        P = 256
+        maxp = L // P
+        npages = cfg.S * maxp + 3
+        g = torch.Generator().manual_seed(4)
+        table = torch.randperm(npages, generator=g)[: cfg.S * maxp].to(torch.int32).reshape(cfg.S, maxp).to(dev)
+        kp = torch.empty(npages, cfg.H, P, cfg.d, device=dev, dtype=kc.dtype)
+        vp = torch.empty_like(kp)
+        cp = torch.empty(npages, cfg.H, P, device=dev, dtype=torch.float32)
+        flat = table.flatten().long()
+        kp[flat] = kc.view(cfg.S, cfg.H, maxp, P, cfg.d).permute(0, 2, 1, 3, 4).reshape(-1, cfg.H, P, cfg.d)
+        vp[flat] = vc.view(cfg.S, cfg.H, maxp, P, cfg.d).permute(0, 2, 1, 3, 4).reshape(-1, cfg.H, P, cfg.d)
+        cp[flat] = cc.view(cfg.S, cfg.H, maxp, P).permute(0, 2, 1, 3).reshape(-1, cfg.H, P)
+        del kc, vc
+        kc = vc = None
+        ld = torch.full((cfg.S,), L, dtype=torch.int32, device=dev)
+        fn = lambda: fox.attn_decode_paged(q, kp, vp, cp, table, ld, lnew, scale=inp["scale"], out=o, lse=lse,  # noqa
+                                           workspace=ws)
+    else:
+        fn = lambda: fox.attn_decode(q, kc, vc, cc, lnew, scale=inp["scale"], out=o, lse=lse, workspace=ws)  # noqa
     _warm(torch, fn, warmup)
     region = _events_time(torch, fn, steps)
-    by = decode_bytes(cfg)
+    by = decode_bytes(cfg, lens)
     ms = region / steps
     achieved = by["total"] / (ms * 1e-3) / 1e9
     res = {
-        "workload": cfg.desc, "ms_per_step": round(ms, 4), "value": round(by["total"] / (ms * 1e-3) / 1e9, 1),
+        "workload": cfg.desc + ("" if cache == "plain" else f", {cache} cache"), "ms_per_step": round(ms, 4),
+        "value": round(by["total"] / (ms * 1e-3) / 1e9, 1),
         "unit": "GB/s", "bytes_per_step": by["total"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": stored_traffic(tag, DECODE_KERNEL, "decode"), "kernel": DECODE_KERNEL,
+                     "traffic": stored_traffic(tag, DECODE_KERNEL, "decode") if cache == "plain" else None,
+                     "kernel": DECODE_KERNEL if cache == "plain" else DECODE_KERNEL.replace(",128>", f",128,{cache}>"),
                      "note": "per call = split kernel + combine kernel; bytes = algorithmic bytes per call"},
         "input_gen_s": round(gen_s, 1),
     }
@@ -446,13 +493,14 @@ def main():
                            "roofline": dict(x["roofline"], kernel=x["kernel"])}
             del x
             torch.cuda.empty_cache()
-        for tag, mode in (("c2", "unmasked"), ("c3", "pruned")):
+        for tag, mode in (("c2", "unmasked"), ("c3", "pruned"), ("c2", "token")):
             x = bench_fwd(torch, fox, fi, tag, max(10, args.steps // 5), max(3, args.warmup // 2), mode=mode)
             print(f"# {x['cfg'].desc}, {mode}: {x['ms_per_step']*1e3:.1f} us/step, {x['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
-            note = ("4*d flop for every (query, key) pair" if mode == "unmasked" else
-                    "effective rate: the causal work over the time of the pruned call (key-norm, prefix-sum and "
-                    "forward kernels); skipped keys weigh < 2^-24 of each row sum")
+            note = {"unmasked": "4*d flop for every (query, key) pair",
+                    "pruned": "effective rate: the causal work over the time of the pruned call (key-norm, "
+                              "prefix-sum and forward kernels); skipped keys weigh < 2^-24 of each row sum",
+                    "token": "q, k, v, o as [B,N,H,d], logf, lse, c as [B,N,H]"}[mode]
             others[f"{tag}_{mode}"] = {"workload": x["cfg"].desc + f", {mode}", "value": round(x["tflops"], 2),
                                        "unit": "TFLOP/s", "ms_per_step": round(x["ms_per_step"], 4),
                                        "note": note, "roofline": dict(x["roofline"], kernel=x["kernel"])}
@@ -468,6 +516,13 @@ def main():
         print(f"# {dec['workload']}: {dec['ms_per_step']*1e3:.1f} us/step, {dec['value']:.0f} GB/s",
               file=sys.stderr, flush=True)
         others["c5_decode"] = dec
+        torch.cuda.empty_cache()
+        for cache in ("ragged", "paged"):
+            x, _ = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2), cache=cache)
+            print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+            others[f"c5_{cache}"] = x
+            torch.cuda.empty_cache()
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
