@@ -608,3 +608,58 @@ def test_bwd_repeatable():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ------------------------------------------------------------------------------ graph capture
+
+def test_graph_replays_match_eager():
+    """The entry points launch kernels only (no allocation, copy, memset or synchronisation), so a
+    forward, backward and decode step captured in a HIP graph replay to the eager results; checked
+    on several replays with eager work and synchronisations between them."""
+    cfg = fi.FwdConfig("graph", 2, 3, 300, 64, "bf16", 2.0, 1.0)
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(9)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    dcfg = fi.DecodeConfig("graph_dec", 2, 3, 500, 64, "bf16", 4.0, 2.0)
+    dinp = fi.decode_inputs(dcfg)
+    qd, kd, vd = (dinp[x].to(DEV) for x in ("q", "k", "v"))
+    c0 = fox.logf_cumsum(dinp["logf_all"].to(DEV))
+    lnew = dinp["logf_all"][..., dcfg.L - 1].contiguous().to(DEV)
+    # preallocated outputs and workspaces, shared by the eager run and the graph
+    o, lse, c = torch.empty_like(q), torch.empty_like(logf), torch.empty_like(logf)
+    dq, dk, dv, dl = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(logf)
+    wsb = torch.empty(fox.attn_bwd_workspace_bytes(2, 3, 300, 64), device=DEV, dtype=torch.uint8)
+    od, lsed = torch.empty_like(qd), torch.empty(2, 3, device=DEV)
+    wsd = torch.empty(fox.decode_workspace_bytes(2, 3, dcfg.L, 64), device=DEV, dtype=torch.uint8)
+    cd = c0.clone()
+
+    def run():
+        fox.attn_fwd(q, k, v, logf, scale=inp["scale"], out=o, lse=lse, c=c)
+        fox.attn_bwd(q, k, v, o, dout, lse, c, scale=inp["scale"], dq=dq, dk=dk, dv=dv, dlogf=dl, workspace=wsb)
+        fox.attn_decode(qd, kd, vd, cd, lnew, scale=dinp["scale"], out=od, lse=lsed, workspace=wsd)
+
+    outs = (o, lse, c, dq, dk, dv, dl, od, lsed, cd)
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        cd.copy_(c0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("o", "lse", "c", "dq", "dk", "dv", "dlogf", "o_dec", "lse_dec", "c_cache"), outs, eager):
+            assert torch.equal(t, e), (rep, name)
+        x = (q.float() @ k.float().transpose(-1, -2)).sum()  # eager work between replays
+        assert torch.isfinite(x)
