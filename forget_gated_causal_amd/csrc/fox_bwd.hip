@@ -107,11 +107,7 @@ __device__ __forceinline__ int sw_off(int r, int e) {
 // LDS on every query tile)
 template <int D>
 constexpr bool kv_in_regs() {
-#ifdef FOX_BWD_KVREG_MIN_D
-  return D >= FOX_BWD_KVREG_MIN_D;
-#else
   return D >= 128;
-#endif
 }
 
 template <int D>
