@@ -119,8 +119,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
   const int wg = blockIdx.x;
   const int sh = wg / nsplit, split = wg - sh * nsplit;
   const int L = lens ? min(max(lens[sh / nh], 1), Lcap) : Lcap;  // this sequence's slots
-  const int start = split * chunk;
-  const int end = min(L, start + chunk);
+  // a sequence's slots are shared evenly by its nsplit workgroups (with every length at the
+  // capacity this is the fixed chunk), so no workgroup of a short sequence sits idle
+  const int ck = lens ? (L + nsplit - 1) / nsplit : chunk;
+  const int start = split * ck;
+  const int end = min(L, start + ck);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % G;
   const int slot = lane / G + KPW * wave;
