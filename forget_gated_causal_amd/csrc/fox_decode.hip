@@ -20,8 +20,8 @@
 //   log-sum-exp rule, writes O, lse and the new prefix sum into cache slot L-1.
 //
 // Ragged caches: with `lens` given, sequence s uses only its first lens[s] slots (clamped to
-// [1, L]) of caches allocated for L, and its new token sits at slot lens[s]-1.  The split
-// grid still covers L slots; splits past a sequence's length leave empty records.
+// [1, L]) of caches allocated for L, and its new token sits at slot lens[s]-1.  Its slots are
+// shared evenly by its nsplit workgroups; a split left without slots writes an empty record.
 // Paged caches (PAGED): logical slot j of sequence s is row j & (P-1) of physical page
 // table[s][j >> log2 P] in pools [pages][heads][P][d] (c: [pages][heads][P]); the capacity L is
 // max_pages * P.  Everything else is the ragged step.
