@@ -137,6 +137,14 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
                           const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
                           void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
                           float scale, fox_dtype_t dtype, int causal, hipStream_t stream) {
+  return fox_attn_bwd_ex(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, workspace_bytes, b, h, n, d, scale,
+                         dtype, causal, FOX_HEAD_MAJOR, stream);
+}
+
+fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                             void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
+                             float scale, fox_dtype_t dtype, int causal, fox_layout_t layout, hipStream_t stream) {
   if (!q || !k || !v || !o || !dout || !lse || !c || !dq || !dk || !dv || !dlogf) return FOX_ERR_INVALID_ARG;
   if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
@@ -144,6 +152,9 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
   if (dtype != FOX_BF16) return FOX_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
   if ((n + 127) / 128 > kMaxGridY) return FOX_ERR_INVALID_ARG;
+  if (layout != FOX_HEAD_MAJOR && layout != FOX_TOKEN_MAJOR) return FOX_ERR_UNSUPPORTED;
+  // token-major: one head's rows span (n-1)*h*d + d elements, addressed with 32-bit byte offsets
+  if (layout == FOX_TOKEN_MAJOR && (n + 256) * h * d * 2 > kI32Max) return FOX_ERR_UNSUPPORTED;
   const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : t16)
     if (!aligned(p, 16)) return FOX_ERR_INVALID_ARG;
@@ -161,7 +172,7 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
     for (int j = 0; j < 12; ++j)
       if (j != 7 + i && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
   return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, static_cast<float*>(workspace),
-                                       bh, (int)n, (int)d, scale, causal != 0, stream));
+                                       b, h, (int)n, (int)d, scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
 }
 
 // Validation shared by the decode entry points.

@@ -50,6 +50,18 @@ constexpr int64_t kFuseMaxBlocks = 1024;  // grids up to this many blocks run bo
 constexpr float kNegInfB = -INFINITY;
 constexpr int kRawBufferCfg = 0x00020000;  // dword 3 of a raw (unswizzled, byte-offset) buffer resource
 
+// Where a head's rows live: q, k, v, o, dO and the gradients share (bs, hs, rs); lse, c and dlog f
+// share (gbs, ghs, gs).  Head-major [B,H,N,d]: rs = d; token-major [B,N,H,d]: rs = H d.
+struct BwdLayout {
+  int64_t bs, hs;    // tensors: batch and head strides (elements)
+  int rs;            // tensors: row (token) stride
+  int64_t gbs, ghs;  // vectors: batch and head strides
+  int gs;            // vectors: row stride
+  int nh;            // heads per batch entry
+  __device__ __forceinline__ int64_t tbase(int bh) const { return (int64_t)(bh / nh) * bs + (bh % nh) * hs; }
+  __device__ __forceinline__ int64_t gbase(int bh) const { return (int64_t)(bh / nh) * gbs + (bh % nh) * ghs; }
+};
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
@@ -159,15 +171,15 @@ __device__ __forceinline__ bf16x8 acc_operand(const f32x16& a, int u) {
   return r;
 }
 
-// Cooperative copy of `rows` rows of d bf16 (global row stride d) into a swizzled LDS tile;
+// Cooperative copy of `rows` rows of d bf16 (global row stride rs) into a swizzled LDS tile;
 // rows at or past `valid` are zero-filled.
 template <int D>
-__device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows, int valid, int tid) {
+__device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows, int valid, int rs, int tid) {
   constexpr int CH = D / 8;
   for (int i = tid; i < rows * CH; i += kBwdThreads) {
     const int r = i / CH, ch = i - r * CH;
     bf16x8 x = bf16x8{};
-    if (r < valid) x = *reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch);
+    if (r < valid) x = *reinterpret_cast<const bf16x8*>(src + (size_t)r * rs + 8 * ch);
     *reinterpret_cast<bf16x8*>(lds + sw_off<D>(r, 8 * ch)) = x;
   }
 }
@@ -179,18 +191,20 @@ __device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows,
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ c,
-                                                      float* __restrict__ rowv, int64_t bh_count, int n, int npad) {
+                                                      float* __restrict__ rowv, int64_t bh_count, int n, int npad,
+                                                      BwdLayout lay) {
   constexpr int G = D / 8;  // lanes per row, 8 elements each
   const int64_t prow = (int64_t)blockIdx.x * (kBwdThreads / G) + threadIdx.x / G;
   const int g = threadIdx.x % G;
   const int64_t bh = prow / npad;
   const int i = (int)(prow - bh * npad);
   const bool live = bh < bh_count && i < n;
-  const int64_t row = bh * n + i;
+  const int64_t trow = live ? lay.tbase((int)bh) + (int64_t)i * lay.rs : 0;
+  const int64_t row = live ? lay.gbase((int)bh) + (int64_t)i * lay.gs : 0;
   float s = 0.0f;
   if (live) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * D + 8 * g);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * D + 8 * g);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + trow + 8 * g);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + trow + 8 * g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
   }
@@ -214,11 +228,12 @@ struct TileLoader {
   static constexpr int CH = D / 8, NI = ROWS * CH / 64, IPW = NI >= 4 ? NI / 4 : 1;
   static_assert(NI >= 1 && (NI < 4 || NI % 4 == 0), "tile instructions per wave");
   uint32_t toff[IPW];
-  __device__ __forceinline__ TileLoader(int wave, int lane) {
+  int rs;  // global row stride (elements)
+  __device__ __forceinline__ TileLoader(int wave, int lane, int rs_) : rs(rs_) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int P = 64 * ((wave * IPW + j) % NI) + lane, r = P / CH, pc = P % CH;
-      toff[j] = (uint32_t)((r * D + 8 * (pc ^ swz<D>(r))) * 2);
+      toff[j] = (uint32_t)((r * rs + 8 * (pc ^ swz<D>(r))) * 2);
     }
   }
   __device__ __forceinline__ void load(bf16* tile, u32x4 rsrc, int row0, int wave) const {
@@ -227,7 +242,7 @@ struct TileLoader {
       const int g = wave * IPW + j;  // wave-uniform
       if (NI >= 4 || g < NI) {
         const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(tile + 64 * 8 * g));
-        lds_load16(m0v, rsrc, toff[j] + (uint32_t)(row0 * D * 2));
+        lds_load16(m0v, rsrc, toff[j] + (uint32_t)row0 * (uint32_t)(rs * 2));
       }
     }
   }
@@ -239,25 +254,29 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
                                              const bf16* __restrict__ dout, const float* __restrict__ rowv,
                                              bf16* __restrict__ dk, bf16* __restrict__ dv,
-                                             float* __restrict__ colsum_out, int n, int npad, float scale) {
+                                             float* __restrict__ colsum_out, int n, int npad, float scale,
+                                             const BwdLayout& lay) {
   constexpr int KK = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int key0 = kb * kBK;
   const int key = key0 + 32 * wave + l32;  // this lane's key (accumulator column)
-  const size_t base = bh * (size_t)n;
+  const size_t base = bh * (size_t)n;  // this head's rows of the column-sum workspace
+  const int64_t tb = lay.tbase((int)bh);
+  const int rs = lay.rs;
   const float scale_log2 = scale * kLog2e;
   const float* blk = rowv + bh * 3 * npad;
 
   // buffer resources over this head's rows: loads past row n return zeros
-  const u32x4 rq = sgpr_rsrc(q + base * D, (uint32_t)(n * D * 2));
-  const u32x4 rdo = sgpr_rsrc(dout + base * D, (uint32_t)(n * D * 2));
+  const uint32_t span = (uint32_t)(((int64_t)(n - 1) * rs + D) * 2);
+  const u32x4 rq = sgpr_rsrc(q + tb, span);
+  const u32x4 rdo = sgpr_rsrc(dout + tb, span);
   const u32x4 rrow = sgpr_rsrc(blk, (uint32_t)(2 * npad * 4));
 
   if constexpr (!kv_in_regs<D>()) {
-    stage_rows<D>(lds.k, k + (base + key0) * D, kBK, n - key0, tid);
-    stage_rows<D>(lds.v, v + (base + key0) * D, kBK, n - key0, tid);
+    stage_rows<D>(lds.k, k + tb + (int64_t)key0 * rs, kBK, n - key0, rs, tid);
+    stage_rows<D>(lds.v, v + tb + (int64_t)key0 * rs, kBK, n - key0, rs, tid);
   }
   // this lane's key row of K and V as the B operands of S = Q K^T and dP = dO V^T (k-elements
   // 16kk + 8hi .. +7), held in registers for the whole query loop where they fit
@@ -267,15 +286,15 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
   for (int kk = 0; kk < KR; ++kk) {
     kreg[kk] = vreg[kk] = bf16x8{};
     if (kv_in_regs<D>() && key < n) {
-      kreg[kk] = *reinterpret_cast<const bf16x8*>(k + (base + key) * D + 16 * kk + 8 * hi);
-      vreg[kk] = *reinterpret_cast<const bf16x8*>(v + (base + key) * D + 16 * kk + 8 * hi);
+      kreg[kk] = *reinterpret_cast<const bf16x8*>(k + tb + (int64_t)key * rs + 16 * kk + 8 * hi);
+      vreg[kk] = *reinterpret_cast<const bf16x8*>(v + tb + (int64_t)key * rs + 16 * kk + 8 * hi);
     }
   }
   // c_j log2 e (+inf past n: every score of the key is then -inf, so P and dS are 0)
   const float bkey = key < n ? blk[2 * npad + key] : INFINITY;
 
   // q and dO tiles (and the tile's 32 a_i, lanes 0..31 of wave 0, and 32 D_i, lanes 32..63)
-  const TileLoader<D, kBQ> tl(wave, lane);
+  const TileLoader<D, kBQ> tl(wave, lane, rs);
   const uint32_t roff = (uint32_t)((hi ? npad : 0) + l32) * 4u;
   auto load_tile = [&](int q0, int buf) {
     tl.load(lds.q[buf], rq, q0, wave);
@@ -461,8 +480,8 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
   // dK = scale dK^T, dV = dV^T: lane = key, dims 32db + 8(r/4) + 4hi + r%4 (runs of 4)
   colsum = pair32_sum(colsum);
   if (key < n) {
-    bf16* dkr = dk + (base + key) * D;
-    bf16* dvr = dv + (base + key) * D;
+    bf16* dkr = dk + tb + (int64_t)key * rs;
+    bf16* dvr = dv + tb + (int64_t)key * rs;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -487,19 +506,22 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
                                              const bf16* __restrict__ dout, const float* __restrict__ rowv,
                                              bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
-                                             float scale) {
+                                             float scale, const BwdLayout& lay) {
   constexpr int KK = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int qw0 = qb * kQB + 32 * wave;  // this wave's first query
   const int qi = qw0 + l32;               // this lane's query (accumulator column of S^T)
-  const size_t base = bh * (size_t)n;
+  const size_t base = bh * (size_t)n;  // this head's rows of the row-sum workspace
+  const int64_t tb = lay.tbase((int)bh);
+  const int rs = lay.rs;
   const float scale_log2 = scale * kLog2e;
   const float* blk = rowv + bh * 3 * npad;
 
-  const u32x4 rk = sgpr_rsrc(k + base * D, (uint32_t)(n * D * 2));
-  const u32x4 rv = sgpr_rsrc(v + base * D, (uint32_t)(n * D * 2));
+  const uint32_t span = (uint32_t)(((int64_t)(n - 1) * rs + D) * 2);
+  const u32x4 rk = sgpr_rsrc(k + tb, span);
+  const u32x4 rv = sgpr_rsrc(v + tb, span);
   const u32x4 rcl = sgpr_rsrc(blk + 2 * npad, (uint32_t)(npad * 4));
 
   // this lane's q and dO rows as the B operands of S^T = K Q^T and dP^T = V dO^T
@@ -508,14 +530,14 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
   for (int kk = 0; kk < KK; ++kk) {
     qreg[kk] = dreg[kk] = bf16x8{};
     if (qi < n) {
-      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + (base + qi) * D + 16 * kk + 8 * hi);
-      dreg[kk] = *reinterpret_cast<const bf16x8*>(dout + (base + qi) * D + 16 * kk + 8 * hi);
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(q + tb + (int64_t)qi * rs + 16 * kk + 8 * hi);
+      dreg[kk] = *reinterpret_cast<const bf16x8*>(dout + tb + (int64_t)qi * rs + 16 * kk + 8 * hi);
     }
   }
   const float aq = qi < n ? blk[qi] : kNegInfB;     // (c_i - lse_i) log2 e; no weight past n
   const float dq_i = qi < n ? blk[npad + qi] : 0.0f;  // D_i
 
-  const TileLoader<D, kKT> tl(wave, lane);
+  const TileLoader<D, kKT> tl(wave, lane, rs);
   auto load_tile = [&](int k0, int buf) {
     tl.load(lds.k[buf], rk, k0, wave);
     tl.load(lds.v[buf], rv, k0, wave);
@@ -666,7 +688,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = qw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (qr < n) dq[(base + qr) * D + 32 * db + l32] = (bf16)(acc[db][r] * scale);
+      if (qr < n) dq[tb + (int64_t)qr * rs + 32 * db + l32] = (bf16)(acc[db][r] * scale);
     }
   }
   // the two lane halves hold the two halves of each 32-key block
@@ -679,21 +701,22 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_kv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
     const float* __restrict__ rowv, bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ colsum_out,
-    int n, int npad, float scale) {
+    int n, int npad, float scale, BwdLayout lay) {
   __shared__ KvLds<D> lds;
   // heads fastest: the key blocks of one head share its q / dO in L2; causal work falls with kb
-  bwd_kv_block<D, CAUSAL>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale);
+  bwd_kv_block<D, CAUSAL>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale,
+                          lay);
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
     const float* __restrict__ rowv, bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
-    float scale) {
+    float scale, BwdLayout lay) {
   __shared__ DqLds<D> lds;
   // the longest causal blocks (the last queries) start first
   bwd_dq_block<D, CAUSAL>(lds, blockIdx.x, (int)(gridDim.y - 1 - blockIdx.y), q, k, v, dout, rowv, dq, rowsum_out, n,
-                          npad, scale);
+                          npad, scale, lay);
 }
 
 // ... and both in one launch for small grids, where each fills the other's tail.  blockIdx.x is the head (the
@@ -704,7 +727,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
     const float* __restrict__ rowv, bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ rowsum_out, float* __restrict__ colsum_out, int n, int npad, float scale) {
+    float* __restrict__ rowsum_out, float* __restrict__ colsum_out, int n, int npad, float scale, BwdLayout lay) {
   __shared__ union {
     KvLds<D> kv;
     DqLds<D> dq;
@@ -712,60 +735,60 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   const size_t bh = blockIdx.x;
   const int j = (int)(blockIdx.y >> 1);
   if ((blockIdx.y & 1) == 0)
-    bwd_kv_block<D, CAUSAL>(lds.kv, bh, j, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale);
+    bwd_kv_block<D, CAUSAL>(lds.kv, bh, j, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale, lay);
   else
     bwd_dq_block<D, CAUSAL>(lds.dq, bh, (int)(gridDim.y >> 1) - 1 - j, q, k, v, dout, rowv, dq, rowsum_out, n, npad,
-                            scale);
+                            scale, lay);
 }
 
 int bwd_npad(int n) { return (n + kPad - 1) / kPad * kPad; }
 
-template <int D>
-hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf, float* ws,
-                        int64_t bh, int n, float scale, bool causal, hipStream_t stream) {
-  const int npad = bwd_npad(n);
-  // workspace: row vectors [bh][3][npad], row sums [bh][n], column sums [bh][n] (fp32)
-  float* rowv = ws;
-  float* rs = rowv + bh * 3 * npad;
-  float* cs = rs + bh * n;
-  constexpr int RPB = kBwdThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((bh * npad + RPB - 1) / RPB)), dim3(kBwdThreads), 0, stream,
-                     (const bf16*)o, (const bf16*)dout, lse, c, rowv, bh, n, npad);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_c(const void* q, const void* k, const void* v, const void* dout, const float* rowv, void* dq,
+                        void* dk, void* dv, float* rsum, float* csum, int64_t bh, int n, int npad, float scale,
+                        const BwdLayout& lay, hipStream_t stream) {
   static_assert(kBK == kQB, "one key block and one query block per block pair");
   const int nb = (n + kBK - 1) / kBK;
   if (2 * bh * nb <= kFuseMaxBlocks) {
-    const dim3 grid((unsigned)bh, (unsigned)(2 * nb));
-    if (causal)
-      hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, (bf16*)dk,
-                         (bf16*)dv, rs, cs, n, npad, scale);
-    else
-      hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, (bf16*)dk,
-                         (bf16*)dv, rs, cs, n, npad, scale);
+    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3((unsigned)bh, (unsigned)(2 * nb)), dim3(kBwdThreads), 0,
+                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, (bf16*)dq,
+                       (bf16*)dk, (bf16*)dv, rsum, csum, n, npad, scale, lay);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)nb);
-    if (causal) {
-      hipLaunchKernelGGL((bwd_kv_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv, cs, n, npad,
-                         scale);
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad, scale);
-    } else {
-      hipLaunchKernelGGL((bwd_kv_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dk, (bf16*)dv,
-                         cs, n, npad, scale);
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const float*)rowv, (bf16*)dq, rs, n, npad,
-                         scale);
-    }
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, (bf16*)dk, (bf16*)dv, csum, n, npad,
+                       scale, lay);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, (bf16*)dq, rsum, n, npad, scale, lay);
   }
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf, float* ws,
+                        int64_t b, int64_t h, int n, float scale, bool causal, bool token_major,
+                        hipStream_t stream) {
+  const int64_t bh = b * h;
+  const int npad = bwd_npad(n);
+  // {bs, hs, rs, gbs, ghs, gs, nh}
+  const BwdLayout lay = token_major
+                            ? BwdLayout{(int64_t)n * h * D, (int64_t)D, (int)(h * D), (int64_t)n * h, 1, (int)h, (int)h}
+                            : BwdLayout{h * n * (int64_t)D, (int64_t)n * D, D, h * (int64_t)n, (int64_t)n, 1, (int)h};
+  // workspace: row vectors [bh][3][npad], row sums [bh][n], column sums [bh][n] (fp32)
+  float* rowv = ws;
+  float* rsum = rowv + bh * 3 * npad;
+  float* csum = rsum + bh * n;
+  constexpr int RPB = kBwdThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((bh * npad + RPB - 1) / RPB)), dim3(kBwdThreads), 0, stream,
+                     (const bf16*)o, (const bf16*)dout, lse, c, rowv, bh, n, npad, lay);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_suffix_sum(rs, cs, dlogf, bh, n, stream);  // dlog f_t = sum_{i >= t} (rs_i - cs_i)
+  e = causal ? launch_bwd_c<D, true>(q, k, v, dout, rowv, dq, dk, dv, rsum, csum, bh, n, npad, scale, lay, stream)
+             : launch_bwd_c<D, false>(q, k, v, dout, rowv, dq, dk, dv, rsum, csum, bh, n, npad, scale, lay, stream);
+  if (e != hipSuccess) return e;
+  // dlog f_t = sum_{i >= t} (rowsum_i - colsum_i), written in the gates' layout
+  return launch_suffix_sum(rsum, csum, dlogf, bh, n, (int)h, token_major, stream);
 }
 
 }  // namespace
@@ -777,12 +800,18 @@ size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d) {
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
-                           float* workspace, int64_t bh, int n, int d, float scale, bool causal, hipStream_t stream) {
+                           float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                           bool token_major, hipStream_t stream) {
   switch (d) {
-    case 32: return launch_bwd_t<32>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, bh, n, scale, causal, stream);
-    case 64: return launch_bwd_t<64>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, bh, n, scale, causal, stream);
+    case 32:
+      return launch_bwd_t<32>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+                              token_major, stream);
+    case 64:
+      return launch_bwd_t<64>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+                              token_major, stream);
     case 128:
-      return launch_bwd_t<128>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, bh, n, scale, causal, stream);
+      return launch_bwd_t<128>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+                               token_major, stream);
   }
   return hipErrorInvalidValue;
 }

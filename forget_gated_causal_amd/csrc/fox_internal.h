@@ -12,8 +12,9 @@ namespace fox {
 // Inclusive prefix sums of `rows` independent rows of length n (fp64 accumulate).
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream);
 // Suffix sums out_t = sum_{i>=t} (x_i - sub_i) of `rows` rows of length n (sub may be null; fp64
-// accumulate).
-hipError_t launch_suffix_sum(const float* x, const float* sub, float* out, int64_t rows, int n, hipStream_t stream);
+// accumulate).  x and sub are [rows, n]; out is [rows, n], or with token_major [rows / nh, n, nh].
+hipError_t launch_suffix_sum(const float* x, const float* sub, float* out, int64_t rows, int n, int nh,
+                             bool token_major, hipStream_t stream);
 
 // FoX forward, causal (decoder mode) or over every key; is_bf16 selects the element type of
 // q/k/v/o; d in {32,64,128}; token_major selects [B,N,H,d] tensors with [B,N,H] gates / lse /
@@ -44,11 +45,13 @@ hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* v
                                     int nh, void* o, float* lse, float* ws, int64_t sh, int d, float scale,
                                     bool is_bf16, hipStream_t stream);
 
-// Backward pass (bf16): dq, dk, dv and dlog f from q, k, v, the forward's o, lse and c, and dO.
-// The workspace holds bh*n*(d + 2) floats (dq accumulator, dO.O per row, dc per key).
+// Backward pass (bf16): dq, dk, dv and dlog f from q, k, v, the forward's o, lse and c, and dO;
+// token_major as launch_attn_fwd.  The workspace holds bh*(3*npad + 2*n) floats (per-row vectors
+// over n padded to 64, row and column sums of dS).
 size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
-                           float* workspace, int64_t bh, int n, int d, float scale, bool causal, hipStream_t stream);
+                           float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                           bool token_major, hipStream_t stream);
 
 }  // namespace fox

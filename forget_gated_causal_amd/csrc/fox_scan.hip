@@ -16,17 +16,25 @@ constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = 4;
 constexpr int kScanChunk = kScanThreads * kScanPerThread;
 
+// Where output row `row` (= batch * nh + head) lives: element t at (row / nh) bs + (row % nh) hs + t es.
+struct OutRows {
+  int nh;
+  int64_t bs, hs;
+  int es;
+};
+
 // REV: the suffix sums out_t = sum_{i>=t} (in_i - sub_i) instead (the same scan over the reversed
-// row; sub may be null).
+// row; sub may be null).  Inputs are [rows, n]; the output rows are placed by `om`.
 template <bool REV>
 __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* __restrict__ logf,
                                                                    const float* __restrict__ sub,
-                                                                   float* __restrict__ c, int n) {
+                                                                   float* __restrict__ c, int n, OutRows om) {
   __shared__ double wave_tot[kScanThreads / 64];
   const size_t row = blockIdx.x;
   const float* src = logf + row * (size_t)n;
   const float* sb = sub ? sub + row * (size_t)n : nullptr;
-  float* dst = c + row * (size_t)n;
+  float* dst = c + (int64_t)(row / om.nh) * om.bs + (int64_t)(row % om.nh) * om.hs;
+  const int64_t es = om.es;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   double carry = 0.0;
   for (int base = 0; base < n; base += kScanChunk) {
@@ -62,7 +70,7 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
     const double pre = before + excl;
 #pragma unroll
     for (int e = 0; e < kScanPerThread; ++e)
-      if (i0 + e < n) dst[REV ? n - 1 - (i0 + e) : i0 + e] = (float)(pre + x[e]);
+      if (i0 + e < n) dst[(REV ? n - 1 - (i0 + e) : i0 + e) * es] = (float)(pre + x[e]);
     carry += chunk;
   }
 }
@@ -71,12 +79,15 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
 
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream) {
   hipLaunchKernelGGL(logf_cumsum_kernel<false>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf,
-                     (const float*)nullptr, c, n);
+                     (const float*)nullptr, c, n, OutRows{1, (int64_t)n, 0, 1});
   return hipGetLastError();
 }
 
-hipError_t launch_suffix_sum(const float* x, const float* sub, float* out, int64_t rows, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(logf_cumsum_kernel<true>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, x, sub, out, n);
+hipError_t launch_suffix_sum(const float* x, const float* sub, float* out, int64_t rows, int n, int nh,
+                             bool token_major, hipStream_t stream) {
+  const OutRows om = token_major ? OutRows{nh, (int64_t)n * nh, 1, nh} : OutRows{1, (int64_t)n, 0, 1};
+  hipLaunchKernelGGL(logf_cumsum_kernel<true>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, x, sub, out, n,
+                     om);
   return hipGetLastError();
 }
 

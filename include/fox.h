@@ -190,6 +190,24 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
                           float scale, fox_dtype_t dtype, int causal, hipStream_t stream);
 
 /*
+ * fox_attn_bwd_ex -- fox_attn_bwd with the tensor layout chosen.
+ *   FoX module page, ForgettingAttention.forward: the projections are formed as
+ *   [batch, seq, heads, head_dim] before the permute to head-major; FOX_TOKEN_MAJOR reads q, k,
+ *   v, o, dout as [b, n, h, d] and lse, c as [b, n, h], and writes dq, dk, dv as [b, n, h, d]
+ *   and dlogf as [b, n, h], the layout fox_attn_fwd_ex(..., FOX_TOKEN_MAJOR) reads and writes.
+ *
+ *   layout : FOX_HEAD_MAJOR or FOX_TOKEN_MAJOR (else FOX_ERR_UNSUPPORTED); with
+ *            FOX_TOKEN_MAJOR, (n + 256) * h * d * 2 must not exceed 2^31 - 1
+ *            (else FOX_ERR_UNSUPPORTED).
+ *   Every other argument, the workspace size, the results (bit for bit, element by element)
+ *   and the errors as fox_attn_bwd.
+ */
+fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                             void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
+                             float scale, fox_dtype_t dtype, int causal, fox_layout_t layout, hipStream_t stream);
+
+/*
  * fox_attn_decode_workspace_bytes -- bytes of scratch fox_attn_decode needs for
  * these sizes (split-K partial results).  Returns 0 for invalid sizes.
  */

@@ -198,15 +198,17 @@ def test_decode_paged_rejects_bad_arguments(L):
     assert _decp(L, ws=0x90_0000_0000) == INVALID  # workspace over the page table
 
 
-def _bwd(L, **kw):
+def _bwd(L, layout=None, **kw):
     I, J, K, M = (0x10_0000_0000 * (i + 9) for i in range(4))
     args = dict(q=A, k=B, v=C, o=D, dout=E, lse=F, c=G, dq=H, dk=I, dv=J, dl=K, ws=M, wsb=1 << 30, b=1, h=2, n=300,
                 d=64, scale=0.125, dt=_lib.FOX_BF16, causal=1)
     args.update(kw)
     a = args
-    return L.fox_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["c"], a["dq"], a["dk"], a["dv"],
-                          a["dl"], a["ws"], a["wsb"], a["b"], a["h"], a["n"], a["d"], a["scale"], a["dt"], a["causal"],
-                          None)
+    pos = (a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["c"], a["dq"], a["dk"], a["dv"], a["dl"], a["ws"],
+           a["wsb"], a["b"], a["h"], a["n"], a["d"], a["scale"], a["dt"], a["causal"])
+    if layout is None:
+        return L.fox_attn_bwd(*pos, None)
+    return L.fox_attn_bwd_ex(*pos, layout, None)
 
 
 def test_bwd_rejects_bad_arguments(L):
@@ -224,6 +226,17 @@ def test_bwd_rejects_bad_arguments(L):
     assert _bwd(L, dv=0x10_0000_0000 * 9) == INVALID  # dv == dk
     assert _bwd(L, dl=F) == INVALID  # dlogf == lse
     assert _bwd(L, ws=H) == INVALID  # workspace == dq
+
+
+def test_bwd_ex_layout_checks(L):
+    # the same argument checks as fox_attn_bwd, then the layout's own
+    assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, dout=None) == INVALID
+    assert _bwd(L, layout=_lib.FOX_HEAD_MAJOR, wsb=64) == WS
+    assert _bwd(L, layout=2) == UNSUP
+    assert _bwd(L, layout=-1) == UNSUP
+    # token-major rows are h*d apart: one head's span must fit 32-bit byte offsets
+    assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, n=1 << 20, h=64, d=128) == UNSUP
+    assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, dt=_lib.FOX_F32) == UNSUP
 
 
 def test_fwd_ex_layout_checks(L):
