@@ -759,8 +759,11 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       for (int w = 0; w < NWR; ++w) all = all && rows.done_it[w] < i;
       if (all) return true;
     }
+    // Token-major: the lane offsets are recomputed from this step's opaque lane copy (with a
+    // run-time row stride the compiler would rather keep them live, and spill them).
     if (kt - 2 >= bot)
-      bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl, so, kt - 2, rw, lane, lead, rs, gs);
+      bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl,
+                              TM ? stage_offsets<D, NWR>(rw, ln, rs) : so, kt - 2, rw, lane, lead, rs, gs);
     // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
     const bool gate_job = lead && kt - 1 >= bot;
     bool gate_done = false;
@@ -811,14 +814,17 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
 
   // ---- epilogue: merge the splits, O = acc / l, lse, c ---------------------------------
   if (SP == 2 && sp == 0 && lead && lane == 0) rows.csplit = carry;  // split 0's gate total
-  __syncthreads();  // rows / cref written by the lead waves are visible; all stages are free
+  double cref_fix = 0.0;  // split 1's frame offset, when tile 0 (which sets cref) was split 1's
   if constexpr (SP == 2) {
     // Split 1 leaves (O, m, l) in LDS in its own lane layout, 16 bytes per lane and write; the
-    // split-0 wave of the same rows reads the same lane's values.  Row-wave r uses the memory
-    // of stage r.
+    // split-0 wave of the same rows reads the same lane's values.  The buffers sit in the two
+    // stages that no wave touches after the last loop position's barrier (those of positions
+    // n0 and n0 + 1, mod 4: no such tiles), so split 1 writes them without waiting for split
+    // 0: row-wave r takes stage (n0 + r / 2) mod 4 of split r mod 2.
     constexpr int NQD = 4 * DB;  // float4 quads of O per lane; one more holds (m, l)
     static_assert((NQD + 1) * 64 * sizeof(f32x4) <= sizeof(Bf16Stage<D>) && NWR <= 4, "merge buffer");
-    Bf16Stage<D>* sr = rw == 0 ? s0 : rw == 1 ? s1 : rw == 2 ? s2 : s3;
+    const int fs = (n0 + (rw >> 1)) & 3;
+    Bf16Stage<D>* sr = (fs == 0 ? s0 : fs == 1 ? s1 : fs == 2 ? s2 : s3) + (rw & 1);
     f32x4* cb = reinterpret_cast<f32x4*>(sr);
     if (sp == 1) {
       const bool worked = active && top >= bot;
@@ -827,17 +833,18 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
         const int db = qd >> 2, r = 4 * (qd & 3);
         cb[qd * 64 + lane] = f32x4{oacc[db][r], oacc[db][r + 1], oacc[db][r + 2], oacc[db][r + 3]};
       }
-      // back to the true frame: split 1's scores were high by -csplit * log2 e
-      cb[NQD * 64 + lane] = f32x4{worked ? m + (float)(rows.csplit * kLog2ed) : kNegInf, lsum, 0.0f, 0.0f};
-      // tile 0 was split 1's: its gate total misses split 0's keys as well
-      if (lead && lane == 0 && top >= bot) rows.cref += rows.csplit;
+      cb[NQD * 64 + lane] = f32x4{worked ? m : kNegInf, lsum, 0.0f, 0.0f};  // split 1's frame
     }
-    __syncthreads();
+    __syncthreads();  // partials, csplit, cref and the row sums are visible
     if (sp == 1) return;
+    const double csplit = rows.csplit;
+    if (kt_hi >= n0) cref_fix = csplit;  // tile 0 was split 1's: its total misses split 0's keys
     if (active) {
       const f32x4 ml = cb[NQD * 64 + lane];
-      const float mm = fmaxf(m, ml[0]);
-      const float a0 = exp2_hw(m - mm), a1 = exp2_hw(ml[0] - mm);
+      // back to the true frame: split 1's scores were high by -csplit * log2 e
+      const float m1 = ml[0] + (float)(csplit * kLog2ed);
+      const float mm = fmaxf(m, m1);
+      const float a0 = exp2_hw(m - mm), a1 = exp2_hw(m1 - mm);
       lsum = lsum * a0 + ml[1] * a1;
 #pragma unroll
       for (int qd = 0; qd < NQD; ++qd) {
@@ -848,6 +855,8 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       }
       m = mm;
     }
+  } else {
+    __syncthreads();  // rows / cref written by the lead wave are visible
   }
   if (!active) return;
   const float ltot = pair32_sum(lsum);
@@ -857,7 +866,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   // the gates of split 0's keys.
   double ri = rows.rowR[my_row - row0];
   if (SP == 2 && !CAUSAL && my_row / kBC <= kt_hi - n0) ri += rows.csplit;
-  const double cref = rows.cref;
+  const double cref = rows.cref + cref_fix;
   const float inv = 1.0f / ltot;
   // All packed words first, then the stores back to back (no store waits on a register
   // that the previous store still has to read).
