@@ -241,6 +241,39 @@ def fwd_bwd_head(q, k, v, logf, scale, do, causal: bool = True):
     return dq, dk, dv, dlogf
 
 
+def fwd_bwd_tail(q, k, v, logf, scale, do, t0: int):
+    """Causal forward and gradients of one head at the positions t0..N-1 only (fp64).
+
+    q, k, v, do: [N, d]; logf: [N].  Returns (O, lse, dq, dk, dv, dlogf), each restricted to
+    positions t0..N-1 (rows for O, lse, dq; keys for dk, dv; gates for dlogf).  The same chain
+    rule as ``fwd_bwd_head``, written for the last rows: with the causal mask a key j >= t0 is
+    seen only by rows i >= j, so dk_j, dv_j and the column sums of dS at j need only the rows
+    t0..N-1; dq_i needs the whole row i (every key j <= i); dlogf_t for t >= t0 is the suffix
+    sum of dc_i over i >= t.  Lets a sequence too long for the full N x N matrices be checked
+    at its end.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    c = logf_cumsum(logf)
+    n = q.shape[0]
+    r = np.arange(t0, n)
+    s = scale * (q[r] @ k.T) + (c[r][:, None] - c[None, :])
+    s = np.where(np.arange(n)[None, :] > r[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    lse = (m + np.log(z))[:, 0]
+    o = p @ v
+    dp = do[r] @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dv = p[:, t0:].T @ do[r]
+    dk = scale * (ds[:, t0:].T @ q[r])
+    dc = ds.sum(axis=1) - ds[:, t0:].sum(axis=0)
+    dlogf = np.cumsum(dc[::-1])[::-1]
+    return o, lse, dq, dk, dv, dlogf
+
+
 def attn_bwd(q, k, v, logf, scale, do, causal: bool = True):
     """Gradients for every (batch, head): q, k, v, do [B,H,N,d], logf [B,H,N].
 

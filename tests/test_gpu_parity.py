@@ -644,6 +644,50 @@ def test_bwd_token_major_equals_head_major(d, B, H, n, causal):
     print(f"  {cfg.desc}: token-major == head-major", flush=True)
 
 
+# ------------------------------------------------------------------------- the largest sequence
+
+MAX_SEQ = 1 << 22  # FOX_MAX_SEQ in include/fox.h
+
+
+def test_max_seq_forward_backward_tail():
+    """One head of FOX_MAX_SEQ = 4,194,304 tokens (d = 64, bf16; gate logits N(6,1): long windows,
+    |c| near 10^4 at the end): the gate prefix sums at every position against the oracle, the last
+    32 rows' O and lse and the last 32 positions' dq, dk, dv and dlogf against the oracle's tail
+    computation (exact for the causal mask), every output finite.  Byte offsets inside one head
+    reach 512 MB here."""
+    n, d, T = MAX_SEQ, 64, 32
+    cfg = fi.FwdConfig("maxseq", 1, 1, n, d, "bf16", 6.0, 1.0)
+    inp = fi.fwd_inputs(cfg)
+    g = torch.Generator().manual_seed(11)
+    dout = torch.randn(1, 1, n, d, generator=g).to(torch.bfloat16)
+    print(f"  {cfg.desc}: inputs ready", flush=True)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    dq, dk, dv, dl = fox.attn_bwd(q, k, v, o, dout.to(DEV), lse, c, scale=inp["scale"])
+    torch.cuda.synchronize()
+    print("  forward and backward done", flush=True)
+    for name, t in (("o", o), ("lse", lse), ("c", c), ("dq", dq), ("dk", dk), ("dv", dv), ("dlogf", dl)):
+        assert torch.isfinite(t).all(), name
+    c_ref = oracle.logf_cumsum(_np(inp["logf"]))
+    ec = np.abs(_np(c) - c_ref).max()
+    assert ec <= _ulp(c_ref), ec
+    ref = oracle.fwd_bwd_tail(_np(inp["q"][0, 0]), _np(inp["k"][0, 0]), _np(inp["v"][0, 0]), _np(inp["logf"][0, 0]),
+                              inp["scale"], _np(dout[0, 0]), n - T)
+    msg = [f"max|dc|={ec:.2e}"]
+    for name, got, r in zip(("o", "lse", "dq", "dk", "dv", "dlogf"), (o, lse, dq, dk, dv, dl), ref):
+        err = np.abs(_np(got[0, 0, n - T:]) - r).max()
+        bound = TOL["bf16"] if name in ("o", "lse") else 2e-2 * max(1.0, np.abs(r).max())
+        msg.append(f"{name} {err:.2e}")
+        assert err <= bound, (name, err, bound)
+    print("  last 32 positions: " + ", ".join(msg), flush=True)
+
+
+def test_max_seq_decode():
+    """Decode of the last token of a FOX_MAX_SEQ-slot cache (one sequence, one head, d = 128)."""
+    cfg = fi.DecodeConfig("maxdec", 1, 1, MAX_SEQ, 128, "bf16", 6.0, 1.0)
+    _check_decode(fi.decode_inputs(cfg), TOL["bf16"])
+
+
 # ------------------------------------------------------------------------------ graph capture
 
 def test_graph_replays_match_eager():

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_bwd, fwd_bwd_head, fwd_head_rows
+from oracle import attn_bwd, fwd_bwd_head, fwd_bwd_tail, fwd_head_rows
 
 TOL = 1e-11
 
@@ -123,6 +123,19 @@ def test_batched_backward_matches_heads():
             ref = fwd_bwd_head(q[b, h], k[b, h], v[b, h], logf[b, h], 0.5, do[b, h])
             for a, x in zip(got, ref):
                 assert np.array_equal(a[b, h], x)
+
+
+@pytest.mark.parametrize("n,t0", [(1, 0), (9, 0), (9, 4), (40, 39), (40, 17), (64, 0), (64, 63)])
+def test_tail_oracle_equals_full_head(n, t0):
+    """fwd_bwd_tail (the last rows of a sequence too long for N x N matrices) against the pinned
+    full-head forward and backward oracles, position by position."""
+    q, k, v, logf, do = _case(400 + n + t0, n, 5)
+    o, lse, dq, dk, dv, dl = fwd_bwd_tail(q, k, v, logf, 0.4, do, t0)
+    fo, flse = fwd_head_rows(q, k, v, logf, 0.4, np.arange(n))
+    fq, fk, fv, fl = fwd_bwd_head(q, k, v, logf, 0.4, do)
+    for got, ref in ((o, fo[t0:]), (lse, flse[t0:]), (dq, fq[t0:]), (dk, fk[t0:]), (dv, fv[t0:]), (dl, fl[t0:])):
+        assert got.shape == ref.shape
+        assert np.abs(got - ref).max() <= TOL * max(1.0, np.abs(ref).max())
 
 
 def _mutant(kind):
