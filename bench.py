@@ -275,7 +275,7 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
 
 def bench_bwd(torch, fox, fi, tag, steps, warmup):
     """fox_attn_bwd on the forward workload `tag`: 10*d flop per causal pair (the recomputed
-    q.k, and dP, dV, dK, dQ), timed whole (pre, main, conversion and scan kernels)."""
+    q.k, and dP, dV, dK, dQ), timed whole (row-vector, key-side, query-side and scan kernels)."""
     cfg = fi.FWD[tag]
     inp = fi.fwd_inputs(cfg)
     dev = "cuda"
