@@ -30,6 +30,8 @@
 //    Writes dq and the row sums of dS.
 //  * bwd_pre_kernel before them: D_i, and per head the padded row vectors both main kernels load;
 //    the reversed prefix scan (fox_scan.hip) after them: dlog f from row sums - column sums.
+// Tensors are head-major [B,H,N,d] or token-major [B,N,H,d] (BwdLayout: row strides d or H d,
+// gate-vector strides 1 or H); the workspace is head-major either way.
 #include <math.h>
 
 #include <type_traits>

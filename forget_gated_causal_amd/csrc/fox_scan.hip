@@ -3,9 +3,11 @@
 // FoX module page, ForgettingAttention.forward: the cumulative sum of log f
 // along the sequence axis.  One 256-thread workgroup per (batch, head) row walks
 // the row in chunks of 1024 elements: each thread sums 4 consecutive gates, a
-// wave64 shuffle scan and a 4-entry LDS scan give the chunk prefix, and a carry
-// links the chunks.  Accumulation is fp64 (|c| reaches ~10^3 at 8k tokens, where
-// an fp32 running sum would drift); each c is rounded to fp32 once.
+// wave64 DPP scan and a 4-entry LDS scan give the chunk prefix, and a carry
+// links the chunks; the next chunk's loads are issued before the current chunk's
+// scan, and the wave totals alternate between two LDS slots (one barrier per
+// chunk).  Accumulation is fp64 (|c| reaches ~10^3 at 8k tokens, where an fp32
+// running sum would drift); each c is rounded to fp32 once.
 #include "fox_device.h"
 #include "fox_internal.h"
 
@@ -29,45 +31,46 @@ template <bool REV>
 __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* __restrict__ logf,
                                                                    const float* __restrict__ sub,
                                                                    float* __restrict__ c, int n, OutRows om) {
-  __shared__ double wave_tot[kScanThreads / 64];
+  __shared__ double wave_tot[2][kScanThreads / 64];  // per chunk parity: one barrier per chunk
   const size_t row = blockIdx.x;
   const float* src = logf + row * (size_t)n;
   const float* sb = sub ? sub + row * (size_t)n : nullptr;
   float* dst = c + (int64_t)(row / om.nh) * om.bs + (int64_t)(row % om.nh) * om.hs;
   const int64_t es = om.es;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  double carry = 0.0;
-  for (int base = 0; base < n; base += kScanChunk) {
+  // the loads of chunk `base` (element i0 + e of the scan order, 0 past n)
+  auto load = [&](int base, float (&xv)[kScanPerThread], float (&sv)[kScanPerThread]) {
     const int i0 = base + tid * kScanPerThread;
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) {
+      const int j = REV ? n - 1 - (i0 + e) : i0 + e;
+      const bool in = i0 + e < n;
+      xv[e] = in ? src[j] : 0.0f;
+      sv[e] = in && sb ? sb[j] : 0.0f;
+    }
+  };
+  float xa[kScanPerThread], sa[kScanPerThread];
+  load(0, xa, sa);
+  double carry = 0.0;
+  for (int base = 0, it = 0; base < n; base += kScanChunk, ++it) {
     double x[kScanPerThread];
 #pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e)
-      if (i0 + e < n) {
-        const int j = REV ? n - 1 - (i0 + e) : i0 + e;
-        x[e] = (double)src[j] - (sb ? (double)sb[j] : 0.0);
-      } else {
-        x[e] = 0.0;
-      }
+    for (int e = 0; e < kScanPerThread; ++e) x[e] = (double)xa[e] - (double)sa[e];
+    if (base + kScanChunk < n) load(base + kScanChunk, xa, sa);  // the next chunk's loads in flight
 #pragma unroll
     for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
-    double t = x[kScanPerThread - 1];  // inclusive over this wave's threads after the loop below
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(t, off);
-      if (lane >= off) t += y;
-    }
-    double excl = __shfl_up(t, 1);
-    if (lane == 0) excl = 0.0;
-    if (lane == 63) wave_tot[wave] = t;
+    const double t = wave_incl_scan(x[kScanPerThread - 1]);  // over this wave's threads
+    const double excl = wave_shr1(t);
+    if (lane == 63) wave_tot[it & 1][wave] = t;
     __syncthreads();
     double before = carry, chunk = 0.0;
 #pragma unroll
     for (int w = 0; w < kScanThreads / 64; ++w) {
-      if (w < wave) before += wave_tot[w];
-      chunk += wave_tot[w];
+      if (w < wave) before += wave_tot[it & 1][w];
+      chunk += wave_tot[it & 1][w];
     }
-    __syncthreads();  // wave_tot is rewritten by the next chunk
     const double pre = before + excl;
+    const int i0 = base + tid * kScanPerThread;
 #pragma unroll
     for (int e = 0; e < kScanPerThread; ++e)
       if (i0 + e < n) dst[(REV ? n - 1 - (i0 + e) : i0 + e) * es] = (float)(pre + x[e]);
