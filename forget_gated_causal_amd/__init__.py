@@ -8,7 +8,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
     o, lse, c    = attn_fwd_noncausal(q, k, v, logf)          # every key, no mask
     o, lse, c    = attn_fwd_ex(q, k, v, logf, causal, layout)  # layout "head" [B,H,N,d] / "token" [B,N,H,d]
-    dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, c)   # gradients (bf16); layout="token" too
+    dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, c)   # gradients (bf16 or fp32); layout="token" too
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
     o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
 """
@@ -175,8 +175,8 @@ def attn_bwd_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
 
 def attn_bwd(q, k, v, o, dout, lse, c, causal: bool = True, scale: float | None = None, dq=None, dk=None, dv=None,
              dlogf=None, workspace=None, layout: str = "head"):
-    """Gradients of FoX attention. q, k, v, o, dout: [B,H,N,d] bf16 (o, lse [B,H,N] and c [B,H,N]
-    as attn_fwd / attn_fwd_noncausal returned them).  Returns (dq, dk, dv, dlogf).
+    """Gradients of FoX attention. q, k, v, o, dout: [B,H,N,d], all bf16 or all fp32 (o, lse [B,H,N]
+    and c [B,H,N] as attn_fwd / attn_fwd_noncausal returned them).  Returns (dq, dk, dv, dlogf).
 
     layout "token" (fox_attn_bwd_ex): every tensor [B,N,H,d] and lse / c / dlogf [B,N,H], as
     attn_fwd_ex(..., layout="token") reads and writes them."""
@@ -188,14 +188,15 @@ def attn_bwd(q, k, v, o, dout, lse, c, causal: bool = True, scale: float | None 
     else:
         B, H, N, d = q.shape
         tshape, vshape = (B, H, N, d), (B, H, N)
-    if q.dtype != torch.bfloat16:
-        raise ValueError("attn_bwd takes bf16 tensors")
+    dt = _DTYPES.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"attn_bwd takes bf16 or fp32 tensors, got {q.dtype}")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     dlogf = torch.empty_like(lse) if dlogf is None else dlogf
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
-        _need(t, name, torch.bfloat16)
+        _need(t, name, q.dtype)
         if tuple(t.shape) != tshape:
             raise ValueError(f"{name} shape {tuple(t.shape)} != {tshape}")
     for name, t in (("lse", lse), ("c", c), ("dlogf", dlogf)):
@@ -207,7 +208,7 @@ def attn_bwd(q, k, v, o, dout, lse, c, causal: bool = True, scale: float | None 
         workspace = torch.empty(max(wb, 16), device=q.device, dtype=torch.uint8)
     scale = _default_scale(d) if scale is None else float(scale)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(c), _ptr(dq), _ptr(dk), _ptr(dv),
-            _ptr(dlogf), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d, scale, FOX_BF16,
+            _ptr(dlogf), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d, scale, dt,
             1 if causal else 0)
     if layout == "token":
         check("fox_attn_bwd_ex", lib().fox_attn_bwd_ex(*args, FOX_TOKEN_MAJOR, _stream()))

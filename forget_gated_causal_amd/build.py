@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfox.so")
-SOURCES = ["fox_api.hip", "fox_scan.hip", "fox_fwd.hip", "fox_decode.hip", "fox_bwd.hip"]
+SOURCES = ["fox_api.hip", "fox_scan.hip", "fox_fwd.hip", "fox_decode.hip", "fox_bwd.hip", "fox_bwd_f32.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
 HIP_FLAGS = [

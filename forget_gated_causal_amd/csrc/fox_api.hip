@@ -149,12 +149,13 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
   if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || !head_dim_ok(d)) return FOX_ERR_UNSUPPORTED;
-  if (dtype != FOX_BF16) return FOX_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
-  if ((n + 127) / 128 > kMaxGridY) return FOX_ERR_INVALID_ARG;
+  const int64_t block_rows = dtype == FOX_F32 ? 64 : 128;  // rows per workgroup along the grid's y
+  if ((n + block_rows - 1) / block_rows > kMaxGridY) return FOX_ERR_INVALID_ARG;
   if (layout != FOX_HEAD_MAJOR && layout != FOX_TOKEN_MAJOR) return FOX_ERR_UNSUPPORTED;
   // token-major: one head's rows span (n-1)*h*d + d elements, addressed with 32-bit byte offsets
-  if (layout == FOX_TOKEN_MAJOR && (n + 256) * h * d * 2 > kI32Max) return FOX_ERR_UNSUPPORTED;
+  if (layout == FOX_TOKEN_MAJOR && (n + 256) * h * d * (int64_t)elem_bytes(dtype) > kI32Max)
+    return FOX_ERR_UNSUPPORTED;
   const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : t16)
     if (!aligned(p, 16)) return FOX_ERR_INVALID_ARG;
@@ -171,6 +172,12 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
   for (int i = 0; i < 5; ++i)  // outs[i] is all[7 + i]
     for (int j = 0; j < 12; ++j)
       if (j != 7 + i && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
+  if (dtype == FOX_F32)
+    return from_hip(fox::launch_attn_bwd_f32(
+        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+        static_cast<const float*>(o), static_cast<const float*>(dout), lse, c, static_cast<float*>(dq),
+        static_cast<float*>(dk), static_cast<float*>(dv), dlogf, static_cast<float*>(workspace), b, h, (int)n, (int)d,
+        scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
   return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, static_cast<float*>(workspace),
                                        b, h, (int)n, (int)d, scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
 }

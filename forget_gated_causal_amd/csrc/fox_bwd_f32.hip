@@ -1,0 +1,288 @@
+// fox_bwd_f32.hip -- backward pass of FoX attention on fp32 tensors (the fp32 forward's gradients).
+//
+// The same chain rule as the bf16 backward (fox_bwd.hip), through the forward definition of the
+// FoX module page (ForgettingAttention.forward), in fp32 throughout (no bf16 rounding of P or dS):
+//   P_ij = exp(s_ij - lse_i) with s_ij = scale q_i.k_j + c_i - c_j (j <= i when causal)
+//   dv = P^T dO;  dP = dO v^T;  dS = P * (dP - D_i), D_i = dO_i . O_i
+//   dq = scale dS k;  dk = scale dS^T q;  dlog f_t = sum_{i >= t} (rowsum(dS)_i - colsum(dS)_i)
+// The fp32 path serves the fp32 forward's (small, correctness-sized) workloads, so it runs on the
+// vector ALU in plain tiles rather than on MFMA:
+//  * bwd_f32_pre_kernel: D_i and the padded per-head row vectors [a | D | cl] (as fox_bwd.hip).
+//  * bwd_f32_kv_kernel<D, CAUSAL>: one 256-thread workgroup per (64-key block, head); the block's K
+//    and V rows sit in LDS, 32-query tiles of q and dO stream through it.  Per tile, thread t forms
+//    P and dS for key t % 64 and queries 8 (t / 64) .. +7 (phase A, into LDS), then accumulates
+//    dV and dK for key t % 64 over dims D/4 (t / 64) .. +D/4 (phase B).  Writes dk, dv and the
+//    column sums of dS.
+//  * bwd_f32_dq_kernel<D, CAUSAL>: one workgroup per (64-query block, head), 32-key tiles; the same
+//    two phases with queries and keys exchanged.  Writes dq and the row sums of dS.
+//  * The reversed gate scan (fox_scan.hip) turns row sums - column sums into dlog f.
+// Every output element has one writer.  LDS rows are padded by one float, so the per-thread row
+// reads (stride D + 1 words) fall in distinct banks.
+#include <math.h>
+
+#include "fox_device.h"
+#include "fox_internal.h"
+
+namespace fox {
+namespace {
+
+constexpr int kF32Threads = 256;
+constexpr int kF32Blk = 64;   // keys (kv kernel) or queries (dq kernel) per workgroup
+constexpr int kF32Tile = 32;  // queries (kv kernel) or keys (dq kernel) per streamed tile
+constexpr int kF32Pad = 64;   // per-head row vectors are padded to a multiple of this
+
+// Strides of one backward call (elements): tensors (bs, hs, rs), gate-sized vectors (gbs, ghs, gs).
+struct F32Layout {
+  int64_t bs, hs;
+  int rs;
+  int64_t gbs, ghs;
+  int gs;
+  int nh;
+  __device__ __forceinline__ int64_t tbase(int bh) const { return (int64_t)(bh / nh) * bs + (bh % nh) * hs; }
+  __device__ __forceinline__ int64_t gbase(int bh) const { return (int64_t)(bh / nh) * gbs + (bh % nh) * ghs; }
+};
+
+int f32_npad(int n) { return (n + kF32Pad - 1) / kF32Pad * kF32Pad; }
+
+// One thread per (head, padded row): D_i = dO_i . O_i and the row vectors of the block.
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void bwd_f32_pre_kernel(const float* __restrict__ o,
+                                                                  const float* __restrict__ dout,
+                                                                  const float* __restrict__ lse,
+                                                                  const float* __restrict__ c,
+                                                                  float* __restrict__ rowv, int64_t bh_count, int n,
+                                                                  int npad, F32Layout lay) {
+  const int64_t prow = (int64_t)blockIdx.x * kF32Threads + threadIdx.x;
+  const int64_t bh = prow / npad;
+  if (bh >= bh_count) return;
+  const int i = (int)(prow - bh * npad);
+  float* blk = rowv + bh * 3 * npad;
+  if (i >= n) {
+    blk[i] = -INFINITY;
+    blk[npad + i] = 0.0f;
+    blk[2 * npad + i] = INFINITY;
+    return;
+  }
+  const float* orow = o + lay.tbase((int)bh) + (int64_t)i * lay.rs;
+  const float* drow = dout + lay.tbase((int)bh) + (int64_t)i * lay.rs;
+  float s = 0.0f;
+#pragma unroll 8
+  for (int e = 0; e < D; ++e) s = fmaf(orow[e], drow[e], s);
+  const int64_t g = lay.gbase((int)bh) + (int64_t)i * lay.gs;
+  blk[i] = (c[g] - lse[g]) * kLog2e;
+  blk[npad + i] = s;
+  blk[2 * npad + i] = c[g] * kLog2e;
+}
+
+// Copy `rows` rows of D floats (global row stride rs) into an LDS tile of row stride D + 1;
+// rows at or past `valid` read as zeros.
+template <int D>
+__device__ __forceinline__ void f32_stage(float* lds, const float* src, int rows, int valid, int rs) {
+  for (int x = threadIdx.x; x < rows * D; x += kF32Threads) {
+    const int r = x / D, e = x - r * D;
+    lds[r * (D + 1) + e] = r < valid ? src[(int64_t)r * rs + e] : 0.0f;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ float f32_dot(const float* a, const float* b) {
+  float s = 0.0f;
+#pragma unroll 8
+  for (int e = 0; e < D; ++e) s = fmaf(a[e], b[e], s);
+  return s;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Threads) void bwd_f32_kv_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dout, const float* __restrict__ rowv, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ colsum_out, int n, int npad, float scale, F32Layout lay) {
+  constexpr int DP = D + 1, DC = D / 4;
+  __shared__ float ks[kF32Blk * DP], vs[kF32Blk * DP];
+  __shared__ float qs[kF32Tile * DP], ds_[kF32Tile * DP];
+  __shared__ float pt[kF32Blk * (kF32Tile + 1)], st[kF32Blk * (kF32Tile + 1)];
+  __shared__ float arow[kF32Tile], drow[kF32Tile], csum[4][kF32Blk];
+  const int bh = blockIdx.x, key0 = blockIdx.y * kF32Blk;
+  const int tid = threadIdx.x, jl = tid & 63, g = tid >> 6;
+  const int j = key0 + jl;
+  const int64_t tb = lay.tbase(bh);
+  const float* blk = rowv + (int64_t)bh * 3 * npad;
+  const float scale_log2 = scale * kLog2e;
+  f32_stage<D>(ks, k + tb + (int64_t)key0 * lay.rs, kF32Blk, n - key0, lay.rs);
+  f32_stage<D>(vs, v + tb + (int64_t)key0 * lay.rs, kF32Blk, n - key0, lay.rs);
+  const float clj = j < n ? blk[2 * npad + j] : INFINITY;
+  float accv[DC], acck[DC];
+#pragma unroll
+  for (int x = 0; x < DC; ++x) accv[x] = acck[x] = 0.0f;
+  float cs = 0.0f;
+  const int qfirst = CAUSAL ? key0 : 0;  // earlier queries see none of these keys
+  for (int q0 = qfirst - qfirst % kF32Tile; q0 < n; q0 += kF32Tile) {
+    __syncthreads();  // the previous tile's phase B is done with qs, ds_, pt, st
+    f32_stage<D>(qs, q + tb + (int64_t)q0 * lay.rs, kF32Tile, n - q0, lay.rs);
+    f32_stage<D>(ds_, dout + tb + (int64_t)q0 * lay.rs, kF32Tile, n - q0, lay.rs);
+    if (tid < kF32Tile) {
+      arow[tid] = q0 + tid < n ? blk[q0 + tid] : -INFINITY;
+      drow[tid] = q0 + tid < n ? blk[npad + q0 + tid] : 0.0f;
+    }
+    __syncthreads();
+    // phase A: P and dS for key j and queries q0 + 8g .. + 7
+#pragma unroll 1
+    for (int u = 0; u < 8; ++u) {
+      const int il = 8 * g + u, i = q0 + il;
+      float p = 0.0f, dsv = 0.0f;
+      if (j < n && i < n && (!CAUSAL || j <= i)) {
+        const float s = f32_dot<D>(&ks[jl * DP], &qs[il * DP]);
+        const float dp = f32_dot<D>(&vs[jl * DP], &ds_[il * DP]);
+        p = exp2_hw(fmaf(s, scale_log2, arow[il]) - clj);
+        dsv = p * (dp - drow[il]);
+      }
+      pt[jl * (kF32Tile + 1) + il] = p;
+      st[jl * (kF32Tile + 1) + il] = dsv;
+      cs += dsv;
+    }
+    __syncthreads();
+    // phase B: dV_j += P_j. dO, dK_j += dS_j. Q over dims DC g .. DC g + DC - 1
+#pragma unroll 1
+    for (int il = 0; il < kF32Tile; ++il) {
+      const float p = pt[jl * (kF32Tile + 1) + il], dsv = st[jl * (kF32Tile + 1) + il];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) {
+        accv[x] = fmaf(p, ds_[il * DP + DC * g + x], accv[x]);
+        acck[x] = fmaf(dsv, qs[il * DP + DC * g + x], acck[x]);
+      }
+    }
+  }
+  csum[g][jl] = cs;
+  __syncthreads();
+  if (j < n) {
+    float* dkr = dk + tb + (int64_t)j * lay.rs + DC * g;
+    float* dvr = dv + tb + (int64_t)j * lay.rs + DC * g;
+#pragma unroll
+    for (int x = 0; x < DC; ++x) {
+      dkr[x] = acck[x] * scale;
+      dvr[x] = accv[x];
+    }
+    if (g == 0) colsum_out[(int64_t)bh * n + j] = (csum[0][jl] + csum[1][jl]) + (csum[2][jl] + csum[3][jl]);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Threads) void bwd_f32_dq_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dout, const float* __restrict__ rowv, float* __restrict__ dq,
+    float* __restrict__ rowsum_out, int n, int npad, float scale, F32Layout lay) {
+  constexpr int DP = D + 1, DC = D / 4;
+  __shared__ float qs[kF32Blk * DP], ds_[kF32Blk * DP];
+  __shared__ float ks[kF32Tile * DP], vs[kF32Tile * DP];
+  __shared__ float st[kF32Blk * (kF32Tile + 1)];
+  __shared__ float clt[kF32Tile], rsum[4][kF32Blk];
+  const int bh = blockIdx.x, qblk0 = blockIdx.y * kF32Blk;
+  const int tid = threadIdx.x, il = tid & 63, g = tid >> 6;
+  const int i = qblk0 + il;
+  const int64_t tb = lay.tbase(bh);
+  const float* blk = rowv + (int64_t)bh * 3 * npad;
+  const float scale_log2 = scale * kLog2e;
+  f32_stage<D>(qs, q + tb + (int64_t)qblk0 * lay.rs, kF32Blk, n - qblk0, lay.rs);
+  f32_stage<D>(ds_, dout + tb + (int64_t)qblk0 * lay.rs, kF32Blk, n - qblk0, lay.rs);
+  const float ai = i < n ? blk[i] : -INFINITY;
+  const float di = i < n ? blk[npad + i] : 0.0f;
+  float acc[DC];
+#pragma unroll
+  for (int x = 0; x < DC; ++x) acc[x] = 0.0f;
+  float rs = 0.0f;
+  const int kend = CAUSAL ? min(n, qblk0 + kF32Blk) : n;  // later keys are masked for every row
+  for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+    __syncthreads();  // the previous tile's phase B is done with ks, vs, st
+    f32_stage<D>(ks, k + tb + (int64_t)k0 * lay.rs, kF32Tile, n - k0, lay.rs);
+    f32_stage<D>(vs, v + tb + (int64_t)k0 * lay.rs, kF32Tile, n - k0, lay.rs);
+    if (tid < kF32Tile) clt[tid] = k0 + tid < n ? blk[2 * npad + k0 + tid] : INFINITY;
+    __syncthreads();
+#pragma unroll 1
+    for (int u = 0; u < 8; ++u) {
+      const int jl = 8 * g + u, j = k0 + jl;
+      float dsv = 0.0f;
+      if (j < n && i < n && (!CAUSAL || j <= i)) {
+        const float s = f32_dot<D>(&qs[il * DP], &ks[jl * DP]);
+        const float dp = f32_dot<D>(&ds_[il * DP], &vs[jl * DP]);
+        const float p = exp2_hw(fmaf(s, scale_log2, ai) - clt[jl]);
+        dsv = p * (dp - di);
+      }
+      st[il * (kF32Tile + 1) + jl] = dsv;
+      rs += dsv;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int jl = 0; jl < kF32Tile; ++jl) {
+      const float dsv = st[il * (kF32Tile + 1) + jl];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) acc[x] = fmaf(dsv, ks[jl * DP + DC * g + x], acc[x]);
+    }
+  }
+  rsum[g][il] = rs;
+  __syncthreads();
+  if (i < n) {
+    float* dqr = dq + tb + (int64_t)i * lay.rs + DC * g;
+#pragma unroll
+    for (int x = 0; x < DC; ++x) dqr[x] = acc[x] * scale;
+    if (g == 0) rowsum_out[(int64_t)bh * n + i] = (rsum[0][il] + rsum[1][il]) + (rsum[2][il] + rsum[3][il]);
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_f32_t(const float* q, const float* k, const float* v, const float* o, const float* dout,
+                            const float* lse, const float* c, float* dq, float* dk, float* dv, float* dlogf,
+                            float* ws, int64_t b, int64_t h, int n, float scale, bool causal, bool token_major,
+                            hipStream_t stream) {
+  const int64_t bh = b * h;
+  const int npad = f32_npad(n);
+  // {bs, hs, rs, gbs, ghs, gs, nh}
+  const F32Layout lay = token_major
+                            ? F32Layout{(int64_t)n * h * D, (int64_t)D, (int)(h * D), (int64_t)n * h, 1, (int)h, (int)h}
+                            : F32Layout{h * n * (int64_t)D, (int64_t)n * D, D, h * (int64_t)n, (int64_t)n, 1, (int)h};
+  // workspace: row vectors [bh][3][npad], row sums [bh][n], column sums [bh][n]
+  float* rowv = ws;
+  float* rsum = rowv + bh * 3 * npad;
+  float* csum = rsum + bh * n;
+  hipLaunchKernelGGL((bwd_f32_pre_kernel<D>), dim3((unsigned)((bh * npad + kF32Threads - 1) / kF32Threads)),
+                     dim3(kF32Threads), 0, stream, o, dout, lse, c, rowv, bh, n, npad, lay);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)bh, (unsigned)((n + kF32Blk - 1) / kF32Blk));
+  if (causal) {
+    hipLaunchKernelGGL((bwd_f32_kv_kernel<D, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
+                       (const float*)rowv, dk, dv, csum, n, npad, scale, lay);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
+                       (const float*)rowv, dq, rsum, n, npad, scale, lay);
+  } else {
+    hipLaunchKernelGGL((bwd_f32_kv_kernel<D, false>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
+                       (const float*)rowv, dk, dv, csum, n, npad, scale, lay);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
+                       (const float*)rowv, dq, rsum, n, npad, scale, lay);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dlog f_t = sum_{i >= t} (rowsum_i - colsum_i), written in the gates' layout
+  return launch_suffix_sum(rsum, csum, dlogf, bh, n, (int)h, token_major, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
+                               const float* lse, const float* c, float* dq, float* dk, float* dv, float* dlogf,
+                               float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                               bool token_major, hipStream_t stream) {
+  switch (d) {
+    case 32:
+      return launch_bwd_f32_t<32>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+                                  token_major, stream);
+    case 64:
+      return launch_bwd_f32_t<64>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+                                  token_major, stream);
+    case 128:
+      return launch_bwd_f32_t<128>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+                                   token_major, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fox

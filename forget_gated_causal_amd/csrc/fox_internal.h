@@ -53,5 +53,10 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
                            float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
                            bool token_major, hipStream_t stream);
+// The same on fp32 tensors (fp32 throughout; same workspace size and layouts).
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
+                               const float* lse, const float* c, float* dq, float* dk, float* dv, float* dlogf,
+                               float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                               bool token_major, hipStream_t stream);
 
 }  // namespace fox

@@ -162,7 +162,7 @@ fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, co
 size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
 
 /*
- * fox_attn_bwd -- gradients of FoX attention (decoder or unmasked mode), head-major, bf16.
+ * fox_attn_bwd -- gradients of FoX attention (decoder or unmasked mode), head-major.
  *   The pages derive no backward pass.  This is the chain rule through fox_attn_fwd's
  *   definition (FoX module page, ForgettingAttention.forward), for a loss whose gradient
  *   with respect to O is dout:
@@ -172,16 +172,18 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
  *   (the row sums of dS vanish in exact arithmetic; the kernels keep them, with both sums
  *   taken over the same bf16-rounded dS, so that their rounding cancels in dlogf).
  *
- *   q, k, v, o, dout : [b, h, n, d] bf16, inputs; o, lse and c as fox_attn_fwd (same mode) wrote
- *                      them for these q, k, v, logf and scale.
+ *   q, k, v, o, dout : [b, h, n, d] of `dtype`, inputs; o, lse and c as fox_attn_fwd (same mode)
+ *                      wrote them for these q, k, v, logf and scale.
  *   lse, c   : [b, h, n] fp32, inputs (fox_attn_fwd's outputs).
- *   dq, dk, dv : [b, h, n, d] bf16, outputs (rounded to nearest even).
+ *   dq, dk, dv : [b, h, n, d] of `dtype`, outputs (bf16: rounded to nearest even).
+ *   dtype    : FOX_BF16 (P and dS rounded to bf16 as MFMA operands, fp32 accumulation) or FOX_F32
+ *              (fp32 throughout, on the vector ALU; n up to 65535 * 64).
  *   dlogf    : [b, h, n] fp32, output: the gradient with respect to logf.
  *   workspace, workspace_bytes : device scratch of at least fox_attn_bwd_workspace_bytes(b, h, n, d)
  *              bytes, 16-byte aligned; contents on entry are ignored.
  *   causal   : nonzero for decoder mode, zero for the unmasked mode.
- *   Errors as fox_attn_fwd; fp32 tensors give FOX_ERR_UNSUPPORTED; every output and the workspace
- *   must not overlap any other buffer (FOX_ERR_INVALID_ARG).
+ *   Errors as fox_attn_fwd; every output and the workspace must not overlap any other buffer
+ *   (FOX_ERR_INVALID_ARG).
  *   Every output element has one writer (no atomics): repeated calls give identical results.
  */
 fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -197,7 +199,7 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   and dlogf as [b, n, h], the layout fox_attn_fwd_ex(..., FOX_TOKEN_MAJOR) reads and writes.
  *
  *   layout : FOX_HEAD_MAJOR or FOX_TOKEN_MAJOR (else FOX_ERR_UNSUPPORTED); with
- *            FOX_TOKEN_MAJOR, (n + 256) * h * d * 2 must not exceed 2^31 - 1
+ *            FOX_TOKEN_MAJOR, (n + 256) * h * d * sizeof(element) must not exceed 2^31 - 1
  *            (else FOX_ERR_UNSUPPORTED).
  *   Every other argument, the workspace size, the results (bit for bit, element by element)
  *   and the errors as fox_attn_bwd.

@@ -216,7 +216,8 @@ def test_bwd_rejects_bad_arguments(L):
     assert _bwd(L, dl=None) == INVALID
     assert _bwd(L, n=0) == INVALID
     assert _bwd(L, d=96) == UNSUP
-    assert _bwd(L, dt=_lib.FOX_F32) == UNSUP  # bf16 only
+    assert _bwd(L, dt=7) == UNSUP  # unknown dtype
+    assert _bwd(L, dt=_lib.FOX_F32, n=65535 * 64 + 1, h=1) == INVALID  # fp32: 64-row blocks along grid y
     assert _bwd(L, scale=float("nan")) == INVALID
     assert _bwd(L, q=A + 8) == INVALID  # 16-byte alignment
     assert _bwd(L, ws=None) == WS
@@ -236,7 +237,8 @@ def test_bwd_ex_layout_checks(L):
     assert _bwd(L, layout=-1) == UNSUP
     # token-major rows are h*d apart: one head's span must fit 32-bit byte offsets
     assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, n=1 << 20, h=64, d=128) == UNSUP
-    assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, dt=_lib.FOX_F32) == UNSUP
+    # fp32 elements are 4 bytes: the same span limit is reached at half the tokens
+    assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, dt=_lib.FOX_F32, n=65536, h=64, d=128) == UNSUP
 
 
 def test_fwd_ex_layout_checks(L):

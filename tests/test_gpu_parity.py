@@ -644,6 +644,44 @@ def test_bwd_token_major_equals_head_major(d, B, H, n, causal):
     print(f"  {cfg.desc}: token-major == head-major", flush=True)
 
 
+# (d, B, H, n, causal): c1's shape in both modes, ragged n, edges, a two-kernel-sized grid
+BWD_F32 = [(32, 1, 2, 128, True), (32, 1, 2, 128, False), (64, 2, 3, 300, True), (128, 1, 2, 257, False),
+           (64, 1, 1, 1, True), (32, 2, 2, 65, True), (128, 2, 2, 1000, True), (64, 1, 1, 63, False)]
+
+
+@pytest.mark.parametrize("d,B,H,n,causal", BWD_F32)
+def test_bwd_f32_parity(d, B, H, n, causal):
+    """fp32 backward (fp32 forward's O, lse, c) against the fp64 oracle, and token-major equal to
+    head-major bit for bit.  Bound: the bias enters through fp32-rounded prefix sums, whose size grows
+    with the position (|c| near 0.18 n at these gates), so P carries a relative error up to about
+    2^-24 |c| log2 e ~ 1e-5 at n = 1000; every gradient element sums such terms.  Checked as
+    max|gpu - ref| <= 1e-4 * max(1, max|ref|) per gradient tensor."""
+    cfg = fi.FwdConfig(f"bwd32_{d}_{B}_{H}_{n}_{causal}", B, H, n, d, "f32", 2.0, 1.0)
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(n * 13 + d)
+    dout = torch.randn(B, H, n, d, generator=g)
+    o, lse, c = fox.attn_fwd_ex(q, k, v, logf, causal=causal, scale=inp["scale"])
+    head = fox.attn_bwd(q, k, v, o, dout.to(DEV), lse, c, causal=causal, scale=inp["scale"])
+    tm = lambda t: t.permute(0, 2, 1, 3).contiguous()  # noqa: E731
+    tv = lambda t: t.permute(0, 2, 1).contiguous()  # noqa: E731
+    tok = fox.attn_bwd(tm(q), tm(k), tm(v), tm(o), tm(dout.to(DEV)), tv(lse), tv(c), causal=causal,
+                       scale=inp["scale"], layout="token")
+    torch.cuda.synchronize()
+    for name, h_, t_ in zip(("dq", "dk", "dv", "dlogf"), head, tok):
+        back = t_.permute(0, 2, 1, 3) if t_.dim() == 4 else t_.permute(0, 2, 1)
+        assert torch.equal(back, h_), name
+    ref = oracle.attn_bwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]), inp["scale"], _np(dout),
+                          causal=causal)
+    msg = []
+    for name, got, r in zip(("dq", "dk", "dv", "dlogf"), head, ref):
+        err = np.abs(_np(got) - r).max()
+        msg.append(f"{name} {err:.2e} (max|ref| {np.abs(r).max():.2e})")
+        assert torch.isfinite(got).all(), name
+        assert err <= 1e-4 * max(1.0, np.abs(r).max()), (name, err)
+    print("  " + cfg.desc + ": " + ", ".join(msg), flush=True)
+
+
 # ------------------------------------------------------------------------- the largest sequence
 
 MAX_SEQ = 1 << 22  # FOX_MAX_SEQ in include/fox.h
