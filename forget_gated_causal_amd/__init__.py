@@ -11,6 +11,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, c)   # gradients (bf16 or fp32); layout="token" too
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
     o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
+    o, lse       = attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, cache_lens, logf_new)
 """
 
 from __future__ import annotations
@@ -20,7 +21,7 @@ import torch
 from ._lib import FOX_BF16, FOX_F32, FOX_HEAD_MAJOR, FOX_TOKEN_MAJOR, FoxError, check, lib, status_string  # noqa: F401
 
 __all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_ex", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes",
-           "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_ragged",
+           "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_ragged", "attn_decode_paged",
            "decode_workspace_bytes", "FoxError", "status_string"]
 
 _DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
