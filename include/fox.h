@@ -170,7 +170,8 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
  *     dq = scale dS k, dk = scale dS^T q, and for the gates, with c_i - c_j in every score,
  *     dlogf_t = sum over i >= t of (rowsum(dS)_i - colsum(dS)_i)
  *   (the row sums of dS vanish in exact arithmetic; the kernels keep them, with both sums
- *   taken over the same bf16-rounded dS, so that their rounding cancels in dlogf).
+ *   taken over the same dS values (bf16-rounded on the bf16 path), so that their rounding
+ *   cancels in dlogf).
  *
  *   q, k, v, o, dout : [b, h, n, d] of `dtype`, inputs; o, lse and c as fox_attn_fwd (same mode)
  *                      wrote them for these q, k, v, logf and scale.
