@@ -282,7 +282,7 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     q, k, v, logf = (inp[n].to(dev) for n in ("q", "k", "v", "logf"))
     o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
     g = torch.Generator().manual_seed(1)
-    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(dev)
+    dout = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dl = torch.empty_like(logf)
     ws = torch.empty(fox.attn_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), device=dev, dtype=torch.uint8)
@@ -293,13 +293,17 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     ms = region / steps
     flops = 2.5 * fwd_flops(cfg)
     achieved = flops / (ms * 1e-3) / 1e12
+    bf16 = cfg.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    kernel = (f"bwd_kv_kernel<{cfg.d},causal> + bwd_dq_kernel<{cfg.d},causal> + 2 small kernels" if bf16 else
+              f"bwd_f32_kv_kernel<{cfg.d},causal> + bwd_f32_dq_kernel<{cfg.d},causal> + 2 small kernels")
     return {"workload": cfg.desc + ", backward", "value": round(achieved, 2), "unit": "TFLOP/s",
             "ms_per_step": round(ms, 4),
             "note": "10*d flop per causal pair (the dq kernel's recomputation of S and dP, 4*d more, is not "
-                    "counted); one call = bwd_pre, bwd_kv, bwd_dq and the gate suffix-sum kernels",
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                         "kernel": f"bwd_kv_kernel<{cfg.d},causal> + bwd_dq_kernel<{cfg.d},causal> + 2 small kernels"}}
+                    "counted); one call = the row-vector, key-side, query-side and gate suffix-sum kernels"
+                    + ("" if bf16 else "; fp32 on the vector ALU, a parity-sized workload (latency-bound)"),
+            "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel}}
 
 
 _DECODE_INPUTS = {}
@@ -488,8 +492,9 @@ def main():
         x = bench_bwd(torch, fox, fi, args.workload, args.steps, args.warmup)
         print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.1f} TFLOP/s", file=sys.stderr,
               flush=True)
-        line.update({"value": x["value"], "unit": "TFLOP/s", "ms_per_step": x["ms_per_step"], "dtype": "bf16",
-                     "config": {"workload": x["workload"]}, "roofline": x["roofline"]})
+        line.update({"value": x["value"], "unit": "TFLOP/s", "ms_per_step": x["ms_per_step"],
+                     "dtype": fi.FWD[args.workload].dtype, "config": {"workload": x["workload"]},
+                     "roofline": x["roofline"]})
         print(json.dumps(line), flush=True)
         return
     r = bench_fwd(torch, fox, fi, args.workload, args.steps, args.warmup)
@@ -531,7 +536,7 @@ def main():
                                        "note": note, "roofline": dict(x["roofline"], kernel=x["kernel"])}
             del x
             torch.cuda.empty_cache()
-        for tag in ("c2", "c3"):
+        for tag in ("c1", "c2", "c3"):
             x = bench_bwd(torch, fox, fi, tag, max(10, args.steps // 5), max(3, args.warmup // 2))
             print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.1f} TFLOP/s", file=sys.stderr,
                   flush=True)
