@@ -215,7 +215,7 @@ def _events_time(torch, fn, k):
     return e0.elapsed_time(e1)
 
 
-def fwd_kernel_name(torch, cfg) -> str:
+def fwd_kernel_name(torch, cfg, causal: bool = True) -> str:
     """The kernel fox_attn_fwd launches for this shape (same rule as the library's dispatch)."""
     if cfg.dtype != "bf16":
         return f"fwd_f32_kernel<{cfg.d}>"
@@ -223,7 +223,8 @@ def fwd_kernel_name(torch, cfg) -> str:
     bh = cfg.B * cfg.H
     if cfg.d >= 64 and bh * ((cfg.N + 255) // 256) >= 2 * cus:
         return f"fwd_bf16_pipe_kernel<{cfg.d},8,1>"
-    if cfg.d <= 64 and bh * ((cfg.N + 127) // 128) < 2 * cus:
+    blocks128 = bh * ((cfg.N + 127) // 128)
+    if cfg.d <= 64 and blocks128 < 2 * cus and (causal or blocks128 <= cus):
         return f"fwd_bf16_pipe_kernel<{cfg.d},4,2>"
     return f"fwd_bf16_pipe_kernel<{cfg.d},4,1>"
 
@@ -261,7 +262,7 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
     ms = region / steps
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (ms * 1e-3) / 1e12
-    kernel = fwd_kernel_name(torch, cfg) + ({"unmasked": " unmasked", "pruned": " pruned",
+    kernel = fwd_kernel_name(torch, cfg, causal=mode != "unmasked") + ({"unmasked": " unmasked", "pruned": " pruned",
                                              "token": " token-major"}.get(mode, ""))
     return {
         "cfg": cfg, "inp": inp,

@@ -1166,7 +1166,9 @@ hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float
       }
     }
     if constexpr (D <= 64) {
-      if (!knorm && blocks128 < 2 * (int64_t)cus)
+      // Unmasked blocks all do the same work: once they need a second round of 8-wave workgroups,
+      // 4-wave workgroups (two per CU, one round) finish first.
+      if (!knorm && blocks128 < 2 * (int64_t)cus && (CAUSAL || blocks128 <= (int64_t)cus))
         return go(fwd_bf16_pipe_kernel<D, 4, 2, false, CAUSAL, TM>, 128, 512);
     }
     if constexpr (CAN_PRUNE)
