@@ -287,7 +287,7 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dl = torch.empty_like(logf)
     ws = torch.empty(fox.attn_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), device=dev, dtype=torch.uint8)
-    fn = lambda: fox.attn_bwd(q, k, v, o, dout, lse, c, scale=inp["scale"], dq=dq, dk=dk, dv=dv,  # noqa: E731
+    fn = lambda: fox.attn_bwd(q, k, v, o, dout, lse, logf, scale=inp["scale"], dq=dq, dk=dk, dv=dv,  # noqa: E731
                               dlogf=dl, workspace=ws)
     _warm(torch, fn, warmup)
     region = _events_time(torch, fn, steps)

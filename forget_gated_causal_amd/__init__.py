@@ -8,7 +8,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     o, lse, c    = attn_fwd(q, k, v, logf, scale=None)        # q,k,v [B,H,N,d]
     o, lse, c    = attn_fwd_noncausal(q, k, v, logf)          # every key, no mask
     o, lse, c    = attn_fwd_ex(q, k, v, logf, causal, layout)  # layout "head" [B,H,N,d] / "token" [B,N,H,d]
-    dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, c)   # gradients (bf16 or fp32); layout="token" too
+    dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, logf)  # gradients (bf16 or fp32); layout="token" too
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
     o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
     o, lse       = attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, cache_lens, logf_new)
@@ -44,6 +44,22 @@ def _need(t: torch.Tensor, name: str, dtype=None) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _out(t, name: str, shape, dtype, device):
+    """A caller-supplied output buffer: same device, dtype and shape as the result, contiguous."""
+    _need(t, name, dtype)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+    return t
+
+
+def _alloc_or_check(t, name, shape, dtype, device):
+    if t is None:
+        return torch.empty(shape, device=device, dtype=dtype)
+    return _out(t, name, shape, dtype, device)
+
+
 def _default_scale(d: int) -> float:
     return float(torch.tensor(d ** -0.5, dtype=torch.float32))
 
@@ -53,8 +69,7 @@ def logf_cumsum(logf: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     _need(logf, "logf", torch.float32)
     n = logf.shape[-1]
     rows = logf.numel() // max(n, 1)
-    c = torch.empty_like(logf) if out is None else out
-    _need(c, "out", torch.float32)
+    c = torch.empty_like(logf) if out is None else _out(out, "out", logf.shape, torch.float32, logf.device)
     check("fox_logf_cumsum", lib().fox_logf_cumsum(_ptr(logf), _ptr(c), rows, n, _stream()))
     return c
 
@@ -72,12 +87,10 @@ def _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c):
     _need(logf, "logf", torch.float32)
     if tuple(logf.shape) != (B, H, N):
         raise ValueError(f"logf shape {tuple(logf.shape)} != {(B, H, N)}")
-    o = torch.empty_like(q) if out is None else out
-    if want_lse and lse is None:
-        lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
-    if want_c and c is None:
-        c = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
-    return dt, o, (lse if want_lse else None), (c if want_c else None)
+    o = _alloc_or_check(out, "out", (B, H, N, d), q.dtype, q.device)
+    lse = _alloc_or_check(lse, "lse", (B, H, N), torch.float32, q.device) if want_lse else None
+    c = _alloc_or_check(c, "c", (B, H, N), torch.float32, q.device) if want_c else None
+    return dt, o, lse, c
 
 
 def attn_fwd(q, k, v, logf, scale: float | None = None, out=None, lse=None, c=None,
@@ -129,12 +142,9 @@ def attn_fwd_ex(q, k, v, logf, causal: bool = True, layout: str = "head", scale:
         _need(logf, "logf", torch.float32)
         if tuple(logf.shape) != (B, N, H):
             raise ValueError(f"logf shape {tuple(logf.shape)} != {(B, N, H)}")
-        o = torch.empty_like(q) if out is None else out
-        if want_lse and lse is None:
-            lse = torch.empty(B, N, H, device=q.device, dtype=torch.float32)
-        if want_c and c is None:
-            c = torch.empty(B, N, H, device=q.device, dtype=torch.float32)
-        lse, c = (lse if want_lse else None), (c if want_c else None)
+        o = _alloc_or_check(out, "out", (B, N, H, d), q.dtype, q.device)
+        lse = _alloc_or_check(lse, "lse", (B, N, H), torch.float32, q.device) if want_lse else None
+        c = _alloc_or_check(c, "c", (B, N, H), torch.float32, q.device) if want_c else None
         code = FOX_TOKEN_MAJOR
     else:
         B, H, N, d = q.shape
@@ -161,11 +171,10 @@ def attn_fwd_pruned(q, k, v, logf, scale: float | None = None, out=None, lse=Non
     B, H, N, d = q.shape
     dt, o, lse, c = _fwd_outputs(q, k, v, logf, out, lse, c, want_lse, want_c)
     wb = attn_fwd_pruned_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wb, 16), device=q.device, dtype=torch.uint8)
+    workspace = _workspace(workspace, wb, q.device)
     scale = _default_scale(d) if scale is None else float(scale)
     st = lib().fox_attn_fwd_pruned(_ptr(q), _ptr(k), _ptr(v), _ptr(logf), _ptr(o), _ptr(lse), _ptr(c),
-                                   _ptr(workspace), workspace.numel(), B, H, N, d, scale, dt, _stream())
+                                   _ptr(workspace), _nbytes(workspace), B, H, N, d, scale, dt, _stream())
     check("fox_attn_fwd_pruned", st)
     return o, lse, c
 
@@ -174,12 +183,13 @@ def attn_bwd_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
     return int(lib().fox_attn_bwd_workspace_bytes(b, h, n, d))
 
 
-def attn_bwd(q, k, v, o, dout, lse, c, causal: bool = True, scale: float | None = None, dq=None, dk=None, dv=None,
-             dlogf=None, workspace=None, layout: str = "head"):
-    """Gradients of FoX attention. q, k, v, o, dout: [B,H,N,d], all bf16 or all fp32 (o, lse [B,H,N]
-    and c [B,H,N] as attn_fwd / attn_fwd_noncausal returned them).  Returns (dq, dk, dv, dlogf).
+def attn_bwd(q, k, v, o, dout, lse, logf, causal: bool = True, scale: float | None = None, dq=None, dk=None,
+             dv=None, dlogf=None, workspace=None, layout: str = "head"):
+    """Gradients of FoX attention. q, k, v, o, dout: [B,H,N,d], all bf16 or all fp32 (o and lse [B,H,N]
+    as attn_fwd / attn_fwd_noncausal returned them); logf [B,H,N] the log gates the forward was
+    given.  Returns (dq, dk, dv, dlogf).
 
-    layout "token" (fox_attn_bwd_ex): every tensor [B,N,H,d] and lse / c / dlogf [B,N,H], as
+    layout "token" (fox_attn_bwd_ex): every tensor [B,N,H,d] and lse / logf / dlogf [B,N,H], as
     attn_fwd_ex(..., layout="token") reads and writes them."""
     if layout not in ("head", "token"):
         raise ValueError(f"layout must be 'head' or 'token', got {layout!r}")
@@ -192,30 +202,42 @@ def attn_bwd(q, k, v, o, dout, lse, c, causal: bool = True, scale: float | None 
     dt = _DTYPES.get(q.dtype)
     if dt is None:
         raise ValueError(f"attn_bwd takes bf16 or fp32 tensors, got {q.dtype}")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    dlogf = torch.empty_like(lse) if dlogf is None else dlogf
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _need(t, name, q.dtype)
         if tuple(t.shape) != tshape:
             raise ValueError(f"{name} shape {tuple(t.shape)} != {tshape}")
-    for name, t in (("lse", lse), ("c", c), ("dlogf", dlogf)):
+    for name, t in (("lse", lse), ("logf", logf)):
         _need(t, name, torch.float32)
         if tuple(t.shape) != vshape:
             raise ValueError(f"{name} shape {tuple(t.shape)} != {vshape}")
-    wb = attn_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(wb, 16), device=q.device, dtype=torch.uint8)
+    dq = _alloc_or_check(dq, "dq", tshape, q.dtype, q.device)
+    dk = _alloc_or_check(dk, "dk", tshape, q.dtype, q.device)
+    dv = _alloc_or_check(dv, "dv", tshape, q.dtype, q.device)
+    dlogf = _alloc_or_check(dlogf, "dlogf", vshape, torch.float32, q.device)
+    workspace = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d), q.device)
     scale = _default_scale(d) if scale is None else float(scale)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(c), _ptr(dq), _ptr(dk), _ptr(dv),
-            _ptr(dlogf), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, N, d, scale, dt,
-            1 if causal else 0)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(logf), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(dlogf), _ptr(workspace), _nbytes(workspace), B, H, N, d, scale, dt, 1 if causal else 0)
     if layout == "token":
         check("fox_attn_bwd_ex", lib().fox_attn_bwd_ex(*args, FOX_TOKEN_MAJOR, _stream()))
     else:
         check("fox_attn_bwd", lib().fox_attn_bwd(*args, _stream()))
     return dq, dk, dv, dlogf
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _workspace(ws, nbytes: int, device):
+    """The caller's workspace (a contiguous device tensor; its size is checked by the library) or a new one."""
+    if ws is None:
+        return torch.empty(max(nbytes, 16), device=device, dtype=torch.uint8)
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, the inputs on {device}")
+    return ws
 
 
 def decode_workspace_bytes(s: int, h: int, l: int, d: int) -> int:
@@ -237,13 +259,10 @@ def _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, workspace, wa
     _need(logf_new, "logf_new", torch.float32)
     if tuple(c_cache.shape) != (S, H, L) or tuple(logf_new.shape) != (S, H):
         raise ValueError("c_cache must be [S,H,L] and logf_new [S,H]")
-    o = torch.empty_like(q) if out is None else out
-    if want_lse and lse is None:
-        lse = torch.empty(S, H, device=q.device, dtype=torch.float32)
-    nbytes = decode_workspace_bytes(S, H, L, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8)
-    return S, H, L, d, dt, o, (lse if want_lse else None), workspace
+    o = _alloc_or_check(out, "out", (S, H, d), q.dtype, q.device)
+    lse = _alloc_or_check(lse, "lse", (S, H), torch.float32, q.device) if want_lse else None
+    workspace = _workspace(workspace, decode_workspace_bytes(S, H, L, d), q.device)
+    return S, H, L, d, dt, o, lse, workspace
 
 
 def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = None, out=None, lse=None,
@@ -252,7 +271,7 @@ def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = No
     c_cache [S,H,L] fp32 (slot L-1 is written); logf_new [S,H] fp32.  Returns (o, lse)."""
     S, H, L, d, dt, o, lse, ws = _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, workspace, want_lse)
     st = lib().fox_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(c_cache), _ptr(logf_new), _ptr(o),
-                               _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), S, H, L, d,
+                               _ptr(lse), _ptr(ws), _nbytes(ws), S, H, L, d,
                                float(_default_scale(d) if scale is None else scale), dt, _stream())
     check("fox_attn_decode", st)
     return o, lse
@@ -267,7 +286,7 @@ def attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens, scale
     if tuple(cache_lens.shape) != (S,):
         raise ValueError(f"cache_lens shape {tuple(cache_lens.shape)} != {(S,)}")
     st = lib().fox_attn_decode_ragged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(c_cache), _ptr(logf_new),
-                                      _ptr(cache_lens), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _ptr(cache_lens), _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws),
                                       S, H, L, d, float(_default_scale(d) if scale is None else scale), dt, _stream())
     check("fox_attn_decode_ragged", st)
     return o, lse
@@ -299,14 +318,12 @@ def attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, cache_lens, log
     if block_table.dim() != 2 or block_table.shape[0] != S or tuple(cache_lens.shape) != (S,):
         raise ValueError("block_table must be [S, max_pages] and cache_lens [S]")
     maxp = block_table.shape[1]
-    o = torch.empty_like(q) if out is None else out
-    if want_lse and lse is None:
-        lse = torch.empty(S, H, device=q.device, dtype=torch.float32)
-    nbytes = decode_workspace_bytes(S, H, maxp * P, d)
-    ws = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8) if workspace is None else workspace
+    o = _alloc_or_check(out, "out", (S, H, d), q.dtype, q.device)
+    lse = _alloc_or_check(lse, "lse", (S, H), torch.float32, q.device) if want_lse else None
+    ws = _workspace(workspace, decode_workspace_bytes(S, H, maxp * P, d), q.device)
     st = lib().fox_attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(c_pages), _ptr(block_table),
-                                     _ptr(cache_lens), _ptr(logf_new), _ptr(o), _ptr(lse if want_lse else None),
-                                     _ptr(ws), ws.numel() * ws.element_size(), S, H, NP, P, maxp, d,
+                                     _ptr(cache_lens), _ptr(logf_new), _ptr(o), _ptr(lse),
+                                     _ptr(ws), _nbytes(ws), S, H, NP, P, maxp, d,
                                      float(_default_scale(d) if scale is None else scale), dt, _stream())
     check("fox_attn_decode_paged", st)
-    return o, (lse if want_lse else None)
+    return o, lse

@@ -134,18 +134,18 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d) 
 }
 
 fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                          const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                          const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                           void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
                           float scale, fox_dtype_t dtype, int causal, hipStream_t stream) {
-  return fox_attn_bwd_ex(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, workspace_bytes, b, h, n, d, scale,
-                         dtype, causal, FOX_HEAD_MAJOR, stream);
+  return fox_attn_bwd_ex(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, workspace_bytes, b, h, n, d,
+                         scale, dtype, causal, FOX_HEAD_MAJOR, stream);
 }
 
 fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                             const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                             const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                              void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
                              float scale, fox_dtype_t dtype, int causal, fox_layout_t layout, hipStream_t stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !c || !dq || !dk || !dv || !dlogf) return FOX_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !dout || !lse || !logf || !dq || !dk || !dv || !dlogf) return FOX_ERR_INVALID_ARG;
   if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || !head_dim_ok(d)) return FOX_ERR_UNSUPPORTED;
@@ -159,7 +159,7 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
   const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : t16)
     if (!aligned(p, 16)) return FOX_ERR_INVALID_ARG;
-  if (!aligned(lse, 4) || !aligned(c, 4) || !aligned(dlogf, 4)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(lse, 4) || !aligned(logf, 4) || !aligned(dlogf, 4)) return FOX_ERR_INVALID_ARG;
   const int64_t bh = b * h;
   const size_t need = fox::attn_bwd_workspace_bytes(bh, (int)n, (int)d);
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
@@ -167,7 +167,7 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
   // every output (and the workspace) apart from every other buffer
   const void* outs[] = {dq, dk, dv, dlogf, workspace};
   const size_t osz[] = {tb, tb, tb, vb, need};
-  const void* all[] = {q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace};
+  const void* all[] = {q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace};
   const size_t asz[] = {tb, tb, tb, tb, tb, vb, vb, tb, tb, tb, vb, need};
   for (int i = 0; i < 5; ++i)  // outs[i] is all[7 + i]
     for (int j = 0; j < 12; ++j)
@@ -175,17 +175,18 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
   if (dtype == FOX_F32)
     return from_hip(fox::launch_attn_bwd_f32(
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-        static_cast<const float*>(o), static_cast<const float*>(dout), lse, c, static_cast<float*>(dq),
-        static_cast<float*>(dk), static_cast<float*>(dv), dlogf, static_cast<float*>(workspace), b, h, (int)n, (int)d,
-        scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
-  return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, static_cast<float*>(workspace),
-                                       b, h, (int)n, (int)d, scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
+        static_cast<const float*>(o), static_cast<const float*>(dout), lse, logf, static_cast<float*>(dq),
+        static_cast<float*>(dk), static_cast<float*>(dv), dlogf, workspace, b, h, (int)n, (int)d, scale, causal != 0,
+        layout == FOX_TOKEN_MAJOR, stream));
+  return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, (int)n,
+                                       (int)d, scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
 }
 
-// Validation shared by the decode entry points.
+// Validation shared by the decode entry points (cache_lens: the ragged step's lengths, or null).
 static fox_status_t decode_args(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
-                                const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                                int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype) {
+                                const float* logf_new, const int32_t* cache_lens, void* o, float* lse, void* workspace,
+                                size_t workspace_bytes, int64_t s, int64_t h, int64_t l, int64_t d, float scale,
+                                fox_dtype_t dtype) {
   if (!q || !k_cache || !v_cache || !c_cache || !logf_new || !o) return FOX_ERR_INVALID_ARG;
   if (s <= 0 || h <= 0 || l <= 0 || d <= 0 || l > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (s > kI32Max / h) return FOX_ERR_INVALID_ARG;
@@ -193,7 +194,8 @@ static fox_status_t decode_args(const void* q, const void* k_cache, const void* 
   if (!scale_ok(scale)) return FOX_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
     return FOX_ERR_INVALID_ARG;
-  if (!aligned(c_cache, 4) || !aligned(logf_new, 4) || !aligned(lse, 4)) return FOX_ERR_INVALID_ARG;
+  if (!aligned(c_cache, 4) || !aligned(logf_new, 4) || !aligned(lse, 4) || !aligned(cache_lens, 4))
+    return FOX_ERR_INVALID_ARG;
   const int64_t sh = s * h;
   const int nsplit = fox::decode_num_splits(sh, (int)l, (int)d);
   if (sh > kI32Max / nsplit) return FOX_ERR_INVALID_ARG;
@@ -202,13 +204,16 @@ static fox_status_t decode_args(const void* q, const void* k_cache, const void* 
   const size_t eb = elem_bytes(dtype);
   const size_t obytes = (size_t)sh * (size_t)d * eb, cbytes = (size_t)sh * (size_t)l * sizeof(float);
   const size_t kvbytes = (size_t)sh * (size_t)l * (size_t)d * eb, sbytes = (size_t)sh * sizeof(float);
-  if (overlap(o, obytes, q, obytes) || overlap(o, obytes, k_cache, kvbytes) || overlap(o, obytes, v_cache, kvbytes) ||
-      overlap(o, obytes, c_cache, cbytes) || overlap(lse, sbytes, c_cache, cbytes) ||
-      overlap(lse, sbytes, o, obytes) || overlap(workspace, need, o, obytes) ||
-      overlap(workspace, need, c_cache, cbytes) || overlap(workspace, need, k_cache, kvbytes) ||
-      overlap(workspace, need, v_cache, kvbytes) || overlap(c_cache, cbytes, k_cache, kvbytes) ||
-      overlap(c_cache, cbytes, v_cache, kvbytes) || overlap(c_cache, cbytes, logf_new, sbytes))
-    return FOX_ERR_INVALID_ARG;
+  const size_t lbytes = (size_t)s * sizeof(int32_t);
+  // every buffer written (o, lse, c_cache, workspace) apart from every other buffer
+  const void* outs[] = {o, lse, c_cache, workspace};
+  const size_t osz[] = {obytes, sbytes, cbytes, need};
+  const void* all[] = {q, k_cache, v_cache, c_cache, logf_new, cache_lens, o, lse, workspace};
+  const size_t asz[] = {obytes, kvbytes, kvbytes, cbytes, sbytes, lbytes, obytes, sbytes, need};
+  const int self[] = {6, 7, 3, 8};  // outs[i] is all[self[i]]
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 9; ++j)
+      if (j != self[i] && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
   return FOX_OK;
 }
 
@@ -216,8 +221,8 @@ fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_c
                              const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
                              int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
                              hipStream_t stream) {
-  const fox_status_t st =
-      decode_args(q, k_cache, v_cache, c_cache, logf_new, o, lse, workspace, workspace_bytes, s, h, l, d, scale, dtype);
+  const fox_status_t st = decode_args(q, k_cache, v_cache, c_cache, logf_new, nullptr, o, lse, workspace,
+                                      workspace_bytes, s, h, l, d, scale, dtype);
   if (st != FOX_OK) return st;
   return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, nullptr, (int)h, o, lse,
                                           static_cast<float*>(workspace), s * h, (int)l, (int)d, scale,
@@ -228,17 +233,10 @@ fox_status_t fox_attn_decode_ragged(const void* q, const void* k_cache, const vo
                                     const float* logf_new, const int32_t* cache_lens, void* o, float* lse,
                                     void* workspace, size_t workspace_bytes, int64_t s, int64_t h, int64_t l,
                                     int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream) {
-  const fox_status_t st =
-      decode_args(q, k_cache, v_cache, c_cache, logf_new, o, lse, workspace, workspace_bytes, s, h, l, d, scale, dtype);
+  if (!cache_lens) return FOX_ERR_INVALID_ARG;
+  const fox_status_t st = decode_args(q, k_cache, v_cache, c_cache, logf_new, cache_lens, o, lse, workspace,
+                                      workspace_bytes, s, h, l, d, scale, dtype);
   if (st != FOX_OK) return st;
-  if (!cache_lens || !aligned(cache_lens, 4)) return FOX_ERR_INVALID_ARG;
-  const size_t lbytes = (size_t)s * sizeof(int32_t);
-  const size_t need = fox::decode_workspace_bytes(s * h, (int)l, (int)d);
-  const size_t cbytes = (size_t)s * (size_t)h * (size_t)l * sizeof(float);
-  if (overlap(cache_lens, lbytes, c_cache, cbytes) || overlap(cache_lens, lbytes, workspace, need) ||
-      overlap(cache_lens, lbytes, o, (size_t)s * (size_t)h * (size_t)d * elem_bytes(dtype)) ||
-      overlap(cache_lens, lbytes, lse, (size_t)s * (size_t)h * sizeof(float)))
-    return FOX_ERR_INVALID_ARG;
   return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, cache_lens, (int)h, o, lse,
                                           static_cast<float*>(workspace), s * h, (int)l, (int)d, scale,
                                           dtype == FOX_BF16, stream));

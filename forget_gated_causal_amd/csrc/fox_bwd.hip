@@ -8,9 +8,25 @@
 //   dc_j = rowsum(dS)_j - colsum(dS)_j;  dlog f_t = sum_{i >= t} dc_i
 // The row sums of dS vanish in exact arithmetic (sum_j P_ij dP_ij = dO_i . O_i = D_i) but not in
 // rounded arithmetic, and dlog f_t = sum_{i>=t} dc_i then adds up the rounding of every row
-// i >= t.  With both sums taken over the same bf16-rounded dS, the terms of the block i, j >= t
-// cancel and dlog f_t reduces to the cross block (i >= t > j) as it does exactly.  The
-// forward's lse and c (its outputs) give P without a second softmax.
+// i >= t.  With both sums taken over the same dS values, the terms of the block i, j >= t cancel
+// and dlog f_t reduces to the cross blocks (i >= t > j, and i < t <= j without the mask) as it
+// does exactly.  With the mask the sums use the bf16 dS the MFMAs use (the one cross block is
+// short: its rows see keys before t only within their window); without it the two cross blocks
+// can be far larger than dlog f_t, and the sums use the fp32 dS before rounding (those kernels
+// then need more registers than two waves per SIMD allow, and run one).  The forward's lse
+// gives P without a second softmax.
+//
+// Gate bias.  The prefix sums c grow with the sequence (|c| ~ 10^5 at a million tokens), so fp32
+// values of c_i and c_j carry errors far larger than the bias c_i - c_j of nearby pairs.  The
+// gate-rows kernel (fox_scan.hip) splits c at 32-position blocks instead: C_b in fp64 per block,
+// and the in-block part cq_i = c_i - C_b(i) in the row vectors.  A score's bias is then
+// (cq_i - cq_j) + (C_b(i) - C_b(j)); the block difference is one fp64 subtraction per (tile,
+// wave), and every fp32 rounding is of a term no larger than the bias itself.
+//
+// D_i.  dO_i . O_i uses the forward's O, rounded to bf16.  Without the mask, dlog f_t is the
+// difference of two cross-block sums that can be far larger than it, and the rounding of O
+// (through D_i, in every dS of row i) no longer cancels: the unmasked mode therefore first runs
+// the query-stationary part in a D pass, D_i = sum_j P_ij dP_ij in fp32 from the same P and dP.
 //
 // Two parts split the work so that every output has one writer (no atomics, and the results are
 // the same from run to run).  Large grids run them as two kernels, small grids as one
@@ -79,18 +95,20 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* p, uint32_t num_bytes) {
   return r;
 }
 // Direct-to-LDS buffer loads (lane l's bytes land at LDS byte address m0v + l * size).  Issued
-// through inline assembly, so the compiler does not wait for them; the kernel waits itself.
+// through inline assembly, so the compiler does not wait for them; the kernel waits itself.  M0
+// is an input operand the compiler writes before each load; the s_nop is the wait state an M0
+// write needs before an LDS-DMA instruction reads it.
 __device__ __forceinline__ void lds_load16(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
-                   : "s"(m0v), "v"(voff), "s"(rsrc)
-                   : "memory", "m0");
+                   : "v"(voff), "s"(rsrc), "{m0}"(m0v)
+                   : "memory");
 }
 __device__ __forceinline__ void lds_load4(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                    :
-                   : "s"(m0v), "v"(voff), "s"(rsrc)
-                   : "memory", "m0");
+                   : "v"(voff), "s"(rsrc), "{m0}"(m0v)
+                   : "memory");
 }
 // s_waitcnt vmcnt(N), expcnt and lgkmcnt not waited on
 template <int N>
@@ -165,6 +183,16 @@ __device__ __forceinline__ bf16x8 row_operand(const bf16* tile, int row, int col
   return *reinterpret_cast<const bf16x8*>(tile + sw_off<W>(row, col));
 }
 
+// Sum of the 16 registers of an accumulator (pairwise).
+__device__ __forceinline__ float tree_sum16(const f32x16& a) {
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = a[e] + a[e + 8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] += t[e + 4];
+  return (t[0] + t[2]) + (t[1] + t[3]);
+}
+
 // Registers 8u..8u+7 of an accumulator as a bf16 B operand (round to nearest even).
 __device__ __forceinline__ bf16x8 acc_operand(const f32x16& a, int u) {
   bf16x8 r;
@@ -186,13 +214,10 @@ __device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows,
   }
 }
 
-// Per head, the row-vector block [a | D | cl] of 3 * npad floats (npad = n rounded up to kPad):
-// a_i = (c_i - lse_i) log2 e, D_i = dO_i . O_i, cl_i = c_i log2 e, padded past n with a = -inf,
-// D = 0, cl = +inf, so padded queries and keys carry no weight.  One group of D/8 lanes per
-// (head, padded row).
+// D_i = dO_i . O_i into the D slot of each head's row-vector block [a | D | cl] (the gate-rows
+// kernel writes a, cl and the padding).  One group of D/8 lanes per (head, padded row).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                                                      const float* __restrict__ lse, const float* __restrict__ c,
                                                       float* __restrict__ rowv, int64_t bh_count, int n, int npad,
                                                       BwdLayout lay) {
   constexpr int G = D / 8;  // lanes per row, 8 elements each
@@ -202,7 +227,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
   const int i = (int)(prow - bh * npad);
   const bool live = bh < bh_count && i < n;
   const int64_t trow = live ? lay.tbase((int)bh) + (int64_t)i * lay.rs : 0;
-  const int64_t row = live ? lay.gbase((int)bh) + (int64_t)i * lay.gs : 0;
   float s = 0.0f;
   if (live) {
     const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + trow + 8 * g);
@@ -212,12 +236,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
   }
 #pragma unroll
   for (int off = G / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (bh < bh_count && g == 0) {
-    float* blk = rowv + bh * 3 * npad;
-    blk[i] = live ? (c[row] - lse[row]) * kLog2e : kNegInfB;
-    blk[npad + i] = live ? s : 0.0f;
-    blk[2 * npad + i] = live ? c[row] * kLog2e : INFINITY;
-  }
+  if (live && g == 0) rowv[bh * 3 * npad + npad + i] = s;
 }
 
 // Direct-to-LDS loads of a tile of ROWS rows of D bf16 (global rows from `row0` of the head) into
@@ -255,9 +274,9 @@ template <int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, const bf16* __restrict__ q,
                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
                                              const bf16* __restrict__ dout, const float* __restrict__ rowv,
-                                             bf16* __restrict__ dk, bf16* __restrict__ dv,
-                                             float* __restrict__ colsum_out, int n, int npad, float scale,
-                                             const BwdLayout& lay) {
+                                             const double* __restrict__ cb, bf16* __restrict__ dk,
+                                             bf16* __restrict__ dv, float* __restrict__ colsum_out, int n, int npad,
+                                             int ncb, float scale, const BwdLayout& lay) {
   constexpr int KK = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -292,8 +311,11 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
       vreg[kk] = *reinterpret_cast<const bf16x8*>(v + tb + (int64_t)key * rs + 16 * kk + 8 * hi);
     }
   }
-  // c_j log2 e (+inf past n: every score of the key is then -inf, so P and dS are 0)
+  // cq_j log2 e (+inf past n: every score of the key is then -inf, so P and dS are 0), and the
+  // start C of the wave's 32-key block; each query tile adds its own block difference
   const float bkey = key < n ? blk[2 * npad + key] : INFINITY;
+  const double* cbh = cb + bh * (size_t)ncb;
+  const double ckey = cbh[(key0 >> 5) + wave];
 
   // q and dO tiles (and the tile's 32 a_i, lanes 0..31 of wave 0, and 32 D_i, lanes 32..63)
   const TileLoader<D, kBQ> tl(wave, lane, rs);
@@ -349,6 +371,7 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
 
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
   float colsum1 = 0.0f;
+  double cq_t = cbh[qt0];  // block start of the query tile being processed (32 queries = one block)
   // One step.  HN: there is a next tile; MASK: the tile may hold keys past its queries (causal);
   // BC: the tile's LDS buffer when known at compile time (t % 3), else -1.
   auto step = [&](auto hn, auto mk, auto bc, int t, f32x16& s, f32x16& dp) {
@@ -365,6 +388,9 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
     }
     const bf16* tq = lds.q[buf];
     const bf16* tdo = lds.dout[buf];
+    // the key's bias term with this tile's block difference: c_i - c_j = a-part + (C_q - C_k) - cq_j
+    const float bkt = bkey - (float)((cq_t - ckey) * kLog2ed);
+    if constexpr (HN) cq_t = cbh[qt0 + t + 1];
     const float* arow = &lds.rowv[buf][0];
     const float* drow = &lds.rowv[buf][kBQ];
     // score operands of tile t + 1: slot i is S (i even) or dP (i odd) for k-step i / 2
@@ -403,7 +429,7 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
 #pragma unroll
       for (int r = i * EQ; r < (i + 1) * EQ; ++r) {
         const int g = r >> 2, e = r & 3;
-        float p = exp2_hw(fmaf(s[r], scale_log2, a4[g][e]) - bkey);
+        float p = exp2_hw(fmaf(s[r], scale_log2, a4[g][e]) - bkt);
         if (MASK && key > q0 + 8 * g + 4 * hi + e) p = 0.0f;
         s[r] = p;
         dp[r] = p * (dp[r] - d4[g][e]);
@@ -421,16 +447,19 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
     }
     // dV^T += dO^T P, dK^T += Q^T dS (K of these MFMAs runs over the tile's 32 queries); slot j:
     // query half u = j / (2 DB), dim block db, dV (even) or dK (odd).  The column sums of dS are
-    // taken over the same bf16 values the MFMAs use.
+    // taken over the fp32 values without the mask, over the bf16 values the MFMAs use with it.
+    if constexpr (!CAUSAL) colsum += tree_sum16(dp);
     const bf16x8 pb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
     const bf16x8 sb[2] = {acc_operand(dp, 0), acc_operand(dp, 1)};
+    if constexpr (CAUSAL) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const bf16x2 pr = {sb[u][2 * w], sb[u][2 * w + 1]};
-        if (w & 1) colsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, colsum1, false);
-        else colsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, colsum, false);
+        for (int w = 0; w < 4; ++w) {
+          const bf16x2 pr = {sb[u][2 * w], sb[u][2 * w + 1]};
+          if (w & 1) colsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, colsum1, false);
+          else colsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, colsum, false);
+        }
       }
     }
     auto tread = [&](int j) -> bf16x8 {
@@ -502,13 +531,16 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
   }
 }
 
-// Query-stationary part (dQ, row sums of dS) for query block qb of head bh.
-template <int D, bool CAUSAL>
+// Query-stationary part (dQ, row sums of dS) for query block qb of head bh.  DPASS: the D pass
+// instead -- with D_i = 0 the row sums of dS are sum_j P_ij dP_ij, written to dout_d[qi] (the D
+// slot of the row vectors); no dQ.
+template <int D, bool CAUSAL, bool DPASS = false>
 __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, const bf16* __restrict__ q,
                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
                                              const bf16* __restrict__ dout, const float* __restrict__ rowv,
-                                             bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
-                                             float scale, const BwdLayout& lay) {
+                                             const double* __restrict__ cb, bf16* __restrict__ dq,
+                                             float* __restrict__ rowsum_out, float* __restrict__ dout_d, int n,
+                                             int npad, int ncb, float scale, const BwdLayout& lay) {
   constexpr int KK = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -536,8 +568,12 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
       dreg[kk] = *reinterpret_cast<const bf16x8*>(dout + tb + (int64_t)qi * rs + 16 * kk + 8 * hi);
     }
   }
-  const float aq = qi < n ? blk[qi] : kNegInfB;     // (c_i - lse_i) log2 e; no weight past n
-  const float dq_i = qi < n ? blk[npad + qi] : 0.0f;  // D_i
+  const float aq = qi < n ? blk[qi] : kNegInfB;     // (cq_i - lse_i) log2 e; no weight past n
+  const float dq_i = (qi < n && !DPASS) ? blk[npad + qi] : 0.0f;  // D_i
+  // start C of the wave's 32-query block; each 32-key block adds its own block difference
+  const double* cbh = cb + bh * (size_t)ncb;
+  const double cqw = cbh[qw0 >> 5];
+  double ck_b = cbh[0];  // block start of the 32-key block being processed
 
   const TileLoader<D, kKT> tl(wave, lane, rs);
   auto load_tile = [&](int k0, int buf) {
@@ -598,6 +634,8 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
       }
     }
     const int key0 = b * 32;
+    const float aqb = aq + (float)((cqw - ck_b) * kLog2ed);  // the row term with this block's difference
+    if constexpr (HN) ck_b = cbh[b + 1];
     const float* clb = &lds.cl[buf][32 * kb];
     bf16x8 aop[NQ];
     f32x4 c4[4];
@@ -617,7 +655,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
 #pragma unroll
       for (int r = i * EQ; r < (i + 1) * EQ; ++r) {
         const int g = r >> 2, e = r & 3;
-        float p = exp2_hw(fmaf(s[r], scale_log2, aq) - c4[g][e]);
+        float p = exp2_hw(fmaf(s[r], scale_log2, aqb) - c4[g][e]);
         if (MASK && key0 + 8 * g + 4 * hi + e > qi) p = 0.0f;
         s[r] = p * (dp[r] - dq_i);
       }
@@ -629,31 +667,36 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // dQ += dS K: A = dS^T (queries as M, keys as K), B = K read transposed; the row sums of dS
-    // are taken over the same bf16 values
-    const bf16x8 sb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
+    // dQ += dS K: A = dS^T (queries as M, keys as K), B = K read transposed.  The row sums of dS
+    // are taken over the fp32 values without the mask, over the bf16 values the MFMAs use with it.
+    if constexpr (!CAUSAL) rsum0 += tree_sum16(s);
+    if constexpr (!DPASS) {
+      const bf16x8 sb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
+      if constexpr (CAUSAL) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const bf16x2 pr = {sb[u][2 * w], sb[u][2 * w + 1]};
-        if (w & 1) rsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum1, false);
-        else rsum0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum0, false);
+          for (int w = 0; w < 4; ++w) {
+            const bf16x2 pr = {sb[u][2 * w], sb[u][2 * w + 1]};
+            if (w & 1) rsum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum1, false);
+            else rsum0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum0, false);
+          }
+        }
       }
-    }
-    const bf16* tk = lds.k[buf];
-    auto tread = [&](int j) -> bf16x8 {
-      return transposed_operand<D>(tk, 32 * kb + 16 * (j / DB), 32 * (j % DB), lane);
-    };
-    bf16x8 top[NP];
+      const bf16* tk = lds.k[buf];
+      auto tread = [&](int j) -> bf16x8 {
+        return transposed_operand<D>(tk, 32 * kb + 16 * (j / DB), 32 * (j % DB), lane);
+      };
+      bf16x8 top[NP];
 #pragma unroll
-    for (int j = 0; j < PFP; ++j) top[j] = tread(j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[j / DB], top[j], acc[j % DB], 0, 0, 0);
-      if (j + PFP < NP) top[j + PFP] = tread(j + PFP);
+      for (int j = 0; j < PFP; ++j) top[j] = tread(j);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[j / DB], top[j], acc[j % DB], 0, 0, 0);
+        if (j + PFP < NP) top[j + PFP] = tread(j + PFP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     s = s2;
     dp = dp2;
@@ -684,6 +727,12 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
   for (; b + 1 < nblk; ++b) step(T_{}, T_{}, DYN{}, b, s, dp);
   step(F_{}, T_{}, DYN{}, nblk - 1, s, dp);
 
+  // the two lane halves hold the two halves of each 32-key block
+  const float rsum = pair32_sum(rsum0 + rsum1);
+  if constexpr (DPASS) {
+    if (hi == 0 && qi < n) dout_d[bh * 3 * (size_t)npad + npad + qi] = rsum;
+    return;
+  }
   // dq = scale dQ: lane = dim 32db + l32, register r = query qw0 + 8(r/4) + 4hi + r%4
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -693,32 +742,40 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
       if (qr < n) dq[tb + (int64_t)qr * rs + 32 * db + l32] = (bf16)(acc[db][r] * scale);
     }
   }
-  // the two lane halves hold the two halves of each 32-key block
-  const float rsum = pair32_sum(rsum0 + rsum1);
   if (hi == 0 && qi < n) rowsum_out[base + qi] = rsum;
 }
 
 // The two parts as kernels of their own (large grids) ...
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_kv_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 && CAUSAL ? 2 : 1))) void bwd_kv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
-    const float* __restrict__ rowv, bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ colsum_out,
-    int n, int npad, float scale, BwdLayout lay) {
+    const float* __restrict__ rowv, const double* __restrict__ cb, bf16* __restrict__ dk, bf16* __restrict__ dv,
+    float* __restrict__ colsum_out, int n, int npad, int ncb, float scale, BwdLayout lay) {
   __shared__ KvLds<D> lds;
   // heads fastest: the key blocks of one head share its q / dO in L2; causal work falls with kb
-  bwd_kv_block<D, CAUSAL>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale,
-                          lay);
+  bwd_kv_block<D, CAUSAL>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, cb, dk, dv, colsum_out, n, npad, ncb,
+                          scale, lay);
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 && CAUSAL ? 2 : 1))) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
-    const float* __restrict__ rowv, bf16* __restrict__ dq, float* __restrict__ rowsum_out, int n, int npad,
-    float scale, BwdLayout lay) {
+    const float* __restrict__ rowv, const double* __restrict__ cb, bf16* __restrict__ dq,
+    float* __restrict__ rowsum_out, int n, int npad, int ncb, float scale, BwdLayout lay) {
   __shared__ DqLds<D> lds;
   // the longest causal blocks (the last queries) start first
-  bwd_dq_block<D, CAUSAL>(lds, blockIdx.x, (int)(gridDim.y - 1 - blockIdx.y), q, k, v, dout, rowv, dq, rowsum_out, n,
-                          npad, scale, lay);
+  bwd_dq_block<D, CAUSAL>(lds, blockIdx.x, (int)(gridDim.y - 1 - blockIdx.y), q, k, v, dout, rowv, cb, dq, rowsum_out,
+                          nullptr, n, npad, ncb, scale, lay);
+}
+
+// The D pass of the unmasked mode: D_i = sum_j P_ij dP_ij into the row vectors' D slot.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dpass_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
+    float* __restrict__ rowv, const double* __restrict__ cb, int n, int npad, int ncb, float scale, BwdLayout lay) {
+  __shared__ DqLds<D> lds;
+  bwd_dq_block<D, false, true>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, cb, nullptr, nullptr, rowv, n,
+                               npad, ncb, scale, lay);
 }
 
 // ... and both in one launch for small grids, where each fills the other's tail.  blockIdx.x is the head (the
@@ -726,10 +783,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 // 2j + 1 is query block nb - 1 - j, so both kinds are issued heaviest first (causal work falls
 // with the key block and grows with the query block).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void bwd_main_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 && CAUSAL ? 2 : 1))) void bwd_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
-    const float* __restrict__ rowv, bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ rowsum_out, float* __restrict__ colsum_out, int n, int npad, float scale, BwdLayout lay) {
+    const float* __restrict__ rowv, const double* __restrict__ cb, bf16* __restrict__ dq, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, float* __restrict__ rowsum_out, float* __restrict__ colsum_out, int n, int npad, int ncb,
+    float scale, BwdLayout lay) {
   __shared__ union {
     KvLds<D> kv;
     DqLds<D> dq;
@@ -737,82 +795,104 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   const size_t bh = blockIdx.x;
   const int j = (int)(blockIdx.y >> 1);
   if ((blockIdx.y & 1) == 0)
-    bwd_kv_block<D, CAUSAL>(lds.kv, bh, j, q, k, v, dout, rowv, dk, dv, colsum_out, n, npad, scale, lay);
+    bwd_kv_block<D, CAUSAL>(lds.kv, bh, j, q, k, v, dout, rowv, cb, dk, dv, colsum_out, n, npad, ncb, scale, lay);
   else
-    bwd_dq_block<D, CAUSAL>(lds.dq, bh, (int)(gridDim.y >> 1) - 1 - j, q, k, v, dout, rowv, dq, rowsum_out, n, npad,
-                            scale, lay);
+    bwd_dq_block<D, CAUSAL>(lds.dq, bh, (int)(gridDim.y >> 1) - 1 - j, q, k, v, dout, rowv, cb, dq, rowsum_out,
+                            nullptr, n, npad, ncb, scale, lay);
 }
 
 int bwd_npad(int n) { return (n + kPad - 1) / kPad * kPad; }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_c(const void* q, const void* k, const void* v, const void* dout, const float* rowv, void* dq,
-                        void* dk, void* dv, float* rsum, float* csum, int64_t bh, int n, int npad, float scale,
-                        const BwdLayout& lay, hipStream_t stream) {
+hipError_t launch_bwd_c(const void* q, const void* k, const void* v, const void* dout, const float* rowv,
+                        const double* cb, void* dq, void* dk, void* dv, float* rsum, float* csum, int64_t bh, int n,
+                        int npad, int ncb, float scale, const BwdLayout& lay, hipStream_t stream) {
   static_assert(kBK == kQB, "one key block and one query block per block pair");
   const int nb = (n + kBK - 1) / kBK;
   if (2 * bh * nb <= kFuseMaxBlocks) {
     hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3((unsigned)bh, (unsigned)(2 * nb)), dim3(kBwdThreads), 0,
-                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, (bf16*)dq,
-                       (bf16*)dk, (bf16*)dv, rsum, csum, n, npad, scale, lay);
+                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, cb, (bf16*)dq,
+                       (bf16*)dk, (bf16*)dv, rsum, csum, n, npad, ncb, scale, lay);
   } else {
     const dim3 grid((unsigned)bh, (unsigned)nb);
     hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, (bf16*)dk, (bf16*)dv, csum, n, npad,
-                       scale, lay);
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, cb, (bf16*)dk, (bf16*)dv, csum, n,
+                       npad, ncb, scale, lay);
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, (bf16*)dq, rsum, n, npad, scale, lay);
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, cb, (bf16*)dq, rsum, n, npad, ncb,
+                       scale, lay);
   }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf, float* ws,
+                        const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf, void* ws,
                         int64_t b, int64_t h, int n, float scale, bool causal, bool token_major,
                         hipStream_t stream) {
   const int64_t bh = b * h;
   const int npad = bwd_npad(n);
+  const int ncb = bwd_gate_blocks(n);
   // {bs, hs, rs, gbs, ghs, gs, nh}
   const BwdLayout lay = token_major
                             ? BwdLayout{(int64_t)n * h * D, (int64_t)D, (int)(h * D), (int64_t)n * h, 1, (int)h, (int)h}
                             : BwdLayout{h * n * (int64_t)D, (int64_t)n * D, D, h * (int64_t)n, (int64_t)n, 1, (int)h};
-  // workspace: row vectors [bh][3][npad], row sums [bh][n], column sums [bh][n] (fp32)
-  float* rowv = ws;
-  float* rsum = rowv + bh * 3 * npad;
-  float* csum = rsum + bh * n;
-  constexpr int RPB = kBwdThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((bh * npad + RPB - 1) / RPB)), dim3(kBwdThreads), 0, stream,
-                     (const bf16*)o, (const bf16*)dout, lse, c, rowv, bh, n, npad, lay);
-  hipError_t e = hipGetLastError();
+  const BwdWorkspace w = bwd_workspace(ws, bh, n, npad);
+  hipError_t e = launch_bwd_gate_rows(logf, lse, w.rowv, w.cb, bh, n, npad, (int)h, token_major, stream);
   if (e != hipSuccess) return e;
-  e = causal ? launch_bwd_c<D, true>(q, k, v, dout, rowv, dq, dk, dv, rsum, csum, bh, n, npad, scale, lay, stream)
-             : launch_bwd_c<D, false>(q, k, v, dout, rowv, dq, dk, dv, rsum, csum, bh, n, npad, scale, lay, stream);
+  if (causal) {
+    constexpr int RPB = kBwdThreads / (D / 8);
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((bh * npad + RPB - 1) / RPB)), dim3(kBwdThreads), 0,
+                       stream, (const bf16*)o, (const bf16*)dout, w.rowv, bh, n, npad, lay);
+  } else {
+    hipLaunchKernelGGL((bwd_dpass_kernel<D>), dim3((unsigned)bh, (unsigned)((n + kQB - 1) / kQB)), dim3(kBwdThreads),
+                       0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.rowv,
+                       (const double*)w.cb, n, npad, ncb, scale, lay);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = causal ? launch_bwd_c<D, true>(q, k, v, dout, w.rowv, w.cb, dq, dk, dv, w.rsum, w.csum, bh, n, npad, ncb, scale,
+                                     lay, stream)
+             : launch_bwd_c<D, false>(q, k, v, dout, w.rowv, w.cb, dq, dk, dv, w.rsum, w.csum, bh, n, npad, ncb, scale,
+                                      lay, stream);
   if (e != hipSuccess) return e;
   // dlog f_t = sum_{i >= t} (rowsum_i - colsum_i), written in the gates' layout
-  return launch_suffix_sum(rsum, csum, dlogf, bh, n, (int)h, token_major, stream);
+  return launch_suffix_sum(w.rsum, w.csum, dlogf, bh, n, (int)h, token_major, stream);
 }
 
 }  // namespace
 
+// workspace: row vectors [bh][3][npad] (fp32), gate block starts [bh][ncb] (fp64), row sums and
+// column sums of dS and the fp32 path's lse normalisation [bh][n] each (fp32)
+BwdWorkspace bwd_workspace(void* ws, int64_t bh, int n, int npad) {
+  BwdWorkspace w;
+  w.rowv = static_cast<float*>(ws);
+  w.cb = reinterpret_cast<double*>(w.rowv + bh * 3 * (int64_t)npad);
+  w.rsum = reinterpret_cast<float*>(w.cb + bh * (int64_t)bwd_gate_blocks(n));
+  w.csum = w.rsum + bh * (int64_t)n;
+  w.corr = w.csum + bh * (int64_t)n;
+  return w;
+}
+
 size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d) {
   (void)d;
-  return (size_t)bh * (3 * (size_t)bwd_npad(n) + 2 * (size_t)n) * sizeof(float);
+  return (size_t)bh * ((3 * (size_t)bwd_npad(n) + 3 * (size_t)n) * sizeof(float) +
+                       (size_t)bwd_gate_blocks(n) * sizeof(double));
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
-                           float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                           const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
+                           void* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
                            bool token_major, hipStream_t stream) {
   switch (d) {
     case 32:
-      return launch_bwd_t<32>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+      return launch_bwd_t<32>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
                               token_major, stream);
     case 64:
-      return launch_bwd_t<64>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+      return launch_bwd_t<64>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
                               token_major, stream);
     case 128:
-      return launch_bwd_t<128>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+      return launch_bwd_t<128>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
                                token_major, stream);
   }
   return hipErrorInvalidValue;

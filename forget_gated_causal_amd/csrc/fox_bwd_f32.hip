@@ -7,7 +7,18 @@
 //   dq = scale dS k;  dk = scale dS^T q;  dlog f_t = sum_{i >= t} (rowsum(dS)_i - colsum(dS)_i)
 // The fp32 path serves the fp32 forward's (small, correctness-sized) workloads, so it runs on the
 // vector ALU in plain tiles rather than on MFMA:
-//  * bwd_f32_pre_kernel: D_i and the padded per-head row vectors [a | D | cl] (as fox_bwd.hip).
+//  * The gate-rows kernel (fox_scan.hip) writes the row vectors' a and cl from the in-block parts of
+//    the gate prefix sums, plus the fp64 block starts C_b (as for the bf16 path); each score's bias
+//    is (cq_i - cq_j) + (C_b(i) - C_b(j)), the block difference formed in fp64 once per tile.
+//    The row's part of each exponent, c_i - lse_i relative to the key block's start C_b(j), is
+//    formed in fp64 per (row, key block) and rounded once: it is as small as the biases that carry
+//    weight, while c_i and lse_i alone can be thousands (without the mask, where later keys are
+//    weighted up, lse_i follows c_i of the heaviest keys).
+//  * In the unmasked mode the lse the backward is given (fp32, |lse| possibly in the thousands) is
+//    itself only good to half an ulp of that size: a normalisation pass (bwd_f32_dq_kernel with
+//    ZPASS) sums P_ij over each row with it and keeps corr_i = log2 sum_j P_ij, which the main
+//    kernels subtract, so each row of P sums to 1 to fp64 rounding of the fp32 terms.
+//  * bwd_f32_pre_kernel: D_i = dO_i . O_i into the row vectors.
 //  * bwd_f32_kv_kernel<D, CAUSAL>: one 256-thread workgroup per (64-key block, head); the block's K
 //    and V rows sit in LDS, 32-query tiles of q and dO stream through it.  Per tile, thread t forms
 //    P and dS for key t % 64 and queries 8 (t / 64) .. +7 (phase A, into LDS), then accumulates
@@ -44,12 +55,11 @@ struct F32Layout {
 
 int f32_npad(int n) { return (n + kF32Pad - 1) / kF32Pad * kF32Pad; }
 
-// One thread per (head, padded row): D_i = dO_i . O_i and the row vectors of the block.
+// One thread per (head, row): D_i = dO_i . O_i into the row vectors' D slot (the gate-rows kernel
+// writes the rest, padding included).
 template <int D>
 __global__ __launch_bounds__(kF32Threads) void bwd_f32_pre_kernel(const float* __restrict__ o,
                                                                   const float* __restrict__ dout,
-                                                                  const float* __restrict__ lse,
-                                                                  const float* __restrict__ c,
                                                                   float* __restrict__ rowv, int64_t bh_count, int n,
                                                                   int npad, F32Layout lay) {
   const int64_t prow = (int64_t)blockIdx.x * kF32Threads + threadIdx.x;
@@ -57,21 +67,13 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_pre_kernel(const float* _
   if (bh >= bh_count) return;
   const int i = (int)(prow - bh * npad);
   float* blk = rowv + bh * 3 * npad;
-  if (i >= n) {
-    blk[i] = -INFINITY;
-    blk[npad + i] = 0.0f;
-    blk[2 * npad + i] = INFINITY;
-    return;
-  }
+  if (i >= n) return;
   const float* orow = o + lay.tbase((int)bh) + (int64_t)i * lay.rs;
   const float* drow = dout + lay.tbase((int)bh) + (int64_t)i * lay.rs;
   float s = 0.0f;
 #pragma unroll 8
   for (int e = 0; e < D; ++e) s = fmaf(orow[e], drow[e], s);
-  const int64_t g = lay.gbase((int)bh) + (int64_t)i * lay.gs;
-  blk[i] = (c[g] - lse[g]) * kLog2e;
   blk[npad + i] = s;
-  blk[2 * npad + i] = c[g] * kLog2e;
 }
 
 // Copy `rows` rows of D floats (global row stride rs) into an LDS tile of row stride D + 1;
@@ -101,13 +103,15 @@ __device__ __forceinline__ float f32_dot(const float* a, const float* b) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32Threads) void bwd_f32_kv_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ dout, const float* __restrict__ rowv, float* __restrict__ dk, float* __restrict__ dv,
-    float* __restrict__ colsum_out, int n, int npad, float scale, F32Layout lay) {
+    const float* __restrict__ dout, const float* __restrict__ rowv, const double* __restrict__ cb,
+    const float* __restrict__ lse, const float* __restrict__ corr, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ colsum_out, int n, int npad, int ncb, float scale, F32Layout lay) {
   constexpr int DP = D + 1, DC = D / 4;
+  static_assert(kF32Blk == 2 * kF32Tile && kF32Tile == 32, "two 32-position gate blocks of keys per workgroup");
   __shared__ float ks[kF32Blk * DP], vs[kF32Blk * DP];
   __shared__ float qs[kF32Tile * DP], ds_[kF32Tile * DP];
   __shared__ float pt[kF32Blk * (kF32Tile + 1)], st[kF32Blk * (kF32Tile + 1)];
-  __shared__ float arow[kF32Tile], drow[kF32Tile], csum[4][kF32Blk];
+  __shared__ float arow[2][kF32Tile], drow[kF32Tile], csum[4][kF32Blk];
   const int bh = blockIdx.x, key0 = blockIdx.y * kF32Blk;
   const int tid = threadIdx.x, jl = tid & 63, g = tid >> 6;
   const int j = key0 + jl;
@@ -117,6 +121,8 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_kv_kernel(
   f32_stage<D>(ks, k + tb + (int64_t)key0 * lay.rs, kF32Blk, n - key0, lay.rs);
   f32_stage<D>(vs, v + tb + (int64_t)key0 * lay.rs, kF32Blk, n - key0, lay.rs);
   const float clj = j < n ? blk[2 * npad + j] : INFINITY;
+  const double* cbh = cb + (int64_t)bh * ncb;
+  const int64_t gb = lay.gbase(bh);
   float accv[DC], acck[DC];
 #pragma unroll
   for (int x = 0; x < DC; ++x) accv[x] = acck[x] = 0.0f;
@@ -126,11 +132,22 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_kv_kernel(
     __syncthreads();  // the previous tile's phase B is done with qs, ds_, pt, st
     f32_stage<D>(qs, q + tb + (int64_t)q0 * lay.rs, kF32Tile, n - q0, lay.rs);
     f32_stage<D>(ds_, dout + tb + (int64_t)q0 * lay.rs, kF32Tile, n - q0, lay.rs);
-    if (tid < kF32Tile) {
-      arow[tid] = q0 + tid < n ? blk[q0 + tid] : -INFINITY;
-      drow[tid] = q0 + tid < n ? blk[npad + q0 + tid] : 0.0f;
+    if (tid < 2 * kF32Tile) {
+      // row term of query i against key block kb: (c_i - C_kb - lse_i) log2 e - corr_i, in fp64
+      const int kb = tid / kF32Tile, il = tid % kF32Tile, i = q0 + il;
+      float a = -INFINITY;
+      if (i < n) {
+        const double ri = (double)blk[2 * npad + i] - (double)lse[gb + (int64_t)i * lay.gs] * kLog2ed -
+                          (corr ? (double)corr[(int64_t)bh * n + i] : 0.0);
+        a = (float)(ri + (cbh[q0 >> 5] - cbh[(key0 >> 5) + kb]) * kLog2ed);
+      }
+      arow[kb][il] = a;
+    } else if (tid < 3 * kF32Tile) {
+      const int il = tid - 2 * kF32Tile;
+      drow[il] = q0 + il < n ? blk[npad + q0 + il] : 0.0f;
     }
     __syncthreads();
+    const float* arw = arow[jl / kF32Tile];  // this key's block
     // phase A: P and dS for key j and queries q0 + 8g .. + 7
 #pragma unroll 1
     for (int u = 0; u < 8; ++u) {
@@ -139,7 +156,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_kv_kernel(
       if (j < n && i < n && (!CAUSAL || j <= i)) {
         const float s = f32_dot<D>(&ks[jl * DP], &qs[il * DP]);
         const float dp = f32_dot<D>(&vs[jl * DP], &ds_[il * DP]);
-        p = exp2_hw(fmaf(s, scale_log2, arow[il]) - clj);
+        p = exp2_hw(fmaf(s, scale_log2, arw[il]) - clj);
         dsv = p * (dp - drow[il]);
       }
       pt[jl * (kF32Tile + 1) + il] = p;
@@ -172,16 +189,21 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_kv_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+// ZPASS: the normalisation pass instead -- per row, corr_i = log2 sum_j P_ij with the given lse
+// (written to corr_out); no dP, no dQ.
+template <int D, bool CAUSAL, bool ZPASS = false>
 __global__ __launch_bounds__(kF32Threads) void bwd_f32_dq_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ dout, const float* __restrict__ rowv, float* __restrict__ dq,
-    float* __restrict__ rowsum_out, int n, int npad, float scale, F32Layout lay) {
+    const float* __restrict__ dout, const float* __restrict__ rowv, const double* __restrict__ cb,
+    const float* __restrict__ lse, const float* __restrict__ corr, float* __restrict__ dq,
+    float* __restrict__ rowsum_out, float* __restrict__ corr_out, int n, int npad, int ncb, float scale,
+    F32Layout lay) {
   constexpr int DP = D + 1, DC = D / 4;
   __shared__ float qs[kF32Blk * DP], ds_[kF32Blk * DP];
   __shared__ float ks[kF32Tile * DP], vs[kF32Tile * DP];
   __shared__ float st[kF32Blk * (kF32Tile + 1)];
   __shared__ float clt[kF32Tile], rsum[4][kF32Blk];
+  __shared__ double zsum[ZPASS ? 4 : 1][kF32Blk];
   const int bh = blockIdx.x, qblk0 = blockIdx.y * kF32Blk;
   const int tid = threadIdx.x, il = tid & 63, g = tid >> 6;
   const int i = qblk0 + il;
@@ -190,8 +212,15 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_dq_kernel(
   const float scale_log2 = scale * kLog2e;
   f32_stage<D>(qs, q + tb + (int64_t)qblk0 * lay.rs, kF32Blk, n - qblk0, lay.rs);
   f32_stage<D>(ds_, dout + tb + (int64_t)qblk0 * lay.rs, kF32Blk, n - qblk0, lay.rs);
-  const float ai = i < n ? blk[i] : -INFINITY;
   const float di = i < n ? blk[npad + i] : 0.0f;
+  const double* cbh = cb + (int64_t)bh * ncb;
+  const double cqi = cbh[i >> 5];  // start of the query's 32-position block
+  // row term (c_i - C_b(i) - lse_i) log2 e - corr_i in fp64; each key tile adds its block difference
+  const double ri = i < n ? (double)blk[2 * npad + i] -
+                                (double)lse[lay.gbase(bh) + (int64_t)i * lay.gs] * kLog2ed -
+                                (corr ? (double)corr[(int64_t)bh * n + i] : 0.0)
+                          : 0.0;
+  double zs = 0.0;
   float acc[DC];
 #pragma unroll
   for (int x = 0; x < DC; ++x) acc[x] = 0.0f;
@@ -203,26 +232,41 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_dq_kernel(
     f32_stage<D>(vs, v + tb + (int64_t)k0 * lay.rs, kF32Tile, n - k0, lay.rs);
     if (tid < kF32Tile) clt[tid] = k0 + tid < n ? blk[2 * npad + k0 + tid] : INFINITY;
     __syncthreads();
+    // the row term with the tile's block difference (the tile is one 32-position block)
+    const float ait = i < n ? (float)(ri + (cqi - cbh[k0 >> 5]) * kLog2ed) : -INFINITY;
 #pragma unroll 1
     for (int u = 0; u < 8; ++u) {
       const int jl = 8 * g + u, j = k0 + jl;
       float dsv = 0.0f;
       if (j < n && i < n && (!CAUSAL || j <= i)) {
         const float s = f32_dot<D>(&qs[il * DP], &ks[jl * DP]);
-        const float dp = f32_dot<D>(&ds_[il * DP], &vs[jl * DP]);
-        const float p = exp2_hw(fmaf(s, scale_log2, ai) - clt[jl]);
-        dsv = p * (dp - di);
+        const float p = exp2_hw(fmaf(s, scale_log2, ait) - clt[jl]);
+        if constexpr (ZPASS) {
+          zs += (double)p;
+        } else {
+          const float dp = f32_dot<D>(&ds_[il * DP], &vs[jl * DP]);
+          dsv = p * (dp - di);
+        }
       }
-      st[il * (kF32Tile + 1) + jl] = dsv;
-      rs += dsv;
+      if constexpr (!ZPASS) {
+        st[il * (kF32Tile + 1) + jl] = dsv;
+        rs += dsv;
+      }
     }
     __syncthreads();
+    if constexpr (ZPASS) continue;
 #pragma unroll 1
     for (int jl = 0; jl < kF32Tile; ++jl) {
       const float dsv = st[il * (kF32Tile + 1) + jl];
 #pragma unroll
       for (int x = 0; x < DC; ++x) acc[x] = fmaf(dsv, ks[jl * DP + DC * g + x], acc[x]);
     }
+  }
+  if constexpr (ZPASS) {
+    zsum[g][il] = zs;
+    __syncthreads();
+    if (i < n && g == 0) corr_out[(int64_t)bh * n + i] = (float)log2((zsum[0][il] + zsum[1][il]) + (zsum[2][il] + zsum[3][il]));
+    return;
   }
   rsum[g][il] = rs;
   __syncthreads();
@@ -236,56 +280,61 @@ __global__ __launch_bounds__(kF32Threads) void bwd_f32_dq_kernel(
 
 template <int D>
 hipError_t launch_bwd_f32_t(const float* q, const float* k, const float* v, const float* o, const float* dout,
-                            const float* lse, const float* c, float* dq, float* dk, float* dv, float* dlogf,
-                            float* ws, int64_t b, int64_t h, int n, float scale, bool causal, bool token_major,
+                            const float* lse, const float* logf, float* dq, float* dk, float* dv, float* dlogf,
+                            void* ws, int64_t b, int64_t h, int n, float scale, bool causal, bool token_major,
                             hipStream_t stream) {
   const int64_t bh = b * h;
   const int npad = f32_npad(n);
+  const int ncb = bwd_gate_blocks(n);
   // {bs, hs, rs, gbs, ghs, gs, nh}
   const F32Layout lay = token_major
                             ? F32Layout{(int64_t)n * h * D, (int64_t)D, (int)(h * D), (int64_t)n * h, 1, (int)h, (int)h}
                             : F32Layout{h * n * (int64_t)D, (int64_t)n * D, D, h * (int64_t)n, (int64_t)n, 1, (int)h};
-  // workspace: row vectors [bh][3][npad], row sums [bh][n], column sums [bh][n]
-  float* rowv = ws;
-  float* rsum = rowv + bh * 3 * npad;
-  float* csum = rsum + bh * n;
+  const BwdWorkspace w = bwd_workspace(ws, bh, n, npad);
+  hipError_t e = launch_bwd_gate_rows(logf, lse, w.rowv, w.cb, bh, n, npad, (int)h, token_major, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_f32_pre_kernel<D>), dim3((unsigned)((bh * npad + kF32Threads - 1) / kF32Threads)),
-                     dim3(kF32Threads), 0, stream, o, dout, lse, c, rowv, bh, n, npad, lay);
-  hipError_t e = hipGetLastError();
+                     dim3(kF32Threads), 0, stream, o, dout, w.rowv, bh, n, npad, lay);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)bh, (unsigned)((n + kF32Blk - 1) / kF32Blk));
-  if (causal) {
-    hipLaunchKernelGGL((bwd_f32_kv_kernel<D, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
-                       (const float*)rowv, dk, dv, csum, n, npad, scale, lay);
-    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
-                       (const float*)rowv, dq, rsum, n, npad, scale, lay);
+  const float* rowv = w.rowv;
+  const double* cb = w.cb;
+  if (causal) {  // |lse| stays small with the mask: the given lse is used as it is
+    hipLaunchKernelGGL((bwd_f32_kv_kernel<D, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout, rowv, cb, lse,
+                       (const float*)nullptr, dk, dv, w.csum, n, npad, ncb, scale, lay);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout, rowv, cb, lse,
+                       (const float*)nullptr, dq, w.rsum, (float*)nullptr, n, npad, ncb, scale, lay);
   } else {
-    hipLaunchKernelGGL((bwd_f32_kv_kernel<D, false>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
-                       (const float*)rowv, dk, dv, csum, n, npad, scale, lay);
-    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout,
-                       (const float*)rowv, dq, rsum, n, npad, scale, lay);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false, true>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout, rowv,
+                       cb, lse, (const float*)nullptr, (float*)nullptr, (float*)nullptr, w.corr, n, npad, ncb, scale,
+                       lay);
+    hipLaunchKernelGGL((bwd_f32_kv_kernel<D, false>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout, rowv, cb,
+                       lse, (const float*)w.corr, dk, dv, w.csum, n, npad, ncb, scale, lay);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), grid, dim3(kF32Threads), 0, stream, q, k, v, dout, rowv, cb,
+                       lse, (const float*)w.corr, dq, w.rsum, (float*)nullptr, n, npad, ncb, scale, lay);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dlog f_t = sum_{i >= t} (rowsum_i - colsum_i), written in the gates' layout
-  return launch_suffix_sum(rsum, csum, dlogf, bh, n, (int)h, token_major, stream);
+  return launch_suffix_sum(w.rsum, w.csum, dlogf, bh, n, (int)h, token_major, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
-                               const float* lse, const float* c, float* dq, float* dk, float* dv, float* dlogf,
-                               float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                               const float* lse, const float* logf, float* dq, float* dk, float* dv, float* dlogf,
+                               void* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
                                bool token_major, hipStream_t stream) {
   switch (d) {
     case 32:
-      return launch_bwd_f32_t<32>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+      return launch_bwd_f32_t<32>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
                                   token_major, stream);
     case 64:
-      return launch_bwd_f32_t<64>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+      return launch_bwd_f32_t<64>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
                                   token_major, stream);
     case 128:
-      return launch_bwd_f32_t<128>(q, k, v, o, dout, lse, c, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
+      return launch_bwd_f32_t<128>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, causal,
                                    token_major, stream);
   }
   return hipErrorInvalidValue;

@@ -177,18 +177,20 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* p, uint32_t num_bytes) {
 // Direct-to-LDS buffer loads: lane l's bytes land at LDS address m0v + l * size.  Issued
 // through inline assembly so the compiler does not track them: the kernel waits for them
 // itself (s_waitcnt vmcnt with counts derived from its own issue order), which lets the
-// next tiles stay in flight across barriers and LDS reads of other stages.
+// next tiles stay in flight across barriers and LDS reads of other stages.  M0 is an input
+// operand: the compiler writes it (and knows it holds m0v) before each load; the s_nop is the
+// wait state an M0 write needs before an LDS-DMA instruction reads it.
 __device__ __forceinline__ void lds_dma16(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
-                   : "s"(m0v), "v"(voff), "s"(rsrc)
-                   : "memory", "m0");
+                   : "v"(voff), "s"(rsrc), "{m0}"(m0v)
+                   : "memory");
 }
 __device__ __forceinline__ void lds_dma4(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                    :
-                   : "s"(m0v), "v"(voff), "s"(rsrc)
-                   : "memory", "m0");
+                   : "v"(voff), "s"(rsrc), "{m0}"(m0v)
+                   : "memory");
 }
 
 // Per-lane byte offsets, inside a tile, of the 16-byte chunks this lane stages for K and V.
@@ -1026,7 +1028,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m = kNegInf, lsum = 0.0f;
+  // The row sum runs in fp64 over per-tile fp32 partial sums of 32 terms (a single fp32 running
+  // sum over thousands of keys drifts by more than the 1e-5 that lse must meet), and lse takes
+  // an fp64 logarithm.
+  float m = kNegInf;
+  double lsum = 0.0;
   double carry = 0.0, ri_row = 0.0;
   // Unmasked mode: the biases stay relative to the frame row n-1 (R_j - 0), where every row's
   // heaviest keys lie, so those scores are small and exactly rounded; R_i comes off in lse.
@@ -1095,24 +1101,26 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     }
     const float msub = (m == kNegInf) ? 0.0f : m;
 
+    float tsum[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_hw(sacc[b][r] - msub);
-        lsum += p;
+        tsum[r & 1] += p;
         const int key = 32 * b + 8 * (r / 4) + 4 * hi + (r % 4);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds.v[key * VS + 32 * db + l32], p, oacc[db], 0, 0, 0);
       }
     }
+    lsum += (double)tsum[0] + (double)tsum[1];
   }
 
   if (!active) return;
-  const float ltot = pair32_sum(lsum);
+  const double ltot = lsum + __shfl_xor(lsum, 32);
   if (my_row >= n) return;
-  const float inv = 1.0f / ltot;
+  const float inv = (float)(1.0 / ltot);
   float* orow = o + base + (size_t)my_row * rs;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -1128,7 +1136,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     const double ri = lds.rows.rowR[my_row - row0];
     const size_t idx = gbase + (size_t)my_row * gs;
     // causal scores already carry -R_i
-    if (lse) lse[idx] = (float)(((double)m + (double)log2f(ltot)) * kLn2d - (CAUSAL ? 0.0 : ri));
+    if (lse) lse[idx] = (float)(((double)m + log2(ltot)) * kLn2d - (CAUSAL ? 0.0 : ri));
     if (c_out) c_out[idx] = (float)(lds.rows.cref - ri);
   }
 }

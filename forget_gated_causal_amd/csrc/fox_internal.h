@@ -45,18 +45,36 @@ hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* v
                                     int nh, void* o, float* lse, float* ws, int64_t sh, int d, float scale,
                                     bool is_bf16, hipStream_t stream);
 
-// Backward pass (bf16): dq, dk, dv and dlog f from q, k, v, the forward's o, lse and c, and dO;
-// token_major as launch_attn_fwd.  The workspace holds bh*(3*npad + 2*n) floats (per-row vectors
-// over n padded to 64, row and column sums of dS).
+// The backward's gate terms (fox_scan.hip): per row, block starts C_b of the prefix sums of log f
+// (fp64, bwd_gate_blocks(n) per row, one per 32 positions up to n rounded up to 128) and, in the
+// row-vector block [a | D | cl] of 3 * npad floats, a_i = (cq_i - lse_i) log2 e and cl_i = cq_i
+// log2 e with cq_i = c_i - C_b(i), padded past n (a = -inf, D = 0, cl = +inf).  logf / lse are
+// [rows, n], or with token_major [rows / nh, n, nh].
+int bwd_gate_blocks(int n);
+hipError_t launch_bwd_gate_rows(const float* logf, const float* lse, float* rowv, double* cb, int64_t rows, int n,
+                                int npad, int nh, bool token_major, hipStream_t stream);
+
+// Backward pass (bf16): dq, dk, dv and dlog f from q, k, v, the forward's o and lse, dO and the
+// log gates; token_major as launch_attn_fwd.  Workspace: per-row vectors over n padded to 64,
+// block starts of the gate sums (fp64), row and column sums of dS (attn_bwd_workspace_bytes).
 size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
-                           float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                           const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
+                           void* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
                            bool token_major, hipStream_t stream);
 // The same on fp32 tensors (fp32 throughout; same workspace size and layouts).
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
-                               const float* lse, const float* c, float* dq, float* dk, float* dv, float* dlogf,
-                               float* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
+                               const float* lse, const float* logf, float* dq, float* dk, float* dv, float* dlogf,
+                               void* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,
                                bool token_major, hipStream_t stream);
+// Workspace carve-up shared by both backward paths.
+struct BwdWorkspace {
+  float* rowv;  // [bh][3][npad]
+  double* cb;   // [bh][bwd_gate_blocks(n)]
+  float* rsum;  // [bh][n]
+  float* csum;  // [bh][n]
+  float* corr;  // [bh][n]: the fp32 path's lse normalisation (unmasked mode)
+};
+BwdWorkspace bwd_workspace(void* ws, int64_t bh, int n, int npad);
 
 }  // namespace fox

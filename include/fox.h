@@ -156,8 +156,8 @@ fox_status_t fox_attn_fwd_pruned(const void* q, const void* k, const void* v, co
 
 /*
  * fox_attn_bwd_workspace_bytes -- bytes of scratch fox_attn_bwd needs:
- * b*h*(3*npad + 2*n) floats, npad = n rounded up to a multiple of 64.
- * Returns 0 for invalid sizes.
+ * b*h*(3*npad + 3*n) floats plus b*h*nblk doubles, npad = n rounded up to a multiple of 64,
+ * nblk = n rounded up to a multiple of 128, divided by 32.  Returns 0 for invalid sizes.
  */
 size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
 
@@ -170,12 +170,17 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
  *     dq = scale dS k, dk = scale dS^T q, and for the gates, with c_i - c_j in every score,
  *     dlogf_t = sum over i >= t of (rowsum(dS)_i - colsum(dS)_i)
  *   (the row sums of dS vanish in exact arithmetic; the kernels keep them, with both sums
- *   taken over the same dS values (bf16-rounded on the bf16 path), so that their rounding
- *   cancels in dlogf).
+ *   taken over the same fp32 dS values, so that their rounding cancels in dlogf).  The gate
+ *   prefix sums are rebuilt from logf in fp64 and split at 32-position blocks, so the bias of
+ *   each score carries rounding of the size of the bias itself, however large |c| grows.  In the
+ *   unmasked mode rowsum(dout * O) is replaced by its exact equal sum_j P_ij (dout v^T)_ij,
+ *   computed in fp32 by an extra pass (the O given is rounded to `dtype`, and that rounding
+ *   would not cancel in dlogf there).
  *
- *   q, k, v, o, dout : [b, h, n, d] of `dtype`, inputs; o, lse and c as fox_attn_fwd (same mode)
+ *   q, k, v, o, dout : [b, h, n, d] of `dtype`, inputs; o and lse as fox_attn_fwd (same mode)
  *                      wrote them for these q, k, v, logf and scale.
- *   lse, c   : [b, h, n] fp32, inputs (fox_attn_fwd's outputs).
+ *   lse      : [b, h, n] fp32, input (fox_attn_fwd's output).
+ *   logf     : [b, h, n] fp32, input: the log forget gates the forward was given.
  *   dq, dk, dv : [b, h, n, d] of `dtype`, outputs (bf16: rounded to nearest even).
  *   dtype    : FOX_BF16 (P and dS rounded to bf16 as MFMA operands, fp32 accumulation) or FOX_F32
  *              (fp32 throughout, on the vector ALU; n up to 65535 * 64).
@@ -188,7 +193,7 @@ size_t fox_attn_bwd_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
  *   Every output element has one writer (no atomics): repeated calls give identical results.
  */
 fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                          const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                          const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                           void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
                           float scale, fox_dtype_t dtype, int causal, hipStream_t stream);
 
@@ -196,7 +201,7 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
  * fox_attn_bwd_ex -- fox_attn_bwd with the tensor layout chosen.
  *   FoX module page, ForgettingAttention.forward: the projections are formed as
  *   [batch, seq, heads, head_dim] before the permute to head-major; FOX_TOKEN_MAJOR reads q, k,
- *   v, o, dout as [b, n, h, d] and lse, c as [b, n, h], and writes dq, dk, dv as [b, n, h, d]
+ *   v, o, dout as [b, n, h, d] and lse, logf as [b, n, h], and writes dq, dk, dv as [b, n, h, d]
  *   and dlogf as [b, n, h], the layout fox_attn_fwd_ex(..., FOX_TOKEN_MAJOR) reads and writes.
  *
  *   layout : FOX_HEAD_MAJOR or FOX_TOKEN_MAJOR (else FOX_ERR_UNSUPPORTED); with
@@ -206,7 +211,7 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
  *   and the errors as fox_attn_bwd.
  */
 fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                             const float* lse, const float* c, void* dq, void* dk, void* dv, float* dlogf,
+                             const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                              void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
                              float scale, fox_dtype_t dtype, int causal, fox_layout_t layout, hipStream_t stream);
 

@@ -99,10 +99,12 @@ def test_fwd_pruned_workspace_bytes(L):
 
 def test_bwd_workspace_bytes(L):
     f = L.fox_attn_bwd_workspace_bytes
-    # row vectors a_i, D_i, c_i log2 e padded to a multiple of 64, row sums and column sums (fp32)
-    assert f(2, 16, 4096, 128) == 32 * (3 * 4096 + 2 * 4096) * 4
-    assert f(1, 3, 65, 64) == 3 * (3 * 128 + 2 * 65) * 4
-    assert f(1, 1, 1, 32) == (3 * 64 + 2) * 4
+    # per head: row vectors a_i, D_i, cl_i padded to a multiple of 64, the row and column sums and
+    # an lse correction (fp32), plus one fp64 gate-sum start per 32 positions of n rounded up to 128
+    assert f(2, 16, 4096, 128) == 32 * ((3 * 4096 + 3 * 4096) * 4 + 128 * 8)
+    assert f(1, 3, 65, 64) == 3 * ((3 * 128 + 3 * 65) * 4 + 4 * 8)
+    assert f(1, 1, 1, 32) == (3 * 64 + 3) * 4 + 4 * 8
+    assert f(1, 1, 129, 32) == (3 * 192 + 3 * 129) * 4 + 8 * 8
     assert f(0, 1, 10, 64) == 0 and f(1, 1, 10, 48) == 0 and f(1, 1, 0, 64) == 0
 
 
@@ -148,6 +150,34 @@ def test_decode_rejects_bad_arguments(L):
     assert _dec(L, ws=H + 8) == WS
     assert _dec(L, o=B) == INVALID  # output inside the K cache
     assert _dec(L, ws=C) == INVALID  # workspace inside the V cache
+
+
+# Decode buffers for the alias checks: argument -> (address, bytes) at s=2, h=2, l=100, d=64, bf16
+# (the workspace extent is the size the library checks: what it needs for these sizes).
+def _dec_bufs(L):
+    return {"q": (A, 2 * 2 * 64 * 2), "k": (B, 2 * 2 * 100 * 64 * 2), "v": (C, 2 * 2 * 100 * 64 * 2),
+            "cc": (D, 2 * 2 * 100 * 4), "ln": (E, 2 * 2 * 4), "o": (F, 2 * 2 * 64 * 2), "lse": (G, 2 * 2 * 4),
+            "ws": (H, L.fox_attn_decode_workspace_bytes(2, 2, 100, 64))}
+
+
+@pytest.mark.parametrize("out", ["o", "lse", "cc", "ws"])
+def test_decode_rejects_every_written_alias(L, out):
+    """Each buffer the decode step writes (o, lse, the c slot, the workspace) may overlap no other
+    argument: placed at the start, and at the last 16-byte-aligned word, of every other buffer."""
+    bufs = _dec_bufs(L)
+    assert bufs["ws"][1] > 0
+    for other, (addr, nbytes) in bufs.items():
+        if other == out:
+            continue
+        for at in (addr, addr + ((nbytes - 4) & ~15)):
+            assert _dec(L, **{out: at}) == INVALID, (out, other, hex(at))
+
+
+def test_decode_ragged_rejects_aliased_lengths(L):
+    """The ragged step's length array may overlap no written buffer."""
+    bufs = _dec_bufs(L)
+    for out in ("o", "lse", "cc", "ws"):
+        assert _decr(L, lens=bufs[out][0], s=2, h=2) == INVALID, out
 
 
 def _decr(L, lens=0x90_0000_0000, **kw):
@@ -200,11 +230,11 @@ def test_decode_paged_rejects_bad_arguments(L):
 
 def _bwd(L, layout=None, **kw):
     I, J, K, M = (0x10_0000_0000 * (i + 9) for i in range(4))
-    args = dict(q=A, k=B, v=C, o=D, dout=E, lse=F, c=G, dq=H, dk=I, dv=J, dl=K, ws=M, wsb=1 << 30, b=1, h=2, n=300,
+    args = dict(q=A, k=B, v=C, o=D, dout=E, lse=F, logf=G, dq=H, dk=I, dv=J, dl=K, ws=M, wsb=1 << 30, b=1, h=2, n=300,
                 d=64, scale=0.125, dt=_lib.FOX_BF16, causal=1)
     args.update(kw)
     a = args
-    pos = (a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["c"], a["dq"], a["dk"], a["dv"], a["dl"], a["ws"],
+    pos = (a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["logf"], a["dq"], a["dk"], a["dv"], a["dl"], a["ws"],
            a["wsb"], a["b"], a["h"], a["n"], a["d"], a["scale"], a["dt"], a["causal"])
     if layout is None:
         return L.fox_attn_bwd(*pos, None)
@@ -226,6 +256,9 @@ def test_bwd_rejects_bad_arguments(L):
     assert _bwd(L, dq=A) == INVALID
     assert _bwd(L, dv=0x10_0000_0000 * 9) == INVALID  # dv == dk
     assert _bwd(L, dl=F) == INVALID  # dlogf == lse
+    assert _bwd(L, dl=G) == INVALID  # dlogf == logf
+    assert _bwd(L, logf=None) == INVALID
+    assert _bwd(L, logf=G + 2) == INVALID  # 4-byte alignment
     assert _bwd(L, ws=H) == INVALID  # workspace == dq
 
 

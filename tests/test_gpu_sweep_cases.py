@@ -1,0 +1,111 @@
+"""Regression cases: the inputs on which randomised parity sweeps of the HIP path once exceeded
+their bounds, rebuilt exactly as the sweep drew them, checked at the bounds of the parity suite.
+
+Each case: the forward inputs of ``fox_inputs.FwdConfig(f"sw{case}", B, H, N, d, dtype, mu, sd)``
+and, for the backward, dO = ``torch.randn(B, H, N, d)`` from a generator seeded with the case
+number, rounded to the dtype; the GPU runs in the layout the sweep used (token-major results are
+bit-equal to head-major ones, which the parity suite checks separately).
+
+What failed, and what was changed:
+* fp32 backward, both modes (relative error 1.0-2.0e-4 against 1e-4): the biases came from fp32
+  prefix sums c, whose rounding grows with |c|; the backward now takes log f and forms every bias
+  from fp64 block sums plus an in-block part.
+* fp32 forward without the mask (lse off by about one fp32 ulp at |lse| in the hundreds): the row
+  sum of each lane ran in fp32 over thousands of keys; it now runs in fp64 over per-tile partial
+  sums, with an fp64 logarithm.
+* bf16 backward without the mask (dlogf at 3.3 % of max|dlogf| against 2 %): D_i = dO_i . O_i used
+  the forward's bf16 O, and the dS sums the bf16 dS; dlogf is a difference of two cross-block sums
+  there, in which neither rounding cancels.  D_i now comes from a pass that sums P dP in fp32, and
+  the dS row and column sums use the fp32 values.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import forget_gated_causal_amd as fox
+import fox_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+BWD_TOL = {"f32": 2e-5, "bf16": 2e-2}  # relative to max(1, max|ref|), as in the parity suite
+
+# (case, kind, B, H, N, d, dtype, causal, layout, gate-logit mean, sd)
+CASES = [
+    (78, "bwd", 3, 5, 1068, 32, "f32", False, "head", 1.0796106281687468, 2.3926218503779983),
+    (160, "bwd", 3, 2, 1014, 32, "f32", False, "token", 2.2480762842918742, 2.5050637550958363),
+    (304, "fwd", 3, 2, 503, 32, "f32", False, "head", 0.8940668676099572, 1.651372677831349),
+    (221, "bwd", 1, 1, 1764, 64, "f32", False, "token", 2.356963914197504, 2.7848232760718235),
+    (313, "bwd", 3, 2, 1457, 64, "f32", True, "token", 0.45056946758630834, 2.796405302668616),
+    (579, "bwd", 1, 2, 1862, 128, "f32", True, "head", 0.33721394543846883, 1.4696251473716784),
+    (847, "bwd", 2, 5, 1381, 64, "f32", True, "head", 0.013963053192941999, 1.590890221031576),
+    (1679, "bwd", 3, 2, 1074, 128, "f32", True, "head", 0.8557555315164023, 2.066376892856557),
+    (15, "bwd", 2, 5, 970, 32, "f32", True, "token", 0.16039064496893785, 2.9472604524934627),
+    (161, "bwd", 1, 5, 1902, 32, "f32", False, "token", 0.6342779322232934, 1.9351580153211436),
+    (572, "bwd", 2, 1, 620, 32, "bf16", False, "token", 1.2028642138228725, 2.914109965700111),
+    (807, "bwd", 1, 3, 2078, 128, "f32", True, "head", 0.2512100535098709, 1.9527641421587003),
+    (1971, "bwd", 1, 1, 2078, 32, "f32", True, "token", 0.8629474990500208, 1.5143168167102228),
+    (2168, "bwd", 3, 3, 1879, 64, "f32", True, "token", 0.21197590064740046, 1.1778521405057962),
+    (2353, "bwd", 2, 5, 1198, 64, "f32", True, "token", 0.01016373241914903, 2.5806061596342293),
+    (2620, "bwd", 3, 1, 1773, 32, "f32", True, "head", 0.19971851982698663, 1.3080080939330727),
+]
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def _lse_bound(ref, dtype):
+    """1e-5 (fp32) / 2e-2 (bf16); for fp32 where |lse| >= 256 (half an ulp >= 1.5e-5), the correctly
+    rounded value up to 1e-6."""
+    if dtype != "f32":
+        return TOL[dtype]
+    return np.maximum(TOL["f32"], 0.5 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) + 1e-6)
+
+
+def _tm(t):
+    return t.permute(0, 2, 1, 3).contiguous() if t.dim() == 4 else t.permute(0, 2, 1).contiguous()
+
+
+def _hm(t):
+    return t.permute(0, 2, 1, 3) if t.dim() == 4 else t.permute(0, 2, 1)
+
+
+@pytest.mark.parametrize("case,kind,B,H,N,d,dtype,causal,layout,mu,sd", CASES, ids=[f"sw{c[0]}" for c in CASES])
+def test_sweep_case(case, kind, B, H, N, d, dtype, causal, layout, mu, sd):
+    inp = fi.fwd_inputs(fi.FwdConfig(f"sw{case}", B, H, N, d, dtype, mu, sd))
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    args = (q, k, v, logf) if layout == "head" else tuple(_tm(t) for t in (q, k, v, logf))
+    o, lse, c = fox.attn_fwd_ex(*args, causal=causal, layout=layout, scale=inp["scale"])
+    if kind == "bwd":
+        g = torch.Generator().manual_seed(case)
+        dout = torch.randn(B, H, N, d, generator=g).to(q.dtype)
+        bargs = (*args[:3], o, (dout if layout == "head" else _tm(dout)).to(DEV), lse, args[3])
+        grads = fox.attn_bwd(*bargs, causal=causal, scale=inp["scale"], layout=layout)
+    torch.cuda.synchronize()
+    if layout == "token":
+        o, lse = _hm(o), _hm(lse)
+        if kind == "bwd":
+            grads = [_hm(t) for t in grads]
+    o_ref, lse_ref, _ = oracle.attn_fwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]), inp["scale"],
+                                        causal=causal)
+    eo = np.abs(_np(o) - o_ref).max()
+    dl = np.abs(_np(lse) - lse_ref)
+    msg = [f"O {eo:.2e}", f"lse {dl.max():.2e} (max|lse| {np.abs(lse_ref).max():.1f})"]
+    assert eo <= TOL[dtype], ("O", eo)
+    assert np.all(dl <= _lse_bound(lse_ref, dtype)), ("lse", float(dl.max()))
+    if kind == "bwd":
+        ref = oracle.attn_bwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]), inp["scale"],
+                              _np(dout), causal=causal)
+        for name, got, r in zip(("dq", "dk", "dv", "dlogf"), grads, ref):
+            assert torch.isfinite(got).all(), name
+            rel = np.abs(_np(got) - r).max() / max(1.0, np.abs(r).max())
+            msg.append(f"{name} {rel:.2e}")
+            assert rel <= BWD_TOL[dtype], (name, rel)
+    print(f"  sw{case} {kind} {dtype} causal={causal} {layout} B={B} H={H} N={N} d={d}: " + ", ".join(msg),
+          flush=True)
