@@ -10,6 +10,7 @@ kernels of libfox.so.  Outputs are allocated with torch when not supplied.
     o, lse, c    = attn_fwd_ex(q, k, v, logf, causal, layout)  # layout "head" [B,H,N,d] / "token" [B,N,H,d]
     dq, dk, dv, dlogf = attn_bwd(q, k, v, o, dout, lse, logf)  # gradients (bf16 or fp32); layout="token" too
     o, lse       = attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale=None)
+    o, lse       = attn_decode_noalloc(q, k_cache, v_cache, c_cache, logf_new)   # no workspace: library scratch
     o, lse       = attn_decode_ragged(q, k_cache, v_cache, c_cache, logf_new, cache_lens)
     o, lse       = attn_decode_paged(q, k_pages, v_pages, c_pages, block_table, cache_lens, logf_new)
 """
@@ -21,7 +22,8 @@ import torch
 from ._lib import FOX_BF16, FOX_F32, FOX_HEAD_MAJOR, FOX_TOKEN_MAJOR, FoxError, check, lib, status_string  # noqa: F401
 
 __all__ = ["logf_cumsum", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_ex", "attn_fwd_pruned", "attn_fwd_pruned_workspace_bytes",
-           "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_ragged", "attn_decode_paged",
+           "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_decode_ragged",
+           "attn_decode_paged",
            "decode_workspace_bytes", "FoxError", "status_string"]
 
 _DTYPES = {torch.float32: FOX_F32, torch.bfloat16: FOX_BF16}
@@ -261,7 +263,8 @@ def _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, workspace, wa
         raise ValueError("c_cache must be [S,H,L] and logf_new [S,H]")
     o = _alloc_or_check(out, "out", (S, H, d), q.dtype, q.device)
     lse = _alloc_or_check(lse, "lse", (S, H), torch.float32, q.device) if want_lse else None
-    workspace = _workspace(workspace, decode_workspace_bytes(S, H, L, d), q.device)
+    if workspace is not False:  # False: no workspace at all (the no-allocation entry point)
+        workspace = _workspace(workspace, decode_workspace_bytes(S, H, L, d), q.device)
     return S, H, L, d, dt, o, lse, workspace
 
 
@@ -274,6 +277,18 @@ def attn_decode(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = No
                                _ptr(lse), _ptr(ws), _nbytes(ws), S, H, L, d,
                                float(_default_scale(d) if scale is None else scale), dt, _stream())
     check("fox_attn_decode", st)
+    return o, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, c_cache, logf_new, scale: float | None = None, out=None, lse=None,
+                        want_lse: bool = True):
+    """fox_attn_decode_noalloc: attn_decode whose split records live in the library's fixed device
+    scratch (no workspace).  Pass ``out`` (and ``lse``) to make the call allocate nothing at all."""
+    S, H, L, d, dt, o, lse, _ = _decode_prep(q, k_cache, v_cache, c_cache, logf_new, out, lse, False, want_lse)
+    st = lib().fox_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(c_cache), _ptr(logf_new),
+                                       _ptr(o), _ptr(lse), S, H, L, d,
+                                       float(_default_scale(d) if scale is None else scale), dt, _stream())
+    check("fox_attn_decode_noalloc", st)
     return o, lse
 
 

@@ -17,6 +17,8 @@ FOX_ERR_INVALID_ARG = 1
 FOX_ERR_UNSUPPORTED = 2
 FOX_ERR_WORKSPACE = 3
 FOX_ERR_HIP = 4
+FOX_ERR_SCRATCH = 5
+FOX_DECODE_SCRATCH_BYTES = 16 << 20  # include/fox.h
 FOX_F32 = 0
 FOX_BF16 = 1
 FOX_HEAD_MAJOR = 0
@@ -39,6 +41,8 @@ SIGNATURES = {
     "fox_attn_decode_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "fox_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _I64, _I64,
                                        ctypes.c_float, ctypes.c_int, _P]),
+    "fox_attn_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                               ctypes.c_int, _P]),
     "fox_attn_decode_ragged": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _I64,
                                               _I64, ctypes.c_float, ctypes.c_int, _P]),
     "fox_attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64,

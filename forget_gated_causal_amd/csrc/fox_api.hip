@@ -39,6 +39,7 @@ const char* fox_status_string(fox_status_t status) {
     case FOX_ERR_UNSUPPORTED: return "unsupported head dim (need 32, 64 or 128) or dtype";
     case FOX_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
     case FOX_ERR_HIP: return "HIP runtime error at kernel launch";
+    case FOX_ERR_SCRATCH: return "sizes need more split-record space than the fixed decode scratch holds";
   }
   return "unknown status";
 }
@@ -182,11 +183,12 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
                                        (int)d, scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
 }
 
-// Validation shared by the decode entry points (cache_lens: the ragged step's lengths, or null).
+// Validation shared by the decode entry points (cache_lens: the ragged step's lengths, or null;
+// ws_required false: no caller workspace, the split records go to the library's scratch).
 static fox_status_t decode_args(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
                                 const float* logf_new, const int32_t* cache_lens, void* o, float* lse, void* workspace,
                                 size_t workspace_bytes, int64_t s, int64_t h, int64_t l, int64_t d, float scale,
-                                fox_dtype_t dtype) {
+                                fox_dtype_t dtype, bool ws_required = true) {
   if (!q || !k_cache || !v_cache || !c_cache || !logf_new || !o) return FOX_ERR_INVALID_ARG;
   if (s <= 0 || h <= 0 || l <= 0 || d <= 0 || l > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (s > kI32Max / h) return FOX_ERR_INVALID_ARG;
@@ -200,7 +202,7 @@ static fox_status_t decode_args(const void* q, const void* k_cache, const void* 
   const int nsplit = fox::decode_num_splits(sh, (int)l, (int)d);
   if (sh > kI32Max / nsplit) return FOX_ERR_INVALID_ARG;
   const size_t need = fox::decode_workspace_bytes(sh, (int)l, (int)d);
-  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
+  if (ws_required && (!workspace || !aligned(workspace, 16) || workspace_bytes < need)) return FOX_ERR_WORKSPACE;
   const size_t eb = elem_bytes(dtype);
   const size_t obytes = (size_t)sh * (size_t)d * eb, cbytes = (size_t)sh * (size_t)l * sizeof(float);
   const size_t kvbytes = (size_t)sh * (size_t)l * (size_t)d * eb, sbytes = (size_t)sh * sizeof(float);
@@ -227,6 +229,20 @@ fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_c
   return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, nullptr, (int)h, o, lse,
                                           static_cast<float*>(workspace), s * h, (int)l, (int)d, scale,
                                           dtype == FOX_BF16, stream));
+}
+
+fox_status_t fox_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                                     const float* logf_new, void* o, float* lse, int64_t s, int64_t h, int64_t l,
+                                     int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream) {
+  const fox_status_t st = decode_args(q, k_cache, v_cache, c_cache, logf_new, nullptr, o, lse, nullptr, 0, s, h, l, d,
+                                      scale, dtype, false);
+  if (st != FOX_OK) return st;
+  if (fox::decode_workspace_bytes(s * h, (int)l, (int)d) > (size_t)FOX_DECODE_SCRATCH_BYTES) return FOX_ERR_SCRATCH;
+  float* ws = nullptr;
+  const hipError_t e = fox::decode_scratch(&ws);
+  if (e != hipSuccess) return FOX_ERR_HIP;
+  return from_hip(fox::launch_attn_decode(q, k_cache, v_cache, c_cache, logf_new, nullptr, (int)h, o, lse, ws, s * h,
+                                          (int)l, (int)d, scale, dtype == FOX_BF16, stream));
 }
 
 fox_status_t fox_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache, float* c_cache,

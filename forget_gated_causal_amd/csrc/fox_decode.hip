@@ -28,7 +28,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
+#include "../../include/fox.h"
 #include "fox_device.h"
 #include "fox_internal.h"
 
@@ -359,6 +361,37 @@ hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, flo
                               float scale, bool is_bf16, hipStream_t stream) {
   const PageMap pm{nullptr, 0, 0, 0};
   return launch_decode_any(q, kc, vc, cc, logf_new, lens, nh, o, lse, ws, sh, l, d, scale, is_bf16, pm, stream);
+}
+
+// Split records of fox_attn_decode_noalloc: a fixed device array instead of a caller workspace,
+// FOX_DECODE_SCRATCH_BYTES per device for the life of the process.  Host code never uses its
+// name as an address (on the host it stands for the variable, not its device location): the
+// device address comes from hipGetSymbolAddress, looked up once per device with that device
+// current, and is what the kernels receive.  The kernels write every record before the combine
+// reads it, so nothing needs clearing between calls; calls that overlap on one device race on it.
+static __device__ __align__(256) float scratch[FOX_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];  // this device's address of `scratch`, once looked up
+}  // namespace
+
+hipError_t decode_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(a);
+    g_scratch[dev].store(p, std::memory_order_release);  // same value from any racing thread
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* vp, float* cp, const int* table,

@@ -38,6 +38,9 @@ size_t decode_workspace_bytes(int64_t sh, int l, int d);
 hipError_t launch_attn_decode(const void* q, const void* kc, const void* vc, float* cc, const float* logf_new,
                               const int* lens, int nh, void* o, float* lse, float* workspace, int64_t sh, int l,
                               int d, float scale, bool is_bf16, hipStream_t stream);
+// Device address of this device's fixed split-record array (FOX_DECODE_SCRATCH_BYTES), looked
+// up on the first call per device (the current one).
+hipError_t decode_scratch(float** out);
 // The same step against paged caches: pools k/v [npages][nh][1 << page_shift][d], c [npages][nh][P],
 // table [sequences][max_pages] (entries clamped to [0, npages)), lens required.
 hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* vp, float* cp, const int* table,

@@ -47,7 +47,8 @@ typedef enum fox_status {
   FOX_ERR_INVALID_ARG = 1, /* null pointer, size <= 0 or too large, bad scale, misaligned pointer */
   FOX_ERR_UNSUPPORTED = 2, /* head dim not in {32, 64, 128}, unknown dtype */
   FOX_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than fox_attn_decode_workspace_bytes() */
-  FOX_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+  FOX_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
+  FOX_ERR_SCRATCH = 5      /* fox_attn_decode_noalloc: the sizes need more than FOX_DECODE_SCRATCH_BYTES */
 } fox_status_t;
 
 typedef enum fox_dtype {
@@ -244,6 +245,30 @@ fox_status_t fox_attn_decode(const void* q, const void* k_cache, const void* v_c
                              const float* logf_new, void* o, float* lse, void* workspace, size_t workspace_bytes,
                              int64_t s, int64_t h, int64_t l, int64_t d, float scale, fox_dtype_t dtype,
                              hipStream_t stream);
+
+/* Bytes of the fixed device scratch behind fox_attn_decode_noalloc (per device, held until the
+ * process ends): fox_attn_decode_workspace_bytes(s, h, l, d) must not exceed it, which admits
+ * up to about 32 000 (sequence, head) pairs at d = 128 (a record of d + 2 floats per pair and
+ * split; at least 8192 records in all when the cache is long). */
+#define FOX_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * fox_attn_decode_noalloc -- fox_attn_decode without a workspace argument, for callers that
+ *   cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ *   that forbid allocation.  The split records go to a fixed device array inside the library
+ *   (FOX_DECODE_SCRATCH_BYTES per device, reserved when the library's code is loaded on the
+ *   device); the call itself allocates, frees and clears nothing.  The kernels and the results
+ *   are those of fox_attn_decode, bit for bit.
+ *
+ *   Arguments, layouts, outputs and errors as fox_attn_decode, without workspace and
+ *   workspace_bytes, plus FOX_ERR_SCRATCH when fox_attn_decode_workspace_bytes(s, h, l, d)
+ *   exceeds FOX_DECODE_SCRATCH_BYTES (nothing is launched).  `stream` must belong to the current
+ *   device.  Every call on one device uses that device's one array: calls that may overlap on a
+ *   device (other streams, other threads) race on it and must be serialised by the caller.
+ */
+fox_status_t fox_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, float* c_cache,
+                                     const float* logf_new, void* o, float* lse, int64_t s, int64_t h, int64_t l,
+                                     int64_t d, float scale, fox_dtype_t dtype, hipStream_t stream);
 
 /*
  * fox_attn_decode_ragged -- fox_attn_decode for a batch of sequences of different lengths.

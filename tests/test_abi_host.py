@@ -180,6 +180,23 @@ def test_decode_ragged_rejects_aliased_lengths(L):
         assert _decr(L, lens=bufs[out][0], s=2, h=2) == INVALID, out
 
 
+def test_decode_noalloc_rejects_bad_arguments(L):
+    """The no-allocation decode validates like fox_attn_decode (no workspace to check) and refuses
+    sizes whose split records exceed the fixed scratch before it touches any device."""
+    def na(q=A, k=B, v=C, cc=D, ln=E, o=F, lse=G, s=2, h=2, l=100, d=64, scale=0.1, dt=_lib.FOX_BF16):
+        return L.fox_attn_decode_noalloc(q, k, v, cc, ln, o, lse, s, h, l, d, scale, dt, None)
+    assert na(q=None) == INVALID
+    assert na(l=0) == INVALID
+    assert na(d=96) == UNSUP
+    assert na(scale=float("inf")) == INVALID
+    assert na(o=B) == INVALID  # output inside the K cache
+    assert na(lse=E) == INVALID  # lse over the new gates
+    # 65536 (sequence, head) pairs at d = 128: 34 MB of split records > FOX_DECODE_SCRATCH_BYTES
+    assert L.fox_attn_decode_workspace_bytes(1024, 64, 1, 128) > _lib.FOX_DECODE_SCRATCH_BYTES
+    assert na(s=1024, h=64, l=1, d=128) == _lib.FOX_ERR_SCRATCH
+    assert L.fox_status_string(_lib.FOX_ERR_SCRATCH).decode().startswith("sizes need more")
+
+
 def _decr(L, lens=0x90_0000_0000, **kw):
     args = dict(q=A, k=B, v=C, cc=D, lnew=E, o=F, lse=G, ws=H, wsb=1 << 24, s=2, h=3, l=100, d=64, scale=0.125,
                 dt=_lib.FOX_BF16)
