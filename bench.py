@@ -1,14 +1,16 @@
 """Benchmark of the causal FoX attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline] [--only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline] [--only]
 
 A step is one call of the library entry point on one batch of synthetic,
 seeded, device-resident input:
   * fox_attn_fwd (gate scan fused in; one kernel) for the forward workloads,
   * fox_attn_decode (split + combine kernels) for the decode workload.
-The headline workload is the bf16 forward B=4 H=12 N=1024 d=64; the JSON line
-also carries the long forward workloads and the decode workload (the metric
-quotes prefill TFLOP/s and decode GB/s) unless --only is given.
+The headline workload is the largest single-GPU forward configuration, bf16
+B=1 H=32 N=16384 d=128 (the metric names no configuration); the JSON line also
+carries the other forward workloads, the backward and the decode workload (the
+metric quotes prefill TFLOP/s and decode GB/s), each with its roofline, unless
+--only is given.
 
 Timing: W untimed warm-up steps, then K back-to-back steps between two HIP events
 on the stream the library launches on (torch's current stream), bracketed by
@@ -62,9 +64,11 @@ def decode_bytes(cfg, lens=None) -> dict:
 # WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain device
 # copy of known size.  The summaries live in profiles/*_traffic.txt with a digest of the kernel
 # sources they were taken on; a summary of older sources is not used (traffic reported as null).
-KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_device.h"], "decode": ["fox_decode.hip", "fox_device.h"]}
+KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_device.h"], "decode": ["fox_decode.hip", "fox_device.h"],
+                  "bwd": ["fox_bwd.hip", "fox_scan.hip", "fox_device.h"]}
 COPY_CAL_BYTES = 1 << 30
 DECODE_KERNEL = "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>"
+BWD_KERNEL = "fox_attn_bwd<{d},causal>: bwd_gate_rows + bwd_pre + bwd_kv + bwd_dq + suffix scan"
 
 
 def kernel_source_digest(kind: str) -> str:
@@ -97,13 +101,14 @@ def stored_traffic(tag: str, kernel: str, kind: str):
 
 
 def _counter_per_dispatch(path, counter, name_part):
-    """Mean value of `counter` per dispatch of each kernel whose name contains name_part, summed
-    over those kernels (one call of an entry point that launches several kernels); and the
-    number of dispatches of the first of them."""
+    """Mean value of `counter` per dispatch of each kernel whose name contains name_part (or one
+    of its "|"-separated parts), summed over those kernels (one call of an entry point that
+    launches several kernels); and the number of dispatches of the first of them."""
     tot, ids = {}, {}
+    parts = name_part.split("|")
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            if r["Counter_Name"] == counter and any(p in r["Kernel_Name"] for p in parts):
                 k = r["Kernel_Name"]
                 tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
                 ids.setdefault(k, set()).add(r["Dispatch_Id"])
@@ -124,9 +129,9 @@ def write_traffic_summary(args):
         f"# rocprofv3 counter summary: HBM-side traffic per launch of {args.kernel} on workload {args.workload}",
         "# commands (one counter per run; <out> is the output directory):",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o p -- python3 bench.py --workload {args.workload} "
-        "--only --no-cpu-baseline --steps 4 --warmup 2",
+        f"--only --no-cpu-baseline --steps 4 --warmup 2{' --backward' if args.kind == 'bwd' else ''}",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o p -- python3 bench.py --workload {args.workload} "
-        "--only --no-cpu-baseline --steps 4 --warmup 2",
+        f"--only --no-cpu-baseline --steps 4 --warmup 2{' --backward' if args.kind == 'bwd' else ''}",
         "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/copy_fetch -o p -- python3 bench.py --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/copy_write -o p -- python3 bench.py --copy-calibration",
         "#   python3 bench.py --traffic-summary ... (this file)",
@@ -298,13 +303,14 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     kernel = (f"bwd_kv_kernel<{cfg.d},causal> + bwd_dq_kernel<{cfg.d},causal> + 2 small kernels" if bf16 else
               f"bwd_f32_kv_kernel<{cfg.d},causal> + bwd_f32_dq_kernel<{cfg.d},causal> + 2 small kernels")
+    traffic = stored_traffic(tag, BWD_KERNEL.format(d=cfg.d), "bwd") if bf16 else None
     return {"workload": cfg.desc + ", backward", "value": round(achieved, 2), "unit": "TFLOP/s",
             "ms_per_step": round(ms, 4),
             "note": "10*d flop per causal pair (the dq kernel's recomputation of S and dP, 4*d more, is not "
                     "counted); one call = the row-vector, key-side, query-side and gate suffix-sum kernels"
                     + ("" if bf16 else "; fp32 on the vector ALU, a parity-sized workload (latency-bound)"),
             "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel}}
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}}
 
 
 _DECODE_INPUTS = {}
@@ -387,30 +393,63 @@ def _blas_threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline_fwd(fi, inp, budget_s=12.0):
-    """The fp64 oracle, as it stands, on a sample of whole heads of the same workload."""
+def _host_info() -> dict:
+    """The host the oracle runs on: logical CPUs, the ones this process may use, and the model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model,
+            "blas_threads": _blas_threads()}
+
+
+def sample_rows(n: int):
+    """The oracle's row sample at long sequences: every 64th row of a head, plus its last 128 rows."""
+    import numpy as np
+    return np.unique(np.concatenate([np.arange(0, n, 64), np.arange(max(0, n - 128), n)]))
+
+
+def cpu_baseline_fwd(fi, inp, budget_s=15.0, rows_sample=False):
+    """The fp64 oracle, as it stands, on heads of the same workload: whole heads, or with
+    rows_sample the rows of sample_rows() of every head, cycling over the heads until the budget
+    is spent.  Its rate counts the algorithmic work of the rows done (4 d flop per causal pair)."""
     import numpy as np
 
     import oracle
-    cores = _blas_threads()
     cfg = inp["cfg"]
-    q, k, v, lf = (inp[n].double().numpy() for n in ("q", "k", "v", "logf"))
+    q, k, v, lf = (inp[n] for n in ("q", "k", "v", "logf"))
     heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    rows = sample_rows(cfg.N) if rows_sample else np.arange(cfg.N)
+    pairs_per_head = float(np.sum(rows + 1))
     done, t0 = 0, time.perf_counter()
-    rows = np.arange(cfg.N)
-    # whole (batch, head) slices, cycling over the workload until the budget is spent
     while time.perf_counter() - t0 < budget_s:
         b, h = heads[done % len(heads)]
-        oracle.fwd_head_rows(q[b, h], k[b, h], v[b, h], lf[b, h], inp["scale"], rows)
+        oracle.fwd_head_rows(q[b, h].double().numpy(), k[b, h].double().numpy(), v[b, h].double().numpy(),
+                             lf[b, h].double().numpy(), inp["scale"], rows)
         done += 1
     dt = time.perf_counter() - t0
-    flops = 4.0 * cfg.d * cfg.N * (cfg.N + 1) / 2 * done
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} (batch, head) slices of the same workload ({len(heads)} per batch, cycled), all "
-                      f"{cfg.N} rows each, fp64 NumPy, {dt:.1f} s wall"}
+    flops = 4.0 * cfg.d * pairs_per_head * done
+    what = (f"rows {{0, 64, 128, ...}} and the last 128 ({len(rows)} of {cfg.N}) of each head" if rows_sample
+            else f"all {cfg.N} rows of each head")
+    info = _host_info()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"{done} (batch, head) slices of the same workload ({len(heads)} in all, cycled), {what}; "
+                      f"fp64 NumPy, {dt:.1f} s wall; rate = the algorithmic flop of those rows / wall time",
+            "host": info}
 
 
-def cpu_baseline_decode(inp, cfg, budget_s=8.0):
+def cpu_baseline_decode(inp, cfg, budget_s=10.0):
+    """The fp64 oracle's decode, as it stands, over whole sequences (all heads) until the budget is
+    spent; bytes counted as the GPU's algorithmic bytes of those sequences."""
     import numpy as np
 
     import oracle
@@ -427,8 +466,10 @@ def cpu_baseline_decode(inp, cfg, budget_s=8.0):
             break
     dt = time.perf_counter() - t0
     by = decode_bytes(cfg)["total"] * done / cfg.S
-    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
-            "sample": f"{done} of {cfg.S} sequences (all heads), fp64 NumPy, {dt:.1f} s wall"}
+    info = _host_info()
+    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"{done} of {cfg.S} sequences (all {cfg.H} heads each), fp64 NumPy, {dt:.1f} s wall",
+            "host": info}
 
 
 def main():
@@ -436,7 +477,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
     ap.add_argument("--backward", action="store_true", help="with --only: time fox_attn_bwd on the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time a captured HIP graph of the K calls")
@@ -446,7 +487,7 @@ def main():
     ap.add_argument("--fetch-csv"), ap.add_argument("--write-csv")
     ap.add_argument("--copy-fetch-csv"), ap.add_argument("--copy-write-csv")
     ap.add_argument("--kernel", help="kernel label as bench.py reports it"), ap.add_argument("--kernel-match")
-    ap.add_argument("--kind", choices=["fwd", "decode"], default="fwd")
+    ap.add_argument("--kind", choices=["fwd", "decode", "bwd"], default="fwd")
     ap.add_argument("--alg-bytes", type=float, default=0.0), ap.add_argument("--out")
     args = ap.parse_args()
     global USE_GRAPH
@@ -505,17 +546,20 @@ def main():
     line.update({
         "value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 5),
         "dtype": cfg.dtype,
-        "config": {"workload": cfg.desc, "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H,
-                   "head_dim": cfg.d, "parallelism": "single GPU"},
+        "config": {"workload": cfg.desc + (" (the largest single-GPU forward configuration)" if args.workload == "c4"
+                                           else ""),
+                   "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.d,
+                   "parallelism": "single GPU"},
         "roofline": dict(r["roofline"], kernel=r["kernel"], launch_us_mean=round(r["launch_ms_mean"] * 1e3, 2),
                          flop_per_launch=r["flop_per_launch"]),
     })
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_fwd(fi, r["inp"])
+        line["cpu_baseline"] = cpu_baseline_fwd(fi, r["inp"], rows_sample=cfg.N >= 8192)
     del r
+    torch.cuda.empty_cache()
     if not args.only:
         others = {}
-        for tag in ("c3", "c4"):
+        for tag in [t for t in ("c2", "c3", "c4") if t != args.workload]:
             x = bench_fwd(torch, fox, fi, tag, max(10, args.steps // 5), max(3, args.warmup // 2))
             print(f"# {x['cfg'].desc}: {x['ms_per_step']*1e3:.1f} us/step, {x['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
@@ -543,9 +587,11 @@ def main():
                   flush=True)
             others[f"{tag}_backward"] = x
             torch.cuda.empty_cache()
-        dec, _ = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))
+        dec, dinp = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))
         print(f"# {dec['workload']}: {dec['ms_per_step']*1e3:.1f} us/step, {dec['value']:.0f} GB/s",
               file=sys.stderr, flush=True)
+        if not args.no_cpu_baseline:
+            dec["cpu_baseline"] = cpu_baseline_decode(dinp, fi.DECODE["c5"])
         others["c5_decode"] = dec
         torch.cuda.empty_cache()
         for cache in ("ragged", "paged"):
