@@ -69,15 +69,15 @@ struct GateRows {          // per workgroup
 // ref), so the lane-order exclusive prefix is the key-order exclusive suffix
 // sum_{u > j} log f_u inside the tile.  `carry` (fp64) is the sum of log f over
 // (tile end, ref] and is advanced by the tile total.  Writes R_j = carry + suffix for
-// the tile (r2 = R_j * log2 e in fp32; r64 = R_j, when given), R_i for the block's own
+// the tile (r2 = R_j * unit in fp32; r64 = R_j, when given), R_i for the block's own
 // rows and, after tile 0, c at the reference row.  Everything is fp64 until the single
 // rounding to fp32.
 __device__ __forceinline__ void gate_finish(double incl, float* r2, double* r64, GateRows& rows, int lane, int kt,
-                                            int row0, int ref, double& carry) {
+                                            int row0, int ref, double& carry, double unit) {
   const double excl = wave_shr1(incl);
   const int jl = 63 - lane;
   const double rj = carry + excl;
-  r2[jl] = (float)(rj * kLog2ed);
+  r2[jl] = (float)(rj * unit);
   if (r64) r64[jl] = rj;
   // Branch-free writes (this code also runs inside the MFMA schedule): rows outside the
   // block and tiles other than tile 0 write to discard slots.
@@ -87,19 +87,20 @@ __device__ __forceinline__ void gate_finish(double incl, float* r2, double* r64,
   *(kt == 0 ? &rows.cref : &rows.cref_discard) = carry;
 }
 __device__ __forceinline__ void gate_tile(float* r2, double* r64, GateRows& rows, int lane, int kt, int row0,
-                                          int ref, float lf_rev, double& carry) {
-  gate_finish(wave_incl_scan((double)lf_rev), r2, r64, rows, lane, kt, row0, ref, carry);
+                                          int ref, float lf_rev, double& carry, double unit) {
+  gate_finish(wave_incl_scan((double)lf_rev), r2, r64, rows, lane, kt, row0, ref, carry, unit);
 }
 
 // The gate sums of one tile as a job that a wave can spread over its MFMA schedule.
 struct GateJob {
   const float* lf;  // the tile's staged log gates
-  float* r2;        // its biases R_j * log2 e (out)
+  float* r2;        // its biases R_j * unit (out)
   int kt;           // tile index
   int row0, ref;    // the block's first and last rows (R_i of these rows is kept)
   int fref;         // frame row: gates past it do not enter the sums
   GateRows* rows;
   double* carry;
+  double unit;      // R_j -> stored bias
 };
 
 // Element strides of one forward call.  Head-major: q/k/v/o [B,H,N,d], gates / lse / c [B,H,N]
@@ -308,70 +309,67 @@ template <int D>
 struct PipeGeom {
   static constexpr int KK = D / 16;  // MFMA k-steps of S (16 dims each)
   static constexpr int DB = D / 32;  // 32-dim output blocks of O
-  // Fold the running max into the S accumulators' initial value (saves one subtraction per
-  // score; costs 16 VGPRs, which the d = 128 schedule does not have to spare).
-  static constexpr bool FOLD = D <= 64;
 };
 
-// S^T of one tile: s[b] = K[32b .. 32b+31] Q^T + cinit (32 keys x 32 queries per block).
-// cinit holds -m / (scale log2 e) of the lane's row in every register, so the scores come
-// out already relative to the running max m (no subtraction per score before exp2).
+// The gate biases of a tile enter the scores as the S accumulators' initial value: the lead
+// wave stores R_j / (scale log2 e) * log2 e = R_j / scale per key, so a finished accumulator
+// holds a_ij = q_i.k_j + R_j / scale, and the base-2 score is a_ij * scale * log2 e.  Per
+// score that leaves one FMA, exp2(a * scale * log2 e - m), and a max on the raw a (the
+// scale is positive, so the max commutes with it).
+//
+// Bias tuple of block b in the accumulator layout of S^T: register 4g+e of lane (l32, hi)
+// is key 32b + 8g + 4hi + e.
+__device__ __forceinline__ f32x16 pipe_bias(const float* r2s, int b, int hi) {
+  f32x16 c;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 r = *reinterpret_cast<const f32x4*>(&r2s[32 * b + 8 * g + 4 * hi]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[4 * g + e] = r[e];
+  }
+  return c;
+}
+
+// S^T of one tile: s[b] = K[32b .. 32b+31] Q^T + bias (32 keys x 32 queries per block).
 template <int D>
 __device__ __forceinline__ void pipe_qk(const Bf16Stage<D>& st, uint32_t koff, const bf16x8 (&qreg)[D / 16],
-                                        const f32x16& cinit, f32x16 (&s)[2]) {
+                                        const float* r2s, int hi, f32x16 (&s)[2]) {
   constexpr int KK = PipeGeom<D>::KK;
+  s[0] = pipe_bias(r2s, 0, hi);
+  s[1] = pipe_bias(r2s, 1, hi);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const uint32_t a = koff ^ (uint32_t)(kk << 5);
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], kk == 0 ? cinit : s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk],
-                                                   kk == 0 ? cinit : s[1], 0, 0, 0);
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a), qreg[kk], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(st.k, a + 64 * D), qreg[kk], s[1], 0, 0, 0);
   }
 }
 
-// Biased base-2 scores of a tile, in place: s = acc * scale * log2 e + R_j * log2 e (minus the
-// running max, through acc's initial value), with the causal mask on the diagonal tile.
-// Returns the tile's row max (both lanes of a row).
+// Causal mask of the first tile (keys past `my_row` -> -inf, in place) and the tile's row
+// max in base-2 units (both lanes of a row).
 template <bool DIAG>
-__device__ __forceinline__ float pipe_scores(f32x16 (&s)[2], const float* r2s, int key0, int my_row, int hi,
-                                             float scale_log2) {
+__device__ __forceinline__ float pipe_scores(f32x16 (&s)[2], int key0, int my_row, int hi, float scale_log2) {
   float mx = kNegInf;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int kl = 32 * b + 8 * g + 4 * hi;
-      const f32x4 r2 = *reinterpret_cast<const f32x4*>(&r2s[kl]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float sv = fmaf(s[b][4 * g + e], scale_log2, r2[e]);
-        if constexpr (DIAG) {
-          if (key0 + kl + e > my_row) sv = kNegInf;
-        }
-        s[b][4 * g + e] = sv;
-        mx = fmaxf(mx, sv);
+    for (int r = 0; r < 16; ++r) {
+      float sv = s[b][r];
+      if constexpr (DIAG) {
+        if (key0 + 32 * b + 8 * (r >> 2) + 4 * hi + (r & 3) > my_row) sv = kNegInf;
       }
+      s[b][r] = sv;
+      mx = fmaxf(mx, sv);
     }
   }
-  return pair32_max(mx);
+  return pair32_max(mx) * scale_log2;
 }
 
-// Broadcast of -m / (scale log2 e), the initial value of every S accumulator.
-__device__ __forceinline__ f32x16 pipe_cinit(float m, float scale_log2) {
-  const float c = -m / scale_log2;
-  f32x16 r;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) r[e] = c;
-  return r;
-}
-
-// Lazy rescale (mx = the tile's row max): raise m only when the tile max exceeds it by more
-// than kTau, and scale O and l to the new max.  With FOLD the scores are relative to m (and
-// shifted along with it, as is the accumulator offset); otherwise they are absolute.
-template <bool FOLD, int DB>
-__device__ __forceinline__ void pipe_rescale(float mx, float& m, float& lsum, f32x16 (&oacc)[DB], f32x16 (&s)[2],
-                                             f32x16& cinit, float scale_log2) {
-  const float rel = FOLD ? mx : mx - m;
+// Lazy rescale (mx = the tile's row max, base 2): raise m only when the tile max exceeds it
+// by more than kTau, and scale O and l to the new max.
+template <int DB>
+__device__ __forceinline__ void pipe_rescale(float mx, float& m, float& lsum, f32x16 (&oacc)[DB]) {
+  const float rel = mx - m;
   const bool need = rel > kTau;
   if (wave_any(need)) {
     const float delta = need ? rel : 0.0f;
@@ -380,36 +378,19 @@ __device__ __forceinline__ void pipe_rescale(float mx, float& m, float& lsum, f3
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     m += delta;
-    if constexpr (FOLD) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) s[b] -= delta;
-      cinit = pipe_cinit(m, scale_log2);
-    }
   }
 }
 
-// First tile of a wave (m is still 0, O and l zero): m becomes the tile's row max.
-template <bool FOLD>
-__device__ __forceinline__ void pipe_first_max(float mx, float& m, f32x16 (&s)[2], f32x16& cinit, float scale_log2) {
-  m = mx;
-  if constexpr (FOLD) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) s[b] -= mx;
-    cinit = pipe_cinit(m, scale_log2);
-  }
-}
-
-// p = exp2(s - m) rounded to bf16 (s already relative to m when FOLD), in the key order of
-// the S^T registers: p[2b+u] holds keys 32b + 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3}, the B
-// operand of O^T += V^T P^T.
-template <bool FOLD>
-__device__ __forceinline__ void pipe_probs(const f32x16 (&s)[2], float m, bf16x8 (&p)[4]) {
+// p = exp2(a * scale * log2 e - m) rounded to bf16, in the key order of the S^T registers:
+// p[2b+u] holds keys 32b + 16u + {4hi .. 4hi+3, 8+4hi .. 8+4hi+3}, the B operand of
+// O^T += V^T P^T.
+__device__ __forceinline__ void pipe_probs(const f32x16 (&s)[2], float m, float scale_log2, bf16x8 (&p)[4]) {
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[2 * b + u][e] = (bf16)exp2_hw(FOLD ? s[b][8 * u + e] : s[b][8 * u + e] - m);
+      for (int e = 0; e < 8; ++e) p[2 * b + u][e] = (bf16)exp2_hw(fmaf(s[b][8 * u + e], scale_log2, -m));
     }
   }
 }
@@ -457,31 +438,29 @@ __device__ __forceinline__ void pipe_pv(const Bf16Stage<D>& st, uint32_t voff, c
 // softmax of both tiles between them.  The schedule is explicit: each slot holds one MFMA,
 // the LDS reads a few slots ahead of their use, and a share of the VALU work that does
 // not depend on in-flight MFMAs; sched_barrier keeps the compiler from regrouping slots.
-//   S slots (2*KK):  MFMA of S(cur); p = exp2(s - m) for 32/(2*KK) scores of prev.
-//   PV slots (4*DB): MFMA of O += V^T P^T; bf16 packing and row sum of P(prev); biased
-//                    scores and row max of cur (block 0 first: its MFMAs finished earlier).
+//   S slots (2*KK):  MFMA of S(cur) (the first of each block starts from the tile's gate
+//                    biases); p = exp2(a * scale log2 e - m) for 32/(2*KK) scores of prev.
+//   PV slots (4*DB): MFMA of O += V^T P^T; bf16 packing and row sum of P(prev); row max of
+//                    cur (block 0 first: its MFMAs finished earlier).
 // With GATE the wave also runs the gate scan of the next tile (GateJob) in the P.V slots, so
 // the wave that owns the scan does not hold the others up at the next barrier.
 template <int D, bool GATE>
 __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float* r2cur, const Bf16Stage<D>& prev,
                                             const LaneOffsets<D>& off, const bf16x8 (&qreg)[D / 16],
-                                            f32x16 (&sp)[2], f32x16 (&sc)[2], f32x16 (&oacc)[D / 32],
-                                            f32x16& cinit, float& m, float& lsum, int lane, float scale_log2,
-                                            const GateJob& gj) {
+                                            f32x16 (&sp)[2], f32x16 (&sc)[2], f32x16 (&oacc)[D / 32], float& m,
+                                            float& lsum, int lane, float scale_log2, const GateJob& gj) {
   const int hi = lane >> 5;
   constexpr int KK = PipeGeom<D>::KK, DB = PipeGeom<D>::DB;
   constexpr int NQ = 2 * KK;   // S MFMAs
   constexpr int NP = 4 * DB;   // P.V MFMAs
   constexpr int PFK = NQ >= 6 ? 4 : NQ - 2;  // K operands in flight
   constexpr int PFV = NP >= 4 ? 4 : NP;      // V operands in flight
-  constexpr int RD = 3;         // slots between loading a gate-bias quad and its first use
   constexpr int EQ = 32 / NQ;  // exponentials per S slot
   constexpr int EP = 32 / NP;  // scores per P.V slot
   static_assert(NQ >= PFK + 2 && NQ >= PFV && NP >= PFV && 32 % NQ == 0 && 32 % NP == 0, "slot shares");
 
   bf16x8 kop[NQ];
   bf16x8 vop[NP];
-  f32x4 r2[8];
   bf16x8 p[4];
   auto kread = [&](int i) -> bf16x8 {
     return lds_read_b128(cur.k, (off.k ^ (uint32_t)((i >> 1) << 5)) + (uint32_t)((i & 1) * 64 * D));
@@ -499,6 +478,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
     for (int e = 0; e < 8; ++e) p[pi][e] = (bf16)sp[b][8 * u + e];
   };
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  const float negm = -m;
   float ls0 = lsum, ls1 = 0.0f;
   float mx0 = kNegInf, mx1 = kNegInf;
   double gx = 0.0, gy = 0.0;  // gate value of key 63-lane of the next tile, its running scan
@@ -510,8 +490,12 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
   if constexpr (GATE) __asm__ volatile("; gate" : "+v"(sp[0]), "+v"(sp[1]));
   else __asm__ volatile("; nogate" : "+v"(sp[0]), "+v"(sp[1]));
   __builtin_amdgcn_sched_barrier(0);
+  // The bias tuples land directly in the (dead) accumulators of cur, ahead of the K operands.
+  sc[0] = pipe_bias(r2cur, 0, hi);
+  kop[0] = kread(0);
+  sc[1] = pipe_bias(r2cur, 1, hi);
 #pragma unroll
-  for (int i = 0; i < PFK; ++i) kop[i] = kread(i);
+  for (int i = 1; i < PFK; ++i) kop[i] = kread(i);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
@@ -519,18 +503,11 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
     // The slot's exponentials go ahead of its MFMA: at the start of a tile they run while the
     // first K operands are still in flight.
 #pragma unroll
-    for (int e = i * EQ; e < (i + 1) * EQ; ++e)
-      sp[e >> 4][e & 15] = exp2_hw(PipeGeom<D>::FOLD ? sp[e >> 4][e & 15] : sp[e >> 4][e & 15] - m);
+    for (int e = i * EQ; e < (i + 1) * EQ; ++e) sp[e >> 4][e & 15] = exp2_hw(fmaf(sp[e >> 4][e & 15], scale_log2, negm));
     __builtin_amdgcn_sched_barrier(0);
-    if (kk == 0)
-      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], cinit, 0, 0, 0);
-    else
-      sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], sc[b], 0, 0, 0);
+    sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qreg[kk], sc[b], 0, 0, 0);
     if (i + PFK < NQ) kop[i + PFK] = kread(i + PFK);
     if (i >= NQ - PFV) vop[i - (NQ - PFV)] = vread(i - (NQ - PFV));  // first V operands of the P.V slots
-#pragma unroll
-    for (int kq = 0; kq < 8; ++kq)  // bias quads needed in the first P.V slots
-      if ((4 * kq) / EP - RD + NQ == i) r2[kq] = *reinterpret_cast<const f32x4*>(&r2cur[8 * kq + 4 * hi]);
     if (i == NQ - 1) pack(0);
     if (GATE && i == 0) gx = (double)((gj.kt * kBC + 63 - lane <= gj.fref) ? gj.lf[63 - lane] : 0.0f);
     __builtin_amdgcn_sched_barrier(0);
@@ -540,9 +517,6 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
     const int pi = i / DB, db = i % DB;
     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], p[pi], oacc[db], 0, 0, 0);
     if (i + PFV < NP) vop[i + PFV] = vread(i + PFV);
-#pragma unroll
-    for (int kq = 0; kq < 8; ++kq)
-      if ((4 * kq) / EP - RD == i) r2[kq] = *reinterpret_cast<const f32x4*>(&r2cur[8 * kq + 4 * hi]);
     if (db == DB - 1 && pi < 3) pack(pi + 1);
     // row sum: the 4 words of p[pi] over the DB slots of pi
 #pragma unroll
@@ -553,9 +527,7 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
     }
 #pragma unroll
     for (int e = i * EP; e < (i + 1) * EP; ++e) {
-      const int b = e >> 4, r = e & 15;
-      const float sv = fmaf(sc[b][r], scale_log2, r2[4 * b + (r >> 2)][r & 3]);
-      sc[b][r] = sv;
+      const float sv = sc[e >> 4][e & 15];
       if (e & 1) mx1 = fmaxf(mx1, sv);
       else mx0 = fmaxf(mx0, sv);
     }
@@ -564,14 +536,14 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
       for (int k = 1; k <= 8; ++k) {
         if ((k - 1) * NP / 8 == i) {
           if (k <= 7) wave_scan_step(k, gx, gy);
-          else gate_finish(gy, gj.r2, nullptr, *gj.rows, lane, gj.kt, gj.row0, gj.ref, *gj.carry);
+          else gate_finish(gy, gj.r2, nullptr, *gj.rows, lane, gj.kt, gj.row0, gj.ref, *gj.carry, gj.unit);
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   lsum = ls0 + ls1;
-  pipe_rescale<PipeGeom<D>::FOLD, DB>(pair32_max(fmaxf(mx0, mx1)), m, lsum, oacc, sc, cinit, scale_log2);
+  pipe_rescale<DB>(pair32_max(fmaxf(mx0, mx1)) * scale_log2, m, lsum, oacc);
 }
 
 // Kernel body.  NWR waves of 32 rows each share a block of 32*NWR query rows; with SP == 2
@@ -723,18 +695,21 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   f32x16 sa[2], sb[2];  // scores of the tiles at even / odd loop positions
   sa[0] = sa[1] = sb[0] = sb[1] = f32x16{};
-  float m = 0.0f, lsum = 0.0f;  // m: running max (base 2); scores are kept relative to it
-  f32x16 cinit = f32x16{};      // -m / (scale log2 e) in every lane register: S accumulators start there
+  float m = 0.0f, lsum = 0.0f;  // m: running max of the base-2 scores
+  // Stored biases R_j / scale: with an accumulator a = q.k + R_j / scale, the base-2 score is
+  // a * scale_log2 (the unit is taken against the fp32 scale_log2 that multiplies it).
+  const double bias_unit = kLog2ed / (double)scale_log2;
   auto gate_in = [&](const float* lf, int t, int ln) {
     return (t * kBC + 63 - ln <= fref) ? lf[63 - ln] : 0.0f;
   };
   if (lead && top >= bot)
-    gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry);
+    gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry,
+              bias_unit);
 
   // Pruning test for tile kt (and so every tile below it), wave-uniform.
   auto prune_stop = [&](int kt, const float* r2t) -> bool {
     (void)kt;
-    const float bound = qn_lds[tid] * rows.kmax + r2t[kBC - 1] + rows.prune_t;
+    const float bound = qn_lds[tid] * rows.kmax + r2t[kBC - 1] * scale_log2 + rows.prune_t;
     const bool ok = my_row >= n || bound < m;
     return __ballot(!ok) == 0;
   };
@@ -769,23 +744,21 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
     const bool gate_job = lead && kt - 1 >= bot;
     bool gate_done = false;
-    const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, fref, &rows, &carry};
+    const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, fref, &rows, &carry, bias_unit};
     const bool stop_here = PRUNE && active && !wdone && kt < kt_first && kt >= bot && prune_stop(kt, gates(J));
     if (active && kt >= bot && kt <= kt_first && !wdone) {
       if (kt == kt_first) {  // first tile of this wave: nothing to overlap with
-        pipe_qk<D>(stage(J)[0], off.k, qreg, cinit, sc);
+        pipe_qk<D>(stage(J)[0], off.k, qreg, gates(J), ln >> 5, sc);
         // split 0's first tile holds the row's diagonal (causal) or the end of the sequence
-        const float mx = sp == 0 ? pipe_scores<true>(sc, gates(J), kt * kBC, CAUSAL ? my_row : n - 1, ln >> 5,
-                                                     scale_log2)
-                                 : pipe_scores<false>(sc, gates(J), 0, 0, ln >> 5, scale_log2);
-        pipe_first_max<PipeGeom<D>::FOLD>(mx, m, sc, cinit, scale_log2);
+        m = sp == 0 ? pipe_scores<true>(sc, kt * kBC, CAUSAL ? my_row : n - 1, ln >> 5, scale_log2)
+                    : pipe_scores<false>(sc, 0, 0, ln >> 5, scale_log2);
       } else if (gate_job) {
-        pipe_steady<D, true>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, cinit, m, lsum, ln,
+        pipe_steady<D, true>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
                              scale_log2, gj);
         gate_done = true;
       } else {
-        pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, cinit, m, lsum,
-                              ln, scale_log2, gj);
+        pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
+                              scale_log2, gj);
       }
       // With pruning, a wave whose remaining keys (tile kt and below) are all negligible still
       // finishes tile kt (same code path) and then stops.
@@ -795,14 +768,15 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
       }
       if (kt == bot || wdone) {  // drain: probabilities and P.V of the split's last tile
         bf16x8 p[4];
-        pipe_probs<PipeGeom<D>::FOLD>(sc, m, p);
+        pipe_probs(sc, m, scale_log2, p);
         pipe_pv<D>(stage(J)[0], off.v, p, oacc);
         lsum = pipe_psum(p, lsum);
       }
     }
     // Otherwise the lead wave runs it here (read by everyone after the next barrier).
     if (gate_job && !gate_done)
-      gate_tile(gates(J1{}), nullptr, rows, ln, kt - 1, row0, ref, gate_in(stage(J1{})[sp].lf, kt - 1, ln), carry);
+      gate_tile(gates(J1{}), nullptr, rows, ln, kt - 1, row0, ref, gate_in(stage(J1{})[sp].lf, kt - 1, ln), carry,
+                bias_unit);
     return false;
   };
 
@@ -1047,7 +1021,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   for (int kt = kt_hi; kt >= 0; --kt) {
     __syncthreads();
     f32_store_tile<D>(tile, lds, tid);
-    if (wave == 0) gate_tile(lds.r2, lds.r64, lds.rows, lane, kt, row0, ref, lf, carry);
+    if (wave == 0) gate_tile(lds.r2, lds.r64, lds.rows, lane, kt, row0, ref, lf, carry, kLog2ed);
     __syncthreads();
     if (kt > 0) {
       f32_load_tile<D>(tile, kb, vb, kt - 1, n, tid, rs);
