@@ -2,10 +2,11 @@
 
 The pages derive no backward pass: the oracle differentiates the forward definition by the chain
 rule (oracle.fwd_bwd_head).  Its pins check that derivation against routes that do not use it:
-finite differences of the pinned forward oracle, PyTorch autograd through a direct transcription
-of the FoX module page's forward (cumsum of log gates, bias cum[i] - cum[j], scaled q k^T, mask,
-softmax, times v), PyTorch's own attention backward when the gates are 1, and the invariance of
-the result to the first gate.  Planted mistakes in copies of the derivation must each fail a pin.
+finite differences of the pinned forward oracle, PyTorch autograd through the decay-product form
+of the weights (foxwindow README, opening paragraph: content term times D_ij, the product of the
+gates between key and query), PyTorch's own attention backward when the gates are 1, and the
+invariance of the result to the first gate.  Planted mistakes in copies of the derivation must each
+fail a pin.
 """
 
 from __future__ import annotations
@@ -56,15 +57,25 @@ def bpin_finite_differences(bwd):
 
 
 def _torch_grads(q, k, v, logf, scale, do, causal):
-    """Autograd through a direct transcription of the module's forward (fp64)."""
+    """Autograd (fp64) through the weights written as content times decay (foxwindow README,
+    opening paragraph): w_ij = exp(scale q_i.k_j) * D_ij with D_ij the product of the gates f_t,
+    j < t <= i, and o_i = sum_j w_ij v_j / sum_j w_ij.  Unmasked, a key j > i takes the reciprocal
+    product over i < t <= j (the same c_i - c_j).  D is built from an explicit indicator of which
+    gates lie between each query and key, not from prefix sums."""
     t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)  # noqa: E731
     tq, tk, tv, tl = t(q), t(k), t(v), t(logf)
-    c = torch.cumsum(tl, 0)
-    s = scale * (tq @ tk.T) + (c[:, None] - c[None, :])
+    n = q.shape[0]
+    ii = torch.arange(n)[:, None, None]
+    jj = torch.arange(n)[None, :, None]
+    tt = torch.arange(n)[None, None, :]
+    between = ((jj < tt) & (tt <= ii)).double() - ((ii < tt) & (tt <= jj)).double()  # [query, key, gate]
+    log_decay = between @ tl
+    logw = scale * (tq @ tk.T) + log_decay
     if causal:
-        n = q.shape[0]
-        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1), float("-inf"))
-    o = torch.softmax(s, dim=-1) @ tv
+        keep = torch.arange(n)[None, :] <= torch.arange(n)[:, None]
+        logw = torch.where(keep, logw, torch.full_like(logw, float("-inf")))
+    w = torch.exp(logw - logw.max(dim=1, keepdim=True).values.detach())
+    o = (w @ tv) / w.sum(dim=1, keepdim=True)
     (o * torch.tensor(do)).sum().backward()
     return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy(), tl.grad.numpy()
 
