@@ -10,7 +10,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfox.so")
+# FOX_LIBRARY selects another build of the same library (the host-sanitizer check build).
+LIB_PATH = os.environ.get("FOX_LIBRARY") or os.path.join(_HERE, "libfox.so")
 
 FOX_OK = 0
 FOX_ERR_INVALID_ARG = 1

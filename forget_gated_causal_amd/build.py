@@ -3,6 +3,12 @@
 Usage: ``python -m forget_gated_causal_amd.build`` (or ``build()`` from Python).
 Every call recompiles; objects go to ``_build/`` at the repository root and the
 shared library to ``forget_gated_causal_amd/libfox.so``.
+
+``python -m forget_gated_causal_amd.build --host-sanitizers`` also builds
+``_build/libfox_hostsan.so``: the same kernels, with the host layer (fox_api.hip: argument
+checks, workspace carving, launches) under AddressSanitizer and UndefinedBehaviorSanitizer.
+It is a check build, loaded through FOX_LIBRARY with the ASan runtime preloaded
+(``host_sanitizer_env()``); device code is never instrumented.
 """
 
 from __future__ import annotations
@@ -26,6 +32,14 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+
+
+# Host-only sanitizers: every -fsanitize= goes to the host pass alone.
+HOST_SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+HOSTSAN_LIB = os.path.join(BUILD, "libfox_hostsan.so")
 
 
 def hipcc() -> str:
@@ -64,5 +78,48 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime (which also carries the UBSan handlers)."""
+    out = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    path = out.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's shared ASan runtime not found")
+    return path
+
+
+def build_host_sanitized() -> str:
+    """libfox with fox_api.hip's host code instrumented; the kernel objects are build()'s."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        if src == "fox_api.hip":
+            obj = os.path.join(BUILD, "fox_api_hostsan.o")
+            _run([cc, *HIP_FLAGS, *HOST_SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        else:
+            obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+            if not os.path.exists(obj):
+                _run([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    tmp = HOSTSAN_LIB + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SAN_FLAGS, *objs, "-o", tmp])
+    os.replace(tmp, HOSTSAN_LIB)
+    return HOSTSAN_LIB
+
+
+def host_sanitizer_env(env=None) -> dict:
+    """Environment for a child process that loads the sanitized build instead of libfox.so."""
+    e = dict(os.environ if env is None else env)
+    e["FOX_LIBRARY"] = HOSTSAN_LIB
+    e["LD_PRELOAD"] = asan_runtime()
+    # Python itself is not built with ASan: leaks at exit and its allocator are not ours.
+    e["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1:halt_on_error=1"
+    e["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    return e
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--host-sanitizers" in sys.argv[1:]:
+        print(build_host_sanitized())

@@ -42,24 +42,30 @@
 extern "C" {
 #endif
 
-typedef enum fox_status {
+/* Status, dtype and layout values travel as int32_t, not as enum types: a caller may pass
+   any integer (an unknown dtype is rejected with FOX_ERR_UNSUPPORTED, an unknown status gets
+   "unknown status"), and an out-of-range value of an enum type would be undefined in C++. */
+typedef int32_t fox_status_t;
+enum fox_status_code {
   FOX_OK = 0,
   FOX_ERR_INVALID_ARG = 1, /* null pointer, size <= 0 or too large, bad scale, misaligned pointer */
   FOX_ERR_UNSUPPORTED = 2, /* head dim not in {32, 64, 128}, unknown dtype */
   FOX_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than fox_attn_decode_workspace_bytes() */
   FOX_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
   FOX_ERR_SCRATCH = 5      /* fox_attn_decode_noalloc: the sizes need more than FOX_DECODE_SCRATCH_BYTES */
-} fox_status_t;
+};
 
-typedef enum fox_dtype {
+typedef int32_t fox_dtype_t;
+enum fox_dtype_code {
   FOX_F32 = 0, /* IEEE binary32 */
   FOX_BF16 = 1 /* bfloat16; products accumulate in fp32, outputs rounded to nearest even */
-} fox_dtype_t;
+};
 
-typedef enum fox_layout {
+typedef int32_t fox_layout_t;
+enum fox_layout_code {
   FOX_HEAD_MAJOR = 0, /* q/k/v/o [b, h, n, d]; logf / lse / c [b, h, n] */
   FOX_TOKEN_MAJOR = 1 /* q/k/v/o [b, n, h, d]; logf / lse / c [b, n, h] */
-} fox_layout_t;
+};
 
 /* Largest sequence length / cache length accepted (keeps all index arithmetic in range). */
 #define FOX_MAX_SEQ (1 << 22)
