@@ -32,6 +32,7 @@ import csv
 import glob
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -150,6 +151,109 @@ def write_traffic_summary(args):
     if args.alg_bytes:
         lines.append(f"algorithmic_bytes_per_launch: {args.alg_bytes:.0f}")
         lines.append(f"traffic_over_algorithmic: {(rd + wr) / args.alg_bytes:.3f}")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def write_trace_summary(args):
+    """A rocprofv3 --kernel-trace --stats table (kernel_stats.csv) plus the bench lines that the same
+    run printed, as a short text summary."""
+    with open(args.stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    bench_lines = []
+    if args.bench_log:
+        with open(args.bench_log) as fh:
+            bench_lines = [l.rstrip() for l in fh if l.startswith("# fox_")]
+    lines = [f"# rocprofv3 kernel-trace summary: {args.title}",
+             "# command (<out> is the output directory):",
+             f"#   cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d <out> -o t -- python3 <repo>/bench.py {args.bench_args}",
+             f"#   python3 bench.py --trace-summary ... (this file)"]
+    lines += [f"# {n}" for n in (args.note or [])]
+    if bench_lines:
+        lines.append("# bench.py's own lines from the same run (HIP events around the timed calls):")
+        lines += ["#   " + b[:400] for b in bench_lines]
+    lines += ["", f"{'kernel':100s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_ms':>9s}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:100]:100s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:9.3f}")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _demangle(name: str) -> str:
+    """Short readable name of one of this library's kernels from its mangled symbol: the name and its
+    integer / bool template arguments (e.g. fwd_bf16_pipe_kernel<128,8,1,0,1,0>); other names as given."""
+    m = re.match(r"_ZN3fox12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    pos = m.end() + int(m.group(1))
+    ident = name[m.end():pos]
+    vals = []
+    if name[pos:pos + 1] == "I":
+        pos += 1
+        arg = re.compile(r"L[ib](-?\d+)E")
+        while (a := arg.match(name, pos)) is not None:
+            vals.append(a.group(1))
+            pos = a.end()
+    return f"{ident}<{','.join(vals)}>" if vals else ident
+
+
+# algorithmic flop per causal pair of each MFMA kernel (the backward's parts count their own share)
+MFMA_KERNEL_FLOP_PER_PAIR_D = {"fwd_bf16_pipe_kernel": 4, "bwd_kv_kernel": 8, "bwd_dq_kernel": 6}
+
+
+def write_mfma_summary(args):
+    """MFMA use per kernel from rocprofv3 --pmc runs of SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 and GRBM_GUI_ACTIVE; --pmc-csv takes workload:kind:path triples."""
+    import fox_inputs as fi
+    lines = ["# rocprofv3 counter summary: MFMA use per kernel",
+             "# commands (one run per workload; <out> is the output directory):",
+             "#   cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE -f csv \\",
+             "#     -d <out>/<w>_<kind> -o p -- python3 <repo>/bench.py --workload <w> --only --no-cpu-baseline --steps 4 "
+             "--warmup 2 [--backward]",
+             "#   python3 bench.py --mfma-summary ... (this file)",
+             "# per dispatch (mean over every dispatch of the kernel in the run, warm-up included):",
+             "#   mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (bf16 MFMA flops executed, masked diagonal halves included)",
+             "#   mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * GRBM_GUI_ACTIVE / 8); GRBM_GUI_ACTIVE is summed over",
+             "#               the 8 XCDs; the busy counter reads 32 cycles per 32x32x16 bf16 MFMA",
+             "#   alg_flop  = 4 d (forward), 8 d (backward key side), 6 d (backward query side, which recomputes S and",
+             "#               dP) per causal pair",
+             "",
+             f"{'workload':10s} {'kernel':44s} {'disp':>5s} {'dur_us':>9s} {'mfma_flop':>11s} {'alg_flop':>11s} "
+             f"{'exec/alg':>8s} {'mfma_util':>9s}"]
+    for spec in args.pmc_csv:
+        tag, kind, path = spec.split(":", 2)
+        cfg = fi.FWD[tag]
+        pairs = cfg.B * cfg.H * cfg.N * (cfg.N + 1) / 2
+        per = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                k = r["Kernel_Name"]
+                d = per.setdefault(k, {"ids": set(), "dur": {}, "c": {}})
+                d["ids"].add(r["Dispatch_Id"])
+                d["dur"][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for k, d in per.items():
+            if not k.startswith("void fox::") and "fox" not in k:
+                continue
+            n = len(d["ids"])
+            mops = d["c"].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) / n
+            busy = d["c"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n
+            act = d["c"].get("GRBM_GUI_ACTIVE", 0.0) / n / 8
+            dur = sum(d["dur"].values()) / n / 1e3
+            short = _demangle(k).replace("fox::(anonymous namespace)::", "").replace("void ", "")
+            short = short.split("(")[0].replace(" ", "")
+            if kind == "bwd" and short.startswith("fwd_"):
+                continue  # the forward that makes the backward's inputs
+            alg = next((m * cfg.d * pairs for nm, m in MFMA_KERNEL_FLOP_PER_PAIR_D.items() if nm in short), 0.0)
+            util = busy / (1024 * act) if act else 0.0
+            ratio = f"{mops * 512 / alg:8.3f}" if alg else f"{'-':>8s}"
+            lines.append(f"{tag:10s} {short[:44]:44s} {n:5d} {dur:9.2f} {mops * 512:11.4e} {alg:11.4e} {ratio} "
+                         f"{100 * util:8.1f}%")
+    lines += [f"# {n}" for n in (args.note or [])]
     with open(args.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -489,7 +593,18 @@ def main():
     ap.add_argument("--kernel", help="kernel label as bench.py reports it"), ap.add_argument("--kernel-match")
     ap.add_argument("--kind", choices=["fwd", "decode", "bwd"], default="fwd")
     ap.add_argument("--alg-bytes", type=float, default=0.0), ap.add_argument("--out")
+    ap.add_argument("--trace-summary", action="store_true", help="write a kernel-trace summary from a stats CSV")
+    ap.add_argument("--stats-csv"), ap.add_argument("--bench-log"), ap.add_argument("--title")
+    ap.add_argument("--bench-args", default=""), ap.add_argument("--note", action="append")
+    ap.add_argument("--mfma-summary", action="store_true", help="write an MFMA-use summary from counter CSVs")
+    ap.add_argument("--pmc-csv", action="append", help="workload:kind:path of one counter run")
     args = ap.parse_args()
+    if args.trace_summary:
+        write_trace_summary(args)
+        return
+    if args.mfma_summary:
+        write_mfma_summary(args)
+        return
     global USE_GRAPH
     USE_GRAPH = args.graph
     if args.traffic_summary:

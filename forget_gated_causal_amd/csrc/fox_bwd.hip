@@ -44,8 +44,10 @@
 //    lane holds one query): S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, and
 //    dQ += dS K with the dS^T accumulators as the A operand (queries as M) and K read transposed.
 //    Writes dq and the row sums of dS.
-//  * bwd_pre_kernel before them: D_i, and per head the padded row vectors both main kernels load;
-//    the reversed prefix scan (fox_scan.hip) after them: dlog f from row sums - column sums.
+//  * before them: the gate-rows kernel (fox_scan.hip: the padded row vectors and the fp64 block
+//    sums C_b that both parts load), then bwd_pre_kernel (D_i = dO_i . O_i, with the mask) or
+//    bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32, without it); after them the reversed
+//    prefix scan (fox_scan.hip): dlog f from row sums - column sums.
 // Tensors are head-major [B,H,N,d] or token-major [B,N,H,d] (BwdLayout: row strides d or H d,
 // gate-vector strides 1 or H); the workspace is head-major either way.
 #include <math.h>

@@ -17,8 +17,10 @@
 //   * Gate bias without a prefix-sum buffer: while walking backwards one wave keeps the fp64
 //     suffix sum R_j = sum_{t=j+1..ref} log f_t (ref = the block's last row).  Then
 //     c_i - c_j = R_j - R_i; the per-row constant R_i drops out of the softmax and is added
-//     back to lse only.  Each score costs one FMA: s2 = acc*scale*log2e + R_j*log2e.  The
-//     block's own c_i = c_ref - R_i is written as the `c` output.
+//     back to lse only.  The biases enter as the initial value of the S accumulators (R_j /
+//     scale per key), so a score costs one FMA into its exponential:
+//     p = exp2(acc * scale * log2e - m).  The block's own c_i = c_ref - R_i is written as the
+//     `c` output.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N), so a lane holds one
 //     query row and 16 keys per 32x32 block: the row max / sum are in-lane plus one
 //     permlane32 swap.  The S^T accumulator registers are, after rounding to bf16, directly
