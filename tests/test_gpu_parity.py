@@ -187,6 +187,27 @@ def test_fwd_noncausal_wide_grid_whole_heads():
     _check_whole_heads(inp, o, lse, [(0, 0), (1, 127)], causal=False, label=cfg.desc + " unmasked")
 
 
+# Gates far from 1 (log f about -3 per step, and a constant -20): the gate biases of a 256-row block
+# reach hundreds to thousands of nats, and the bf16 forward carries them in its fp32 S accumulators
+# (as R_j / scale) through every k-step.  Both the 4-wave and the 8-wave kernels, both modes.
+STRONG = [(64, 2, 2, 1000, "lsig", -3.0), (128, 2, 2, 1000, "lsig", -3.0), (128, 2, 2, 1000, "const", 20.0),
+          (128, 2, 128, 1000, "lsig", -3.0), (128, 2, 128, 1000, "const", 20.0)]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "unmasked"])
+@pytest.mark.parametrize("d,B,H,n,gate,g", STRONG)
+def test_fwd_strong_gates(d, B, H, n, gate, g, causal):
+    if gate == "const":
+        cfg = fi.FwdConfig(f"strong_{d}_{B}_{H}_{n}_c{g}", B, H, n, d, "bf16", gate="const", m=g)
+    else:
+        cfg = fi.FwdConfig(f"strong_{d}_{B}_{H}_{n}_{g}", B, H, n, d, "bf16", g, 1.0)
+    inp = fi.fwd_inputs(cfg)
+    o, lse, _ = _run_fwd(inp) if causal else _run_fwd_nc(inp)
+    heads = [(0, 0), (B - 1, H - 1)]
+    _check_whole_heads(inp, o, lse, heads, causal=causal, label=cfg.desc + ("" if causal else " unmasked"))
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
 # ---------------------------------------------------------------- forward without the causal mask
 
 def _run_fwd_nc(inp):
