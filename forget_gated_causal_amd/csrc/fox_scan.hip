@@ -106,11 +106,25 @@ __global__ __launch_bounds__(kScanThreads) void bwd_gate_rows_kernel(const float
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int span = ncb * kGateBlock;  // >= npad
   double carry = 0.0;
+  // A chunk's log f and lse are loaded one chunk ahead, so the loads of the next chunk are in
+  // flight while this one is scanned and written.
+  float lfv[kScanPerThread], lsv[kScanPerThread];
+  auto load_chunk = [&](int base, float (&lf)[kScanPerThread], float (&ls)[kScanPerThread]) {
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) {
+      const int i = base + tid * kScanPerThread + e;
+      lf[e] = i < n ? logf[g0 + (int64_t)i * gi.gs] : 0.0f;
+      ls[e] = i < n ? lse[g0 + (int64_t)i * gi.gs] : 0.0f;
+    }
+  };
+  load_chunk(0, lfv, lsv);
   for (int base = 0, it = 0; base < span; base += kScanChunk, ++it) {
     const int i0 = base + tid * kScanPerThread;
+    float nlf[kScanPerThread] = {}, nls[kScanPerThread] = {};
+    if (base + kScanChunk < span) load_chunk(base + kScanChunk, nlf, nls);
     double x[kScanPerThread];
 #pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e) x[e] = i0 + e < n ? (double)logf[g0 + (int64_t)(i0 + e) * gi.gs] : 0.0;
+    for (int e = 0; e < kScanPerThread; ++e) x[e] = (double)lfv[e];
 #pragma unroll
     for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
     const double t = wave_incl_scan(x[kScanPerThread - 1]);
@@ -137,14 +151,18 @@ __global__ __launch_bounds__(kScanThreads) void bwd_gate_rows_kernel(const float
       if (i < npad) {
         const double cq = (pre + x[e]) - cblk;
         const bool live = i < n;
-        const float ls = live ? lse[g0 + (int64_t)i * gi.gs] : 0.0f;
-        blk[i] = live ? (float)((cq - (double)ls) * kLog2ed) : -INFINITY;
+        blk[i] = live ? (float)((cq - (double)lsv[e]) * kLog2ed) : -INFINITY;
         blk[2 * npad + i] = live ? (float)(cq * kLog2ed) : INFINITY;
         if (!live) blk[npad + i] = 0.0f;
       }
     }
     if ((lane & (LPB - 1)) == 0 && i0 < span) cbr[i0 / kGateBlock] = cblk;
     carry += chunk;
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) {
+      lfv[e] = nlf[e];
+      lsv[e] = nls[e];
+    }
   }
 }
 
