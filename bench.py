@@ -69,7 +69,7 @@ KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_device.h"], "decode": ["fox_decode
                   "bwd": ["fox_bwd.hip", "fox_scan.hip", "fox_device.h"]}
 COPY_CAL_BYTES = 1 << 30
 DECODE_KERNEL = "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>"
-BWD_KERNEL = "fox_attn_bwd<{d},causal>: bwd_gate_rows + bwd_pre + bwd_kv + bwd_dq + suffix scan"
+BWD_KERNEL = "fox_attn_bwd<{d},causal>: bwd_rows (gate rows + D) + bwd_kv + bwd_dq + suffix scan"
 
 
 def kernel_source_digest(kind: str) -> str:

@@ -44,10 +44,10 @@
 //    lane holds one query): S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, and
 //    dQ += dS K with the dS^T accumulators as the A operand (queries as M) and K read transposed.
 //    Writes dq and the row sums of dS.
-//  * before them: the gate-rows kernel (fox_scan.hip: the padded row vectors and the fp64 block
-//    sums C_b that both parts load), then bwd_pre_kernel (D_i = dO_i . O_i, with the mask) or
-//    bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32, without it); after them the reversed
-//    prefix scan (fox_scan.hip): dlog f from row sums - column sums.
+//  * before them: the gate rows (gate_rows_block: the padded row vectors and the fp64 block sums
+//    C_b that both parts load) and D_i = dO_i . O_i in one launch (bwd_rows_kernel) with the
+//    mask; without it the gate rows, then bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32).
+//    After them the reversed prefix scan (fox_scan.hip): dlog f from row sums - column sums.
 // Tensors are head-major [B,H,N,d] or token-major [B,N,H,d] (BwdLayout: row strides d or H d,
 // gate-vector strides 1 or H); the workspace is head-major either way.
 #include <math.h>
@@ -216,14 +216,114 @@ __device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows,
   }
 }
 
+// The backward's gate terms of one (batch, head) row.  The prefix sums are split at blocks of
+// kGateBlock positions: C_b = sum_{t < 32b} log f_t (fp64, one per block) and the in-block part
+// cq_i = sum_{32b(i) <= t <= i} log f_t, so that c_i - c_j = (cq_i - cq_j) + (C_b(i) - C_b(j)).
+// Every term the backward kernels round to fp32 is then as small as the bias it belongs to, not
+// as large as |c| (which grows with the sequence).  Written into the head's row-vector block
+// [a | D | cl] of 3 * npad floats: a_i = (cq_i - lse_i) log2 e, cl_i = cq_i log2 e, and D_i = 0
+// past n (a = -inf, cl = +inf there, so padded rows and keys carry no weight); C_b for the ncb
+// blocks into cb.  One 256-thread workgroup per row, chunks of 1024 positions, each thread 4 of them, fp64 scan
+// (a wave DPP scan and a 4-entry LDS scan per chunk, a carry between chunks).
+constexpr int kGateBlock = 32;
+struct GateRowsIn {  // logf / lse of row r: (r / nh) gbs + (r % nh) ghs + t gs
+  int nh;
+  int64_t gbs, ghs;
+  int gs;
+};
+GateRowsIn gate_rows_in(int nh, int n, bool token_major) {
+  return token_major ? GateRowsIn{nh, (int64_t)n * nh, 1, nh} : GateRowsIn{1, (int64_t)n, 0, 1};
+}
+constexpr int kScanThreads = 256;
+constexpr int kScanPerThread = 4;
+constexpr int kScanChunk = kScanThreads * kScanPerThread;
+__device__ __forceinline__ void gate_rows_block(const float* __restrict__ logf, const float* __restrict__ lse,
+                                                float* __restrict__ rowv, double* __restrict__ cb, int n, int npad,
+                                                int ncb, const GateRowsIn& gi, int64_t row) {
+  static_assert(kGateBlock % kScanPerThread == 0 && 64 % (kGateBlock / kScanPerThread) == 0, "block lanes");
+  constexpr int LPB = kGateBlock / kScanPerThread;  // lanes per block
+  __shared__ double wave_tot[2][kScanThreads / 64];
+  const int64_t g0 = (row / gi.nh) * gi.gbs + (row % gi.nh) * gi.ghs;
+  float* blk = rowv + row * 3 * (int64_t)npad;
+  double* cbr = cb + row * (int64_t)ncb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int span = ncb * kGateBlock;  // >= npad
+  double carry = 0.0;
+  // A chunk's log f and lse are loaded one chunk ahead, so the loads of the next chunk are in
+  // flight while this one is scanned and written.
+  float lfv[kScanPerThread], lsv[kScanPerThread];
+  auto load_chunk = [&](int base, float (&lf)[kScanPerThread], float (&ls)[kScanPerThread]) {
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) {
+      const int i = base + tid * kScanPerThread + e;
+      lf[e] = i < n ? logf[g0 + (int64_t)i * gi.gs] : 0.0f;
+      ls[e] = i < n ? lse[g0 + (int64_t)i * gi.gs] : 0.0f;
+    }
+  };
+  load_chunk(0, lfv, lsv);
+  for (int base = 0, it = 0; base < span; base += kScanChunk, ++it) {
+    const int i0 = base + tid * kScanPerThread;
+    float nlf[kScanPerThread] = {}, nls[kScanPerThread] = {};
+    if (base + kScanChunk < span) load_chunk(base + kScanChunk, nlf, nls);
+    double x[kScanPerThread];
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) x[e] = (double)lfv[e];
+#pragma unroll
+    for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
+    const double t = wave_incl_scan(x[kScanPerThread - 1]);
+    const double excl = wave_shr1(t);
+    if (lane == 63) wave_tot[it & 1][wave] = t;
+    __syncthreads();
+    double before = carry, chunk = 0.0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      if (w < wave) before += wave_tot[it & 1][w];
+      chunk += wave_tot[it & 1][w];
+    }
+    const double pre = before + excl;  // sum of log f before position i0
+    // C_b: the prefix before the block's first position, held by the block's first lane
+    const int src = lane & ~(LPB - 1);
+    const u32x2 pw = __builtin_bit_cast(u32x2, pre);
+    u32x2 cw;
+    cw[0] = (uint32_t)__shfl((int)pw[0], src);
+    cw[1] = (uint32_t)__shfl((int)pw[1], src);
+    const double cblk = __builtin_bit_cast(double, cw);
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) {
+      const int i = i0 + e;
+      if (i < npad) {
+        const double cq = (pre + x[e]) - cblk;
+        const bool live = i < n;
+        blk[i] = live ? (float)((cq - (double)lsv[e]) * kLog2ed) : -INFINITY;
+        blk[2 * npad + i] = live ? (float)(cq * kLog2ed) : INFINITY;
+        if (!live) blk[npad + i] = 0.0f;
+      }
+    }
+    if ((lane & (LPB - 1)) == 0 && i0 < span) cbr[i0 / kGateBlock] = cblk;
+    carry += chunk;
+#pragma unroll
+    for (int e = 0; e < kScanPerThread; ++e) {
+      lfv[e] = nlf[e];
+      lsv[e] = nls[e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void bwd_gate_rows_kernel(const float* __restrict__ logf,
+                                                                     const float* __restrict__ lse,
+                                                                     float* __restrict__ rowv, double* __restrict__ cb,
+                                                                     int n, int npad, int ncb, GateRowsIn gi) {
+  gate_rows_block(logf, lse, rowv, cb, n, npad, ncb, gi, blockIdx.x);
+}
+
 // D_i = dO_i . O_i into the D slot of each head's row-vector block [a | D | cl] (the gate-rows
 // kernel writes a, cl and the padding).  One group of D/8 lanes per (head, padded row).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                                                      float* __restrict__ rowv, int64_t bh_count, int n, int npad,
-                                                      BwdLayout lay) {
+__device__ __forceinline__ void pre_block(const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                                          float* __restrict__ rowv, int64_t bh_count, int n, int npad,
+                                          const BwdLayout& lay, int64_t blk) {
   constexpr int G = D / 8;  // lanes per row, 8 elements each
-  const int64_t prow = (int64_t)blockIdx.x * (kBwdThreads / G) + threadIdx.x / G;
+  const int64_t prow = blk * (kBwdThreads / G) + threadIdx.x / G;
   const int g = threadIdx.x % G;
   const int64_t bh = prow / npad;
   const int i = (int)(prow - bh * npad);
@@ -239,6 +339,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 #pragma unroll
   for (int off = G / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
   if (live && g == 0) rowv[bh * 3 * npad + npad + i] = s;
+}
+
+// With the mask, one launch runs both: workgroups below `rows` build the gate terms of one head's
+// row (gate_rows_block), the rest take D_i for kBwdThreads / (D / 8) padded rows each.  The two
+// write disjoint parts of the row vectors.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const float* __restrict__ logf, const float* __restrict__ lse,
+                                                       const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                                                       float* __restrict__ rowv, double* __restrict__ cb,
+                                                       int64_t rows, int n, int npad, int ncb, GateRowsIn gi,
+                                                       BwdLayout lay) {
+  static_assert(kScanThreads == kBwdThreads, "one block size for both parts");
+  if ((int64_t)blockIdx.x < rows) gate_rows_block(logf, lse, rowv, cb, n, npad, ncb, gi, blockIdx.x);
+  else pre_block<D>(o, dout, rowv, rows, n, npad, lay, (int64_t)blockIdx.x - rows);
 }
 
 // Direct-to-LDS loads of a tile of ROWS rows of D bf16 (global rows from `row0` of the head) into
@@ -840,13 +954,16 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                             ? BwdLayout{(int64_t)n * h * D, (int64_t)D, (int)(h * D), (int64_t)n * h, 1, (int)h, (int)h}
                             : BwdLayout{h * n * (int64_t)D, (int64_t)n * D, D, h * (int64_t)n, (int64_t)n, 1, (int)h};
   const BwdWorkspace w = bwd_workspace(ws, bh, n, npad);
-  hipError_t e = launch_bwd_gate_rows(logf, lse, w.rowv, w.cb, bh, n, npad, (int)h, token_major, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (causal) {
     constexpr int RPB = kBwdThreads / (D / 8);
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((bh * npad + RPB - 1) / RPB)), dim3(kBwdThreads), 0,
-                       stream, (const bf16*)o, (const bf16*)dout, w.rowv, bh, n, npad, lay);
+    const int64_t pre_blocks = (bh * npad + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)(bh + pre_blocks)), dim3(kBwdThreads), 0, stream, logf,
+                       lse, (const bf16*)o, (const bf16*)dout, w.rowv, w.cb, bh, n, npad, ncb,
+                       gate_rows_in((int)h, n, token_major), lay);
   } else {
+    e = launch_bwd_gate_rows(logf, lse, w.rowv, w.cb, bh, n, npad, (int)h, token_major, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dpass_kernel<D>), dim3((unsigned)bh, (unsigned)((n + kQB - 1) / kQB)), dim3(kBwdThreads),
                        0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.rowv,
                        (const double*)w.cb, n, npad, ncb, scale, lay);
@@ -863,6 +980,15 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
 }
 
 }  // namespace
+
+int bwd_gate_blocks(int n) { return (n + 127) / 128 * (128 / kGateBlock); }
+
+hipError_t launch_bwd_gate_rows(const float* logf, const float* lse, float* rowv, double* cb, int64_t rows, int n,
+                                int npad, int nh, bool token_major, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_gate_rows_kernel, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf, lse, rowv, cb,
+                     n, npad, bwd_gate_blocks(n), gate_rows_in(nh, n, token_major));
+  return hipGetLastError();
+}
 
 // workspace: row vectors [bh][3][npad] (fp32), gate block starts [bh][ncb] (fp64), row sums and
 // column sums of dS and the fp32 path's lse normalisation [bh][n] each (fp32)

@@ -48,7 +48,7 @@ hipError_t launch_attn_decode_paged(const void* q, const void* kp, const void* v
                                     int nh, void* o, float* lse, float* ws, int64_t sh, int d, float scale,
                                     bool is_bf16, hipStream_t stream);
 
-// The backward's gate terms (fox_scan.hip): per row, block starts C_b of the prefix sums of log f
+// The backward's gate terms (fox_bwd.hip): per row, block starts C_b of the prefix sums of log f
 // (fp64, bwd_gate_blocks(n) per row, one per 32 positions up to n rounded up to 128) and, in the
 // row-vector block [a | D | cl] of 3 * npad floats, a_i = (cq_i - lse_i) log2 e and cl_i = cq_i
 // log2 e with cq_i = c_i - C_b(i), padded past n (a = -inf, D = 0, cl = +inf).  logf / lse are

@@ -78,105 +78,7 @@ __global__ __launch_bounds__(kScanThreads) void logf_cumsum_kernel(const float* 
   }
 }
 
-// The backward's gate terms of one (batch, head) row.  The prefix sums are split at blocks of
-// kGateBlock positions: C_b = sum_{t < 32b} log f_t (fp64, one per block) and the in-block part
-// cq_i = sum_{32b(i) <= t <= i} log f_t, so that c_i - c_j = (cq_i - cq_j) + (C_b(i) - C_b(j)).
-// Every term the backward kernels round to fp32 is then as small as the bias it belongs to, not
-// as large as |c| (which grows with the sequence).  Written into the head's row-vector block
-// [a | D | cl] of 3 * npad floats: a_i = (cq_i - lse_i) log2 e, cl_i = cq_i log2 e, and D_i = 0
-// past n (a = -inf, cl = +inf there, so padded rows and keys carry no weight); C_b for the ncb
-// blocks into cb.  One 256-thread workgroup per row, chunks of 1024 positions, fp64 scan as above.
-constexpr int kGateBlock = 32;
-struct GateRowsIn {  // logf / lse of row r: (r / nh) gbs + (r % nh) ghs + t gs
-  int nh;
-  int64_t gbs, ghs;
-  int gs;
-};
-__global__ __launch_bounds__(kScanThreads) void bwd_gate_rows_kernel(const float* __restrict__ logf,
-                                                                     const float* __restrict__ lse,
-                                                                     float* __restrict__ rowv, double* __restrict__ cb,
-                                                                     int n, int npad, int ncb, GateRowsIn gi) {
-  static_assert(kGateBlock % kScanPerThread == 0 && 64 % (kGateBlock / kScanPerThread) == 0, "block lanes");
-  constexpr int LPB = kGateBlock / kScanPerThread;  // lanes per block
-  __shared__ double wave_tot[2][kScanThreads / 64];
-  const int64_t row = blockIdx.x;
-  const int64_t g0 = (row / gi.nh) * gi.gbs + (row % gi.nh) * gi.ghs;
-  float* blk = rowv + row * 3 * (int64_t)npad;
-  double* cbr = cb + row * (int64_t)ncb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int span = ncb * kGateBlock;  // >= npad
-  double carry = 0.0;
-  // A chunk's log f and lse are loaded one chunk ahead, so the loads of the next chunk are in
-  // flight while this one is scanned and written.
-  float lfv[kScanPerThread], lsv[kScanPerThread];
-  auto load_chunk = [&](int base, float (&lf)[kScanPerThread], float (&ls)[kScanPerThread]) {
-#pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e) {
-      const int i = base + tid * kScanPerThread + e;
-      lf[e] = i < n ? logf[g0 + (int64_t)i * gi.gs] : 0.0f;
-      ls[e] = i < n ? lse[g0 + (int64_t)i * gi.gs] : 0.0f;
-    }
-  };
-  load_chunk(0, lfv, lsv);
-  for (int base = 0, it = 0; base < span; base += kScanChunk, ++it) {
-    const int i0 = base + tid * kScanPerThread;
-    float nlf[kScanPerThread] = {}, nls[kScanPerThread] = {};
-    if (base + kScanChunk < span) load_chunk(base + kScanChunk, nlf, nls);
-    double x[kScanPerThread];
-#pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e) x[e] = (double)lfv[e];
-#pragma unroll
-    for (int e = 1; e < kScanPerThread; ++e) x[e] += x[e - 1];
-    const double t = wave_incl_scan(x[kScanPerThread - 1]);
-    const double excl = wave_shr1(t);
-    if (lane == 63) wave_tot[it & 1][wave] = t;
-    __syncthreads();
-    double before = carry, chunk = 0.0;
-#pragma unroll
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-      if (w < wave) before += wave_tot[it & 1][w];
-      chunk += wave_tot[it & 1][w];
-    }
-    const double pre = before + excl;  // sum of log f before position i0
-    // C_b: the prefix before the block's first position, held by the block's first lane
-    const int src = lane & ~(LPB - 1);
-    const u32x2 pw = __builtin_bit_cast(u32x2, pre);
-    u32x2 cw;
-    cw[0] = (uint32_t)__shfl((int)pw[0], src);
-    cw[1] = (uint32_t)__shfl((int)pw[1], src);
-    const double cblk = __builtin_bit_cast(double, cw);
-#pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e) {
-      const int i = i0 + e;
-      if (i < npad) {
-        const double cq = (pre + x[e]) - cblk;
-        const bool live = i < n;
-        blk[i] = live ? (float)((cq - (double)lsv[e]) * kLog2ed) : -INFINITY;
-        blk[2 * npad + i] = live ? (float)(cq * kLog2ed) : INFINITY;
-        if (!live) blk[npad + i] = 0.0f;
-      }
-    }
-    if ((lane & (LPB - 1)) == 0 && i0 < span) cbr[i0 / kGateBlock] = cblk;
-    carry += chunk;
-#pragma unroll
-    for (int e = 0; e < kScanPerThread; ++e) {
-      lfv[e] = nlf[e];
-      lsv[e] = nls[e];
-    }
-  }
-}
-
 }  // namespace
-
-int bwd_gate_blocks(int n) { return (n + 127) / 128 * (128 / kGateBlock); }
-
-hipError_t launch_bwd_gate_rows(const float* logf, const float* lse, float* rowv, double* cb, int64_t rows, int n,
-                                int npad, int nh, bool token_major, hipStream_t stream) {
-  const GateRowsIn gi = token_major ? GateRowsIn{nh, (int64_t)n * nh, 1, nh} : GateRowsIn{1, (int64_t)n, 0, 1};
-  hipLaunchKernelGGL(bwd_gate_rows_kernel, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf, lse, rowv, cb,
-                     n, npad, bwd_gate_blocks(n), gi);
-  return hipGetLastError();
-}
 
 hipError_t launch_logf_cumsum(const float* logf, float* c, int64_t rows, int n, hipStream_t stream) {
   hipLaunchKernelGGL(logf_cumsum_kernel<false>, dim3((unsigned)rows), dim3(kScanThreads), 0, stream, logf,
