@@ -218,9 +218,17 @@ __device__ __forceinline__ StageOffsets<D, NW> stage_offsets(int wave, int lane,
   return so;
 }
 
-// Issue this wave's loads of key tile t into stage `s`: (the gate wave) one for the tile's 64
-// log gates, then 2 * OPS for K and V.  Number of instructions issued, per wave, is what the
-// vmcnt waits below count.
+// One load instruction of the gate wave: tile t's 64 log gates into lf.
+__device__ __forceinline__ void bf16_stage_gates(float* lf, u32x4 rl, int t, int gs) {
+  // lane index recomputed here (volatile, so not hoisted) rather than kept live across the tile loop
+  uint32_t ln;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  lds_dma4(lds_addr(lf), rl, ((uint32_t)(t * kBC) + ln) * (uint32_t)(gs * (int)sizeof(float)));
+}
+
+// Issue this wave's loads of key tile t into stage `s`: (the gate wave, when asked) one for the
+// tile's 64 log gates, then 2 * OPS for K and V.  Number of instructions issued, per wave, is what
+// the vmcnt waits below count.
 template <int D, int NW>
 __device__ __forceinline__ void bf16_stage_tile(Bf16Stage<D>& s, float* lf, u32x4 rk, u32x4 rv, u32x4 rl,
                                                 const StageOffsets<D, NW>& so, int t, int wave, int lane,
@@ -228,12 +236,7 @@ __device__ __forceinline__ void bf16_stage_tile(Bf16Stage<D>& s, float* lf, u32x
   using G = Bf16Geom<D, NW>;
   const uint32_t tile_off = (uint32_t)t * (uint32_t)(kBC * rs * (int)sizeof(bf16));
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations are wave-uniform (M0)
-  if (gate_wave) {
-    // lane index recomputed here (volatile, so not hoisted) rather than kept live across the tile loop
-    uint32_t ln;
-    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    lds_dma4(lds_addr(lf), rl, ((uint32_t)(t * kBC) + ln) * (uint32_t)(gs * (int)sizeof(float)));
-  }
+  if (gate_wave) bf16_stage_gates(lf, rl, t, gs);
 #pragma unroll
   for (int o = 0; o < G::OPS; ++o) {
     const int g = wv * G::OPS + o;
@@ -440,14 +443,17 @@ __device__ __forceinline__ void pipe_pv(const Bf16Stage<D>& st, uint32_t voff, c
 // softmax of both tiles between them.  The schedule is explicit: each slot holds one MFMA,
 // the LDS reads a few slots ahead of their use, and a share of the VALU work that does
 // not depend on in-flight MFMAs; sched_barrier keeps the compiler from regrouping slots.
-//   S slots (2*KK):  MFMA of S(cur) (the first of each block starts from the tile's gate
-//                    biases); p = exp2(a * scale log2 e - m) for 32/(2*KK) scores of prev.
+//   S slots (2*KK):  MFMA of S(cur); sc arrives holding cur's gate-bias tuples, the initial
+//                    value of its accumulators; p = exp2(a * scale log2 e - m) for 32/(2*KK)
+//                    scores of prev.
 //   PV slots (4*DB): MFMA of O += V^T P^T; bf16 packing and row sum of P(prev); row max of
-//                    cur (block 0 first: its MFMAs finished earlier).
-// With GATE the wave also runs the gate scan of the next tile (GateJob) in the P.V slots, so
+//                    cur (block 0 first: its MFMAs finished earlier); once a block of prev is
+//                    packed, its registers take the next tile's bias tuple (r2next): they are
+//                    the next step's accumulators.
+// With GATE the wave also runs the gate scan of a later tile (GateJob) in the P.V slots, so
 // the wave that owns the scan does not hold the others up at the next barrier.
 template <int D, bool GATE>
-__device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float* r2cur, const Bf16Stage<D>& prev,
+__device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float* r2next, const Bf16Stage<D>& prev,
                                             const LaneOffsets<D>& off, const bf16x8 (&qreg)[D / 16],
                                             f32x16 (&sp)[2], f32x16 (&sc)[2], f32x16 (&oacc)[D / 32], float& m,
                                             float& lsum, int lane, float scale_log2, const GateJob& gj) {
@@ -492,12 +498,8 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
   if constexpr (GATE) __asm__ volatile("; gate" : "+v"(sp[0]), "+v"(sp[1]));
   else __asm__ volatile("; nogate" : "+v"(sp[0]), "+v"(sp[1]));
   __builtin_amdgcn_sched_barrier(0);
-  // The bias tuples land directly in the (dead) accumulators of cur, ahead of the K operands.
-  sc[0] = pipe_bias(r2cur, 0, hi);
-  kop[0] = kread(0);
-  sc[1] = pipe_bias(r2cur, 1, hi);
 #pragma unroll
-  for (int i = 1; i < PFK; ++i) kop[i] = kread(i);
+  for (int i = 0; i < PFK; ++i) kop[i] = kread(i);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
@@ -532,6 +534,16 @@ __device__ __forceinline__ void pipe_steady(const Bf16Stage<D>& cur, const float
       const float sv = sc[e >> 4][e & 15];
       if (e & 1) mx1 = fmaxf(mx1, sv);
       else mx0 = fmaxf(mx0, sv);
+    }
+    // next tile's bias quads: block 0 once pack(1) has consumed sp[0], block 1 after pack(3)
+#pragma unroll
+    for (int qd = 0; qd < 8; ++qd) {
+      const int b = qd >> 2, g = qd & 3;
+      if ((b == 0 ? DB + (2 * DB * g) / 4 : 3 * DB + (DB * g) / 4) == i) {
+        const f32x4 r = *reinterpret_cast<const f32x4*>(&r2next[32 * b + 8 * g + 4 * hi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[b][4 * g + e] = r[e];
+      }
     }
     if constexpr (GATE) {  // scan steps 1..7 and the finish, spread evenly over the slots
 #pragma unroll
@@ -684,12 +696,15 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   // that shifts all of split 1's scores alike and is added back to its max at the merge.
   double carry = 0.0;
 
-  // Prologue: tiles top and top-1 (the i-th tile of the split lives in stage i % 4; the
-  // loop issues tile kt-2 while computing tile kt).
+  // Prologue: tiles top and top-1, and the log gates of top-2 (the i-th tile of the split lives
+  // in stage i % 4; the loop issues the K/V of tile kt-2 and the gates of tile kt-3 while
+  // computing tile kt, whose lead wave scans the gates of tile kt-2).
+  using I2 = std::integral_constant<int, 2>;
   if (top >= bot)
     bf16_stage_tile<D, NWR>(stage(I0{})[sp], stage(I0{})[sp].lf, rk, rv, rl, so, top, rw, lane, lead, rs, gs);
   if (top - 1 >= bot)
     bf16_stage_tile<D, NWR>(stage(I1{})[sp], stage(I1{})[sp].lf, rk, rv, rl, so, top - 1, rw, lane, lead, rs, gs);
+  if (lead && top - 2 >= bot) bf16_stage_gates(stage(I2{})[sp].lf, rl, top - 2, gs);
   wait_vmcnt<0>();
 
   f32x16 oacc[DB];
@@ -707,6 +722,9 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   if (lead && top >= bot)
     gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry,
               bias_unit);
+  if (lead && top - 1 >= bot)
+    gate_tile(gates(I1{}), nullptr, rows, lane, top - 1, row0, ref, gate_in(stage(I1{})[sp].lf, top - 1, lane),
+              carry, bias_unit);
 
   // Pruning test for tile kt (and so every tile below it), wave-uniform.
   auto prune_stop = [&](int kt, const float* r2t) -> bool {
@@ -721,15 +739,16 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     using JP = std::integral_constant<int, j + NS - 1>;  // position of tile kt+1
     using JN = std::integral_constant<int, j + 2>;       // position of tiles kt+2 / kt-2
     using J1 = std::integral_constant<int, j + 1>;       // position of tile kt-1
+    using J3 = std::integral_constant<int, j + 3>;       // position of tile kt-3 (stage of kt+1)
     f32x16(&sc)[2] = (j & 1) ? sb : sa;
     f32x16(&sp_)[2] = (j & 1) ? sa : sb;
     const int kt = top - i;
     const int ln = opaque_lane(lane);  // per-tile copy: keeps stage addresses out of the loop-invariant set
-    // Own loads of tile kt, and the gate load of tile kt-1 (issued first for its tile), are
-    // complete once at most the K/V loads of tile kt-1 remain.
+    // Own loads of tile kt, and the lead's gate load of tile kt-2 (issued before tile kt-1's K/V),
+    // are complete once at most the K/V loads of tile kt-1 remain.
     if (kt - 1 >= bot) wait_vmcnt<2 * G::OPS>();
     else wait_vmcnt<0>();
-    barrier_lds();  // tile kt and its gate sums visible; every wave is done with tile kt+2's stage
+    barrier_lds();  // tiles kt, kt-1 and their gate sums visible; every wave is done with tile kt+2's stage
     if constexpr (PRUNE) {
       // Leave when every wave stopped before this position (those marks are all visible now;
       // a mark set during this position would read as "running" to every wave alike).
@@ -740,13 +759,16 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     }
     // Token-major: the lane offsets are recomputed from this step's opaque lane copy (with a
     // run-time row stride the compiler would rather keep them live, and spill them).
+    // (Tile kt+1's stage holds tile kt-3's gates: its own were scanned three steps ago.)
+    if (lead && kt - 3 >= bot) bf16_stage_gates(stage(J3{})[sp].lf, rl, kt - 3, gs);
     if (kt - 2 >= bot)
       bf16_stage_tile<D, NWR>(stage(JN{})[sp], stage(JN{})[sp].lf, rk, rv, rl,
-                              TM ? stage_offsets<D, NWR>(rw, ln, rs) : so, kt - 2, rw, lane, lead, rs, gs);
-    // The lead wave's gate scan of tile kt-1 rides in its steady-state schedule when it has one.
-    const bool gate_job = lead && kt - 1 >= bot;
+                              TM ? stage_offsets<D, NWR>(rw, ln, rs) : so, kt - 2, rw, lane, false, rs, gs);
+    // The lead wave's gate scan of tile kt-2 rides in its steady-state schedule when it has one
+    // (tile kt-1's biases, scanned in the previous step, are what this step's P.V slots load).
+    const bool gate_job = lead && kt - 2 >= bot;
     bool gate_done = false;
-    const GateJob gj = {stage(J1{})[sp].lf, gates(J1{}), kt - 1, row0, ref, fref, &rows, &carry, bias_unit};
+    const GateJob gj = {stage(JN{})[sp].lf, gates(JN{}), kt - 2, row0, ref, fref, &rows, &carry, bias_unit};
     const bool stop_here = PRUNE && active && !wdone && kt < kt_first && kt >= bot && prune_stop(kt, gates(J));
     if (active && kt >= bot && kt <= kt_first && !wdone) {
       if (kt == kt_first) {  // first tile of this wave: nothing to overlap with
@@ -754,12 +776,15 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
         // split 0's first tile holds the row's diagonal (causal) or the end of the sequence
         m = sp == 0 ? pipe_scores<true>(sc, kt * kBC, CAUSAL ? my_row : n - 1, ln >> 5, scale_log2)
                     : pipe_scores<false>(sc, 0, 0, ln >> 5, scale_log2);
+        // the next tile's bias tuples into the next step's accumulators
+        sp_[0] = pipe_bias(gates(J1{}), 0, ln >> 5);
+        sp_[1] = pipe_bias(gates(J1{}), 1, ln >> 5);
       } else if (gate_job) {
-        pipe_steady<D, true>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
+        pipe_steady<D, true>(stage(J)[0], gates(J1{}), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
                              scale_log2, gj);
         gate_done = true;
       } else {
-        pipe_steady<D, false>(stage(J)[0], gates(J), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
+        pipe_steady<D, false>(stage(J)[0], gates(J1{}), stage(JP{})[0], off, qreg, sp_, sc, oacc, m, lsum, ln,
                               scale_log2, gj);
       }
       // With pruning, a wave whose remaining keys (tile kt and below) are all negligible still
@@ -777,7 +802,7 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
     }
     // Otherwise the lead wave runs it here (read by everyone after the next barrier).
     if (gate_job && !gate_done)
-      gate_tile(gates(J1{}), nullptr, rows, ln, kt - 1, row0, ref, gate_in(stage(J1{})[sp].lf, kt - 1, ln), carry,
+      gate_tile(gates(JN{}), nullptr, rows, ln, kt - 2, row0, ref, gate_in(stage(JN{})[sp].lf, kt - 2, ln), carry,
                 bias_unit);
     return false;
   };
