@@ -7,7 +7,7 @@
 //   dq = scale dS k;  dk = scale dS^T q;  dlog f_t = sum_{i >= t} (rowsum(dS)_i - colsum(dS)_i)
 // The fp32 path serves the fp32 forward's (small, correctness-sized) workloads, so it runs on the
 // vector ALU in plain tiles rather than on MFMA:
-//  * The gate-rows kernel (fox_scan.hip) writes the row vectors' a and cl from the in-block parts of
+//  * The gate-rows kernel (fox_bwd.hip) writes the row vectors' a and cl from the in-block parts of
 //    the gate prefix sums, plus the fp64 block starts C_b (as for the bf16 path); each score's bias
 //    is (cq_i - cq_j) + (C_b(i) - C_b(j)), the block difference formed in fp64 once per tile.
 //    The row's part of each exponent, c_i - lse_i relative to the key block's start C_b(j), is
