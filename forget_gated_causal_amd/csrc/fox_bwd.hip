@@ -18,7 +18,7 @@
 //
 // Gate bias.  The prefix sums c grow with the sequence (|c| ~ 10^5 at a million tokens), so fp32
 // values of c_i and c_j carry errors far larger than the bias c_i - c_j of nearby pairs.  The
-// gate-rows kernel (fox_scan.hip) splits c at 32-position blocks instead: C_b in fp64 per block,
+// gate rows (gate_rows_block below) split c at 32-position blocks instead: C_b in fp64 per block,
 // and the in-block part cq_i = c_i - C_b(i) in the row vectors.  A score's bias is then
 // (cq_i - cq_j) + (C_b(i) - C_b(j)); the block difference is one fp64 subtraction per (tile,
 // wave), and every fp32 rounding is of a term no larger than the bias itself.
