@@ -187,6 +187,26 @@ def test_fwd_noncausal_wide_grid_whole_heads():
     _check_whole_heads(inp, o, lse, [(0, 0), (1, 127)], causal=False, label=cfg.desc + " unmasked")
 
 
+# Tile counts around the staging depths: the lead wave scans a tile's gates two tiles ahead of its
+# MFMAs and loads them three ahead, so splits of 1..6 tiles (and their key-split halves) each take a
+# different path through the prologue and the last steps.  Small grids (the key-split kernel at
+# d = 64, 4-wave blocks at d = 128) and the 8-wave kernel, both modes, every row.
+EDGES = [(d, B, H, n) for d in (64, 128) for (B, H) in ((1, 2), (2, 128)) for n in (128, 192, 193, 257, 320, 383)]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "unmasked"])
+@pytest.mark.parametrize("d,B,H,n", EDGES)
+def test_fwd_tile_count_edges(d, B, H, n, causal):
+    cfg = fi.FwdConfig(f"edges_{d}_{B}_{H}_{n}", B, H, n, d, "bf16", 1.0, 2.0)
+    inp = fi.fwd_inputs(cfg)
+    o, lse, c = _run_fwd(inp) if causal else _run_fwd_nc(inp)
+    heads = [(0, 0), (B - 1, H - 1)]
+    _check_whole_heads(inp, o, lse, heads, causal=causal, label=cfg.desc + ("" if causal else " unmasked"))
+    c_ref = oracle.logf_cumsum(_np(inp["logf"]))
+    assert np.abs(_np(c) - c_ref).max() <= _ulp(c_ref)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
 # Gates far from 1 (log f about -3 per step, and a constant -20): the gate biases of a 256-row block
 # reach hundreds to thousands of nats, and the bf16 forward carries them in its fp32 S accumulators
 # (as R_j / scale) through every k-step.  Both the 4-wave and the 8-wave kernels, both modes.
