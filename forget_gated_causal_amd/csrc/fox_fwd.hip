@@ -29,9 +29,8 @@
 //     stages (XOR-swizzled rows, no padding).  The PV operand, which needs 8 keys of one dim
 //     per lane, comes from gfx950's transposing LDS read (ds_read_b64_tr_b16).
 //   * Each wave software-pipelines its tiles: the MFMAs of S for tile t run beside the
-//     exponentials of tile t+1, the MFMAs of O += V^T P^T for tile t+1 beside the scores and
-//     row max of tile t (MFMA and VALU work overlap only within one wave's instruction
-//     stream on this chip).
+//     exponentials of tile t+1, the MFMAs of O += V^T P^T for tile t+1 beside the row max of
+//     tile t (a two-wave split of MFMA and VALU roles measured slower on this chip).
 //   * Online softmax in base 2 with lazy rescaling: the running max is only raised when a
 //     row's tile max exceeds it by more than kTau (exact: the final normalisation uses the
 //     same stale max; p stays <= 2^kTau).  The row sum adds the bf16-rounded p, the same
@@ -301,14 +300,13 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
 // ------------------------------------------------------------------------------------------
 // bf16, software-pipelined form
 // ------------------------------------------------------------------------------------------
-// On gfx950 an MFMA and VALU work overlap when both come from the same wave and the VALU
-// instructions sit between the MFMAs of its instruction stream; a wave that only issues
-// MFMAs leaves the VALU idle even when the other wave of the SIMD has softmax work.  So each
-// wave runs its own two-stage pipeline over key tiles: while the MFMAs of S(t) = K_t Q^T
+// Each wave runs its own two-stage pipeline over key tiles: while the MFMAs of S(t) = K_t Q^T
 // execute, the wave computes the probabilities of tile t+1 (the previous tile in visiting
-// order); while the MFMAs of O += V_{t+1}^T P^T execute, it forms the biased scores and the
-// row max of tile t.  Four LDS stages hold tile t+1 (V still read), tile t, and the two
-// tiles in flight.
+// order); while the MFMAs of O += V_{t+1}^T P^T execute, it takes the row max of tile t.  A
+// wave issues at most about one VALU instruction per 8 clocks, so its VALU work sits between
+// its own MFMAs, and the two waves of a SIMD overlap each other's MFMAs as well (a split of
+// the two roles between the waves, switching at barriers, measured slower).  Four LDS stages
+// hold tile t+1 (V still read), tile t, and the two tiles in flight.
 
 template <int D>
 struct PipeGeom {
