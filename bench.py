@@ -611,7 +611,7 @@ def main():
         write_traffic_summary(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: the library runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is not built", file=sys.stderr)
         sys.exit(2)
 
