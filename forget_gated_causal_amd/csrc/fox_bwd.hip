@@ -14,14 +14,16 @@
 // short: its rows see keys before t only within their window); without it the two cross blocks
 // can be far larger than dlog f_t, and the sums use the fp32 dS before rounding (those kernels
 // then need more registers than two waves per SIMD allow, and run one).  The forward's lse
-// gives P without a second softmax.
+// gives P without a second softmax (rescaled to unit row sums without the mask: the D pass).
 //
 // Gate bias.  The prefix sums c grow with the sequence (|c| ~ 10^5 at a million tokens), so fp32
 // values of c_i and c_j carry errors far larger than the bias c_i - c_j of nearby pairs.  The
 // gate rows (gate_rows_block below) split c at 32-position blocks instead: C_b in fp64 per block,
 // and the in-block part cq_i = c_i - C_b(i) in the row vectors.  A score's bias is then
 // (cq_i - cq_j) + (C_b(i) - C_b(j)); the block difference is one fp64 subtraction per (tile,
-// wave), and every fp32 rounding is of a term no larger than the bias itself.
+// wave), and every fp32 rounding is of a term bounded by 32 |log f| rather than by |c|.  (With
+// strong gates that bound still exceeds the bias of a weighted pair -- 10^-5 relative in P at
+// |log f| = 4.5, well inside bf16 bounds; the fp32 backward forms each bias in fp64 instead.)
 //
 // D_i.  dO_i . O_i uses the forward's O, rounded to bf16.  Without the mask, dlog f_t is the
 // difference of two cross-block sums that can be far larger than it, and the rounding of O
@@ -46,7 +48,8 @@
 //    Writes dq and the row sums of dS.
 //  * before them: the gate rows (gate_rows_block: the padded row vectors and the fp64 block sums
 //    C_b that both parts load) and D_i = dO_i . O_i in one launch (bwd_rows_kernel) with the
-//    mask; without it the gate rows, then bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32).
+//    mask; without it the gate rows, then bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32, and
+//    the row terms rescaled so that each row of P sums to 1 in fp32).
 //    After them the reversed prefix scan (fox_scan.hip): dlog f from row sums - column sums.
 // Tensors are head-major [B,H,N,d] or token-major [B,N,H,d] (BwdLayout: row strides d or H d,
 // gate-vector strides 1 or H); the workspace is head-major either way.
@@ -219,8 +222,8 @@ __device__ __forceinline__ void stage_rows(bf16* lds, const bf16* src, int rows,
 // The backward's gate terms of one (batch, head) row.  The prefix sums are split at blocks of
 // kGateBlock positions: C_b = sum_{t < 32b} log f_t (fp64, one per block) and the in-block part
 // cq_i = sum_{32b(i) <= t <= i} log f_t, so that c_i - c_j = (cq_i - cq_j) + (C_b(i) - C_b(j)).
-// Every term the backward kernels round to fp32 is then as small as the bias it belongs to, not
-// as large as |c| (which grows with the sequence).  Written into the head's row-vector block
+// Every term the backward kernels round to fp32 is then bounded by 32 |log f|, not by |c| (which
+// grows with the sequence).  Written into the head's row-vector block
 // [a | D | cl] of 3 * npad floats: a_i = (cq_i - lse_i) log2 e, cl_i = cq_i log2 e, and D_i = 0
 // past n (a = -inf, cl = +inf there, so padded rows and keys carry no weight); C_b for the ncb
 // blocks into cb.  One 256-thread workgroup per row, chunks of 1024 positions, each thread 4 of them, fp64 scan
@@ -648,8 +651,13 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
 }
 
 // Query-stationary part (dQ, row sums of dS) for query block qb of head bh.  DPASS: the D pass
-// instead -- with D_i = 0 the row sums of dS are sum_j P_ij dP_ij, written to dout_d[qi] (the D
-// slot of the row vectors); no dQ.
+// instead, no dQ.  With D_i = 0 the row sums of dS are sum_j P_ij dP_ij; the pass also sums
+// Z_i = sum_j P_ij.  The lse it is given normalised the forward's bf16-rounded probabilities,
+// so these fp32 ones sum to Z_i = 1 + O(2^-9), and that excess, taken once per row, adds up in
+// the suffix sums of dlog f over every row.  The pass divides it out: it writes D_i / Z_i to the
+// D slot and a_i - log2 Z_i to the row term slot (dout_d: the row vectors, whose row term slot of
+// its own rows it reads and rewrites only through dout_d), so the main parts see P with unit row
+// sums.
 template <int D, bool CAUSAL, bool DPASS = false>
 __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, const bf16* __restrict__ q,
                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -684,7 +692,8 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
       dreg[kk] = *reinterpret_cast<const bf16x8*>(dout + tb + (int64_t)qi * rs + 16 * kk + 8 * hi);
     }
   }
-  const float aq = qi < n ? blk[qi] : kNegInfB;     // (cq_i - lse_i) log2 e; no weight past n
+  // (cq_i - lse_i) log2 e; no weight past n
+  const float aq = qi >= n ? kNegInfB : DPASS ? dout_d[bh * 3 * (size_t)npad + qi] : blk[qi];
   const float dq_i = (qi < n && !DPASS) ? blk[npad + qi] : 0.0f;  // D_i
   // start C of the wave's 32-query block; each 32-key block adds its own block difference
   const double* cbh = cb + bh * (size_t)ncb;
@@ -703,7 +712,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
   f32x16 acc[DB];  // dQ: lane = dim 32db + l32, register r = query 8(r/4) + 4hi + r%4
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float rsum0 = 0.0f, rsum1 = 0.0f;
+  float rsum0 = 0.0f, rsum1 = 0.0f, zsum = 0.0f;
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
   const int kend = CAUSAL ? min(n, (qb + 1) * kQB) : n;  // keys this block sees
@@ -755,7 +764,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
     const float* clb = &lds.cl[buf][32 * kb];
     bf16x8 aop[NQ];
     f32x4 c4[4];
-    f32x16 s2 = f32x16{}, dp2 = f32x16{};
+    f32x16 s2 = f32x16{}, dp2 = f32x16{}, pz;
     c4[0] = *reinterpret_cast<const f32x4*>(&clb[4 * hi]);
     if constexpr (HN) {
 #pragma unroll
@@ -773,6 +782,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
         const int g = r >> 2, e = r & 3;
         float p = exp2_hw(fmaf(s[r], scale_log2, aqb) - c4[g][e]);
         if (MASK && key0 + 8 * g + 4 * hi + e > qi) p = 0.0f;
+        if constexpr (DPASS) pz[r] = p;
         s[r] = p * (dp[r] - dq_i);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -786,6 +796,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
     // dQ += dS K: A = dS^T (queries as M, keys as K), B = K read transposed.  The row sums of dS
     // are taken over the fp32 values without the mask, over the bf16 values the MFMAs use with it.
     if constexpr (!CAUSAL) rsum0 += tree_sum16(s);
+    if constexpr (DPASS) zsum += tree_sum16(pz);
     if constexpr (!DPASS) {
       const bf16x8 sb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
       if constexpr (CAUSAL) {
@@ -846,7 +857,13 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
   // the two lane halves hold the two halves of each 32-key block
   const float rsum = pair32_sum(rsum0 + rsum1);
   if constexpr (DPASS) {
-    if (hi == 0 && qi < n) dout_d[bh * 3 * (size_t)npad + npad + qi] = rsum;
+    float z = pair32_sum(zsum);
+    if (!(z > 0.0f && z < INFINITY)) z = 1.0f;  // an lse that does not belong to these scores
+    if (hi == 0 && qi < n) {
+      float* row = dout_d + bh * 3 * (size_t)npad;
+      row[qi] = aq - log2f(z);
+      row[npad + qi] = rsum / z;
+    }
     return;
   }
   // dq = scale dQ: lane = dim 32db + l32, register r = query qw0 + 8(r/4) + 4hi + r%4
@@ -884,7 +901,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
                           nullptr, n, npad, ncb, scale, lay);
 }
 
-// The D pass of the unmasked mode: D_i = sum_j P_ij dP_ij into the row vectors' D slot.
+// The D pass of the unmasked mode: D_i = sum_j P_ij dP_ij into the row vectors' D slot, with P
+// rescaled to unit row sums (the row term slot takes the rescaling).
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dpass_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
