@@ -25,6 +25,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfox.so")
 SOURCES = ["fox_api.hip", "fox_scan.hip", "fox_fwd.hip", "fox_decode.hip", "fox_bwd.hip", "fox_bwd_f32.hip"]
+# Per-source flags.  fox_bwd.hip keeps its d = 128 accumulators in AGPRs by inline assembly and
+# wants its builtin MFMAs (the scores) in VGPR form, which the compiler would otherwise switch to
+# AGPR form for a kernel with more than 256 registers.
+SOURCE_FLAGS = {"fox_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
 HIP_FLAGS = [
@@ -65,7 +69,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        out = _run([cc, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out, file=sys.stderr)
         return obj
@@ -100,7 +104,7 @@ def build_host_sanitized() -> str:
         else:
             obj = os.path.join(BUILD, src.replace(".hip", ".o"))
             if not os.path.exists(obj):
-                _run([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+                _run([cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     tmp = HOSTSAN_LIB + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SAN_FLAGS, *objs, "-o", tmp])

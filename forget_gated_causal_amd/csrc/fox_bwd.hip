@@ -172,6 +172,25 @@ __device__ __forceinline__ bf16x4 tr16(const bf16* p) {
 }
 
 // Operand of an MFMA whose M (or N) is a block of 32 columns and whose K runs over 16 rows of a
+// Accumulating MFMAs of the d = 128 kernels (one wave per SIMD, 512 registers): dK^T and dV^T
+// (key side) and dQ (query side) stay in AGPRs, written only by these inline-assembly MFMAs, while
+// the score MFMAs (builtins; this file is compiled with the MFMA VGPR form forced) write VGPRs
+// that the VALU reads directly, with no AGPR-to-VGPR copies.  The compiler does not see an MFMA
+// here: the _nop form keeps the 2 wait states an XDL MFMA needs after a VALU write of its A or
+// B operand (first use of each freshly packed P or dS), and agpr_fence the 11 an XDL result
+// needs before the VALU reads it (16 here; the AGPRs are operands, so no access moves across).
+__device__ __forceinline__ void mfma_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_nop(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  __asm__ volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void agpr_fence(f32x16 (&c)[N]) {
+  static_assert(N == 4, "d = 128 accumulators");
+  __asm__ volatile("s_nop 15" : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3]));
+}
+
 // swizzled row-major [row][column] LDS tile: lane (l32, hi) gets column dim0 + l32 of rows
 // {row0 + 4hi .. +3, row0 + 8 + 4hi .. +3}, the row order of the accumulator registers 8u..8u+7.
 template <int W>
@@ -592,8 +611,13 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int u = j / (2 * DB), db = (j >> 1) % DB;
-      if (j & 1) dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[j], sb[u], dkt[db], 0, 0, 0);
-      else dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[j], pb[u], dvt[db], 0, 0, 0);
+      if constexpr (D == 128) {  // P and dS were packed just before: first reads with the wait states
+        if (j & 1) (j < 2 ? mfma_acc_nop : mfma_acc)(dkt[db], top[j], sb[u]);
+        else (j < 2 ? mfma_acc_nop : mfma_acc)(dvt[db], top[j], pb[u]);
+      } else {
+        if (j & 1) dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[j], sb[u], dkt[db], 0, 0, 0);
+        else dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[j], pb[u], dvt[db], 0, 0, 0);
+      }
       if (j + PFP < NP) top[j + PFP] = tread(j + PFP);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -628,6 +652,10 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
   colsum += colsum1;
 
   // dK = scale dK^T, dV = dV^T: lane = key, dims 32db + 8(r/4) + 4hi + r%4 (runs of 4)
+  if constexpr (D == 128) {
+    agpr_fence(dkt);
+    agpr_fence(dvt);
+  }
   colsum = pair32_sum(colsum);
   if (key < n) {
     bf16* dkr = dk + tb + (int64_t)key * rs;
@@ -820,7 +848,10 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
-        acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[j / DB], top[j], acc[j % DB], 0, 0, 0);
+        if constexpr (D == 128)  // dS was packed just before: first reads with the wait states
+          (j % DB == 0 ? mfma_acc_nop : mfma_acc)(acc[j % DB], sb[j / DB], top[j]);
+        else
+          acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[j / DB], top[j], acc[j % DB], 0, 0, 0);
         if (j + PFP < NP) top[j + PFP] = tread(j + PFP);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -867,6 +898,7 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
     return;
   }
   // dq = scale dQ: lane = dim 32db + l32, register r = query qw0 + 8(r/4) + 4hi + r%4
+  if constexpr (D == 128) agpr_fence(acc);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
