@@ -73,10 +73,14 @@ BWD_KERNEL = "fox_attn_bwd<{d},causal>: bwd_rows (gate rows + D) + bwd_kv + bwd_
 
 
 def kernel_source_digest(kind: str) -> str:
+    """Digest of the sources a kernel kind is built from, with their per-source compiler flags."""
+    from forget_gated_causal_amd.build import SOURCE_FLAGS
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "forget_gated_causal_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+        if SOURCE_FLAGS.get(f):
+            h.update(" ".join(SOURCE_FLAGS[f]).encode())
     return h.hexdigest()[:16]
 
 
