@@ -694,16 +694,21 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   // that shifts all of split 1's scores alike and is added back to its max at the merge.
   double carry = 0.0;
 
-  // Prologue: tiles top and top-1, and the log gates of top-2 (the i-th tile of the split lives
-  // in stage i % 4; the loop issues the K/V of tile kt-2 and the gates of tile kt-3 while
-  // computing tile kt, whose lead wave scans the gates of tile kt-2).
+  // Prologue: the log gates of tiles top, top-1 and top-2, then the K/V of tiles top and top-1 (the
+  // i-th tile of the split lives in stage i % 4; the loop issues the K/V of tile kt-2 and the gates
+  // of tile kt-3 while computing tile kt, whose lead wave scans the gates of tile kt-2).  The lead
+  // wave scans the first two tiles' gates as soon as those have landed, while the K/V loads are
+  // still in flight.
   using I2 = std::integral_constant<int, 2>;
+  if (lead) {
+    if (top >= bot) bf16_stage_gates(stage(I0{})[sp].lf, rl, top, gs);
+    if (top - 1 >= bot) bf16_stage_gates(stage(I1{})[sp].lf, rl, top - 1, gs);
+    if (top - 2 >= bot) bf16_stage_gates(stage(I2{})[sp].lf, rl, top - 2, gs);
+  }
   if (top >= bot)
-    bf16_stage_tile<D, NWR>(stage(I0{})[sp], stage(I0{})[sp].lf, rk, rv, rl, so, top, rw, lane, lead, rs, gs);
+    bf16_stage_tile<D, NWR>(stage(I0{})[sp], stage(I0{})[sp].lf, rk, rv, rl, so, top, rw, lane, false, rs, gs);
   if (top - 1 >= bot)
-    bf16_stage_tile<D, NWR>(stage(I1{})[sp], stage(I1{})[sp].lf, rk, rv, rl, so, top - 1, rw, lane, lead, rs, gs);
-  if (lead && top - 2 >= bot) bf16_stage_gates(stage(I2{})[sp].lf, rl, top - 2, gs);
-  wait_vmcnt<0>();
+    bf16_stage_tile<D, NWR>(stage(I1{})[sp], stage(I1{})[sp].lf, rk, rv, rl, so, top - 1, rw, lane, false, rs, gs);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -717,12 +722,19 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   auto gate_in = [&](const float* lf, int t, int ln) {
     return (t * kBC + 63 - ln <= fref) ? lf[63 - ln] : 0.0f;
   };
-  if (lead && top >= bot)
+  if (lead && top >= bot) {
+    // the gates of tiles top and top-1 have landed once at most the gates of top-2 and the K/V
+    // loads issued after them remain
+    if (top - 2 >= bot) wait_vmcnt<1 + 4 * G::OPS>();
+    else if (top - 1 >= bot) wait_vmcnt<4 * G::OPS>();
+    else wait_vmcnt<2 * G::OPS>();
     gate_tile(gates(I0{}), nullptr, rows, lane, top, row0, ref, gate_in(stage(I0{})[sp].lf, top, lane), carry,
               bias_unit);
-  if (lead && top - 1 >= bot)
-    gate_tile(gates(I1{}), nullptr, rows, lane, top - 1, row0, ref, gate_in(stage(I1{})[sp].lf, top - 1, lane),
-              carry, bias_unit);
+    if (top - 1 >= bot)
+      gate_tile(gates(I1{}), nullptr, rows, lane, top - 1, row0, ref, gate_in(stage(I1{})[sp].lf, top - 1, lane),
+                carry, bias_unit);
+  }
+  wait_vmcnt<0>();
 
   // Pruning test for tile kt (and so every tile below it), wave-uniform.
   auto prune_stop = [&](int kt, const float* r2t) -> bool {
