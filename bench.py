@@ -65,7 +65,7 @@ def decode_bytes(cfg, lens=None) -> dict:
 # WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a plain device
 # copy of known size.  The summaries live in profiles/*_traffic.txt with a digest of the kernel
 # sources they were taken on; a summary of older sources is not used (traffic reported as null).
-KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_device.h"], "decode": ["fox_decode.hip", "fox_device.h"],
+KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_fwd_gates.h", "fox_device.h"], "decode": ["fox_decode.hip", "fox_device.h"],
                   "bwd": ["fox_bwd.hip", "fox_scan.hip", "fox_device.h"]}
 COPY_CAL_BYTES = 1 << 30
 DECODE_KERNEL = "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>"

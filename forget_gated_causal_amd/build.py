@@ -24,11 +24,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfox.so")
-SOURCES = ["fox_api.hip", "fox_scan.hip", "fox_fwd.hip", "fox_decode.hip", "fox_bwd.hip", "fox_bwd_f32.hip"]
-# Per-source flags.  fox_bwd.hip keeps its d = 128 accumulators in AGPRs by inline assembly and
-# wants its builtin MFMAs (the scores) in VGPR form, which the compiler would otherwise switch to
-# AGPR form for a kernel with more than 256 registers.
-SOURCE_FLAGS = {"fox_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+SOURCES = ["fox_api.hip", "fox_scan.hip", "fox_fwd.hip", "fox_fwd_f32.hip", "fox_decode.hip", "fox_bwd.hip",
+           "fox_bwd_f32.hip"]
+# Per-source flags.  For a kernel with more than 256 registers (one wave per SIMD) the compiler
+# puts every MFMA in AGPR form, and the scores then reach the VALU through AGPR-to-VGPR copies.
+# The VGPR form is forced instead: fox_bwd.hip keeps its d = 128 accumulators in AGPRs by inline
+# assembly, and fox_fwd.hip's one-wave kernels (4-wave blocks at d = 128) then fit 256 VGPRs.  The
+# fp32 forward (fox_fwd_f32.hip) keeps the default: at d = 128 it needs the AGPRs.
+SOURCE_FLAGS = {"fox_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+                "fox_fwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
 HIP_FLAGS = [

@@ -36,84 +36,18 @@
 //     same stale max; p stays <= 2^kTau).  The row sum adds the bf16-rounded p, the same
 //     weights the P.V products use.
 //
-// fp32 inputs use a non-pipelined schedule with v_mfma_f32_32x32x2f32 and fp32 P; there the
-// bias R_j - R_i is formed per score in fp64 (kept in LDS), so no fp32 rounding of a
-// block-relative gate sum enters the scores.
+// fp32 inputs run the kernel of fox_fwd_f32.hip (launch_fwd_f32); the gate-sum scan and the tile
+// constants both use are in fox_fwd_gates.h.
 #include <math.h>
 
 #include <type_traits>
 
 #include "fox_device.h"
+#include "fox_fwd_gates.h"
 #include "fox_internal.h"
 
 namespace fox {
 namespace {
-
-constexpr int kThreads = 256;  // fp32 kernel; the bf16 kernel runs 64 * NW threads
-constexpr int kBR = 128;       // query rows per workgroup of the fp32 kernel (32 per wave)
-constexpr int kMaxBR = 256;    // largest query block (bf16, 8 waves)
-constexpr int kBC = 64;       // keys per tile
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
-constexpr float kNegInf = -INFINITY;
-
-struct GateRows {          // per workgroup
-  double rowR[kMaxBR + 1]; // R_i for the block's own rows; the last slot takes discarded writes
-  double cref;             // c at the frame row of the gate sums (sum of log f up to it)
-  double cref_discard;     // takes the cref write of tiles other than tile 0
-  double csplit;           // key split: sum of log f over split 0's keys (split 1's frame offset)
-  float kmax;              // pruning: largest key norm of the block's key range
-  float prune_t;           // pruning: margin 25 + log2 n (base-2 units)
-  int done_it[16];         // pruning: loop position at which each wave stopped (INT_MAX: still running)
-};
-
-// Wave 0: gate sums for tile kt.  Lane t holds log f of key 63-t of the tile (0 beyond
-// ref), so the lane-order exclusive prefix is the key-order exclusive suffix
-// sum_{u > j} log f_u inside the tile.  `carry` (fp64) is the sum of log f over
-// (tile end, ref] and is advanced by the tile total.  Writes R_j = carry + suffix for
-// the tile (r2 = R_j * unit in fp32; r64 = R_j, when given), R_i for the block's own
-// rows and, after tile 0, c at the reference row.  Everything is fp64 until the single
-// rounding to fp32.
-__device__ __forceinline__ void gate_finish(double incl, float* r2, double* r64, GateRows& rows, int lane, int kt,
-                                            int row0, int ref, double& carry, double unit) {
-  const double excl = wave_shr1(incl);
-  const int jl = 63 - lane;
-  const double rj = carry + excl;
-  r2[jl] = (float)(rj * unit);
-  if (r64) r64[jl] = rj;
-  // Branch-free writes (this code also runs inside the MFMA schedule): rows outside the
-  // block and tiles other than tile 0 write to discard slots.
-  const int j = kt * kBC + jl;
-  rows.rowR[(j >= row0 && j <= ref) ? j - row0 : kMaxBR] = rj;
-  carry += wave_last(incl);
-  *(kt == 0 ? &rows.cref : &rows.cref_discard) = carry;
-}
-__device__ __forceinline__ void gate_tile(float* r2, double* r64, GateRows& rows, int lane, int kt, int row0,
-                                          int ref, float lf_rev, double& carry, double unit) {
-  gate_finish(wave_incl_scan((double)lf_rev), r2, r64, rows, lane, kt, row0, ref, carry, unit);
-}
-
-// The gate sums of one tile as a job that a wave can spread over its MFMA schedule.
-struct GateJob {
-  const float* lf;  // the tile's staged log gates
-  float* r2;        // its biases R_j * unit (out)
-  int kt;           // tile index
-  int row0, ref;    // the block's first and last rows (R_i of these rows is kept)
-  int fref;         // frame row: gates past it do not enter the sums
-  GateRows* rows;
-  double* carry;
-  double unit;      // R_j -> stored bias
-};
-
-// Element strides of one forward call.  Head-major: q/k/v/o [B,H,N,d], gates / lse / c [B,H,N]
-// (rows d apart).  Token-major: q/k/v/o [B,N,H,d], gates / lse / c [B,N,H] (rows h*d apart),
-// the layout the projections produce before the head permute.
-struct FwdLayout {
-  int64_t bs, hs;    // q/k/v/o: batch and head strides
-  int rs;            // q/k/v/o: row (token) stride
-  int64_t gbs, ghs;  // gates, lse, c: batch and head strides
-  int gs;            // gates, lse, c: row stride
-  int nh;            // heads per batch entry
-};
 
 // ------------------------------------------------------------------------------------------
 // bf16
@@ -948,210 +882,6 @@ __global__ __launch_bounds__(256) void key_tile_norm_kernel(const bf16* __restri
   if (lane == 0) kn[bh * nt + t] = sqrtf(nm);
 }
 
-// ------------------------------------------------------------------------------------------
-// fp32
-// ------------------------------------------------------------------------------------------
-template <int D>
-struct F32Tile {
-  static constexpr int KS = D + 1;  // K row stride (floats): odd, so column reads spread over banks
-  static constexpr int VS = D + 8;  // V row stride (floats)
-  static constexpr int GROUPS = D / 4;
-  static constexpr int KPT = kBC * GROUPS / kThreads;
-  static_assert(KPT >= 1 && KPT * kThreads == kBC * GROUPS, "loader mapping");
-  f32x4 k[KPT];
-  f32x4 v[KPT];
-};
-
-template <int D>
-struct F32Lds {
-  float k[kBC * F32Tile<D>::KS];
-  float v[kBC * F32Tile<D>::VS];
-  float r2[kBC];
-  double r64[kBC];  // R_j in fp64: the fp32-input kernel forms R_j - R_i exactly from these
-  GateRows rows;
-};
-
-template <int D>
-__device__ __forceinline__ void f32_load_tile(F32Tile<D>& t, const float* kb, const float* vb, int kt, int n,
-                                              int tid, int rs) {
-  constexpr int G = F32Tile<D>::GROUPS, KPT = F32Tile<D>::KPT;
-  const int c = tid % G, a = tid / G;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int key = kt * kBC + a * KPT + i;
-    if (key < n) {
-      t.k[i] = *reinterpret_cast<const f32x4*>(kb + (size_t)key * rs + 4 * c);
-      t.v[i] = *reinterpret_cast<const f32x4*>(vb + (size_t)key * rs + 4 * c);
-    } else {
-      t.k[i] = f32x4{};
-      t.v[i] = f32x4{};
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void f32_store_tile(const F32Tile<D>& t, F32Lds<D>& s, int tid) {
-  constexpr int G = F32Tile<D>::GROUPS, KPT = F32Tile<D>::KPT, KS = F32Tile<D>::KS, VS = F32Tile<D>::VS;
-  const int c = tid % G, a = tid / G;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int key = a * KPT + i;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s.k[key * KS + 4 * c + e] = t.k[i][e];
-    *reinterpret_cast<f32x4*>(&s.v[key * VS + 4 * c]) = t.v[i];
-  }
-}
-
-template <int D, bool CAUSAL, bool TM>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                          const float* __restrict__ v,
-                                                          const float* __restrict__ logf, float* __restrict__ o,
-                                                          float* __restrict__ lse, float* __restrict__ c_out, int n,
-                                                          float scale_log2, const FwdLayout lay) {
-  constexpr int KS = F32Tile<D>::KS, VS = F32Tile<D>::VS, KK = D / 2, DB = D / 32;
-  __shared__ F32Lds<D> lds;
-
-  const int bh = blockIdx.x;
-  const int qb = gridDim.y - 1 - blockIdx.y;
-  const int row0 = qb * kBR;
-  const int ref = min(row0 + kBR - 1, n - 1);  // the block's last row
-  const int fref = CAUSAL ? ref : n - 1;       // frame row of the gate sums
-  const int kt_hi = fref / kBC;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int bb = bh / lay.nh, hh = bh - bb * lay.nh;
-  const size_t base = TM ? (size_t)bb * lay.bs + (size_t)hh * lay.hs : (size_t)bh * n * D;  // q/k/v/o
-  const size_t gbase = TM ? (size_t)bb * lay.gbs + (size_t)hh * lay.ghs : (size_t)bh * n;  // gates/lse/c
-  const int rs = TM ? lay.rs : D, gs = TM ? lay.gs : 1;
-  const float* kb = k + base;
-  const float* vb = v + base;
-  const float* lfb = logf + gbase;
-
-  const int wrow0 = row0 + wave * 32;
-  const bool active = wrow0 < n;
-  const int kt_first = !active ? -1 : (CAUSAL ? min(wrow0 + 31, n - 1) / kBC : kt_hi);
-  const int my_row = wrow0 + l32;
-
-  float qf[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qf[kk] = (my_row < n) ? q[base + (size_t)my_row * rs + 2 * kk + hi] : 0.0f;
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  // The row sum runs in fp64 over per-tile fp32 partial sums of 32 terms (a single fp32 running
-  // sum over thousands of keys drifts by more than the 1e-5 that lse must meet), and lse takes
-  // an fp64 logarithm.
-  float m = kNegInf;
-  double lsum = 0.0;
-  double carry = 0.0, ri_row = 0.0;
-  // Unmasked mode: the biases stay relative to the frame row n-1 (R_j - 0), where every row's
-  // heaviest keys lie, so those scores are small and exactly rounded; R_i comes off in lse.
-  F32Tile<D> tile;
-  f32_load_tile<D>(tile, kb, vb, kt_hi, n, tid, rs);
-  float lf = 0.0f;  // wave 0: log f of key 63-lane of the next tile
-  if (wave == 0) {
-    const int j = kt_hi * kBC + 63 - lane;
-    lf = (j <= fref) ? lfb[(size_t)j * gs] : 0.0f;
-  }
-
-  for (int kt = kt_hi; kt >= 0; --kt) {
-    __syncthreads();
-    f32_store_tile<D>(tile, lds, tid);
-    if (wave == 0) gate_tile(lds.r2, lds.r64, lds.rows, lane, kt, row0, ref, lf, carry, kLog2ed);
-    __syncthreads();
-    if (kt > 0) {
-      f32_load_tile<D>(tile, kb, vb, kt - 1, n, tid, rs);
-      if (wave == 0) lf = lfb[(size_t)((kt - 1) * kBC + 63 - lane) * gs];
-    }
-    if (!active || kt > kt_first) continue;
-
-    f32x16 sacc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sacc[b] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds.k[(32 * b + l32) * KS + 2 * kk + hi], qf[kk], sacc[b],
-                                                       0, 0, 0);
-    }
-
-    // This row's R_i is in the gate LDS from the wave's first (diagonal) tile on.
-    if (CAUSAL && kt == kt_first) ri_row = (my_row < n) ? lds.rows.rowR[my_row - row0] : 0.0;
-    // causal: keys past the row; otherwise only keys past the end of the sequence
-    const int last_key = CAUSAL ? my_row : n - 1;
-    const bool diag = CAUSAL ? kt * kBC + kBC - 1 > wrow0 : kt * kBC + kBC > n;
-    float mx = kNegInf;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kl = 32 * b + 8 * g + 4 * hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // full bias sum_{t=j+1..i} log f_t = R_j - R_i, formed in fp64 and rounded once
-          const float bias2 = (float)((lds.r64[kl + e] - ri_row) * kLog2ed);
-          float s = fmaf(sacc[b][4 * g + e], scale_log2, bias2);
-          if (diag && kt * kBC + kl + e > last_key) s = kNegInf;
-          sacc[b][4 * g + e] = s;
-          mx = fmaxf(mx, s);
-        }
-      }
-    }
-    mx = pair32_max(mx);
-
-    const float mcand = fmaxf(m, mx);
-    const bool need = mcand > m + kTau;
-    if (wave_any(need)) {
-      const float mn = need ? mcand : m;
-      const float alpha = exp2_hw(m - mn);
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m = mn;
-    }
-    const float msub = (m == kNegInf) ? 0.0f : m;
-
-    float tsum[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(sacc[b][r] - msub);
-        tsum[r & 1] += p;
-        const int key = 32 * b + 8 * (r / 4) + 4 * hi + (r % 4);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds.v[key * VS + 32 * db + l32], p, oacc[db], 0, 0, 0);
-      }
-    }
-    lsum += (double)tsum[0] + (double)tsum[1];
-  }
-
-  if (!active) return;
-  const double ltot = lsum + __shfl_xor(lsum, 32);
-  if (my_row >= n) return;
-  const float inv = (float)(1.0 / ltot);
-  float* orow = o + base + (size_t)my_row * rs;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
-      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hi) = w;
-    }
-  }
-  if (hi == 0) {
-    const double ri = lds.rows.rowR[my_row - row0];
-    const size_t idx = gbase + (size_t)my_row * gs;
-    // causal scores already carry -R_i
-    if (lse) lse[idx] = (float)(((double)m + log2(ltot)) * kLn2d - (CAUSAL ? 0.0 : ri));
-    if (c_out) c_out[idx] = (float)(lds.rows.cref - ri);
-  }
-}
-
 // Kernel choice for the bf16 forward (knorm != nullptr selects the pruned, causal kernels):
 //  * 256-row blocks (8 waves) stage each K/V tile for twice the compute of 128-row blocks,
 //    halving the L2 -> LDS traffic per flop; used when there are enough blocks to keep every
@@ -1159,66 +889,52 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 //  * d <= 64 with fewer than two 128-row blocks per CU: 128-row blocks whose key tiles are
 //    split over two wave sets;
 //  * otherwise 128-row blocks of 4 waves.
-template <typename T, int D, bool CAUSAL, bool TM>
+template <int D, bool CAUSAL, bool TM>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse,
                         float* c, int64_t bh, int n, float scale_log2, const float* knorm, const FwdLayout& lay,
                         hipStream_t stream) {
-  if constexpr (sizeof(T) == 2) {
-    int cus = 256, dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t blocks256 = bh * (int64_t)((n + 255) / 256);
-    const int64_t blocks128 = bh * (int64_t)((n + 127) / 128);
-    const bf16 *qq = (const bf16*)q, *kk = (const bf16*)k, *vv = (const bf16*)v;
-    bf16* oo = (bf16*)o;
-    auto go = [&](auto kernel, int rows, int threads) {
-      const dim3 grid((unsigned)bh, (unsigned)((n + rows - 1) / rows));
-      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, qq, kk, vv, logf, oo, lse, c, n, scale_log2, knorm,
-                         lay);
-      return hipGetLastError();
-    };
-    constexpr bool CAN_PRUNE = CAUSAL && !TM;
-    if constexpr (D >= 64) {
-      if (blocks256 >= 2 * (int64_t)cus) {
-        if constexpr (CAN_PRUNE)
-          if (knorm) return go(fwd_bf16_pipe_kernel<D, 8, 1, true, true, false>, 256, 512);
-        return go(fwd_bf16_pipe_kernel<D, 8, 1, false, CAUSAL, TM>, 256, 512);
-      }
-    }
-    if constexpr (D <= 64) {
-      // Unmasked blocks all do the same work: once they need a second round of 8-wave workgroups,
-      // 4-wave workgroups (two per CU, one round) finish first.
-      if (!knorm && blocks128 < 2 * (int64_t)cus && (CAUSAL || blocks128 <= (int64_t)cus))
-        return go(fwd_bf16_pipe_kernel<D, 4, 2, false, CAUSAL, TM>, 128, 512);
-    }
-    if constexpr (CAN_PRUNE)
-      if (knorm) return go(fwd_bf16_pipe_kernel<D, 4, 1, true, true, false>, 128, 256);
-    return go(fwd_bf16_pipe_kernel<D, 4, 1, false, CAUSAL, TM>, 128, 256);
-  } else {
-    const dim3 grid((unsigned)bh, (unsigned)((n + kBR - 1) / kBR));
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TM>), grid, dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
-                       (const float*)v, logf, (float*)o, lse, c, n, scale_log2, lay);
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t blocks256 = bh * (int64_t)((n + 255) / 256);
+  const int64_t blocks128 = bh * (int64_t)((n + 127) / 128);
+  const bf16 *qq = (const bf16*)q, *kk = (const bf16*)k, *vv = (const bf16*)v;
+  bf16* oo = (bf16*)o;
+  auto go = [&](auto kernel, int rows, int threads) {
+    const dim3 grid((unsigned)bh, (unsigned)((n + rows - 1) / rows));
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, qq, kk, vv, logf, oo, lse, c, n, scale_log2, knorm,
+                       lay);
     return hipGetLastError();
+  };
+  constexpr bool CAN_PRUNE = CAUSAL && !TM;
+  if constexpr (D >= 64) {
+    if (blocks256 >= 2 * (int64_t)cus) {
+      if constexpr (CAN_PRUNE)
+        if (knorm) return go(fwd_bf16_pipe_kernel<D, 8, 1, true, true, false>, 256, 512);
+      return go(fwd_bf16_pipe_kernel<D, 8, 1, false, CAUSAL, TM>, 256, 512);
+    }
   }
+  if constexpr (D <= 64) {
+    // Unmasked blocks all do the same work: once they need a second round of 8-wave workgroups,
+    // 4-wave workgroups (two per CU, one round) finish first.
+    if (!knorm && blocks128 < 2 * (int64_t)cus && (CAUSAL || blocks128 <= (int64_t)cus))
+      return go(fwd_bf16_pipe_kernel<D, 4, 2, false, CAUSAL, TM>, 128, 512);
+  }
+  if constexpr (CAN_PRUNE)
+    if (knorm) return go(fwd_bf16_pipe_kernel<D, 4, 1, true, true, false>, 128, 256);
+  return go(fwd_bf16_pipe_kernel<D, 4, 1, false, CAUSAL, TM>, 128, 256);
 }
 
 template <bool CAUSAL, bool TM>
 hipError_t launch_fwd_l(const void* q, const void* k, const void* v, const float* logf, void* o, float* lse, float* c,
                         int64_t bh, int n, int d, float scale_log2, bool is_bf16, const FwdLayout& lay,
                         const float* knorm, hipStream_t stream) {
-  if (is_bf16) {
-    switch (d) {
-      case 32: return launch_fwd_t<bf16, 32, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
-      case 64: return launch_fwd_t<bf16, 64, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
-      case 128:
-        return launch_fwd_t<bf16, 128, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
-    }
-  } else {
-    switch (d) {
-      case 32: return launch_fwd_t<float, 32, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, lay, stream);
-      case 64: return launch_fwd_t<float, 64, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, lay, stream);
-      case 128:
-        return launch_fwd_t<float, 128, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, nullptr, lay, stream);
-    }
+  if (!is_bf16)
+    return launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, logf, (float*)o, lse, c, bh, n, d,
+                          scale_log2, CAUSAL, TM, lay, stream);
+  switch (d) {
+    case 32: return launch_fwd_t<32, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
+    case 64: return launch_fwd_t<64, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
+    case 128: return launch_fwd_t<128, CAUSAL, TM>(q, k, v, logf, o, lse, c, bh, n, scale_log2, knorm, lay, stream);
   }
   return hipErrorInvalidValue;
 }
