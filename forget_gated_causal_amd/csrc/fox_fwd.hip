@@ -37,9 +37,7 @@
 //     weights the P.V products use.
 //
 // fp32 inputs run the kernel of fox_fwd_f32.hip (launch_fwd_f32); the gate-sum scan and the tile
-// constants both use are in fox_fwd_gates.h.  This file is compiled with the MFMA VGPR form
-// forced: the 4-wave d = 128 kernels (one wave per SIMD, room for more than 256 registers) would
-// otherwise get every MFMA in AGPR form and copy each score out for the VALU.
+// constants both use are in fox_fwd_gates.h.
 #include <math.h>
 
 #include <type_traits>
