@@ -22,6 +22,7 @@
 // Ragged caches: with `lens` given, sequence s uses only its first lens[s] slots (clamped to
 // [1, L]) of caches allocated for L, and its new token sits at slot lens[s]-1.  Its slots are
 // shared evenly by its nsplit workgroups; a split left without slots writes an empty record.
+// The split workgroups take the sequences in decreasing order of length.
 // Paged caches (PAGED): logical slot j of sequence s is row j & (P-1) of physical page
 // table[s][j >> log2 P] in pools [pages][heads][P][d] (c: [pages][heads][P]); the capacity L is
 // max_pages * P.  Everything else is the ragged step.
@@ -40,6 +41,7 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDecU = 4;
+constexpr int kRankSeqs = 1024;  // ragged caches: sequences ordered by length on the device up to this many
 constexpr float kTau = 8.0f;
 constexpr float kNegInf = -INFINITY;
 
@@ -118,7 +120,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(const T* __re
   __shared__ float s_m[kDecWaves], s_l[kDecWaves];
   __shared__ float s_acc[kDecWaves][D];
 
-  const int wg = blockIdx.x;
+  // Ragged caches: the workgroups take the sequences longest first (decreasing length, ties by
+  // index), so that no long sequence's splits start last and hold up the end of the grid.  Each
+  // (sequence, head, split) computes what it does in plain order; only the dispatch order changes.
+  int wg = blockIdx.x;
+  if (lens) {
+    const int per = nh * nsplit;  // workgroups per sequence
+    const int nseq = (int)(gridDim.x / (unsigned)per);
+    if (nseq <= kRankSeqs) {
+      __shared__ int s_len[kRankSeqs];
+      __shared__ int s_pick;
+      for (int t = threadIdx.x; t < nseq; t += kDecThreads) s_len[t] = min(max(lens[t], 1), Lcap);
+      __syncthreads();
+      const int r = wg / per;  // this workgroup serves the sequence of rank r
+      for (int t = threadIdx.x; t < nseq; t += kDecThreads) {
+        const int lt = s_len[t];
+        int rank = 0;
+        for (int u = 0; u < nseq; ++u) rank += (s_len[u] > lt) || (s_len[u] == lt && u < t);
+        if (rank == r) s_pick = t;
+      }
+      __syncthreads();
+      wg = s_pick * per + (wg - r * per);
+    }
+  }
   const int sh = wg / nsplit, split = wg - sh * nsplit;
   const int L = lens ? min(max(lens[sh / nh], 1), Lcap) : Lcap;  // this sequence's slots
   // a sequence's slots are shared evenly by its nsplit workgroups (with every length at the
