@@ -171,7 +171,6 @@ __device__ __forceinline__ bf16x4 tr16(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)(p));
 }
 
-// Operand of an MFMA whose M (or N) is a block of 32 columns and whose K runs over 16 rows of a
 // Accumulating MFMAs of the d = 128 kernels (one wave per SIMD, 512 registers): dK^T and dV^T
 // (key side) and dQ (query side) stay in AGPRs, written only by these inline-assembly MFMAs, while
 // the score MFMAs (builtins; this file is compiled with the MFMA VGPR form forced) write VGPRs
@@ -191,6 +190,7 @@ __device__ __forceinline__ void agpr_fence(f32x16 (&c)[N]) {
   __asm__ volatile("s_nop 15" : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3]));
 }
 
+// Operand of an MFMA whose M (or N) is a block of 32 columns and whose K runs over 16 rows of a
 // swizzled row-major [row][column] LDS tile: lane (l32, hi) gets column dim0 + l32 of rows
 // {row0 + 4hi .. +3, row0 + 8 + 4hi .. +3}, the row order of the accumulator registers 8u..8u+7.
 template <int W>
