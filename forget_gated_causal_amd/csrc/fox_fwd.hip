@@ -838,8 +838,14 @@ __device__ __forceinline__ void fwd_pipe_body(Bf16Stage<D>* s0, Bf16Stage<D>* s1
   }
 }
 
+// Waves per SIMD the register budget is set for: two, except the 4-wave blocks at d = 128, whose
+// VGPR-form MFMAs need more than 256 registers (one wave per SIMD).
+template <int D, int NWR>
+constexpr int kFwdWavesPerSimd = D == 128 && NWR == 4 ? 1 : 2;
+
 template <int D, int NWR, int SP, bool PRUNE, bool CAUSAL, bool TM>
-__global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pipe_kernel(
+__global__ __launch_bounds__(64 * NWR * SP) __attribute__((amdgpu_waves_per_eu(
+    kFwdWavesPerSimd<D, NWR>, kFwdWavesPerSimd<D, NWR>))) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ logf, bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_out, int n,
     float scale_log2, const float* __restrict__ knorm, const FwdLayout lay) {
