@@ -563,6 +563,14 @@ def test_decode_ragged_parity(dtype, d, L):
     _check_decode_ragged(fi.decode_inputs(cfg), _ragged_lens(5, L, L + d), TOL[dtype])
 
 
+@pytest.mark.parametrize("S", [1024, 1025])
+def test_decode_ragged_many_sequences(S):
+    """The split workgroups take the sequences longest first when there are at most 1024 of them
+    (ranked on the device), in index order beyond that: both sides of the limit."""
+    cfg = fi.DecodeConfig(f"ragged_many_{S}", S, 1, 40, 32, "bf16", 4.0, 2.0)
+    _check_decode_ragged(fi.decode_inputs(cfg), _ragged_lens(S, cfg.L, 11), TOL["bf16"])
+
+
 def test_decode_ragged_full_size_sampled():
     cfg = fi.DECODE["c5"]
     inp = fi.decode_inputs(cfg)
