@@ -70,6 +70,8 @@ KERNEL_SOURCES = {"fwd": ["fox_fwd.hip", "fox_fwd_gates.h", "fox_device.h"], "de
 COPY_CAL_BYTES = 1 << 30
 DECODE_KERNEL = "decode_split_kernel<bf16,128> + decode_combine_kernel<bf16,128>"
 BWD_KERNEL = "fox_attn_bwd<{d},causal>: bwd_rows (gate rows + D) + bwd_kv + bwd_dq + suffix scan"
+BWD_STAGED_KERNEL = ("fox_attn_bwd_staged<{d}>: bwd_rows (gate rows + D) + bwd_kv (dS staged) + bwd_dq_staged "
+                     "+ suffix scan")
 
 
 def kernel_source_digest(kind: str) -> str:
@@ -134,9 +136,9 @@ def write_traffic_summary(args):
         f"# rocprofv3 counter summary: HBM-side traffic per launch of {args.kernel} on workload {args.workload}",
         "# commands (one counter per run; <out> is the output directory):",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o p -- python3 bench.py --workload {args.workload} "
-        f"--only --no-cpu-baseline --steps 4 --warmup 2{' --backward' if args.kind == 'bwd' else ''}",
+        f"--only --no-cpu-baseline --steps 4 --warmup 2{' --backward' if args.kind == 'bwd' else ''}{' --staged' if getattr(args, 'staged', False) else ''}",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o p -- python3 bench.py --workload {args.workload} "
-        f"--only --no-cpu-baseline --steps 4 --warmup 2{' --backward' if args.kind == 'bwd' else ''}",
+        f"--only --no-cpu-baseline --steps 4 --warmup 2{' --backward' if args.kind == 'bwd' else ''}{' --staged' if getattr(args, 'staged', False) else ''}",
         "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/copy_fetch -o p -- python3 bench.py --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/copy_write -o p -- python3 bench.py --copy-calibration",
         "#   python3 bench.py --traffic-summary ... (this file)",
@@ -387,9 +389,10 @@ def bench_fwd(torch, fox, fi, tag, steps, warmup, mode="causal"):
     }
 
 
-def bench_bwd(torch, fox, fi, tag, steps, warmup):
+def bench_bwd(torch, fox, fi, tag, steps, warmup, staged=False):
     """fox_attn_bwd on the forward workload `tag`: 10*d flop per causal pair (the recomputed
-    q.k, and dP, dV, dK, dQ), timed whole (row-vector, key-side, query-side and scan kernels)."""
+    q.k, and dP, dV, dK, dQ), timed whole (row-vector, key-side, query-side and scan kernels).
+    staged: fox_attn_bwd_staged (bf16, d = 128), whose key side stores dS for the dQ contraction."""
     cfg = fi.FWD[tag]
     inp = fi.fwd_inputs(cfg)
     dev = "cuda"
@@ -399,9 +402,15 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     dout = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dl = torch.empty_like(logf)
-    ws = torch.empty(fox.attn_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), device=dev, dtype=torch.uint8)
-    fn = lambda: fox.attn_bwd(q, k, v, o, dout, lse, logf, scale=inp["scale"], dq=dq, dk=dk, dv=dv,  # noqa: E731
-                              dlogf=dl, workspace=ws)
+    if staged:
+        ws = torch.empty(fox.attn_bwd_staged_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), device=dev,
+                         dtype=torch.uint8)
+        fn = lambda: fox.attn_bwd_staged(q, k, v, o, dout, lse, logf, scale=inp["scale"], dq=dq, dk=dk,  # noqa: E731
+                                         dv=dv, dlogf=dl, workspace=ws)
+    else:
+        ws = torch.empty(fox.attn_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), device=dev, dtype=torch.uint8)
+        fn = lambda: fox.attn_bwd(q, k, v, o, dout, lse, logf, scale=inp["scale"], dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                  dlogf=dl, workspace=ws)
     _warm(torch, fn, warmup)
     region = _events_time(torch, fn, steps)
     ms = region / steps
@@ -411,12 +420,18 @@ def bench_bwd(torch, fox, fi, tag, steps, warmup):
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     kernel = (f"bwd_kv_kernel<{cfg.d},causal> + bwd_dq_kernel<{cfg.d},causal> + 2 small kernels" if bf16 else
               f"bwd_f32_kv_kernel<{cfg.d},causal> + bwd_f32_dq_kernel<{cfg.d},causal> + 2 small kernels")
-    traffic = stored_traffic(tag, BWD_KERNEL.format(d=cfg.d), "bwd") if bf16 else None
-    return {"workload": cfg.desc + ", backward", "value": round(achieved, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(ms, 4),
-            "note": "10*d flop per causal pair (the dq kernel's recomputation of S and dP, 4*d more, is not "
-                    "counted); one call = the row-vector, key-side, query-side and gate suffix-sum kernels"
-                    + ("" if bf16 else "; fp32 on the vector ALU, a parity-sized workload (latency-bound)"),
+    label = BWD_KERNEL
+    note = ("10*d flop per causal pair (the dq kernel's recomputation of S and dP, 4*d more, is not "
+            "counted); one call = the row-vector, key-side, query-side and gate suffix-sum kernels"
+            + ("" if bf16 else "; fp32 on the vector ALU, a parity-sized workload (latency-bound)"))
+    if staged:
+        kernel = f"bwd_kv_kernel<{cfg.d},causal,staged> + bwd_dq_staged_kernel<{cfg.d}> + 2 small kernels"
+        label = BWD_STAGED_KERNEL
+        note = ("10*d flop per causal pair; fox_attn_bwd_staged: the key side stores the bf16 dS "
+                f"({ws.numel() / 1e9:.2f} GB of workspace) and dQ is contracted from it, no recomputation")
+    traffic = stored_traffic(tag, label.format(d=cfg.d), "bwd") if bf16 else None
+    return {"workload": cfg.desc + (", backward, staged dS" if staged else ", backward"), "value": round(achieved, 2),
+            "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "note": note,
             "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}}
 
@@ -587,6 +602,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c2_f1", "c2_alibi", "c3", "c4", "c5"])
     ap.add_argument("--backward", action="store_true", help="with --only: time fox_attn_bwd on the workload")
+    ap.add_argument("--staged", action="store_true", help="with --backward: time fox_attn_bwd_staged instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time a captured HIP graph of the K calls")
     ap.add_argument("--only", action="store_true", help="measure the selected workload only")
@@ -650,7 +666,7 @@ def main():
         return
 
     if args.backward:
-        x = bench_bwd(torch, fox, fi, args.workload, args.steps, args.warmup)
+        x = bench_bwd(torch, fox, fi, args.workload, args.steps, args.warmup, staged=args.staged)
         print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.1f} TFLOP/s", file=sys.stderr,
               flush=True)
         line.update({"value": x["value"], "unit": "TFLOP/s", "ms_per_step": x["ms_per_step"],
@@ -706,6 +722,12 @@ def main():
                   flush=True)
             others[f"{tag}_backward"] = x
             torch.cuda.empty_cache()
+        x = bench_bwd(torch, fox, fi, "c3", max(10, args.steps // 5), max(3, args.warmup // 2), staged=True)
+        print(f"# {x['workload']}: {x['ms_per_step']*1e3:.1f} us/step, {x['value']:.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+        others["c3_backward_staged"] = x
+        del x
+        torch.cuda.empty_cache()
         dec, dinp = bench_decode(torch, fox, fi, "c5", max(10, args.steps // 5), max(3, args.warmup // 2))
         print(f"# {dec['workload']}: {dec['ms_per_step']*1e3:.1f} us/step, {dec['value']:.0f} GB/s",
               file=sys.stderr, flush=True)

@@ -227,6 +227,39 @@ def attn_bwd(q, k, v, o, dout, lse, logf, causal: bool = True, scale: float | No
     return dq, dk, dv, dlogf
 
 
+def attn_bwd_staged_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
+    return int(lib().fox_attn_bwd_staged_workspace_bytes(b, h, n, d))
+
+
+def attn_bwd_staged(q, k, v, o, dout, lse, logf, scale: float | None = None, dq=None, dk=None, dv=None,
+                    dlogf=None, workspace=None):
+    """attn_bwd in decoder mode for head-major bf16 tensors with d = 128 through fox_attn_bwd_staged:
+    the key-side kernel stores dS (about N*N bytes per head of workspace) and dQ is contracted
+    from it.  Returns (dq, dk, dv, dlogf)."""
+    B, H, N, d = q.shape
+    tshape, vshape = (B, H, N, d), (B, H, N)
+    if q.dtype != torch.bfloat16:
+        raise ValueError(f"attn_bwd_staged takes bf16 tensors, got {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, q.dtype)
+        if tuple(t.shape) != tshape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {tshape}")
+    for name, t in (("lse", lse), ("logf", logf)):
+        _need(t, name, torch.float32)
+        if tuple(t.shape) != vshape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {vshape}")
+    dq = _alloc_or_check(dq, "dq", tshape, q.dtype, q.device)
+    dk = _alloc_or_check(dk, "dk", tshape, q.dtype, q.device)
+    dv = _alloc_or_check(dv, "dv", tshape, q.dtype, q.device)
+    dlogf = _alloc_or_check(dlogf, "dlogf", vshape, torch.float32, q.device)
+    workspace = _workspace(workspace, attn_bwd_staged_workspace_bytes(B, H, N, d), q.device)
+    scale = _default_scale(d) if scale is None else float(scale)
+    check("fox_attn_bwd_staged", lib().fox_attn_bwd_staged(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(logf), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dlogf), _ptr(workspace), _nbytes(workspace), B, H, N, d, scale, FOX_BF16, _stream()))
+    return dq, dk, dv, dlogf
+
+
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 

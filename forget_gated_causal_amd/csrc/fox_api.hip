@@ -142,10 +142,11 @@ fox_status_t fox_attn_bwd(const void* q, const void* k, const void* v, const voi
                          scale, dtype, causal, FOX_HEAD_MAJOR, stream);
 }
 
-fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+// Validation shared by the backward entry points; need: the workspace bytes the call uses.
+static fox_status_t bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
                              const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                              void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
-                             float scale, fox_dtype_t dtype, int causal, fox_layout_t layout, hipStream_t stream) {
+                             float scale, fox_dtype_t dtype, fox_layout_t layout, size_t need) {
   if (!q || !k || !v || !o || !dout || !lse || !logf || !dq || !dk || !dv || !dlogf) return FOX_ERR_INVALID_ARG;
   if (b <= 0 || h <= 0 || n <= 0 || d <= 0 || n > FOX_MAX_SEQ) return FOX_ERR_INVALID_ARG;
   if (b > kI32Max / h) return FOX_ERR_INVALID_ARG;
@@ -162,7 +163,6 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
     if (!aligned(p, 16)) return FOX_ERR_INVALID_ARG;
   if (!aligned(lse, 4) || !aligned(logf, 4) || !aligned(dlogf, 4)) return FOX_ERR_INVALID_ARG;
   const int64_t bh = b * h;
-  const size_t need = fox::attn_bwd_workspace_bytes(bh, (int)n, (int)d);
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FOX_ERR_WORKSPACE;
   const size_t tb = (size_t)bh * (size_t)n * (size_t)d * elem_bytes(dtype), vb = (size_t)bh * (size_t)n * sizeof(float);
   // every output (and the workspace) apart from every other buffer
@@ -173,6 +173,17 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
   for (int i = 0; i < 5; ++i)  // outs[i] is all[7 + i]
     for (int j = 0; j < 12; ++j)
       if (j != 7 + i && overlap(outs[i], osz[i], all[j], asz[j])) return FOX_ERR_INVALID_ARG;
+  return FOX_OK;
+}
+
+fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
+                             void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
+                             float scale, fox_dtype_t dtype, int causal, fox_layout_t layout, hipStream_t stream) {
+  const size_t need = fox_attn_bwd_workspace_bytes(b, h, n, d);
+  const fox_status_t st = bwd_args(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, workspace_bytes, b, h,
+                                   n, d, scale, dtype, layout, need);
+  if (st != FOX_OK) return st;
   if (dtype == FOX_F32)
     return from_hip(fox::launch_attn_bwd_f32(
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
@@ -181,6 +192,27 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
         layout == FOX_TOKEN_MAJOR, stream));
   return from_hip(fox::launch_attn_bwd(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, (int)n,
                                        (int)d, scale, causal != 0, layout == FOX_TOKEN_MAJOR, stream));
+}
+
+// The staged dS of one head is addressed with 32-bit byte offsets.
+static bool staged_size_ok(int64_t n) { return fox::attn_bwd_staged_head_bytes((int)n) <= kI32Max; }
+
+size_t fox_attn_bwd_staged_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d) {
+  if (b <= 0 || h <= 0 || n <= 0 || n > FOX_MAX_SEQ || d != 128 || b > kI32Max / h || !staged_size_ok(n)) return 0;
+  return fox::attn_bwd_staged_workspace_bytes(b * h, (int)n);
+}
+
+fox_status_t fox_attn_bwd_staged(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
+                                 void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
+                                 float scale, fox_dtype_t dtype, hipStream_t stream) {
+  const size_t need = fox_attn_bwd_staged_workspace_bytes(b, h, n, d);
+  const fox_status_t st = bwd_args(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, workspace_bytes, b, h,
+                                   n, d, scale, dtype, FOX_HEAD_MAJOR, need);
+  if (st != FOX_OK) return st;
+  if (dtype != FOX_BF16 || d != 128 || !staged_size_ok(n)) return FOX_ERR_UNSUPPORTED;
+  return from_hip(fox::launch_attn_bwd_staged(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, (int)n,
+                                              scale, stream));
 }
 
 // Validation shared by the decode entry points (cache_lens: the ragged step's lengths, or null;

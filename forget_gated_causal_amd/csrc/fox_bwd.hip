@@ -70,6 +70,17 @@ constexpr int kKT = 64;   // keys per tile of the query-stationary kernel
 constexpr int kBwdThreads = 256;
 constexpr int kPad = 64;  // per-head row vectors are padded to a multiple of this
 constexpr int64_t kFuseMaxBlocks = 1024;  // grids up to this many blocks run both parts in one launch
+
+// Staged dS (fox_attn_bwd_staged): per head, key block kb holds the query tiles 4 kb .. nqt - 1
+// (those at or below its diagonal), each a [128 keys][32 queries] bf16 tile; the blocks follow
+// one another, so block kb starts at tile kb nqt - 2 kb (kb - 1).
+__host__ __device__ __forceinline__ int64_t staged_tile0(int kb, int nqt) {
+  return (int64_t)kb * nqt - 2 * (int64_t)kb * (kb - 1);
+}
+__host__ __device__ __forceinline__ int64_t staged_tiles(int n) {
+  const int nqt = (n + kBQ - 1) / kBQ, nkb = (n + kBK - 1) / kBK;
+  return staged_tile0(nkb, nqt);
+}
 constexpr float kNegInfB = -INFINITY;
 constexpr int kRawBufferCfg = 0x00020000;  // dword 3 of a raw (unswizzled, byte-offset) buffer resource
 
@@ -105,6 +116,13 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* p, uint32_t num_bytes) {
 // write needs before an LDS-DMA instruction reads it.
 __device__ __forceinline__ void lds_load16(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
   __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "{m0}"(m0v)
+                   : "memory");
+}
+// ... with the streaming hint, for data read once (the staged dS)
+__device__ __forceinline__ void lds_load16_nt(uint32_t m0v, u32x4 rsrc, uint32_t voff) {
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                    :
                    : "v"(voff), "s"(rsrc), "{m0}"(m0v)
                    : "memory");
@@ -407,14 +425,16 @@ struct TileLoader {
   }
 };
 
-// Key-stationary part (dK, dV, column sums of dS) for key block kb of head bh.
-template <int D, bool CAUSAL>
+// Key-stationary part (dK, dV, column sums of dS) for key block kb of head bh.  STAGE: also write
+// the bf16 dS of every query tile to ds_stage (the block's first staged tile; see bwd_dq_staged_kernel).
+template <int D, bool CAUSAL, bool STAGE = false>
 __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, const bf16* __restrict__ q,
                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
                                              const bf16* __restrict__ dout, const float* __restrict__ rowv,
                                              const double* __restrict__ cb, bf16* __restrict__ dk,
                                              bf16* __restrict__ dv, float* __restrict__ colsum_out, int n, int npad,
-                                             int ncb, float scale, const BwdLayout& lay) {
+                                             int ncb, float scale, const BwdLayout& lay,
+                                             bf16* __restrict__ ds_stage = nullptr) {
   constexpr int KK = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -518,9 +538,13 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
     const int q0 = (qt0 + t) * kBQ;
     const int buf = BC >= 0 ? BC : t % 3, nb = BC >= 0 ? (BC + 1) % 3 : (t + 1) % 3;
     if constexpr (HN) {
-      // this wave's loads of tile t + 1 are the only vector-memory instructions in flight; after
-      // the barrier every wave's loads are visible and tile t - 1's buffer is no longer read
-      wait_vmem<0>();
+      // this wave's loads of tile t + 1 are the only vector-memory instructions in flight (with
+      // STAGE, besides the 2 stores of tile t - 1's dS issued after them); after the barrier every
+      // wave's loads are visible and tile t - 1's buffer is no longer read
+      if (STAGE && t > 0)
+        wait_vmem<2>();
+      else
+        wait_vmem<0>();
       __syncthreads();
       if (t + 2 < nt) load_tile(q0 + 2 * kBQ, BC >= 0 ? (BC + 2) % 3 : (t + 2) % 3);
     }
@@ -589,6 +613,15 @@ __device__ __forceinline__ void bwd_kv_block(KvLds<D>& lds, size_t bh, int kb, c
     if constexpr (!CAUSAL) colsum += tree_sum16(dp);
     const bf16x8 pb[2] = {acc_operand(s, 0), acc_operand(s, 1)};
     const bf16x8 sb[2] = {acc_operand(dp, 0), acc_operand(dp, 1)};
+    if constexpr (STAGE) {
+      // tile t of dS in two halves u of [128 keys][2 lane halves] x 8 bf16: sb[u] of this lane
+      // (queries 16u + 4hi + 0..3 and 16u + 8 + 4hi + 0..3 of its key), so that each store
+      // instruction writes 1 KiB in one piece; streaming stores, read once by the dQ kernel
+      bf16* tile = ds_stage + (size_t)t * (kBK * kBQ) + (32 * wave + l32) * 16 + 8 * hi;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        __builtin_nontemporal_store(sb[u], reinterpret_cast<bf16x8*>(tile + u * (kBK * 16)));
+    }
     if constexpr (CAUSAL) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -911,15 +944,19 @@ __device__ __forceinline__ void bwd_dq_block(DqLds<D>& lds, size_t bh, int qb, c
 }
 
 // The two parts as kernels of their own (large grids) ...
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool STAGE = false>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 && CAUSAL ? 2 : 1))) void bwd_kv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ dout,
     const float* __restrict__ rowv, const double* __restrict__ cb, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ colsum_out, int n, int npad, int ncb, float scale, BwdLayout lay) {
+    float* __restrict__ colsum_out, int n, int npad, int ncb, float scale, BwdLayout lay, bf16* __restrict__ ds = nullptr,
+    int64_t ds_head = 0) {
   __shared__ KvLds<D> lds;
   // heads fastest: the key blocks of one head share its q / dO in L2; causal work falls with kb
-  bwd_kv_block<D, CAUSAL>(lds, blockIdx.x, (int)blockIdx.y, q, k, v, dout, rowv, cb, dk, dv, colsum_out, n, npad, ncb,
-                          scale, lay);
+  const int kb = (int)blockIdx.y;
+  bf16* ds_stage = nullptr;
+  if constexpr (STAGE) ds_stage = ds + blockIdx.x * ds_head + staged_tile0(kb, (n + kBQ - 1) / kBQ) * (kBK * kBQ);
+  bwd_kv_block<D, CAUSAL, STAGE>(lds, blockIdx.x, kb, q, k, v, dout, rowv, cb, dk, dv, colsum_out, n, npad, ncb, scale,
+                                 lay, ds_stage);
 }
 
 template <int D, bool CAUSAL>
@@ -931,6 +968,120 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
   // the longest causal blocks (the last queries) start first
   bwd_dq_block<D, CAUSAL>(lds, blockIdx.x, (int)(gridDim.y - 1 - blockIdx.y), q, k, v, dout, rowv, cb, dq, rowsum_out,
                           nullptr, n, npad, ncb, scale, lay);
+}
+
+// dQ and the row sums of dS from the staged dS (fox_attn_bwd_staged: causal, d = 128).  One
+// workgroup of 4 waves per (128-query block, head); wave w owns query tile 4 qb + w.  Stage s is
+// half s % 2 of key block s / 2: 64 keys of K and the matching 64 rows of the 4 waves' dS tiles,
+// brought in by direct-to-LDS loads into a ring of 4 stages, two ahead of use.  dQ^T = K^T dS^T on
+// v_mfma_f32_32x32x16_bf16 with dims as M and queries as N (A: K read transposed, B: the dS tile
+// read transposed), so every accumulator lane holds one query; the row sums add the same bf16 dS
+// values that the key-stationary kernel summed into the column sums.
+constexpr int kStageKeys = 64;
+
+template <int D>
+struct alignas(16) StagedLds {
+  bf16 k[4][kStageKeys * D];          // K rows of each stage (swizzled, W = D)
+  bf16 ds[4][4][kStageKeys * kBQ];    // per stage and wave: dS rows [key][32 queries] (W = 32)
+};
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_staged_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ ds, bf16* __restrict__ dq, float* __restrict__ rowsum_out,
+    int n, int64_t ds_head, float scale, BwdLayout lay) {
+  constexpr int DB = D / 32;
+  __shared__ StagedLds<D> lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t bh = blockIdx.x;
+  const int qb = (int)(gridDim.y - 1 - blockIdx.y);  // the longest blocks first
+  const int nqt = (n + kBQ - 1) / kBQ;
+  const int qt = 4 * qb + wave;   // this wave's query tile (past the last one: loads and barriers only)
+  // this lane's query: column l32 of the LDS dS rows (staged order, above)
+  const int qi = qt * kBQ + 16 * (l32 >> 4) + 4 * ((l32 >> 3) & 1) + (l32 & 3) + 8 * ((l32 >> 2) & 1);
+  const int64_t tb = lay.tbase((int)bh);
+  const int rs = lay.rs;
+  const int ns = 2 * (qb + 1);  // stages: key blocks 0..qb, two halves each
+
+  // buffer resources: K rows past n and dS past the head's staged tiles read as zeros
+  const u32x4 rk = sgpr_rsrc(k + tb, (uint32_t)(((int64_t)(n - 1) * rs + D) * 2));
+  const u32x4 rds = sgpr_rsrc(ds + bh * ds_head, (uint32_t)(ds_head * 2));
+  const TileLoader<D, kStageKeys> tl(wave, lane, rs);
+  // this wave's 64 dS rows in LDS as [key][32 queries] with the queries in the staged order: chunk c
+  // of a row is the 16 bytes a lane half c % 2 stored from register block c / 2, i.e. queries
+  // 16 (c/2) + 4 (c%2) + {0..3, 8..11}.  4 loads of 16 rows: lane l of load j lands at chunk
+  // position 4 (16 j + l / 4) + l % 4 of the stage, which holds chunk (l % 4) ^ swz<32>(row).
+  uint32_t dsoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * j + (lane >> 2), c = (lane & 3) ^ swz<kBQ>(r);
+    dsoff[j] = (uint32_t)(((c >> 1) * (kBK * 16) + r * 16 + 8 * (c & 1)) * 2);
+  }
+  auto issue = [&](int st) {  // 8 vector-memory instructions per wave
+    const int slot = st & 3, kbk = st >> 1, half = st & 1;
+    tl.load(lds.k[slot], rk, kbk * kBK + half * kStageKeys, wave);
+    const int64_t tile = staged_tile0(kbk, nqt) + (qt - 4 * kbk);
+    const uint32_t base = (uint32_t)((tile * (kBK * kBQ) + half * (kStageKeys * 16)) * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lds_load16_nt((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&lds.ds[slot][wave][64 * 8 * j])), rds,
+                    base + dsoff[j]);
+  };
+
+  f32x16 acc[DB];  // dQ^T: lane = query, register r = dim 32mb + 8(r/4) + 4hi + r%4
+#pragma unroll
+  for (int mb = 0; mb < DB; ++mb) acc[mb] = f32x16{};
+  float rs0 = 0.0f, rs1 = 0.0f;
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+
+  issue(0);
+  if (ns > 1) issue(1);
+  if (ns > 2) issue(2);
+  for (int st = 0; st < ns; ++st) {
+    // stage st has landed once at most the stages issued after it are in flight
+    const int after = min(ns - 1, st + 2) - st;
+    if (after >= 2)
+      wait_vmem<16>();
+    else if (after == 1)
+      wait_vmem<8>();
+    else
+      wait_vmem<0>();
+    __syncthreads();  // every wave's loads of stage st are visible; stage st - 1's slot is free
+    if (st + 3 < ns) issue(st + 3);
+    const int slot = st & 3;
+    const bf16* kt = lds.k[slot];
+    const bf16* dt = lds.ds[slot][wave];
+#pragma unroll
+    for (int ks = 0; ks < kStageKeys / 16; ++ks) {
+      const bf16x8 bop = transposed_operand<kBQ>(dt, 16 * ks, 0, lane);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 pr = {bop[2 * w], bop[2 * w + 1]};
+        if (w & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs1, false);
+        else rs0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs0, false);
+      }
+#pragma unroll
+      for (int mb = 0; mb < DB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(transposed_operand<D>(kt, 16 * ks, 32 * mb, lane), bop,
+                                                          acc[mb], 0, 0, 0);
+    }
+  }
+  const float rsum = pair32_sum(rs0 + rs1);
+  if (qt < nqt && qi < n) {
+    bf16* dqr = dq + tb + (int64_t)qi * rs;
+#pragma unroll
+    for (int mb = 0; mb < DB; ++mb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = (bf16)(acc[mb][4 * g + e] * scale);
+        *reinterpret_cast<bf16x4*>(dqr + 32 * mb + 8 * g + 4 * hi) = a;
+      }
+    }
+    if (hi == 0) rowsum_out[bh * (size_t)n + qi] = rsum;
+  }
 }
 
 // The D pass of the unmasked mode: D_i = sum_j P_ij dP_ij into the row vectors' D slot, with P
@@ -972,9 +1123,21 @@ int bwd_npad(int n) { return (n + kPad - 1) / kPad * kPad; }
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_c(const void* q, const void* k, const void* v, const void* dout, const float* rowv,
                         const double* cb, void* dq, void* dk, void* dv, float* rsum, float* csum, int64_t bh, int n,
-                        int npad, int ncb, float scale, const BwdLayout& lay, hipStream_t stream) {
+                        int npad, int ncb, float scale, const BwdLayout& lay, hipStream_t stream, bf16* ds,
+                        int64_t ds_head) {
   static_assert(kBK == kQB, "one key block and one query block per block pair");
   const int nb = (n + kBK - 1) / kBK;
+  if constexpr (D == 128 && CAUSAL) {
+    if (ds) {  // staged dS: the key-stationary kernel writes it, a contraction with K gives dQ
+      const dim3 grid((unsigned)bh, (unsigned)nb);
+      hipLaunchKernelGGL((bwd_kv_kernel<D, true, true>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, cb, (bf16*)dk, (bf16*)dv, csum, n,
+                         npad, ncb, scale, lay, ds, ds_head);
+      hipLaunchKernelGGL((bwd_dq_staged_kernel<D>), grid, dim3(kBwdThreads), 0, stream, (const bf16*)k,
+                         (const bf16*)ds, (bf16*)dq, rsum, n, ds_head, scale, lay);
+      return hipGetLastError();
+    }
+  }
   if (2 * bh * nb <= kFuseMaxBlocks) {
     hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3((unsigned)bh, (unsigned)(2 * nb)), dim3(kBwdThreads), 0,
                        stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, rowv, cb, (bf16*)dq,
@@ -995,7 +1158,7 @@ template <int D>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf, void* ws,
                         int64_t b, int64_t h, int n, float scale, bool causal, bool token_major,
-                        hipStream_t stream) {
+                        hipStream_t stream, bf16* ds = nullptr, int64_t ds_head = 0) {
   const int64_t bh = b * h;
   const int npad = bwd_npad(n);
   const int ncb = bwd_gate_blocks(n);
@@ -1021,9 +1184,9 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = causal ? launch_bwd_c<D, true>(q, k, v, dout, w.rowv, w.cb, dq, dk, dv, w.rsum, w.csum, bh, n, npad, ncb, scale,
-                                     lay, stream)
+                                     lay, stream, ds, ds_head)
              : launch_bwd_c<D, false>(q, k, v, dout, w.rowv, w.cb, dq, dk, dv, w.rsum, w.csum, bh, n, npad, ncb, scale,
-                                      lay, stream);
+                                      lay, stream, nullptr, 0);
   if (e != hipSuccess) return e;
   // dlog f_t = sum_{i >= t} (rowsum_i - colsum_i), written in the gates' layout
   return launch_suffix_sum(w.rsum, w.csum, dlogf, bh, n, (int)h, token_major, stream);
@@ -1074,6 +1237,24 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                                token_major, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// Staged backward: the workspace of attn_bwd_workspace_bytes, then (256-byte aligned) the staged dS
+// of every head, staged_tiles(n) tiles of 128 x 32 bf16 each.
+size_t attn_bwd_staged_workspace_bytes(int64_t bh, int n) {
+  const size_t base = (attn_bwd_workspace_bytes(bh, n, 128) + 255) / 256 * 256;
+  return base + (size_t)bh * (size_t)staged_tiles(n) * (kBK * kBQ) * sizeof(bf16);
+}
+
+int64_t attn_bwd_staged_head_bytes(int n) { return staged_tiles(n) * (kBK * kBQ) * (int64_t)sizeof(bf16); }
+
+hipError_t launch_attn_bwd_staged(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                  const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
+                                  void* workspace, int64_t b, int64_t h, int n, float scale, hipStream_t stream) {
+  const size_t base = (attn_bwd_workspace_bytes(b * h, n, 128) + 255) / 256 * 256;
+  bf16* ds = reinterpret_cast<bf16*>(static_cast<char*>(workspace) + base);
+  return launch_bwd_t<128>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, true, false,
+                           stream, ds, staged_tiles(n) * (kBK * kBQ));
 }
 
 }  // namespace fox

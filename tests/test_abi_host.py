@@ -279,6 +279,53 @@ def test_bwd_rejects_bad_arguments(L):
     assert _bwd(L, ws=H) == INVALID  # workspace == dq
 
 
+def _staged_tiles(n):
+    nqt, nkb = -(-n // 32), -(-n // 128)
+    return nkb * nqt - 2 * nkb * (nkb - 1)
+
+
+def test_bwd_staged_workspace_bytes(L):
+    f = L.fox_attn_bwd_staged_workspace_bytes
+    # the staged tiles: (128-key block, 32-query tile) pairs at or below the diagonal, counted by brute force
+    for n in (1, 31, 32, 127, 128, 129, 1000, 4096):
+        assert _staged_tiles(n) == sum(1 for kb in range(-(-n // 128)) for t in range(-(-n // 32)) if t >= 4 * kb)
+    # fox_attn_bwd's workspace rounded up to 256 bytes, then 8 KiB (128 x 32 bf16) per staged tile
+    for b, h, n in ((2, 16, 4096), (1, 1, 1), (1, 3, 1000), (1, 32, 16384)):
+        base = -(-L.fox_attn_bwd_workspace_bytes(b, h, n, 128) // 256) * 256
+        assert f(b, h, n, 128) == base + b * h * _staged_tiles(n) * 8192
+    assert f(1, 1, 4096, 64) == 0 and f(1, 1, 0, 128) == 0 and f(0, 1, 10, 128) == 0
+    # one head's staged tiles are addressed with 32-bit byte offsets
+    assert _staged_tiles(46272) * 8192 <= 2**31 - 1 < _staged_tiles(46273) * 8192
+    assert f(1, 1, 46272, 128) > 0 and f(1, 1, 46273, 128) == 0
+
+
+def _bwds(L, **kw):
+    I, J, K, M = (0x10_0000_0000 * (i + 9) for i in range(4))
+    a = dict(q=A, k=B, v=C, o=D, dout=E, lse=F, logf=G, dq=H, dk=I, dv=J, dl=K, ws=M, wsb=1 << 30, b=1, h=2, n=300,
+             d=128, scale=0.125, dt=_lib.FOX_BF16)
+    a.update(kw)
+    return L.fox_attn_bwd_staged(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["logf"], a["dq"], a["dk"],
+                                 a["dv"], a["dl"], a["ws"], a["wsb"], a["b"], a["h"], a["n"], a["d"], a["scale"],
+                                 a["dt"], None)
+
+
+def test_bwd_staged_rejects_bad_arguments(L):
+    # fox_attn_bwd's checks, with the staged workspace
+    assert _bwds(L, dout=None) == INVALID
+    assert _bwds(L, n=0) == INVALID
+    assert _bwds(L, scale=float("nan")) == INVALID
+    assert _bwds(L, q=A + 8) == INVALID
+    assert _bwds(L, ws=None) == WS
+    assert _bwds(L, wsb=L.fox_attn_bwd_staged_workspace_bytes(1, 2, 300, 128) - 1) == WS
+    assert _bwds(L, ws=0x10_0000_0000 * 8) == INVALID  # workspace == dq
+    assert _bwds(L, dv=0x10_0000_0000 * 9) == INVALID  # dv == dk
+    # then its own: bf16, d = 128, and n whose staged tiles fit 32-bit offsets
+    assert _bwds(L, d=64) == UNSUP
+    assert _bwds(L, d=96) == UNSUP
+    assert _bwds(L, dt=_lib.FOX_F32) == UNSUP
+    assert _bwds(L, n=46273, h=1) == UNSUP
+
+
 def test_bwd_ex_layout_checks(L):
     # the same argument checks as fox_attn_bwd, then the layout's own
     assert _bwd(L, layout=_lib.FOX_TOKEN_MAJOR, dout=None) == INVALID

@@ -738,6 +738,80 @@ def test_bwd_c3_full_size_sampled_heads():
         print(f"  c3 head ({b},{h}): " + ", ".join(msg), flush=True)
 
 
+# (B, H, n, gate-logit mean, sd): d = 128, decoder mode.  n covers one row, a partial tile, a
+# partial and exactly one 128-key block, several blocks with a ragged tail, and a query block whose
+# last waves lie past n (n not a multiple of 128).
+BWD_STAGED = [(1, 1, 1, 2.0, 1.0), (1, 2, 31, 2.0, 1.0), (1, 1, 128, 2.0, 1.0), (2, 2, 257, 3.0, 1.5),
+              (1, 3, 1000, 4.0, 2.0), (2, 3, 1500, -1.0, 1.0), (1, 2, 2049, 6.0, 1.0)]
+
+
+def _bwd_case(cfg, seed):
+    inp = fi.fwd_inputs(cfg)
+    g = torch.Generator().manual_seed(seed)
+    dout = torch.randn(cfg.B, cfg.H, cfg.N, cfg.d, generator=g).to(torch.bfloat16)
+    return inp, dout
+
+
+@pytest.mark.parametrize("B,H,n,mu,sigma", BWD_STAGED)
+def test_bwd_staged_parity(B, H, n, mu, sigma):
+    """fox_attn_bwd_staged against the fp64 oracle (bound as test_bwd_parity), and against
+    fox_attn_bwd: dk and dv come from the same key-side arithmetic (bit-equal); dq and dlogf take
+    the staged dS and agree with the default path to bf16 rounding."""
+    cfg = fi.FwdConfig(f"bwd_staged_{B}_{H}_{n}", B, H, n, 128, "bf16", mu, sigma)
+    inp, dout = _bwd_case(cfg, n * 7 + 3)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    ws = torch.full((fox.attn_bwd_staged_workspace_bytes(B, H, n, 128),), 0xFF, dtype=torch.uint8, device=DEV)
+    got = fox.attn_bwd_staged(q, k, v, o, dout.to(DEV), lse, logf, scale=inp["scale"], workspace=ws)
+    base = fox.attn_bwd(q, k, v, o, dout.to(DEV), lse, logf, scale=inp["scale"])
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(_np(inp["q"]), _np(inp["k"]), _np(inp["v"]), _np(inp["logf"]), inp["scale"], _np(dout))
+    msg = []
+    for name, a, r in zip(("dq", "dk", "dv", "dlogf"), got, ref):
+        err = np.abs(_np(a) - r).max()
+        bound = 2e-2 * max(1.0, np.abs(r).max())
+        msg.append(f"{name} {err:.2e} (max|ref| {np.abs(r).max():.2e})")
+        assert torch.isfinite(a).all(), name
+        assert err <= bound, (name, err, bound)
+    assert torch.equal(got[1], base[1]) and torch.equal(got[2], base[2])
+    for name, a, b in (("dq", got[0], base[0]), ("dlogf", got[3], base[3])):
+        scale_ = max(1.0, b.float().abs().max().item())
+        assert (a.float() - b.float()).abs().max().item() <= 8e-3 * scale_, name
+    print("  " + cfg.desc + " staged: " + ", ".join(msg), flush=True)
+
+
+def test_bwd_staged_c3_full_size_sampled_heads():
+    """The staged backward at c3's full size, in the bench's launch configuration: two whole heads
+    against the fp64 oracle, every head's dk, dv bit-equal to fox_attn_bwd, and a second call
+    (the workspace keeping the first call's dS) bit-equal to the first."""
+    cfg = fi.FWD["c3"]
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(1)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    ws = torch.empty(fox.attn_bwd_staged_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.uint8, device=DEV)
+    got = fox.attn_bwd_staged(q, k, v, o, dout.to(DEV), lse, logf, scale=inp["scale"], workspace=ws)
+    again = fox.attn_bwd_staged(q, k, v, o, dout.to(DEV), lse, logf, scale=inp["scale"], workspace=ws)
+    base = fox.attn_bwd(q, k, v, o, dout.to(DEV), lse, logf, scale=inp["scale"])
+    torch.cuda.synchronize()
+    for x, y in zip(got, again):
+        assert torch.equal(x, y)
+    assert torch.equal(got[1], base[1]) and torch.equal(got[2], base[2])
+    for t in got:
+        assert torch.isfinite(t).all()
+    for b, h in ((0, 0), (cfg.B - 1, cfg.H - 1)):
+        ref = oracle.fwd_bwd_head(_np(inp["q"][b, h]), _np(inp["k"][b, h]), _np(inp["v"][b, h]),
+                                  _np(inp["logf"][b, h]), inp["scale"], _np(dout[b, h]))
+        msg = []
+        for name, a, r in zip(("dq", "dk", "dv", "dlogf"), got, ref):
+            err = np.abs(_np(a[b, h]) - r).max()
+            bound = 2e-2 * max(1.0, np.abs(r).max())
+            msg.append(f"{name} {err:.2e} (max|ref| {np.abs(r).max():.2e})")
+            assert err <= bound, (b, h, name, err, bound)
+        print(f"  c3 staged head ({b},{h}): " + ", ".join(msg), flush=True)
+
+
 def test_bwd_repeatable():
     """Every backward output has one writer: two calls give bit-identical gradients."""
     cfg = fi.FwdConfig("bwd_rep", 2, 3, 700, 64, "bf16", 2.0, 1.0)
