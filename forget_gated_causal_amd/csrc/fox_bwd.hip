@@ -973,20 +973,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(D <
 // dQ and the row sums of dS from the staged dS (fox_attn_bwd_staged: causal, d = 128).  One
 // workgroup of 4 waves per (128-query block, head); wave w owns query tile 4 qb + w.  Stage s is
 // half s % 2 of key block s / 2: 64 keys of K and the matching 64 rows of the 4 waves' dS tiles,
-// brought in by direct-to-LDS loads into a ring of 4 stages, two ahead of use.  dQ^T = K^T dS^T on
+// brought in by direct-to-LDS loads into a ring of kStageSlots stages, the next kStageSlots - 1 in
+// flight while one is read.  Two slots (64 KiB) let two workgroups share a CU, each one stage ahead;
+// that ran 2-3 % faster than one workgroup with three or four stages in flight.  dQ^T = K^T dS^T on
 // v_mfma_f32_32x32x16_bf16 with dims as M and queries as N (A: K read transposed, B: the dS tile
 // read transposed), so every accumulator lane holds one query; the row sums add the same bf16 dS
 // values that the key-stationary kernel summed into the column sums.
 constexpr int kStageKeys = 64;
+constexpr int kStageSlots = 2;
 
 template <int D>
 struct alignas(16) StagedLds {
-  bf16 k[4][kStageKeys * D];          // K rows of each stage (swizzled, W = D)
-  bf16 ds[4][4][kStageKeys * kBQ];    // per stage and wave: dS rows [key][32 queries] (W = 32)
+  bf16 k[kStageSlots][kStageKeys * D];        // K rows of each stage (swizzled, W = D)
+  bf16 ds[kStageSlots][4][kStageKeys * kBQ];  // per stage and wave: dS rows [key][32 queries] (W = 32)
 };
 
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dq_staged_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kStageSlots <= 2 ? 2 : 1))) void bwd_dq_staged_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ ds, bf16* __restrict__ dq, float* __restrict__ rowsum_out,
     int n, int64_t ds_head, float scale, BwdLayout lay) {
   constexpr int DB = D / 32;
@@ -1019,7 +1022,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1))
     dsoff[j] = (uint32_t)(((c >> 1) * (kBK * 16) + r * 16 + 8 * (c & 1)) * 2);
   }
   auto issue = [&](int st) {  // 8 vector-memory instructions per wave
-    const int slot = st & 3, kbk = st >> 1, half = st & 1;
+    const int slot = st % kStageSlots, kbk = st >> 1, half = st & 1;
     tl.load(lds.k[slot], rk, kbk * kBK + half * kStageKeys, wave);
     const int64_t tile = staged_tile0(kbk, nqt) + (qt - 4 * kbk);
     const uint32_t base = (uint32_t)((tile * (kBK * kBQ) + half * (kStageKeys * 16)) * 2);
@@ -1035,21 +1038,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1))
   float rs0 = 0.0f, rs1 = 0.0f;
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
-  issue(0);
-  if (ns > 1) issue(1);
-  if (ns > 2) issue(2);
+  static_assert(kStageSlots >= 2 && kStageSlots <= 5, "the waits below allow up to 3 later stages in flight");
+  for (int st = 0; st < kStageSlots - 1 && st < ns; ++st) issue(st);
   for (int st = 0; st < ns; ++st) {
     // stage st has landed once at most the stages issued after it are in flight
-    const int after = min(ns - 1, st + 2) - st;
-    if (after >= 2)
+    const int after = min(ns - 1, st + kStageSlots - 2) - st;
+    if (after >= 3)
+      wait_vmem<24>();
+    else if (after == 2)
       wait_vmem<16>();
     else if (after == 1)
       wait_vmem<8>();
     else
       wait_vmem<0>();
     __syncthreads();  // every wave's loads of stage st are visible; stage st - 1's slot is free
-    if (st + 3 < ns) issue(st + 3);
-    const int slot = st & 3;
+    if (st + kStageSlots - 1 < ns) issue(st + kStageSlots - 1);
+    const int slot = st % kStageSlots;
     const bf16* kt = lds.k[slot];
     const bf16* dt = lds.ds[slot][wave];
 #pragma unroll
