@@ -208,7 +208,8 @@ def _demangle(name: str) -> str:
 
 
 # algorithmic flop per causal pair of each MFMA kernel (the backward's parts count their own share)
-MFMA_KERNEL_FLOP_PER_PAIR_D = {"fwd_bf16_pipe_kernel": 4, "bwd_kv_kernel": 8, "bwd_dq_kernel": 6}
+MFMA_KERNEL_FLOP_PER_PAIR_D = {"fwd_bf16_pipe_kernel": 4, "bwd_kv_kernel": 8, "bwd_dq_kernel": 6,
+                               "bwd_dq_staged_kernel": 2}
 
 
 def write_mfma_summary(args):
@@ -219,19 +220,20 @@ def write_mfma_summary(args):
              "# commands (one run per workload; <out> is the output directory):",
              "#   cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE -f csv \\",
              "#     -d <out>/<w>_<kind> -o p -- python3 <repo>/bench.py --workload <w> --only --no-cpu-baseline --steps 4 "
-             "--warmup 2 [--backward]",
+             "--warmup 2 [--backward [--staged]]",
              "#   python3 bench.py --mfma-summary ... (this file)",
              "# per dispatch (mean over every dispatch of the kernel in the run, warm-up included):",
              "#   mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (bf16 MFMA flops executed, masked diagonal halves included)",
              "#   mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * GRBM_GUI_ACTIVE / 8); GRBM_GUI_ACTIVE is summed over",
              "#               the 8 XCDs; the busy counter reads 32 cycles per 32x32x16 bf16 MFMA",
              "#   alg_flop  = 4 d (forward), 8 d (backward key side), 6 d (backward query side, which recomputes S and",
-             "#               dP) per causal pair",
+             "#               dP), 2 d (the staged-dS backward's dQ kernel) per causal pair",
              "",
              f"{'workload':10s} {'kernel':44s} {'disp':>5s} {'dur_us':>9s} {'mfma_flop':>11s} {'alg_flop':>11s} "
              f"{'exec/alg':>8s} {'mfma_util':>9s}"]
     for spec in args.pmc_csv:
         tag, kind, path = spec.split(":", 2)
+        kind = "bwd" if kind == "bwd_staged" else kind
         cfg = fi.FWD[tag]
         pairs = cfg.B * cfg.H * cfg.N * (cfg.N + 1) / 2
         per = {}
