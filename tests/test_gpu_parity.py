@@ -1032,6 +1032,48 @@ def test_graph_replays_match_eager():
         assert torch.isfinite(x)
 
 
+def test_graph_replays_staged_backward():
+    """fox_attn_bwd_staged launches kernels only as well: captured in a HIP graph, every replay
+    (outputs and staged dS NaN-filled before it, eager work between replays) equals the eager call."""
+    cfg = fi.FwdConfig("graph_staged", 1, 2, 300, 128, "bf16", 3.0, 1.5)
+    inp = fi.fwd_inputs(cfg)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    g = torch.Generator().manual_seed(19)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    o, lse, _ = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    dq, dk, dv, dl = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(logf)
+    ws = torch.empty(fox.attn_bwd_staged_workspace_bytes(1, 2, 300, 128), device=DEV, dtype=torch.uint8)
+
+    def run():
+        fox.attn_bwd_staged(q, k, v, o, dout, lse, logf, scale=inp["scale"], dq=dq, dk=dk, dv=dv, dlogf=dl,
+                            workspace=ws)
+
+    outs = (dq, dk, dv, dl)
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("dq", "dk", "dv", "dlogf"), outs, eager):
+            assert torch.equal(t, e), (rep, name)
+        x = (q.float() @ k.float().transpose(-1, -2)).sum()  # eager work between replays
+        assert torch.isfinite(x)
+
+
 # ------------------------------------------------------------------ binding: caller-supplied outputs
 
 def test_binding_rejects_bad_outputs():
