@@ -51,6 +51,10 @@
 //    mask; without it the gate rows, then bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32, and
 //    the row terms rescaled so that each row of P sums to 1 in fp32).
 //    After them the reversed prefix scan (fox_scan.hip): dlog f from row sums - column sums.
+//  * staged dS (fox_attn_bwd_staged; causal, head-major, d = 128): the key-stationary kernel also
+//    stores the bf16 dS it packed for its own dK^T MFMAs into the workspace, and
+//    bwd_dq_staged_kernel contracts dQ = dS K and the row sums from it in place of bwd_dq_kernel,
+//    which would form S and dP a second time (about n^2 bytes of workspace per head instead).
 // Tensors are head-major [B,H,N,d] or token-major [B,N,H,d] (BwdLayout: row strides d or H d,
 // gate-vector strides 1 or H); the workspace is head-major either way.
 #include <math.h>
