@@ -232,12 +232,18 @@ def attn_bwd_staged_workspace_bytes(b: int, h: int, n: int, d: int) -> int:
 
 
 def attn_bwd_staged(q, k, v, o, dout, lse, logf, scale: float | None = None, dq=None, dk=None, dv=None,
-                    dlogf=None, workspace=None):
-    """attn_bwd in decoder mode for head-major bf16 tensors with d = 128 through fox_attn_bwd_staged:
-    the key-side kernel stores dS (about N*N bytes per head of workspace) and dQ is contracted
-    from it.  Returns (dq, dk, dv, dlogf)."""
-    B, H, N, d = q.shape
-    tshape, vshape = (B, H, N, d), (B, H, N)
+                    dlogf=None, workspace=None, layout: str = "head"):
+    """attn_bwd in decoder mode for bf16 tensors with d = 128 through fox_attn_bwd_staged: the
+    key-side kernel stores dS (about N*N bytes per head of workspace) and dQ is contracted from it.
+    layout as attn_bwd.  Returns (dq, dk, dv, dlogf)."""
+    if layout not in ("head", "token"):
+        raise ValueError(f"layout must be 'head' or 'token', got {layout!r}")
+    if layout == "token":
+        B, N, H, d = q.shape
+        tshape, vshape = (B, N, H, d), (B, N, H)
+    else:
+        B, H, N, d = q.shape
+        tshape, vshape = (B, H, N, d), (B, H, N)
     if q.dtype != torch.bfloat16:
         raise ValueError(f"attn_bwd_staged takes bf16 tensors, got {q.dtype}")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -256,7 +262,8 @@ def attn_bwd_staged(q, k, v, o, dout, lse, logf, scale: float | None = None, dq=
     scale = _default_scale(d) if scale is None else float(scale)
     check("fox_attn_bwd_staged", lib().fox_attn_bwd_staged(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(logf), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(dlogf), _ptr(workspace), _nbytes(workspace), B, H, N, d, scale, FOX_BF16, _stream()))
+        _ptr(dlogf), _ptr(workspace), _nbytes(workspace), B, H, N, d, scale, FOX_BF16,
+        FOX_TOKEN_MAJOR if layout == "token" else FOX_HEAD_MAJOR, _stream()))
     return dq, dk, dv, dlogf
 
 

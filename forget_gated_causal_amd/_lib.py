@@ -55,7 +55,7 @@ SIGNATURES = {
                                        _I64, _I64, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
     "fox_attn_bwd_staged_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "fox_attn_bwd_staged": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64,
-                                           _I64, _I64, ctypes.c_float, ctypes.c_int, _P]),
+                                           _I64, _I64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _P]),
     "fox_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

@@ -205,14 +205,14 @@ size_t fox_attn_bwd_staged_workspace_bytes(int64_t b, int64_t h, int64_t n, int6
 fox_status_t fox_attn_bwd_staged(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                  const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                                  void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
-                                 float scale, fox_dtype_t dtype, hipStream_t stream) {
+                                 float scale, fox_dtype_t dtype, fox_layout_t layout, hipStream_t stream) {
   const size_t need = fox_attn_bwd_staged_workspace_bytes(b, h, n, d);
   const fox_status_t st = bwd_args(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, workspace_bytes, b, h,
-                                   n, d, scale, dtype, FOX_HEAD_MAJOR, need);
+                                   n, d, scale, dtype, layout, need);
   if (st != FOX_OK) return st;
   if (dtype != FOX_BF16 || d != 128 || !staged_size_ok(n)) return FOX_ERR_UNSUPPORTED;
   return from_hip(fox::launch_attn_bwd_staged(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, (int)n,
-                                              scale, stream));
+                                              scale, layout == FOX_TOKEN_MAJOR, stream));
 }
 
 // Validation shared by the decode entry points (cache_lens: the ragged step's lengths, or null;

@@ -51,7 +51,7 @@
 //    mask; without it the gate rows, then bwd_dpass_kernel (D_i = sum_j P_ij dP_ij in fp32, and
 //    the row terms rescaled so that each row of P sums to 1 in fp32).
 //    After them the reversed prefix scan (fox_scan.hip): dlog f from row sums - column sums.
-//  * staged dS (fox_attn_bwd_staged; causal, head-major, d = 128): the key-stationary kernel also
+//  * staged dS (fox_attn_bwd_staged; causal, d = 128): the key-stationary kernel also
 //    stores the bf16 dS it packed for its own dK^T MFMAs into the workspace, and
 //    bwd_dq_staged_kernel contracts dQ = dS K and the row sums from it in place of bwd_dq_kernel,
 //    which would form S and dP a second time (about n^2 bytes of workspace per head instead).
@@ -1258,11 +1258,12 @@ int64_t attn_bwd_staged_head_bytes(int n) { return staged_tiles(n) * (kBK * kBQ)
 
 hipError_t launch_attn_bwd_staged(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                   const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
-                                  void* workspace, int64_t b, int64_t h, int n, float scale, hipStream_t stream) {
+                                  void* workspace, int64_t b, int64_t h, int n, float scale, bool token_major,
+                                  hipStream_t stream) {
   const size_t base = (attn_bwd_workspace_bytes(b * h, n, 128) + 255) / 256 * 256;
   bf16* ds = reinterpret_cast<bf16*>(static_cast<char*>(workspace) + base);
-  return launch_bwd_t<128>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, true, false,
-                           stream, ds, staged_tiles(n) * (kBK * kBQ));
+  return launch_bwd_t<128>(q, k, v, o, dout, lse, logf, dq, dk, dv, dlogf, workspace, b, h, n, scale, true,
+                           token_major, stream, ds, staged_tiles(n) * (kBK * kBQ));
 }
 
 }  // namespace fox

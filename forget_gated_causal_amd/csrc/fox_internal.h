@@ -61,13 +61,14 @@ hipError_t launch_bwd_gate_rows(const float* logf, const float* lse, float* rowv
 // log gates; token_major as launch_attn_fwd.  Workspace: per-row vectors over n padded to 64,
 // block starts of the gate sums (fp64), row and column sums of dS (attn_bwd_workspace_bytes).
 size_t attn_bwd_workspace_bytes(int64_t bh, int n, int d);
-// the staged backward (causal, head-major, bf16, d = 128): its workspace, the staged dS bytes of
+// the staged backward (causal, bf16, d = 128): its workspace, the staged dS bytes of
 // one head, and the launch
 size_t attn_bwd_staged_workspace_bytes(int64_t bh, int n);
 int64_t attn_bwd_staged_head_bytes(int n);
 hipError_t launch_attn_bwd_staged(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                   const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
-                                  void* workspace, int64_t b, int64_t h, int n, float scale, hipStream_t stream);
+                                  void* workspace, int64_t b, int64_t h, int n, float scale, bool token_major,
+                                  hipStream_t stream);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                            void* workspace, int64_t b, int64_t h, int n, int d, float scale, bool causal,

@@ -232,7 +232,7 @@ fox_status_t fox_attn_bwd_ex(const void* q, const void* k, const void* v, const 
 size_t fox_attn_bwd_staged_workspace_bytes(int64_t b, int64_t h, int64_t n, int64_t d);
 
 /*
- * fox_attn_bwd_staged -- fox_attn_bwd in decoder mode for head-major bf16 tensors with d = 128,
+ * fox_attn_bwd_staged -- fox_attn_bwd_ex in decoder mode for bf16 tensors with d = 128,
  *   trading memory for time: the key-stationary kernel writes the bf16 dS it forms (the values its
  *   own dK and column sums use) to the workspace, and dQ = scale dS k and the row sums of dS are
  *   read from there by a contraction kernel, instead of a query-stationary kernel forming S and
@@ -240,17 +240,18 @@ size_t fox_attn_bwd_staged_workspace_bytes(int64_t b, int64_t h, int64_t n, int6
  *   ForgettingAttention.forward); results agree with fox_attn_bwd to bf16 rounding of dq (not bit
  *   for bit: the row sums of dS and dQ are taken from the key side's dS).
  *
- *   Arguments as fox_attn_bwd (decoder mode, FOX_HEAD_MAJOR), with
+ *   Arguments as fox_attn_bwd_ex (decoder mode; layout FOX_HEAD_MAJOR or FOX_TOKEN_MAJOR, the
+ *   results of the two bit for bit the same), with
  *   workspace, workspace_bytes : device scratch of at least
  *              fox_attn_bwd_staged_workspace_bytes(b, h, n, d) bytes, 16-byte aligned, not
  *              overlapping any other argument; contents on entry are ignored.
- *   Errors as fox_attn_bwd, and FOX_ERR_UNSUPPORTED for a dtype other than FOX_BF16, d other
+ *   Errors as fox_attn_bwd_ex, and FOX_ERR_UNSUPPORTED for a dtype other than FOX_BF16, d other
  *   than 128, or n too large for the staged tiles (see the workspace query).
  */
 fox_status_t fox_attn_bwd_staged(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                  const float* lse, const float* logf, void* dq, void* dk, void* dv, float* dlogf,
                                  void* workspace, size_t workspace_bytes, int64_t b, int64_t h, int64_t n, int64_t d,
-                                 float scale, fox_dtype_t dtype, hipStream_t stream);
+                                 float scale, fox_dtype_t dtype, fox_layout_t layout, hipStream_t stream);
 
 /*
  * fox_attn_decode_workspace_bytes -- bytes of scratch fox_attn_decode needs for

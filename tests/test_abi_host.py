@@ -306,7 +306,7 @@ def _bwds(L, **kw):
     a.update(kw)
     return L.fox_attn_bwd_staged(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["logf"], a["dq"], a["dk"],
                                  a["dv"], a["dl"], a["ws"], a["wsb"], a["b"], a["h"], a["n"], a["d"], a["scale"],
-                                 a["dt"], None)
+                                 a["dt"], a.get("layout", _lib.FOX_HEAD_MAJOR), None)
 
 
 def test_bwd_staged_rejects_bad_arguments(L):
@@ -324,6 +324,10 @@ def test_bwd_staged_rejects_bad_arguments(L):
     assert _bwds(L, d=96) == UNSUP
     assert _bwds(L, dt=_lib.FOX_F32) == UNSUP
     assert _bwds(L, n=46273, h=1) == UNSUP
+    # the layout as fox_attn_bwd_ex: unknown values, and token-major spans past 32-bit offsets
+    assert _bwds(L, layout=2) == UNSUP
+    assert _bwds(L, layout=_lib.FOX_TOKEN_MAJOR, n=40000, h=512) == UNSUP
+    assert _bwds(L, layout=_lib.FOX_TOKEN_MAJOR, dout=None) == INVALID
 
 
 def test_bwd_ex_layout_checks(L):

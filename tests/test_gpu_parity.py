@@ -780,6 +780,24 @@ def test_bwd_staged_parity(B, H, n, mu, sigma):
     print("  " + cfg.desc + " staged: " + ", ".join(msg), flush=True)
 
 
+@pytest.mark.parametrize("B,H,n", [(1, 2, 65), (2, 3, 300), (1, 16, 2100)])
+def test_bwd_staged_token_major_equals_head_major(B, H, n):
+    """fox_attn_bwd_staged on [B,N,H,d] tensors gives the head-major call's gradients bit for bit
+    (only addresses differ), which test_bwd_staged_parity checks against the oracle."""
+    cfg = fi.FwdConfig(f"bwd_staged_tm_{B}_{H}_{n}", B, H, n, 128, "bf16", 3.0, 1.5)
+    inp, dout = _bwd_case(cfg, n + 17)
+    q, k, v, logf = (inp[x].to(DEV) for x in ("q", "k", "v", "logf"))
+    dout = dout.to(DEV)
+    o, lse, c = fox.attn_fwd(q, k, v, logf, scale=inp["scale"])
+    head = fox.attn_bwd_staged(q, k, v, o, dout, lse, logf, scale=inp["scale"])
+    tm = lambda t: t.transpose(1, 2).contiguous()  # noqa: E731
+    tok = fox.attn_bwd_staged(tm(q), tm(k), tm(v), tm(o), tm(dout), tm(lse), tm(logf), scale=inp["scale"],
+                              layout="token")
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dlogf"), head, tok):
+        assert torch.equal(a, b.transpose(1, 2)), name
+
+
 def test_bwd_staged_c3_full_size_sampled_heads():
     """The staged backward at c3's full size, in the bench's launch configuration: two whole heads
     against the fp64 oracle, every head's dk, dv bit-equal to fox_attn_bwd, and a second call
